@@ -1,0 +1,236 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet token mixer library for MI355X (gfx950).
+ *
+ * The mixer ("Inside Qwen3.5: a hybrid linear + full attention LLM",
+ * sections 4-5 and the config note) is:
+ *   1. a causal depthwise convolution of width 4 over the concatenated
+ *      [q | k | v] channels, followed by SiLU;
+ *   2. L2 normalisation of q and k per head;
+ *   3. the gated delta rule per V head h (QK head h / (h_v / h_qk)):
+ *        S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *        o_t = scale * S_t q_t,   alpha_t = exp(g_t),
+ *      with a fixed d_v x d_k state per V head, updated in place.
+ *   Decode is the same recurrence applied one token at a time: a
+ *   read-modify-write of the fixed-size state ("Inside Qwen3.5", section 8).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers, row-major and contiguous
+ *     unless a stride argument says otherwise.  The caller allocates and owns
+ *     every buffer; the library allocates nothing and keeps no global mutable
+ *     state other than a thread-local error string.
+ *   - Every call is asynchronous and ordered on the given HIP stream
+ *     (0 = the null stream).  Nothing is synchronised implicitly.
+ *   - Each call takes a pointer to an argument struct whose first field is
+ *     struct_size (set it to sizeof the struct).
+ *   - Validation errors return before anything is launched and write
+ *     nothing.  A failed launch returns GDN_ERR_HIP; gdn_last_error() gives
+ *     the detail.  No C++ exception crosses this boundary.
+ *   - Identical inputs give bitwise identical outputs (no atomics in any
+ *     reduction).
+ *   - Token counts and element offsets are 64-bit.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* null pointer, bad size or shape            */
+  GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. d_k = 96)  */
+  GDN_ERR_ALIGNMENT = 3,   /* a pointer or stride breaks the alignment rule */
+  GDN_ERR_WORKSPACE = 4,   /* workspace missing or too small             */
+  GDN_ERR_HIP = 5          /* the HIP runtime reported an error          */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;
+
+/* flags */
+#define GDN_FLAG_L2NORM_QK 1u /* L2-normalise q and k per head (eps 1e-6 inside the sqrt) */
+
+/* ------------------------------------------------------------------------
+ * gdn_conv1d -- causal depthwise convolution (+ optional SiLU) over packed
+ * sequences, with a per-sequence conv state.
+ *
+ * Defined by "Inside Qwen3.5", section 5 (a kernel-4 causal convolution ahead
+ * of the recurrence) and "Mamba hybrid model selection", per-request memory
+ * section (a (channels, kernel width - 1) conv state per sequence):
+ *   y[t, c] = act( sum_{j<W} w[c, j] * x[t - (W-1) + j, c] + bias[c] )
+ * where inputs before a sequence's first token come from that sequence's
+ * conv state (oldest first), or are zero when conv_state is NULL.
+ *
+ *   dtype        GDN_BF16 or GDN_F32: dtype of x, weight, bias, y, conv_state
+ *                (accumulation is fp32).
+ *   n_seqs       number of packed sequences (>= 1).
+ *   total_tokens T, sum of the sequence lengths (>= 0).
+ *   channels     C (multiple of 8).
+ *   width        W, 2..4.
+ *   activation   GDN_ACT_NONE or GDN_ACT_SILU.
+ *   x            [T, C] input, 16-byte aligned.
+ *   weight       [C, W].
+ *   bias         [C] or NULL.
+ *   y            [T, C] output; must not overlap x.
+ *   conv_state   [n_seqs, C, W-1] in/out, or NULL.  On return it holds the
+ *                last W-1 inputs of (old state ++ sequence), oldest first; a
+ *                zero-length sequence keeps its state.
+ *   cu_seqlens   [n_seqs + 1] int32 device array of sequence offsets
+ *                (0 = cu[0] <= cu[1] <= ... = T), or NULL for one sequence.
+ *                Values are trusted (not validated on the host).
+ * ---------------------------------------------------------------------- */
+typedef struct gdn_conv1d_args {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t n_seqs;
+  int32_t channels;
+  int64_t total_tokens;
+  int32_t width;
+  int32_t activation;
+  const void* x;
+  const void* weight;
+  const void* bias;
+  void* y;
+  void* conv_state;
+  const int32_t* cu_seqlens;
+} gdn_conv1d_args;
+
+gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_prefill -- chunked gated delta rule over packed sequences.
+ *
+ * Computes, for every sequence and V head, the recurrence stated at the top
+ * of this file ("Inside Qwen3.5", sections 4-5), exactly up to rounding, by
+ * the chunked WY / UT-transform rearrangement (chunks restart at each
+ * sequence start; the last chunk may be partial).
+ *
+ *   io_dtype     GDN_BF16 or GDN_F32: dtype of q, k, v and o.  The state is
+ *                always fp32; accumulation is fp32.  With GDN_BF16 the dense
+ *                chunk contractions run on bf16 MFMA; with GDN_F32 on fp32
+ *                MFMA.
+ *   flags        GDN_FLAG_L2NORM_QK to normalise q and k inside the call.
+ *   n_seqs       >= 1.    total_tokens T >= 0.
+ *   h_qk, h_v    head counts, h_v % h_qk == 0.
+ *   d_k, d_v     head widths: both 64 or both 128.
+ *   chunk        16, 32 or 64.
+ *   scale        output scale (1.0 reproduces o = S q).
+ *   q, k         [T, h_qk, d_k] with token stride q_stride / k_stride
+ *                (elements; heads contiguous inside a token).  q, k and v may
+ *                be column slices of the conv output [T, C].
+ *   v            [T, h_v, d_v] with token stride v_stride.
+ *   g, beta      [T, h_v] fp32: log-decay (alpha = exp(g) in (0, 1]) and
+ *                write strength.
+ *   initial_state [n_seqs, h_v, d_v, d_k] fp32, or NULL for zeros.
+ *   final_state  [n_seqs, h_v, d_v, d_k] fp32, or NULL; may alias
+ *                initial_state.
+ *   o            [T, h_v, d_v] in io_dtype.
+ *   cu_seqlens   as in gdn_conv1d.
+ *   workspace    device scratch of at least gdn_prefill_workspace_size()
+ *                bytes, 256-byte aligned.  Contents on entry are ignored.
+ * ---------------------------------------------------------------------- */
+typedef struct gdn_prefill_args {
+  uint32_t struct_size;
+  uint32_t flags;
+  int32_t io_dtype;
+  int32_t n_seqs;
+  int64_t total_tokens;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t chunk;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_stride;
+  int64_t k_stride;
+  int64_t v_stride;
+  const float* g;
+  const float* beta;
+  const float* initial_state;
+  float* final_state;
+  void* o;
+  const int32_t* cu_seqlens;
+  void* workspace;
+  size_t workspace_bytes;
+} gdn_prefill_args;
+
+/* Bytes of workspace gdn_prefill needs for these arguments (pointers are not
+ * read).  Returns 0 when the arguments are invalid. */
+size_t gdn_prefill_workspace_size(const gdn_prefill_args* args);
+
+gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_decode_step -- one new token for each of n_seqs independent sequences.
+ *
+ * Fuses, per sequence: the conv step over the new token (reading the W-1
+ * stored inputs, then shifting the new input into the conv state), SiLU, the
+ * split into [q | k | v], the optional L2 norm, and one step of the gated
+ * delta rule on that sequence's state, which is read once and written once
+ * ("Inside Qwen3.5", section 8: decode is a read-modify-write of the
+ * fixed-size state every token; "Mamba hybrid model selection", decode
+ * section: the step is bounded by the bytes it moves over HBM bandwidth).
+ *
+ *   io_dtype     GDN_BF16 or GDN_F32: dtype of x, conv_weight, conv_bias,
+ *                conv_state and o.
+ *   state_dtype  GDN_BF16 (stored with round-to-nearest-even, accumulated in
+ *                fp32) or GDN_F32.
+ *   flags        GDN_FLAG_L2NORM_QK.
+ *   n_seqs       >= 0.   h_qk, h_v (h_v % h_qk == 0), d_k = d_v in {64, 128}.
+ *   width        conv width W in 2..4 (ignored without conv_weight).
+ *   activation   GDN_ACT_SILU or GDN_ACT_NONE.
+ *   scale        output scale.
+ *   x            [n_seqs, C] new inputs, C = 2 h_qk d_k + h_v d_v.
+ *   conv_weight  [C, W], or NULL: then x already holds q|k|v (no conv, no
+ *                activation, conv_state unused).
+ *   conv_bias    [C] or NULL.
+ *   conv_state   [n_seqs, C, W-1] in/out (oldest first); required with a conv.
+ *   g, beta      [n_seqs, h_v] fp32.
+ *   state        [n_seqs, h_v, d_v, d_k] in/out, in state_dtype.
+ *   o            [n_seqs, h_v, d_v] in io_dtype.
+ * ---------------------------------------------------------------------- */
+typedef struct gdn_decode_args {
+  uint32_t struct_size;
+  uint32_t flags;
+  int32_t io_dtype;
+  int32_t state_dtype;
+  int32_t n_seqs;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t width;
+  int32_t activation;
+  float scale;
+  const void* x;
+  const void* conv_weight;
+  const void* conv_bias;
+  void* conv_state;
+  const float* g;
+  const float* beta;
+  void* state;
+  void* o;
+} gdn_decode_args;
+
+gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
+
+/* Diagnostics. */
+const char* gdn_status_string(gdn_status status);
+const char* gdn_last_error(void); /* thread-local detail of the last failure */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,256 @@
+"""Gated DeltaNet token mixer on MI355X (gfx950): Python binding of libgdn.so.
+
+This module only marshals arguments: it checks torch-level properties
+(device, dtype, contiguity), fills the C argument structs declared in
+include/gdn.h and calls the library on torch's current HIP stream.  Every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if libgdn.so is missing or fails to load, every call raises.
+
+Entry points (same names as the C ABI):
+    conv1d       causal depthwise conv (+ SiLU) with per-sequence conv state
+    prefill      chunked gated delta rule over packed sequences
+    decode_step  one token per sequence: conv step + recurrence, state in place
+and gdn_layer, which chains conv1d and prefill for a whole token mixer layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["conv1d", "prefill", "decode_step", "gdn_layer", "prefill_workspace_size", "lib",
+           "GdnError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+F32, BF16 = 0, 1
+ACT_NONE, ACT_SILU = 0, 1
+FLAG_L2NORM_QK = 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_c_void_p = ctypes.c_void_p
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("dtype", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("width", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("x", _c_void_p), ("weight", _c_void_p),
+                ("bias", _c_void_p), ("y", _c_void_p), ("conv_state", _c_void_p),
+                ("cu_seqlens", _c_void_p)]
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("io_dtype", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("h_qk", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("scale", ctypes.c_float), ("q", _c_void_p),
+                ("k", _c_void_p), ("v", _c_void_p), ("q_stride", ctypes.c_int64),
+                ("k_stride", ctypes.c_int64), ("v_stride", ctypes.c_int64), ("g", _c_void_p),
+                ("beta", _c_void_p), ("initial_state", _c_void_p), ("final_state", _c_void_p),
+                ("o", _c_void_p), ("cu_seqlens", _c_void_p), ("workspace", _c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("flags", ctypes.c_uint32),
+                ("io_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("h_qk", ctypes.c_int32), ("h_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("scale", ctypes.c_float), ("x", _c_void_p),
+                ("conv_weight", _c_void_p), ("conv_bias", _c_void_p), ("conv_state", _c_void_p),
+                ("g", _c_void_p), ("beta", _c_void_p), ("state", _c_void_p), ("o", _c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so (raises GdnError when it is missing or unloadable)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GdnError(f"{LIB_PATH} is not built; run python -m linear_attention_token_conv1d_amd._build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, argt in (("gdn_conv1d", ConvArgs), ("gdn_prefill", PrefillArgs),
+                           ("gdn_decode_step", DecodeArgs)):
+            f = getattr(L, name)
+            f.argtypes = [ctypes.POINTER(argt), _c_void_p]
+            f.restype = ctypes.c_int
+        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
+        L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        if L.gdn_abi_version() != 1:
+            raise GdnError("libgdn.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        L = lib()
+        raise GdnError(f"{what}: {L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise GdnError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _contig(t, name, dtype=None):
+    _dev(t, name, dtype)
+    if not t.is_contiguous():
+        raise GdnError(f"{name} must be contiguous")
+    return t
+
+
+def _cu(cu_seqlens, n_tokens):
+    if cu_seqlens is None:
+        return None, 1
+    _contig(cu_seqlens, "cu_seqlens", torch.int32)
+    return cu_seqlens, cu_seqlens.numel() - 1
+
+
+def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="silu", out=None):
+    """Causal depthwise conv over packed sequences: x [T, C] -> y [T, C].
+
+    weight [C, W]; conv_state [N, C, W-1] is read and then updated in place
+    (None: zero history, nothing written)."""
+    _contig(x, "x")
+    T, C = x.shape
+    _contig(weight, "weight", x.dtype)
+    if bias is not None:
+        _contig(bias, "bias", x.dtype)
+    if conv_state is not None:
+        _contig(conv_state, "conv_state", x.dtype)
+    cu, N = _cu(cu_seqlens, T)
+    y = torch.empty_like(x) if out is None else _contig(out, "out", x.dtype)
+    a = ConvArgs(ctypes.sizeof(ConvArgs), _DT[x.dtype], N, C, T, weight.shape[1],
+                 ACT_SILU if activation == "silu" else ACT_NONE, _ptr(x), _ptr(weight), _ptr(bias),
+                 _ptr(y), _ptr(conv_state), _ptr(cu))
+    _check(lib().gdn_conv1d(ctypes.byref(a), _stream(x.device)), "gdn_conv1d")
+    return y
+
+
+def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
+                  workspace=None):
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    a = PrefillArgs(ctypes.sizeof(PrefillArgs), FLAG_L2NORM_QK if l2norm else 0, _DT[q.dtype], N, T,
+                    h_qk, h_v, d_k, d_v, chunk, scale, _ptr(q), _ptr(k), _ptr(v), q.stride(0),
+                    k.stride(0), v.stride(0), _ptr(g), _ptr(beta), _ptr(initial_state),
+                    _ptr(final_state), _ptr(o), _ptr(cu), _ptr(workspace),
+                    0 if workspace is None else workspace.numel())
+    return a
+
+
+def prefill_workspace_size(q, v, n_seqs=1, chunk=64):
+    T, h_qk, d_k = q.shape
+    a = PrefillArgs(struct_size=ctypes.sizeof(PrefillArgs), n_seqs=n_seqs, total_tokens=T, h_qk=h_qk,
+                    h_v=v.shape[1], d_k=d_k, d_v=v.shape[2], chunk=chunk)
+    return lib().gdn_prefill_workspace_size(ctypes.byref(a))
+
+
+def _head_view(t, name, heads_dim_ok=True):
+    """q/k/v: [T, H, d] with heads contiguous inside a token (token stride free)."""
+    _dev(t, name)
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise GdnError(f"{name} must be [T, H, d] with contiguous heads")
+    return t
+
+
+def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, scale=1.0,
+            l2norm=True, output_final_state=True, o=None, final_state=None, workspace=None):
+    """Chunked gated delta rule.  q, k [T, H_qk, d], v [T, H_v, d] (bf16 or fp32,
+    token stride free), g, beta [T, H_v] fp32, initial_state [N, H_v, d, d] fp32.
+
+    Returns (o [T, H_v, d], final_state [N, H_v, d, d] fp32 or None)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _head_view(t, nm)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError("q, k and v must share a dtype")
+    T = q.shape[0]
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    cu, N = _cu(cu_seqlens, T)
+    h_v, d_v = v.shape[1], v.shape[2]
+    if initial_state is not None:
+        _contig(initial_state, "initial_state", torch.float32)
+    if o is None:
+        o = torch.empty((T, h_v, d_v), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, h_v, d_v, q.shape[2]), dtype=torch.float32, device=q.device)
+    need = prefill_workspace_size(q, v, N, chunk)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
+                      workspace if need else None)
+    _check(lib().gdn_prefill(ctypes.byref(a), _stream(q.device)), "gdn_prefill")
+    return o, final_state
+
+
+def split_qkv(y, h_qk, d_k, h_v, d_v):
+    """Column views [q | k | v] of the conv output y [T, C] as [T, H, d] tensors."""
+    T = y.shape[0]
+    nq = h_qk * d_k
+    q = y[:, :nq].unflatten(1, (h_qk, d_k))
+    k = y[:, nq:2 * nq].unflatten(1, (h_qk, d_k))
+    v = y[:, 2 * nq:2 * nq + h_v * d_v].unflatten(1, (h_v, d_v))
+    return q, k, v
+
+
+def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv_state=None,
+              initial_state=None, cu_seqlens=None, chunk=64, scale=1.0, l2norm=True, y=None):
+    """The whole mixer: conv1d(+SiLU) over [q|k|v], then the chunked recurrence
+    reading q, k, v as column slices of the conv output (no copies)."""
+    y = conv1d(x, conv_weight, conv_bias, conv_state, cu_seqlens, "silu", out=y)
+    q, k, v = split_qkv(y, h_qk, d_k, h_v, d_v)
+    o, S = prefill(q, k, v, g, beta, initial_state, cu_seqlens, chunk, scale, l2norm)
+    return o, S
+
+
+def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=None, conv_bias=None,
+                activation="silu", l2norm=True, scale=1.0, o=None):
+    """One token for each of N sequences.  x [N, C] (pre-conv, or q|k|v when
+    conv_weight is None); state [N, H_v, d, d] (bf16 or fp32) and conv_state
+    [N, C, W-1] are updated in place.  Returns o [N, H_v, d]."""
+    _contig(x, "x")
+    N = x.shape[0]
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    _contig(state, "state")
+    if conv_weight is not None:
+        _contig(conv_weight, "conv_weight", x.dtype)
+        _contig(conv_state, "conv_state", x.dtype)
+    if conv_bias is not None:
+        _contig(conv_bias, "conv_bias", x.dtype)
+    if o is None:
+        o = torch.empty((N, h_v, d), dtype=x.dtype, device=x.device)
+    W = conv_weight.shape[1] if conv_weight is not None else 4
+    a = DecodeArgs(ctypes.sizeof(DecodeArgs), FLAG_L2NORM_QK if l2norm else 0, _DT[x.dtype],
+                   _DT[state.dtype], N, h_qk, h_v, d, d, W,
+                   ACT_SILU if activation == "silu" else ACT_NONE, scale, _ptr(x), _ptr(conv_weight),
+                   _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), _ptr(o))
+    _check(lib().gdn_decode_step(ctypes.byref(a), _stream(x.device)), "gdn_decode_step")
+    return o

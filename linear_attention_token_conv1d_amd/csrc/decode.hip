@@ -1,0 +1,174 @@
+// gdn_decode_step kernel: one token for each of N sequences.
+//
+// One workgroup owns (sequence n, QK head hq) and therefore the grp = h_v/h_qk
+// V heads that read that QK head.  It
+//   1. runs the conv step (+ SiLU) for its q, k and v channels, shifting the
+//      new input into the conv state (each channel is read and written by the
+//      thread that owns it, so the in-place update is race-free);
+//   2. L2-normalises q and k (one wave, fp32);
+//   3. streams the grp*d_v state rows once: each row S_i (d_k values) is
+//      loaded by 16 lanes, reduced against k and q with DPP row sums, then
+//        a_i = S_i.k,  b_i = S_i.q,  d_i = beta (v_i - alpha a_i)
+//        S_i <- alpha S_i + d_i k^T,  o_i = scale (alpha b_i + d_i (k.q))
+//      and written back.  Rows are independent, so one pass suffices: the
+//      kernel reads and writes each state byte exactly once.
+// The state of a workgroup (grp*d_v rows of d_k) is contiguous in memory, so a
+// wave moves 4 consecutive rows (1 KiB of bf16) per 16-byte-per-lane access.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // row groups whose loads are in flight together
+
+template <int EPL, typename T>
+__device__ __forceinline__ void load_row(const T* p, float (&v)[EPL]) {
+  if constexpr (EPL == 8) load8(p, v); else load4(p, v);
+}
+template <int EPL, typename T>
+__device__ __forceinline__ void store_row(T* p, const float (&v)[EPL]) {
+  if constexpr (EPL == 8) store8(p, v); else store4(p, v);
+}
+
+template <typename IoT, typename StT, int D>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  constexpr int EPL = D / 16;  // state elements per lane per row
+  extern __shared__ float smem[];
+  const int grp = p.h_v / p.h_qk;
+  const int n = blockIdx.x / p.h_qk;
+  const int hq = blockIdx.x - n * p.h_qk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  float* s_q = smem;               // [D]        q, then k, then v: channel order
+  float* s_k = s_q + D;            // [D]
+  float* s_v = s_k + D;            // [grp*D]
+  float* s_o = s_v + grp * D;      // [grp*D]
+  float* s_al = s_o + grp * D;     // [grp] alpha
+  float* s_be = s_al + grp;        // [grp] beta
+  float* s_sc = s_be + grp;        // rq, rk, k.q
+
+  // ---- 1. conv step + activation over this workgroup's channels
+  const int64_t C = (int64_t)(2 * p.h_qk + p.h_v) * D;
+  const IoT* x = reinterpret_cast<const IoT*>(p.x) + (int64_t)n * C;
+  const int nloc = (2 + grp) * D;
+  const int W = p.width;
+  for (int cl = tid; cl < nloc; cl += kThreads) {
+    int64_t c;
+    if (cl < D) c = (int64_t)hq * D + cl;
+    else if (cl < 2 * D) c = (int64_t)(p.h_qk + hq) * D + (cl - D);
+    else c = (int64_t)2 * p.h_qk * D + (int64_t)hq * grp * D + (cl - 2 * D);
+    const IoT xr = x[c];
+    float y = to_f32(xr);
+    if (p.conv_weight) {
+      const IoT* w = reinterpret_cast<const IoT*>(p.conv_weight) + c * W;
+      IoT* st = reinterpret_cast<IoT*>(p.conv_state) + ((int64_t)n * C + c) * (W - 1);
+      IoT h0 = st[0];
+      IoT h1 = W > 2 ? st[1] : h0;
+      IoT h2 = W > 3 ? st[2] : h0;
+      float acc = p.conv_bias ? to_f32(reinterpret_cast<const IoT*>(p.conv_bias)[c]) : 0.f;
+      acc += to_f32(w[0]) * to_f32(h0);
+      if (W > 2) acc += to_f32(w[1]) * to_f32(h1);
+      if (W > 3) acc += to_f32(w[2]) * to_f32(h2);
+      acc += to_f32(w[W - 1]) * y;
+      // shift the new input in: the state keeps the last W-1 inputs, oldest first
+      if (W == 2) { st[0] = xr; }
+      else if (W == 3) { st[0] = h1; st[1] = xr; }
+      else { st[0] = h1; st[1] = h2; st[2] = xr; }
+      y = p.act ? silu(acc) : acc;
+    }
+    s_q[cl] = y;
+  }
+  if (tid < grp) {
+    const int64_t gi = (int64_t)n * p.h_v + (int64_t)hq * grp + tid;
+    s_al[tid] = __expf(p.g[gi]);
+    s_be[tid] = p.beta[gi];
+  }
+  __syncthreads();
+
+  // ---- 2. L2 norms of q and k, and k.q after normalisation
+  if (wave == 0) {
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+    for (int i = lane; i < D; i += 64) {
+      const float a = s_q[i], b = s_k[i];
+      sq += a * a; sk += b * b; sqk += a * b;
+    }
+    sq = wave_sum(sq); sk = wave_sum(sk); sqk = wave_sum(sqk);
+    if (lane == 0) {
+      const float rq = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+      const float rk = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+      s_sc[0] = rq; s_sc[1] = rk; s_sc[2] = sqk * rq * rk;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. stream the state rows once
+  const float rq = s_sc[0], rk = s_sc[1], kq = s_sc[2];
+  const int sub = lane & 15;
+  float kf[EPL], qf[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    kf[e] = s_k[sub * EPL + e] * rk;
+    qf[e] = s_q[sub * EPL + e] * rq;
+  }
+  StT* S = reinterpret_cast<StT*>(p.state) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D * D +
+           sub * EPL;
+  const int rows = grp * D;  // a multiple of 16
+  for (int rb = wave * 4 + (lane >> 4); rb < rows; rb += 16 * kUnroll) {
+    float sv[kUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int r = rb + 16 * u;
+      if (r < rows) load_row<EPL>(S + (int64_t)r * D, sv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int r = rb + 16 * u;
+      if (r < rows) {  // uniform across each wave (rows % 16 == 0)
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { a += sv[u][e] * kf[e]; b += sv[u][e] * qf[e]; }
+        a = row16_sum(a);
+        b = row16_sum(b);
+        const int hl = r / D;
+        const float al = s_al[hl];
+        const float dl = s_be[hl] * (s_v[r] - al * a);
+        float nv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
+        store_row<EPL>(S + (int64_t)r * D, nv);
+        if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
+      }
+    }
+  }
+  __syncthreads();
+  IoT* o = reinterpret_cast<IoT*>(p.o) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D;
+  for (int i = tid; i < rows; i += kThreads) o[i] = from_f32<IoT>(s_o[i]);
+}
+
+template <typename IoT, typename StT, int D>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  const int grp = p.h_v / p.h_qk;
+  const size_t shmem = sizeof(float) * ((size_t)(2 + 2 * grp) * D + 2 * grp + 4);
+  const unsigned blocks = (unsigned)((int64_t)p.n_seqs * p.h_qk);
+  hipLaunchKernelGGL((decode_kernel<IoT, StT, D>), dim3(blocks), dim3(kThreads), shmem, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int io_dtype, int state_dtype, int d,
+                         hipStream_t stream) {
+  const bool io_bf = io_dtype == 1, st_bf = state_dtype == 1;
+  if (d == 128) {
+    if (io_bf) return st_bf ? launch_t<__bf16, __bf16, 128>(p, stream) : launch_t<__bf16, float, 128>(p, stream);
+    return st_bf ? launch_t<float, __bf16, 128>(p, stream) : launch_t<float, float, 128>(p, stream);
+  }
+  if (io_bf) return st_bf ? launch_t<__bf16, __bf16, 64>(p, stream) : launch_t<__bf16, float, 64>(p, stream);
+  return st_bf ? launch_t<float, __bf16, 64>(p, stream) : launch_t<float, float, 64>(p, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,112 @@
+// Device helpers shared by the gfx950 kernels: bf16 <-> fp32 conversion,
+// 16-byte vector loads/stores, wave64 DPP reductions and MFMA fragments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+// ------------------------------------------------------ 8-element vectors
+// load8/store8 move 8 consecutive elements (16 B of bf16, 32 B of fp32);
+// the pointer must be aligned to the vector size.
+
+__device__ __forceinline__ void load8(const __bf16* p, float (&v)[8]) {
+  uint4 w = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(__bf16* p, const float (&v)[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = w;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+// 4-element variants (8 B of bf16, 16 B of fp32).
+__device__ __forceinline__ void load4(const __bf16* p, float (&v)[4]) {
+  uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+}
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void store4(__bf16* p, const float (&v)[4]) {
+  uint2 w;
+  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// ---------------------------------------------------------- reductions
+// DPP controls (GCN/CDNA encoding).
+enum : int {
+  DPP_QUAD_1032 = 0xB1,      // quad_perm [1,0,3,2]: partner lane ^ 1
+  DPP_QUAD_2301 = 0x4E,      // quad_perm [2,3,0,1]: partner lane ^ 2
+  DPP_ROW_MIRROR = 0x140,    // lane i <- lane 15 - i within a row of 16
+  DPP_ROW_HALF_MIRROR = 0x141  // lane i <- lane 7 - i within a half row of 8
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of 16 consecutive lanes; every lane receives its group's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<DPP_QUAD_1032>(v);
+  v += dpp_f32<DPP_QUAD_2301>(v);
+  v += dpp_f32<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f32<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+// Sum over the whole wave of 64 lanes; every lane receives the sum.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+
+}  // namespace gdn

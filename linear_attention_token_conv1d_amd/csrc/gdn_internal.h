@@ -1,0 +1,74 @@
+// Host-side interface between the C ABI (gdn_api.cpp) and the kernel
+// launchers (*.hip).  Arguments here have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ConvParams {
+  const void* x;
+  const void* weight;
+  const void* bias;
+  void* y;
+  void* conv_state;
+  const int32_t* cu_seqlens;  // nullptr: one sequence
+  int64_t total_tokens;
+  int32_t n_seqs;
+  int32_t channels;
+  int32_t width;
+  int32_t act;
+};
+hipError_t launch_conv1d(const ConvParams& p, int dtype, hipStream_t stream);
+
+struct DecodeParams {
+  const void* x;
+  const void* conv_weight;  // nullptr: x already holds q|k|v
+  const void* conv_bias;
+  void* conv_state;
+  const float* g;
+  const float* beta;
+  void* state;
+  void* o;
+  int32_t n_seqs;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t width;
+  int32_t act;
+  int32_t l2norm;
+  float scale;
+};
+hipError_t launch_decode(const DecodeParams& p, int io_dtype, int state_dtype, int d,
+                         hipStream_t stream);
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_stride;
+  int64_t k_stride;
+  int64_t v_stride;
+  const float* g;
+  const float* beta;
+  const float* initial_state;
+  float* final_state;
+  void* o;
+  const int32_t* cu_seqlens;
+  int64_t total_tokens;
+  int32_t n_seqs;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t chunk;
+  int32_t l2norm;
+  float scale;
+  void* workspace;
+  size_t workspace_bytes;
+};
+size_t prefill_workspace_bytes(int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d,
+                               int chunk);
+bool prefill_supported(int io_dtype, int d, int chunk);
+hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,118 @@
+"""CPU checks of the C-ABI library: it loads, exports every function declared
+in include/gdn.h, its argument structs match the header's layout (checked
+with a C compiler), and host-side validation rejects bad arguments before
+any launch (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import linear_attention_token_conv1d_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_ ]*?\**\s*(gdn_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"gdn_conv1d", "gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size",
+            "gdn_status_string", "gdn_last_error", "gdn_abi_version"} <= set(names)
+    L = gdn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+    assert L.gdn_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    src = r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "gdn.h"
+#define P(s, f) printf(#s "." #f " %zu\n", offsetof(s, f))
+int main(void) {
+  printf("conv %zu\nprefill %zu\ndecode %zu\n", sizeof(gdn_conv1d_args), sizeof(gdn_prefill_args),
+         sizeof(gdn_decode_args));
+  P(gdn_conv1d_args, total_tokens); P(gdn_conv1d_args, cu_seqlens);
+  P(gdn_prefill_args, total_tokens); P(gdn_prefill_args, scale); P(gdn_prefill_args, q_stride);
+  P(gdn_prefill_args, workspace_bytes); P(gdn_decode_args, scale); P(gdn_decode_args, o);
+  return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        lines = dict(l.rsplit(" ", 1) for l in subprocess.run([exe], capture_output=True, text=True,
+                                                               check=True).stdout.split("\n") if l)
+    assert int(lines["conv"]) == ctypes.sizeof(gdn.ConvArgs)
+    assert int(lines["prefill"]) == ctypes.sizeof(gdn.PrefillArgs)
+    assert int(lines["decode"]) == ctypes.sizeof(gdn.DecodeArgs)
+    for key, val in lines.items():
+        if "." in key:
+            s, f = key.split(".")
+            cls = {"gdn_conv1d_args": gdn.ConvArgs, "gdn_prefill_args": gdn.PrefillArgs,
+                   "gdn_decode_args": gdn.DecodeArgs}[s]
+            assert getattr(cls, f).offset == int(val), key
+
+
+def _prefill(**kw):
+    base = dict(struct_size=ctypes.sizeof(gdn.PrefillArgs), io_dtype=1, n_seqs=1, total_tokens=64,
+                h_qk=2, h_v=6, d_k=128, d_v=128, chunk=64, scale=1.0, q=0x1000, k=0x2000, v=0x3000,
+                q_stride=256, k_stride=256, v_stride=768, g=0x4000, beta=0x5000, o=0x6000)
+    base.update(kw)
+    a = gdn.PrefillArgs(**base)
+    st = gdn.lib().gdn_prefill(ctypes.byref(a), None)
+    return st, gdn.lib().gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_v=5), 1), (dict(d_k=96, d_v=96), 2), (dict(d_v=64), 2), (dict(chunk=48), 2),
+    (dict(q=0), 1), (dict(n_seqs=0), 1), (dict(n_seqs=2), 1), (dict(io_dtype=7), 1),
+    (dict(q_stride=100), 1), (dict(q_stride=260), 3), (dict(q=0x1001), 3), (dict(flags=8), 1),
+    (dict(struct_size=8), 1), (dict(total_tokens=-1), 1),
+    (dict(io_dtype=0, d_k=128, d_v=128, chunk=64), 2),
+])
+def test_prefill_validation(kw, code):
+    st, msg = _prefill(**kw)
+    assert st == code, msg
+    assert msg.startswith("gdn_prefill")
+
+
+def test_conv_and_decode_validation():
+    L = gdn.lib()
+    a = gdn.ConvArgs(struct_size=ctypes.sizeof(gdn.ConvArgs), dtype=1, n_seqs=1, channels=12,
+                     total_tokens=4, width=4, activation=1, x=0x1000, weight=0x2000, y=0x3000)
+    assert L.gdn_conv1d(ctypes.byref(a), None) == 2  # channels % 8
+    a.channels, a.width = 16, 5
+    assert L.gdn_conv1d(ctypes.byref(a), None) == 2
+    a.width, a.y = 4, 0x1010  # y overlaps x
+    assert L.gdn_conv1d(ctypes.byref(a), None) == 1
+    assert b"overlap" in L.gdn_last_error()
+    d = gdn.DecodeArgs(struct_size=ctypes.sizeof(gdn.DecodeArgs), io_dtype=1, state_dtype=1, n_seqs=4,
+                       h_qk=2, h_v=6, d_k=128, d_v=128, width=4, activation=1, scale=1.0, x=0x1000,
+                       conv_weight=0x2000, conv_state=0, g=0x3000, beta=0x4000, state=0x5000, o=0x6000)
+    assert L.gdn_decode_step(ctypes.byref(d), None) == 1  # conv without a conv state
+    d.conv_weight = 0
+    d.h_qk, d.h_v = 1, 32
+    assert L.gdn_decode_step(ctypes.byref(d), None) == 2  # more than 16 V heads per QK head
+    d.h_qk, d.h_v, d.state = 2, 6, 0x5008
+    assert L.gdn_decode_step(ctypes.byref(d), None) == 3
+
+
+def test_workspace_size_query():
+    a = gdn.PrefillArgs(struct_size=ctypes.sizeof(gdn.PrefillArgs), n_seqs=1, total_tokens=1024, h_qk=16,
+                        h_v=48, d_k=128, d_v=128, chunk=64)
+    assert gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a)) >= 0
+    assert gdn.lib().gdn_status_string(5) == b"GDN_ERR_HIP"
