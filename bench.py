@@ -1,0 +1,238 @@
+"""Throughput of the Gated DeltaNet token mixer on one MI355X.
+
+A step is one pass of the prefill hot path over one synthetic layer input:
+gdn_conv1d (causal conv + SiLU over [q|k|v]) then gdn_prefill (chunked gated
+delta rule), inputs already resident in HBM.  The default workload is the
+9B-shaped layer (B=1, T=8192, 32 QK / 32 V heads, d=128, chunk 64).  The line
+also carries the decode leg: gdn_decode_step on the 27B-shaped batch of 256
+sequences x 48 V heads with a bf16 state, 64 consecutive steps.
+
+Prints ONE JSON line.  `value` is prefill tokens/s/layer (conv + prefill).
+`roofline` is for the dominant kernel (the prefill kernel): algorithmic
+FLOPs per launch / its average duration from HIP events on the stream it
+runs on.  `cpu_baseline` is the fp64 oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "GDN prefill tokens/s/layer (%MFMA peak); decode steps/s (%HBM BW), 1 MI355X"
+
+
+def prefill_flops_per_token(cfg):
+    """Algorithmic FLOPs per token of the chunked form: per V head the W/U-sized
+    C x C products (2 C d_k + 4 C d_v: T-apply, intra-chunk output) and the
+    d_k x d_v state products (6 d_k d_v: S k, S q, state update), plus the two
+    Gram matrices once per QK head (4 C d_k)."""
+    C, dk, dv = cfg["chunk"], cfg["d_k"], cfg["d_v"]
+    return cfg["h_v"] * (2 * C * dk + 4 * C * dv + 6 * dk * dv) + cfg["h_qk"] * 4 * C * dk
+
+
+def decode_bytes_per_step(cfg):
+    """HBM bytes one decode step must move: state read + write, conv-state
+    history read (W-1) and one new slot written, x, g and beta, o, conv weights."""
+    N, hv, dk, dv, W = cfg["n_seqs"], cfg["h_v"], cfg["d_k"], cfg["d_v"], cfg["width"]
+    C = 2 * cfg["h_qk"] * dk + hv * dv
+    sb = 2 if cfg["state"] == "bf16" else 4
+    return (2 * N * hv * dv * dk * sb + N * C * W * 2 + N * C * 2 + N * hv * 8 + N * hv * dv * 2
+            + C * W * 2)
+
+
+_SHARED = {}  # oracle inputs handed to forked workers without pickling
+
+
+def _oracle_heads(heads):
+    from oracle import gdn_oracle as orc
+    s = _SHARED
+    orc.gdn_layer(s["x"], s["w"], s["g"], s["b"], s["hq"], s["d"], s["hv"], s["d"], v_heads=heads)
+    return len(heads)
+
+
+def cpu_baseline_prefill(inp, cfg, tokens):
+    """Oracle (fp64 numpy, token by token) over the first `tokens` tokens of the
+    workload, all V heads, split over a process pool by V head."""
+    import numpy as np
+    cores = min(len(os.sched_getaffinity(0)), cfg["h_v"], 16)
+    tokens = min(tokens, inp["T"])
+    x = inp["x"][:tokens].double().numpy()
+    w = inp["conv_weight"].double().numpy()
+    g = inp["g"][:tokens].double().numpy()
+    b = inp["beta"][:tokens].double().numpy()
+    jobs = [list(h) for h in np.array_split(np.arange(cfg["h_v"]), cores)]
+    _SHARED.update(x=x, w=w, g=g, b=b, hq=cfg["h_qk"], d=cfg["d_k"], hv=cfg["h_v"])
+    ctx = mp.get_context("fork")
+    t = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        done = sum(pool.map(_oracle_heads, jobs))
+    dt = time.perf_counter() - t
+    assert done == cfg["h_v"]
+    return {"value": tokens / dt, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": f"first {tokens} of {cfg['T']} tokens, all {cfg['h_v']} V heads, conv + recurrence, "
+                      f"fp64 numpy, {cores} processes split by V head; {dt:.1f} s"}
+
+
+def run_prefill(name, steps, warmup, do_cpu, cpu_tokens):
+    import torch
+    import gdn_inputs
+    import linear_attention_token_conv1d_amd as gdn
+
+    inp = gdn_inputs.prefill_inputs(name)
+    cfg = inp["cfg"]
+    dev = torch.device("cuda:0")
+    x = inp["x"].to(dev)
+    w = inp["conv_weight"].to(dev)
+    g = inp["g"].to(dev)
+    beta = inp["beta"].to(dev)
+    s0 = None if inp["initial_state"] is None else inp["initial_state"].to(dev)
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].to(dev)
+    T, hq, hv, d = inp["T"], cfg["h_qk"], cfg["h_v"], cfg["d_k"]
+    y = torch.empty_like(x)
+    o = torch.empty((T, hv, d), dtype=x.dtype, device=dev)
+    fs = torch.empty((inp["n_seqs"], hv, d, d), dtype=torch.float32, device=dev)
+    q0, _, v0 = gdn.split_qkv(y, hq, d, hv, d)
+    ws = torch.empty(max(1, gdn.prefill_workspace_size(q0, v0, inp["n_seqs"], cfg["chunk"])),
+                     dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        gdn.conv1d(x, w, None, None, cu, "silu", out=y)
+        q, k, v = gdn.split_qkv(y, hq, d, hv, d)
+        if ev is not None:
+            ev[0].record()
+        gdn.prefill(q, k, v, g, beta, s0, cu, cfg["chunk"], 1.0, True, True, o=o, final_state=fs,
+                    workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    k_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    flops = prefill_flops_per_token(cfg) * T
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    res = {
+        "tokens_per_s": T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "prefill_kernel_ms": k_ms,
+        "prefill_only_tokens_per_s": T / (k_ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<bf16,128,64>",
+                     "flops_per_launch": flops},
+        "config": {"workload": f"{name}: B={inp['n_seqs']} T={T} h_qk={hq} h_v={hv} d={d} "
+                               f"chunk={cfg['chunk']} conv{cfg['width']}+SiLU, bf16 io, fp32 state",
+                   "tokens": T, "h_qk": hq, "h_v": hv, "d": d, "chunk": cfg["chunk"]},
+    }
+    if do_cpu:
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, cfg, cpu_tokens)
+    return res
+
+
+def run_decode(steps, warmup, do_cpu):
+    import numpy as np
+    import torch
+    import gdn_inputs
+    import linear_attention_token_conv1d_amd as gdn
+
+    inp = gdn_inputs.decode_inputs("qwen35_27b_decode")
+    cfg = inp["cfg"]
+    dev = torch.device("cuda:0")
+    S = inp["state"].to(dev)
+    cs = inp["conv_state"].to(dev)
+    w = inp["conv_weight"].to(dev)
+    xs, gs, bs = inp["x"].to(dev), inp["g"].to(dev), inp["beta"].to(dev)
+    N, hq, hv, d = cfg["n_seqs"], cfg["h_qk"], cfg["h_v"], cfg["d_k"]
+    o = torch.empty((N, hv, d), dtype=torch.bfloat16, device=dev)
+    nsteps = xs.shape[0]
+    for i in range(warmup):
+        gdn.decode_step(xs[i % nsteps], gs[i % nsteps], bs[i % nsteps], S, hq, hv, d, conv_weight=w,
+                        conv_state=cs, o=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(nsteps):
+        gdn.decode_step(xs[i], gs[i], bs[i], S, hq, hv, d, conv_weight=w, conv_state=cs, o=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / nsteps
+    nbytes = decode_bytes_per_step(cfg)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"value": 1e3 / ms, "unit": "steps/s", "tokens_per_s": N * 1e3 / ms, "ms_per_step": ms,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "kernel": "decode_kernel<bf16,bf16,128>", "bytes_per_launch": nbytes},
+           "config": {"workload": f"qwen35_27b_decode: {N} sequences x 1 token, h_qk={hq} h_v={hv} d={d}, "
+                                  f"bf16 state, conv4+SiLU, {nsteps} consecutive steps"}}
+    if do_cpu:
+        from oracle import gdn_oracle as orc
+        sample = 8
+        st = inp["state"][:sample].double().numpy()
+        ct = inp["conv_state"][:sample].double().numpy()
+        wn = inp["conv_weight"].double().numpy()
+        t = time.perf_counter()
+        for i in range(4):
+            _, st, ct = orc.decode_step(inp["x"][i, :sample].double().numpy(), wn,
+                                        inp["g"][i, :sample].double().numpy(),
+                                        inp["beta"][i, :sample].double().numpy(), st, ct, hq, d, hv, d)
+        dt = (time.perf_counter() - t) / 4 * (N / sample)
+        res["cpu_baseline"] = {"value": 1.0 / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{sample} of {N} sequences x 4 steps, fp64 numpy, one process; "
+                                         f"time scaled by {N // sample}"}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen35_9b_prefill",
+                    choices=["qwen35_9b_prefill", "qwen35_27b_prefill", "qwen35_27b_varlen"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the mixer shards by (sequence, V head) with no "
+              "exchange, so there is no multi-GPU step to time here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    pre = run_prefill(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_tokens)
+    line = {"metric": METRIC, "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s/layer",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(pre["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": pre["config"], "roofline": pre["roofline"],
+            "prefill_kernel_ms": round(pre["prefill_kernel_ms"], 4),
+            "prefill_only_tokens_per_s": round(pre["prefill_only_tokens_per_s"], 1)}
+    if "cpu_baseline" in pre:
+        line["cpu_baseline"] = pre["cpu_baseline"]
+    if not args.no_decode:
+        line["decode"] = run_decode(args.steps, args.warmup, not args.no_cpu_baseline)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -167,8 +167,8 @@ def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk,
 
 def prefill_workspace_size(q, v, n_seqs=1, chunk=64):
     T, h_qk, d_k = q.shape
-    a = PrefillArgs(struct_size=ctypes.sizeof(PrefillArgs), n_seqs=n_seqs, total_tokens=T, h_qk=h_qk,
-                    h_v=v.shape[1], d_k=d_k, d_v=v.shape[2], chunk=chunk)
+    a = PrefillArgs(struct_size=ctypes.sizeof(PrefillArgs), io_dtype=_DT[q.dtype], n_seqs=n_seqs,
+                    total_tokens=T, h_qk=h_qk, h_v=v.shape[1], d_k=d_k, d_v=v.shape[2], chunk=chunk)
     return lib().gdn_prefill_workspace_size(ctypes.byref(a))
 
 

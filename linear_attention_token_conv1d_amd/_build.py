@@ -30,6 +30,9 @@ FLAGS = [
     "-Wno-unused-function",
     # packed-fp32 instructions are kept off (plain fp32 VALU code only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators live in ordinary VGPRs: the scan's accumulator tiles
+    # feed VALU math every chunk, and AGPR copies would double that traffic
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

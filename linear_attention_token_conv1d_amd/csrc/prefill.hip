@@ -1,8 +1,8 @@
 // gdn_prefill: chunked gated delta rule on gfx950.
 //
-// Math (per sequence, V head; within a chunk of L <= C tokens, G_r the
+// Math (per sequence and V head; within a chunk of L <= C tokens, G_r is the
 // inclusive cumulative sum of g, gamma_r = e^{G_r}, e_r = e^{G_{L-1} - G_r},
-// k^_r = rk_r k_r and q^_r = rq_r q_r the L2-normalised rows):
+// and k^_r = rk_r k_r, q^_r = rq_r q_r are the L2-normalised rows):
 //   A_rj  = beta_r e^{G_r - G_j} (k^_r . k^_j)            j <  r   (strict lower)
 //   T     = (I + A)^-1,   Tb = T diag(beta)
 //   P_rj  = scale e^{G_r - G_j} (q^_r . k^_j)              j <= r
@@ -12,56 +12,81 @@
 //   O     = diag(scale gamma rq) Y + P U
 //   S^T  <- gamma_{L-1} S^T + K^T diag(e rk) U
 // This is the recurrence S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T,
-// o_t = scale S_t q_t ("Inside Qwen3.5", sections 4-5) unrolled over a chunk;
-// only e^{x} with x <= 0 is ever formed.
+// o_t = scale S_t q_t ("Inside Qwen3.5", sections 4-5) unrolled over one
+// chunk; only e^{x} with x <= 0 is ever formed.
 //
-// Work split: one workgroup per (sequence, V head, block of 64 d_v columns),
-// 4 waves; wave w owns 16 d_v columns of the fp32 state S^T (d_k x 16) in MFMA
-// accumulators for the whole sequence.  Every state-dependent product (X1, Y,
-// U, O, the state update) uses the previous result's accumulator tiles
-// directly as the B operand of the next MFMA: a 16x16 accumulator holds rows
-// 4g+i (g = lane/16) of column lane%16, which is a valid B fragment once the
-// A operand reads its k index in the same order (k = 4g+i, then 16+4g+i).
-// So the serial chain never leaves registers; shared per-chunk operands (K,
-// Q, K^T, Tb, P) sit in LDS.
+// Three launches on the caller's stream:
+//  plan  one workgroup: chunk offsets of every packed sequence (workspace).
+//  prep  one workgroup per (chunk, QK head), all chunks in parallel: row norms,
+//        the two Gram matrices (MFMA) once per QK head, then per V head of the
+//        group the decay masks, the UT solve T = (I + A)^-1 (fp32) and the
+//        chunk operands Tb, P and the per-token scalars, written to workspace.
+//  scan  one workgroup per (sequence, V head, block of 16*NW d_v columns),
+//        walking its chunks in order.  Wave w owns 16 d_v columns of the fp32
+//        state S^T (d_k x 16) in MFMA accumulators for the whole sequence.
+//        Every state-dependent product uses the previous result's accumulator
+//        tiles directly as the B operand of the next MFMA (a 16x16 accumulator
+//        holds rows 4g+i, g = lane/16, of column lane%16: a valid B fragment
+//        once the A operand reads its k index in the same order), so the
+//        serial chain never leaves registers.  The chunk's K, Q, Tb, P are
+//        double-buffered in LDS and the next chunk is prefetched into
+//        registers while the current one is computed; K^T fragments for the
+//        state update come straight from the row-major K tile through the
+//        gfx950 LDS transpose read (ds_read_b64_tr_b16).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kCols = 64;  // d_v columns per workgroup (4 waves x 16)
+constexpr int kPrepThreads = 256;
 
 // ------------------------------------------------------------------ MFMA
 // A 32-deep k-step: lane l supplies 8 k values for row/column l%16, in the
 // order k = 4g + j (j < 4) then 16 + 4g + (j - 4), g = l / 16.
 template <typename T> struct Mma;
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
 template <> struct Mma<__bf16> {
   using frag = bf16x8;
-  static __device__ __forceinline__ frag zero() { return frag{}; }
-  // from LDS row `row` (k contiguous): elements kb+4g..+3 and kb+16+4g..+3
+  // from LDS row `row` (k contiguous): elements 4g..4g+3 and 16+4g..16+4g+3
   static __device__ __forceinline__ frag lds(const __bf16* row, int g, bool half) {
     const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * g);
     uint2 hi = make_uint2(0u, 0u);
     if (!half) hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
     return __builtin_bit_cast(frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
+  // K^T fragment (m = d_k column dcol0 + lane%16, k = token) from the
+  // row-major tile K[token][d_k] at tokens tok0 + 4g + {0..3} and +16.  In
+  // each 16-lane group, lane j reads 4 consecutive d_k of token 4g + j/4; the
+  // transpose read hands lane i element i%4 of the rows read by lanes
+  // i/4 + 4e (e = 0..3), i.e. K[tok0 + 4g + e][dcol0 + i].
+  static __device__ __forceinline__ frag lds_tr(const __bf16* K, int ld, int tok0, int dcol0, int l16,
+                                                int g, bool half) {
+    const __bf16* p = K + (tok0 + 4 * g + (l16 >> 2)) * ld + dcol0 + 4 * (l16 & 3);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(__attribute__((address_space(3))) __bf16*)(p));
+    short4_t hi = {0, 0, 0, 0};
+    if (!half)
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(__attribute__((address_space(3))) __bf16*)(p + 16 * ld));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
+  }
   // from two accumulator tiles (rows 4g+i of tile a, then of tile b)
   static __device__ __forceinline__ frag acc(const f32x4& a, const f32x4& b) {
     return __builtin_bit_cast(frag, make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
                                                pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])));
   }
-  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b, bool half) {
-    (void)half;
+  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b, bool) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 
 template <> struct Mma<float> {
   struct frag { float v[8]; };
-  static __device__ __forceinline__ frag zero() { frag f; for (int j = 0; j < 8; ++j) f.v[j] = 0.f; return f; }
   static __device__ __forceinline__ frag lds(const float* row, int g, bool half) {
     frag f;
     const float4 lo = *reinterpret_cast<const float4*>(row + 4 * g);
@@ -71,8 +96,19 @@ template <> struct Mma<float> {
     f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
     return f;
   }
+  static __device__ __forceinline__ frag lds_tr(const float* K, int ld, int tok0, int dcol0, int l16,
+                                                int g, bool half) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.v[e] = K[(tok0 + 4 * g + e) * ld + dcol0 + l16];
+      f.v[4 + e] = half ? 0.f : K[(tok0 + 16 + 4 * g + e) * ld + dcol0 + l16];
+    }
+    return f;
+  }
   static __device__ __forceinline__ frag acc(const f32x4& a, const f32x4& b) {
     frag f;
+#pragma unroll
     for (int j = 0; j < 4; ++j) { f.v[j] = a[j]; f.v[4 + j] = b[j]; }
     return f;
   }
@@ -87,27 +123,24 @@ template <> struct Mma<float> {
   }
 };
 
-// ------------------------------------------------------------ LDS layout
-template <typename T, int D, int C>
-struct Layout {
-  static constexpr int NT = C / 16;            // 16-token tiles per chunk
-  static constexpr int DT = D / 16;            // 16-row tiles of d_k
-  static constexpr int PADE = 32 / sizeof(T);  // 32 bytes of padding per row
-  static constexpr int LDK = D + PADE;         // pitch of K, Q rows (token-major)
-  static constexpr int LDC = C + PADE;         // pitch of K^T, Tb, P rows
-  static constexpr int LDF = C + 4;            // pitch of fp32 A / T work arrays
-  // byte offsets
-  static constexpr int oK = 0;
-  static constexpr int oQ = oK + C * LDK * (int)sizeof(T);
-  static constexpr int oKT = oQ + C * LDK * (int)sizeof(T);
-  static constexpr int oTb = oKT + D * LDC * (int)sizeof(T);
-  static constexpr int oP = oTb + C * LDC * (int)sizeof(T);
-  static constexpr int oA = oP + C * LDC * (int)sizeof(T);
-  static constexpr int oTf = oA + C * LDF * 4;
-  static constexpr int oZ = oTf + C * LDF * 4;          // 16 x C fp32 scratch
-  static constexpr int oVec = oZ + 16 * LDF * 4;        // per-token fp32 vectors
-  static constexpr int NVEC = 8;                        // g, beta, G, gamma*rk, scale*gamma*rq, e*rk, rk, rq
-  static constexpr int bytes = oVec + NVEC * C * 4 + 16;
+// 8 consecutive elements as raw bits (16 B of bf16, 32 B of fp32)
+template <typename T> struct Raw8;
+template <> struct Raw8<__bf16> {
+  uint4 a;
+  static __device__ __forceinline__ Raw8 load(const __bf16* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+  static __device__ __forceinline__ Raw8 zero() { return {make_uint4(0u, 0u, 0u, 0u)}; }
+  __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<uint4*>(p) = a; }
+};
+template <> struct Raw8<float> {
+  uint4 a, b;
+  static __device__ __forceinline__ Raw8 load(const float* p) {
+    return {reinterpret_cast<const uint4*>(p)[0], reinterpret_cast<const uint4*>(p)[1]};
+  }
+  static __device__ __forceinline__ Raw8 zero() { return {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)}; }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<uint4*>(p)[0] = a;
+    reinterpret_cast<uint4*>(p)[1] = b;
+  }
 };
 
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
@@ -120,307 +153,752 @@ __device__ __forceinline__ f32x4 tile_hi(const f32x4 (&t)[NT], int s) {
   return i < NT ? t[i < NT ? i : 0] : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// ------------------------------------------------------------- workspace
+// [chunk offsets: n_seqs+1 int32, padded to 256 B]
+// [per (chunk, V head) record: Tb [C][C] T | P [C][C] T | vec [4][C] fp32]
+//  vec rows: gamma*rk, scale*gamma*rq, e*rk, gamma_last (broadcast)
+template <typename T, int C>
+struct Rec {
+  static constexpr size_t mat = (size_t)C * C * sizeof(T);
+  static constexpr size_t bytes = 2 * mat + 16 * (size_t)C;
+};
+
+__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs + 1) * 4 + 255) / 256 * 256; }
+
+__host__ __device__ inline int64_t max_chunks(int64_t T, int n_seqs, int C) { return T / C + n_seqs; }
+
+// ------------------------------------------------------------------ plan
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs, int64_t total, int C,
+                                                   int32_t* chunk_off) {
+  __shared__ int32_t part[256];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry = 0; chunk_off[0] = 0; }
+  __syncthreads();
+  for (int base = 0; base < n_seqs; base += 256) {
+    const int i = base + tid;
+    int cnt = 0;
+    if (i < n_seqs) {
+      const int64_t s = cu ? cu[i] : 0, e = cu ? cu[i + 1] : total;
+      cnt = (int)((e - s + C - 1) / C);
+    }
+    part[tid] = cnt;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    if (i < n_seqs) chunk_off[i + 1] = carry + part[tid];
+    __syncthreads();
+    if (tid == 255) carry += part[255];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ prep
 template <typename T, int D, int C>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
-  using L = Layout<T, D, C>;
+struct PrepLayout {
+  static constexpr int NT = C / 16;
+  static constexpr int PADE = 16 / (int)sizeof(T);
+  static constexpr int LDK = D + PADE;
+  static constexpr int LDC = C + PADE;
+  static constexpr int LDF = C + 4;
+  static constexpr int LDZ = 20;
+  static constexpr int oK = 0;
+  static constexpr int oQ = oK + C * LDK * (int)sizeof(T);
+  static constexpr int oA = oQ + C * LDK * (int)sizeof(T);
+  static constexpr int oZ = oA + C * LDF * 4;
+  static constexpr int oSt = oZ + 4 * 16 * LDZ * 4;
+  static constexpr int oVec = oSt + C * LDC * (int)sizeof(T);
+  static constexpr int bytes = oVec + 6 * C * 4;
+};
+
+// Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
+__device__ __forceinline__ int owner(const int32_t* off, int n_seqs, int c) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, unsigned char* ws) {
+  using L = PrepLayout<T, D, C>;
   using M = Mma<T>;
-  constexpr int NT = L::NT, DT = L::DT;
+  using R8 = Raw8<T>;
+  constexpr int NT = L::NT;
+  constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
+  constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
   extern __shared__ __align__(16) unsigned char smem[];
   T* K_s = reinterpret_cast<T*>(smem + L::oK);
   T* Q_s = reinterpret_cast<T*>(smem + L::oQ);
-  T* KT_s = reinterpret_cast<T*>(smem + L::oKT);
-  T* Tb_s = reinterpret_cast<T*>(smem + L::oTb);
-  T* P_s = reinterpret_cast<T*>(smem + L::oP);
   float* A_s = reinterpret_cast<float*>(smem + L::oA);
-  float* T_s = reinterpret_cast<float*>(smem + L::oTf);
   float* Z_s = reinterpret_cast<float*>(smem + L::oZ);
-  float* vec = reinterpret_cast<float*>(smem + L::oVec);
-  float* g_s = vec;            // g
-  float* b_s = vec + C;        // beta
-  float* G_s = vec + 2 * C;    // cumulative g
-  float* grk_s = vec + 3 * C;  // gamma_r rk_r
-  float* grq_s = vec + 4 * C;  // scale gamma_r rq_r
-  float* erk_s = vec + 5 * C;  // e_r rk_r
-  float* rk_s = vec + 6 * C;
-  float* rq_s = vec + 7 * C;
-  float* misc = vec + 8 * C;   // [0] = gamma_{L-1}
+  T* St = reinterpret_cast<T*>(smem + L::oSt);
+  float* g_s = reinterpret_cast<float*>(smem + L::oVec);
+  float* b_s = g_s + C;
+  float* G_s = g_s + 2 * C;
+  float* rk_s = g_s + 3 * C;
+  float* rq_s = g_s + 4 * C;
 
-  const int nblk = D / kCols > 0 ? D / kCols : 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, l16 = lane & 15;
-  const int blk = blockIdx.x % nblk;
-  const int h = (blockIdx.x / nblk) % p.h_v;
-  const int n = blockIdx.x / (nblk * p.h_v);
-  const int hq = h / (p.h_v / p.h_qk);
-  const int col = blk * kCols + wave * 16 + l16;  // this lane's d_v column
-  const bool col_ok = col < D;                    // D = 64 uses one block of 64
-
+  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
+  const int ci = blockIdx.x, hq = blockIdx.y;
+  if (ci >= off[p.n_seqs]) return;
+  const int n = owner(off, p.n_seqs, ci);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
+  const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
+  const int Lc = (int)min((int64_t)C, seq_end - t0);
+  const int grp = p.h_v / p.h_qk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
 
-  const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
+  // K, Q rows of this chunk and QK head; rows >= Lc are zero
   const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
-  const T* vg = reinterpret_cast<const T*>(p.v) + (int64_t)h * D;
-  T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D;
-  const int64_t o_stride = (int64_t)p.h_v * D;
+  const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
+  for (int e = tid; e < C * (D / 8); e += kPrepThreads) {
+    const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
+    const bool ok = r < Lc;
+    (ok ? R8::load(kg + (t0 + r) * p.k_stride + d0) : R8::zero()).store(K_s + r * L::LDK + d0);
+    (ok ? R8::load(qg + (t0 + r) * p.q_stride + d0) : R8::zero()).store(Q_s + r * L::LDK + d0);
+  }
+  __syncthreads();
 
-  // ---- state S^T (d_k x 16 columns of this wave) in DT accumulator tiles
-  f32x4 st[DT];
-  const size_t sbase = ((size_t)n * p.h_v + h) * D * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    st[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (p.initial_state && col_ok) {
-      const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + sbase + (size_t)col * D + dt * 16 + 4 * g4);
-      st[dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+  // row norms (4 lanes per row)
+  for (int r = tid >> 2; r < C; r += kPrepThreads / 4) {
+    const int part = tid & 3;
+    float sk = 0.f, sq = 0.f;
+    for (int d = part; d < D; d += 4) {
+      const float a = to_f32(K_s[r * L::LDK + d]);
+      const float b = to_f32(Q_s[r * L::LDK + d]);
+      sk += a * a; sq += b * b;
+    }
+    sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk);
+    sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq);
+    if (part == 0) {
+      rk_s[r] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+      rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
     }
   }
 
-  for (int64_t t0 = seq_start; t0 < seq_end; t0 += C) {
-    const int Lc = (int)min((int64_t)C, seq_end - t0);
-
-    // ================= chunk prep (state independent) =================
-    // K, Q rows -> LDS (token-major) and K^T (d_k-major); rows >= Lc are zero
-    for (int e = tid; e < C * (D / 8); e += kThreads) {
-      const int r = e / (D / 8);
-      const int d0 = (e % (D / 8)) * 8;
-      float kv[8], qv[8];
-      if (r < Lc) {
-        load8(kg + (t0 + r) * p.k_stride + d0, kv);
-        load8(qg + (t0 + r) * p.q_stride + d0, qv);
-      } else {
+  // raw Gram tiles (lower triangle): jobs [0, NLT) are K K^T, [NLT, 2 NLT) are Q K^T
+  f32x4 gram[NJ];
+  int jmt[NJ], jnt[NJ];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { kv[j] = 0.f; qv[j] = 0.f; }
-      }
-      store8(K_s + r * L::LDK + d0, kv);
-      store8(Q_s + r * L::LDK + d0, qv);
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int job = wave + 4 * jj;
+    gram[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    jmt[jj] = jnt[jj] = 0;
+    if (job < 2 * NLT) {
+      int tj = job >= NLT ? job - NLT : job, mt = 0;
+      while (tj > mt) { tj -= mt + 1; ++mt; }
+      jmt[jj] = mt; jnt[jj] = tj;
+      const T* Arow = (job >= NLT ? Q_s : K_s) + (mt * 16 + l16) * L::LDK;
+      const T* Brow = K_s + (tj * 16 + l16) * L::LDK;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) KT_s[(d0 + j) * L::LDC + r] = from_f32<T>(kv[j]);
+      for (int s = 0; s < D / 32; ++s)
+        M::mma(gram[jj], M::lds(Arow + 32 * s, g4, false), M::lds(Brow + 32 * s, g4, false), false);
     }
+  }
+
+  const size_t rec_base = off_bytes(p.n_seqs);
+  for (int vh = 0; vh < grp; ++vh) {
+    const int h = hq * grp + vh;
+    unsigned char* rec = ws + rec_base + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
+    T* Tb_g = reinterpret_cast<T*>(rec);
+    T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
+    float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
+
     if (tid < C) {
       const bool ok = tid < Lc;
       g_s[tid] = ok ? p.g[(t0 + tid) * p.h_v + h] : 0.f;
       b_s[tid] = ok ? p.beta[(t0 + tid) * p.h_v + h] : 0.f;
     }
-    __syncthreads();
-
-    // row norms (4 lanes per row) and the cumulative log-decay (wave 0)
-    for (int r = tid >> 2; r < C; r += kThreads / 4) {
-      const int part = tid & 3;
-      float sk = 0.f, sq = 0.f;
-      for (int d = part; d < D; d += 4) {
-        const float a = to_f32(K_s[r * L::LDK + d]);
-        const float b = to_f32(Q_s[r * L::LDK + d]);
-        sk += a * a; sq += b * b;
-      }
-      sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk);
-      sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq);
-      if (part == 0) {
-        rk_s[r] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-        rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-      }
-    }
+    __syncthreads();  // also publishes the norms (first head)
     if (wave == 0) {
       float G = lane < C ? g_s[lane] : 0.f;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(G, off, 64);
-        if (lane >= off) G += o;
+      for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(G, o, 64);
+        if (lane >= o) G += u;
       }
       if (lane < C) G_s[lane] = G;
+      const float Gl = __shfl(G, Lc - 1, 64);
+      if (lane < C) {
+        const float eg = fexp(G);
+        vec_g[lane] = eg * rk_s[lane];
+        vec_g[C + lane] = p.scale * eg * rq_s[lane];
+        vec_g[2 * C + lane] = fexp(Gl - G) * rk_s[lane];
+        vec_g[3 * C + lane] = fexp(Gl);
+      }
     }
     __syncthreads();
-    if (tid < C) {
-      const float Gl = G_s[Lc - 1];
-      const float G = G_s[tid];
-      grk_s[tid] = fexp(G) * rk_s[tid];
-      grq_s[tid] = p.scale * fexp(G) * rq_s[tid];
-      erk_s[tid] = fexp(Gl - G) * rk_s[tid];
-      if (tid == 0) misc[0] = fexp(Gl);
-    }
 
-    // Gram tiles: KK^T -> A (strict lower, fp32), QK^T -> P (lower incl. diagonal)
-    constexpr int NLT = NT * (NT + 1) / 2;
-    for (int job = wave; job < 2 * NLT; job += 4) {
-      const bool isP = job >= NLT;
-      int tj = isP ? job - NLT : job;
-      int mt = 0;
-      while (tj > mt) { tj -= mt + 1; ++mt; }
-      const int nt = tj;  // nt <= mt
-      const T* Arow = (isP ? Q_s : K_s) + (mt * 16 + l16) * L::LDK;
-      const T* Brow = K_s + (nt * 16 + l16) * L::LDK;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // decay-masked Gram tiles: A (strict lower, fp32) and P (lower incl. diagonal)
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        M::mma(acc, M::lds(Arow + 32 * s, g4, false), M::lds(Brow + 32 * s, g4, false), false);
-      const int j = nt * 16 + l16;
-      // G_s, b_s and the norms were published before the last barrier
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = wave + 4 * jj;
+      if (job < 2 * NLT) {
+        const bool isP = job >= NLT;
+        const int j = jnt[jj] * 16 + l16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * g4 + i;
-        const float dec = (j <= r) ? fexp(G_s[r] - G_s[j]) : 0.f;
-        if (!isP) {
-          A_s[r * L::LDF + j] = (j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * acc[i] : 0.f;
-        } else {
-          P_s[r * L::LDC + j] = from_f32<T>((j <= r) ? p.scale * dec * rq_s[r] * rk_s[j] * acc[i] : 0.f);
+        for (int i = 0; i < 4; ++i) {
+          const int r = jmt[jj] * 16 + 4 * g4 + i;
+          const float dec = (j <= r) ? fexp(G_s[r] - G_s[j]) : 0.f;
+          if (!isP)
+            A_s[r * L::LDF + j] = (j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f;
+          else
+            St[r * L::LDC + j] = from_f32<T>(p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]);
         }
       }
     }
-    // upper tiles of P are zero
-    for (int e = tid; e < C * C; e += kThreads) {
+    for (int e = tid; e < C * C; e += kPrepThreads) {
       const int r = e / C, j = e % C;
-      if ((j >> 4) > (r >> 4)) P_s[r * L::LDC + j] = from_f32<T>(0.f);
+      if ((j >> 4) > (r >> 4)) St[r * L::LDC + j] = from_f32<T>(0.f);
     }
     __syncthreads();
 
-    // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ...
-    if (wave < NT && l16 == lane) {
+    // P -> workspace; diagonal 16x16 blocks of T = (I + A)^-1 in place
+    for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+      const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
+      R8::load(St + r * L::LDC + j0).store(P_g + r * C + j0);
+    }
+    if (wave < NT && lane < 16) {
       const int b = wave, c = lane;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
         float s = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < r; ++j) s -= A_s[(16 * b + r) * L::LDF + 16 * b + j] * x[j];
+        for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
         x[r] = s;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) T_s[(16 * b + r) * L::LDF + 16 * b + c] = x[r];
-    }
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int r = e / C, j = e % C;
-      if ((j >> 4) > (r >> 4)) T_s[r * L::LDF + j] = 0.f;
-    }
-    __syncthreads();
-    // ... then block rows: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-    for (int bi = 1; bi < NT; ++bi) {
-      for (int e = tid; e < bi * 256; e += kThreads) {
-        const int bj = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        float z = 0.f;
-        for (int k = 16 * bj; k < 16 * bi; ++k)
-          z += A_s[(16 * bi + rr) * L::LDF + k] * T_s[k * L::LDF + 16 * bj + cc];
-        Z_s[rr * L::LDF + 16 * bj + cc] = z;
-      }
-      __syncthreads();
-      for (int e = tid; e < bi * 256; e += kThreads) {
-        const int bj = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        float t = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          t -= T_s[(16 * bi + rr) * L::LDF + 16 * bi + m] * Z_s[m * L::LDF + 16 * bj + cc];
-        T_s[(16 * bi + rr) * L::LDF + 16 * bj + cc] = t;
-      }
-      __syncthreads();
-    }
-    // Tb = T diag(beta)
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int r = e / C, j = e % C;
-      Tb_s[r * L::LDC + j] = from_f32<T>(T_s[r * L::LDF + j] * b_s[j]);
+      for (int r = 0; r < 16; ++r) A_s[(16 * b + r) * L::LDF + 16 * b + c] = x[r];
     }
     __syncthreads();
 
-    // ================= state-dependent chain (per wave) =================
-    f32x4 x1[NT], yq[NT];
+    // off-diagonal blocks, in place (each A block is consumed by the
+    // product that produces the T block in its position)
+    auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
+    auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
+    const int rr = tid >> 4, cc = tid & 15;
+    if constexpr (NT >= 2) {
+      // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) { x1[mt] = f32x4{0.f, 0.f, 0.f, 0.f}; yq[mt] = x1[mt]; }
+      for (int b = 0; b < NT / 2; ++b) {
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
+        Zel(b, rr, cc) = z;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < NT / 2; ++b) {
+        float t = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
+        Ael(2 * b + 1, 2 * b, rr, cc) = t;
+      }
+      __syncthreads();
+    }
+    if constexpr (NT == 4) {
+      // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
+      float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
+        z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
+        z21 += Ael(2, 1, rr, m) * t11;
+        z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
+        z31 += Ael(3, 1, rr, m) * t11;
+      }
+      Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
+      __syncthreads();
+      float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
+        t20 -= a22 * Zel(0, m, cc);
+        t21 -= a22 * Zel(1, m, cc);
+        t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
+        t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
+      }
+      Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
+      __syncthreads();
+    }
+
+    // Tb = T diag(beta) (upper blocks zero) -> staging -> workspace
+    for (int e = tid; e < C * C; e += kPrepThreads) {
+      const int r = e / C, j = e % C;
+      St[r * L::LDC + j] = from_f32<T>((j >> 4) > (r >> 4) ? 0.f : A_s[r * L::LDF + j] * b_s[j]);
+    }
+    __syncthreads();
+    for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+      const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
+      R8::load(St + r * L::LDC + j0).store(Tb_g + r * C + j0);
+    }
+    __syncthreads();  // St, A_s, g_s are rewritten for the next V head
+  }
+}
+
+// ------------------------------------------------------------------ scan
+// Row order inside a pair of 16-row MFMA tiles.  Row m of tile 2s+b stands
+// for index 32s + 8(m/4) + 4b + m%4 (tokens of a chunk, or d_k of the state).
+// An accumulator tile holds rows 4g+i (g = lane/16) of column lane%16; with
+// this order the two tiles 2s, 2s+1 give lane group g the 8 consecutive
+// indices 32s + 8g .. 32s + 8g + 7, so the B fragment built from them pairs
+// with an A fragment that is one contiguous 16-byte read.  A chunk of 16
+// tokens (a single tile) keeps the plain order and half-empty k-steps.
+template <int NT>
+__device__ __forceinline__ int pidx(int t, int m) {
+  if constexpr (NT == 1) return m;
+  else return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+}
+
+// Swizzled LDS tiles.  A tile holds rows of RB bytes (RB/16 sixteen-byte
+// chunks); chunk j of row r sits at slot j ^ f(r).  The two row functions
+// below keep the 16-byte fragment reads (16 rows of one tile pair, one chunk)
+// and the per-column V reads of a wave on distinct banks.  The layout is
+// dense, so a wave's direct-to-LDS load (64 lanes x 16 B into 1 KiB of
+// consecutive LDS) fills it without a register round trip.
+template <int RB>
+struct Swz {
+  static constexpr int CPR = RB / 16;
+  static_assert(CPR >= 1 && (CPR & (CPR - 1)) == 0, "row of 2^k chunks");
+  static __device__ __forceinline__ int f(int r) {
+    if constexpr (CPR >= 16) return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) | ((r >> 4) & 1);
+    else return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);
+  }
+  static __device__ __forceinline__ int slot(int r, int j) { return (j ^ f(r)) & (CPR - 1); }
+  // byte offset of byte b of row r
+  static __device__ __forceinline__ int off(int r, int b) { return r * RB + (slot(r, b >> 4) << 4) + (b & 15); }
+};
+
+// Direct-to-LDS copy of ROWS rows of RB bytes.  Global row r (clamped to
+// rmax - 1) starts at gbase + r * gstride bytes.  Instruction k of wave w
+// fills LDS chunks [(k * NWAVES + w) * 64, +64): lane l writes chunk q and
+// fetches the global chunk whose swizzled slot is q.
+template <int RB, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, const unsigned char* gbase, int64_t gstride,
+                                         int rmax, int wave, int lane) {
+  using S = Swz<RB>;
+  constexpr int TOTAL = ROWS * S::CPR;
+#pragma unroll
+  for (int k = 0; k * NWAVES * 64 < TOTAL; ++k) {
+    const int q0 = (k * NWAVES + wave) * 64;
+    const int q = q0 + lane;
+    if (q0 < TOTAL && q < TOTAL) {
+      const int r = q / S::CPR;
+      const int j = S::slot(r, q % S::CPR);  // slot(r, .) is an involution
+      const unsigned char* src = gbase + (int64_t)min(r, rmax - 1) * gstride + j * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
+    }
+  }
+}
+
+// Plain direct-to-LDS copy of NB bytes (a multiple of 16).
+template <int NB, int NWAVES>
+__device__ __forceinline__ void dma_linear(unsigned char* lds, const unsigned char* g, int wave, int lane) {
+  constexpr int TOTAL = NB / 16;
+#pragma unroll
+  for (int k = 0; k * NWAVES * 64 < TOTAL; ++k) {
+    const int q0 = (k * NWAVES + wave) * 64;
+    const int q = q0 + lane;
+    if (q0 < TOTAL && q < TOTAL)
+      __builtin_amdgcn_global_load_lds(g + q * 16, (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
+  }
+}
+
+// A fragment: 8 consecutive elements k0..k0+7 of row `row` of a swizzled
+// tile (4 elements and 4 zeros when `half`).
+template <typename T, int RB>
+__device__ __forceinline__ typename Mma<T>::frag frag_row(const unsigned char* tile, int row, int k0, bool half) {
+  using S = Swz<RB>;
+  if constexpr (sizeof(T) == 2) {
+    if (half) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(tile + S::off(row, k0 * 2));
+      return __builtin_bit_cast(typename Mma<T>::frag, make_uint4(lo.x, lo.y, 0u, 0u));
+    }
+    return __builtin_bit_cast(typename Mma<T>::frag, *reinterpret_cast<const uint4*>(tile + S::off(row, k0 * 2)));
+  } else {
+    typename Mma<T>::frag f;
+    const float4 lo = *reinterpret_cast<const float4*>(tile + S::off(row, k0 * 4));
+    float4 hi = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!half) hi = *reinterpret_cast<const float4*>(tile + S::off(row, k0 * 4 + 16));
+    f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+    f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+    return f;
+  }
+}
+
+// K^T fragment for the state update: rows m = d_k index dk(m) of state
+// tile t, k = the 8 (or 4) tokens tok0 .. tok0+7 of lane group g, from the
+// swizzled token-major K tile.  bf16: in each 16-lane group, lane j reads 4
+// consecutive d_k (those of state rows 4(j%4)..4(j%4)+3) of token tok0 + j/4,
+// and the transpose read hands lane i element i%4 of the rows read by lanes
+// i/4 + 4e, i.e. K[tok0 + e][dk(i)]; the second read covers tok0 + 4..7.
+template <typename T, int RB, int DTP>
+__device__ __forceinline__ typename Mma<T>::frag frag_kt(const unsigned char* tile, int t, int tok0, int l16,
+                                                         bool half) {
+  using S = Swz<RB>;
+  if constexpr (sizeof(T) == 2) {
+    const int row = tok0 + (l16 >> 2);
+    const int b = pidx<DTP>(t, 4 * (l16 & 3)) * 2;
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4*)(__attribute__((address_space(3))) unsigned char*)(tile + S::off(row, b)));
+    short4_t hi = {0, 0, 0, 0};
+    if (!half)
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(__attribute__((address_space(3))) unsigned char*)(tile + S::off(row + 4, b)));
+    const uint2 a = __builtin_bit_cast(uint2, lo), c = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(typename Mma<T>::frag, make_uint4(a.x, a.y, c.x, c.y));
+  } else {
+    typename Mma<T>::frag f;
+    const int b = pidx<DTP>(t, l16) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.v[e] = *reinterpret_cast<const float*>(tile + S::off(tok0 + e, b));
+      f.v[4 + e] = half ? 0.f : *reinterpret_cast<const float*>(tile + S::off(tok0 + 4 + e, b));
+    }
+    return f;
+  }
+}
+
+template <typename T, int D, int C, int NW, int CT>
+struct ScanLayout {
+  static constexpr int NT = C / 16;
+  static constexpr int DT = D / 16;
+  static constexpr int E = (int)sizeof(T);
+  static constexpr int threads = 64 * NW;
+  static constexpr int cols = 16 * CT * NW;
+  static constexpr int RBK = D * E;     // K, Q rows
+  static constexpr int RBC = C * E;     // Tb, P rows
+  static constexpr int RBV = cols * E;  // V rows (this workgroup's columns)
+  static constexpr int oK = 0;
+  static constexpr int oQ = oK + C * RBK;
+  static constexpr int oTb = oQ + C * RBK;
+  static constexpr int oP = oTb + C * RBC;
+  static constexpr int oV = oP + C * RBC;
+  static constexpr int oVec = oV + C * RBV;
+  static constexpr int buf = oVec + 16 * C;
+  static constexpr int PADO = 16 / E;
+  static constexpr int LDO = cols + PADO;  // O staging rows [token][cols]
+  static constexpr int obuf = C * LDO * E;
+  // O leaves through the staging tiles when they fit in LDS (every bf16
+  // shape); otherwise (large fp32 tiles) each lane stores its elements.
+  static constexpr bool stage_o = 2 * buf + 2 * obuf <= 160 * 1024;
+  static constexpr int bytes = 2 * buf + (stage_o ? 2 * obuf : 0);
+  static constexpr int NOV = (C * cols / 8 + threads - 1) / threads;  // O vectors per thread
+};
+
+template <typename T, int D, int C, int NW, int CT>
+__global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const unsigned char* ws, int nwg) {
+  using L = ScanLayout<T, D, C, NW, CT>;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int NT = L::NT, DT = L::DT;
+  constexpr int NB = D / L::cols;  // column blocks per V head
+  // Two chunk buffers and two O staging tiles as separate LDS objects: the
+  // compiler can then see that the next chunk's direct-to-LDS loads never
+  // touch what the current chunk reads, and inserts no wait for them.
+  __shared__ __align__(16) unsigned char sb0[L::buf];
+  __shared__ __align__(16) unsigned char sb1[L::buf];
+  __shared__ __align__(16) unsigned char so0[L::stage_o ? L::obuf : 16];
+  __shared__ __align__(16) unsigned char so1[L::stage_o ? L::obuf : 16];
+
+  // XCD-aware order: hardware places consecutive workgroups on consecutive
+  // XCDs, so logical neighbours (the blocks and V heads that read the same K
+  // and Q) are spread as (id % 8) * per_xcd + id / 8 to share an L2.
+  const int per_xcd = (nwg + 7) / 8;
+  const int wid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wid >= nwg) return;
+  const int blk = wid % NB;
+  const int h = (wid / NB) % p.h_v;
+  const int n = wid / (NB * p.h_v);
+  const int hq = h / (p.h_v / p.h_qk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  // this lane's column in the workgroup block for column tile ct
+  auto lcol = [&](int ct) { return (wave * CT + ct) * 16 + l16; };
+
+  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
+  const unsigned char* recs = ws + off_bytes(p.n_seqs);
+  const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
+  const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
+  const int c0 = off[n];
+  const int nch = off[n + 1] - c0;
+
+  const unsigned char* qg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + (int64_t)hq * D);
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + (int64_t)hq * D);
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + (int64_t)h * D +
+                                                                   blk * L::cols);
+  const int64_t o_stride = (int64_t)p.h_v * D;
+  T* og_blk = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols;
+
+  // direct-to-LDS loads of chunk c into `b`; rows past a partial chunk
+  // re-read its last row: they only ever meet zero columns of Tb and zero
+  // rows of U (beta = 0 there), so any finite values are harmless
+  auto issue = [&](int c, unsigned char* b) {
+    const int64_t t0 = seq_start + (int64_t)c * C;
+    const int Lc = (int)min((int64_t)C, seq_end - t0);
+    const unsigned char* rec = recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes;
+    dma_tile<L::RBK, C, NW>(b + L::oK, kg + t0 * p.k_stride * L::E, p.k_stride * L::E, Lc, wave, lane);
+    dma_tile<L::RBK, C, NW>(b + L::oQ, qg + t0 * p.q_stride * L::E, p.q_stride * L::E, Lc, wave, lane);
+    dma_tile<L::RBC, C, NW>(b + L::oTb, rec, L::RBC, C, wave, lane);
+    dma_tile<L::RBC, C, NW>(b + L::oP, rec + Rec<T, C>::mat, L::RBC, C, wave, lane);
+    dma_tile<L::RBV, C, NW>(b + L::oV, vg + t0 * p.v_stride * L::E, p.v_stride * L::E, Lc, wave, lane);
+    dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, wave, lane);
+  };
+  // O rows of chunk c leave the staging tile in 16-byte row pieces
+  auto store_o = [&](const unsigned char* so, int64_t t0, int Lc) {
+    const T* Ot = reinterpret_cast<const T*>(so);
+#pragma unroll
+    for (int i = 0; i < L::NOV; ++i) {
+      const int e = tid + i * L::threads;
+      const int r = e / (L::cols / 8), c8 = (e % (L::cols / 8)) * 8;
+      if (e < C * L::cols / 8 && r < Lc)
+        Raw8<T>::load(Ot + r * L::LDO + c8).store(og_blk + (t0 + r) * o_stride + c8);
+    }
+  };
+  // per-token scalars of tile mt, rows 4g..4g+3: four consecutive tokens
+  auto vec4 = [&](const float* v, int mt) { return *reinterpret_cast<const float4*>(v + pidx<NT>(mt, 4 * g4)); };
+
+  // state S^T (d_k x 16 columns per column tile) in DT accumulator tiles;
+  // row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
+  f32x4 st[CT][DT];
+  const size_t sbase = ((size_t)n * p.h_v + h) * D * D + (size_t)(blk * L::cols) * D;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      st[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p.initial_state) {
+        const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + sbase + (size_t)lcol(ct) * D +
+                                                           pidx<DT>(dt, 4 * g4));
+        st[ct][dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+      }
+    }
+
+  // one chunk: store the previous chunk's O, start the next chunk's loads
+  // into `nxt`, compute this chunk from `cur`, stage its O in `ocur`
+  auto step = [&](int c, const unsigned char* cur, unsigned char* nxt, unsigned char* ocur,
+                  const unsigned char* oprev) {
+    const int64_t t0 = seq_start + (int64_t)c * C;
+    const unsigned char* K_t = cur + L::oK;
+    const unsigned char* Q_t = cur + L::oQ;
+    const unsigned char* Tb_t = cur + L::oTb;
+    const unsigned char* P_t = cur + L::oP;
+    const unsigned char* V_t = cur + L::oV;
+    const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
+    if constexpr (L::stage_o) {
+      if (c > 0) store_o(oprev, t0 - C, C);
+    }
+    if (c + 1 < nch) issue(c + 1, nxt);
+    constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
+    constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
+
+    // X1 = K S^T, Y = Q S^T: each K/Q fragment feeds every column tile
+    f32x4 x1[CT][NT], yq[CT][NT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) { x1[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; yq[ct][mt] = x1[ct][mt]; }
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const typename M::frag bs = M::acc(st[2 * s], st[2 * s + 1]);
+      frag bs[CT], ak[NT], aq[NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(st[ct][2 * s], st[ct][2 * s + 1]);
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
-        const int row = (mt * 16 + l16) * L::LDK + 32 * s;
-        M::mma(x1[mt], M::lds(K_s + row, g4, false), bs, false);
-        M::mma(yq[mt], M::lds(Q_s + row, g4, false), bs, false);
+        const int row = pidx<NT>(mt, l16);
+        ak[mt] = frag_row<T, L::RBK>(K_t, row, 32 * s + 8 * g4, false);
+        aq[mt] = frag_row<T, L::RBK>(Q_t, row, 32 * s + 8 * g4, false);
       }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          M::mma(x1[ct][mt], ak[mt], bs[ct], false);
+          M::mma(yq[ct][mt], aq[mt], bs[ct], false);
+        }
     }
     // R = V - diag(gamma rk) X1   (in place in x1)
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+    for (int mt = 0; mt < NT; ++mt) {
+      const float4 vq = vec4(vec, mt);
+      const float vs[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * g4 + i;
-        const float vv = (r < Lc && col_ok) ? to_f32(vg[(t0 + r) * p.v_stride + col]) : 0.f;
-        x1[mt][i] = vv - grk_s[r] * x1[mt][i];
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = pidx<NT>(mt, 4 * g4 + i);
+          const float vv = to_f32(*reinterpret_cast<const T*>(V_t + Swz<L::RBV>::off(r, lcol(ct) * L::E)));
+          x1[ct][mt][i] = vv - vs[i] * x1[ct][mt][i];
+        }
+    }
     // U = Tb R
-    f32x4 u[NT];
+    f32x4 u[CT][NT];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) u[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int s = 0; s < (NT + 1) / 2; ++s) {
-      const bool half = 2 * s + 1 >= NT;
-      const typename M::frag bs = M::acc(x1[2 * s], tile_hi<NT>(x1, s));
+      for (int mt = 0; mt < NT; ++mt) u[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag bs[CT], at[NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(x1[ct][2 * s], tile_hi<NT>(x1[ct], s));
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
-        M::mma(u[mt], M::lds(Tb_s + (mt * 16 + l16) * L::LDC + 32 * s, g4, half), bs, half);
+        at[mt] = frag_row<T, L::RBC>(Tb_t, pidx<NT>(mt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) M::mma(u[ct][mt], at[mt], bs[ct], HALF);
     }
     // O = diag(scale gamma rq) Y + P U
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) x1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int s = 0; s < (NT + 1) / 2; ++s) {
-      const bool half = 2 * s + 1 >= NT;
-      const typename M::frag bs = M::acc(u[2 * s], tile_hi<NT>(u, s));
+      for (int mt = 0; mt < NT; ++mt) x1[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag bs[CT], ap[NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(u[ct][2 * s], tile_hi<NT>(u[ct], s));
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
-        M::mma(x1[mt], M::lds(P_s + (mt * 16 + l16) * L::LDC + 32 * s, g4, half), bs, half);
+        ap[mt] = frag_row<T, L::RBC>(P_t, pidx<NT>(mt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) M::mma(x1[ct][mt], ap[mt], bs[ct], HALF);
     }
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+    for (int mt = 0; mt < NT; ++mt) {
+      const float4 vq = vec4(vec + C, mt);
+      const float vs[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * g4 + i;
-        if (r < Lc && col_ok)
-          og[(t0 + r) * o_stride + col] = from_f32<T>(x1[mt][i] + grq_s[r] * yq[mt][i]);
+      for (int ct = 0; ct < CT; ++ct) {
+        if constexpr (L::stage_o) {
+          T* Ot = reinterpret_cast<T*>(ocur) + lcol(ct);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Ot[pidx<NT>(mt, 4 * g4 + i) * L::LDO] = from_f32<T>(x1[ct][mt][i] + vs[i] * yq[ct][mt][i]);
+        } else {
+          const int Lc = (int)min((int64_t)C, seq_end - t0);
+          T* og = og_blk + lcol(ct);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = pidx<NT>(mt, 4 * g4 + i);
+            if (r < Lc) og[(t0 + r) * o_stride] = from_f32<T>(x1[ct][mt][i] + vs[i] * yq[ct][mt][i]);
+          }
+        }
       }
-    // S^T <- gamma_last S^T + K^T diag(e rk) U
-    const float gl = misc[0];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[mt][i] *= erk_s[mt * 16 + 4 * g4 + i];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st[dt] *= gl;
-#pragma unroll
-    for (int s = 0; s < (NT + 1) / 2; ++s) {
-      const bool half = 2 * s + 1 >= NT;
-      const typename M::frag bs = M::acc(u[2 * s], tile_hi<NT>(u, s));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        M::mma(st[dt], M::lds(KT_s + (dt * 16 + l16) * L::LDC + 32 * s, g4, half), bs, half);
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    // S^T <- gamma_last S^T + K^T diag(e rk) U: each K^T fragment feeds every column tile
+    const float gl = vec[3 * C];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      const float4 vq = vec4(vec + 2 * C, mt);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        u[ct][mt][0] *= vq.x; u[ct][mt][1] *= vq.y; u[ct][mt][2] *= vq.z; u[ct][mt][3] *= vq.w;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st[ct][dt] *= gl;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag bs[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(u[ct][2 * s], tile_hi<NT>(u[ct], s));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const frag ak = frag_kt<T, L::RBK, DT>(K_t, dt, HALF ? 4 * g4 : 32 * s + 8 * g4, l16, HALF);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], ak, bs[ct], HALF);
+      }
+    }
+    __syncthreads();  // waits for the next chunk's loads; frees `cur`
+  };
+
+  if (nch > 0) issue(0, sb0);
+  __syncthreads();  // waits for the loads of chunk 0
+  for (int c = 0; c < nch; c += 2) {
+    step(c, sb0, sb1, so0, so1);
+    if (c + 1 < nch) step(c + 1, sb1, sb0, so1, so0);
+  }
+  if (L::stage_o && nch > 0) {
+    const int64_t tl = seq_start + (int64_t)(nch - 1) * C;
+    store_o(((nch - 1) & 1) ? so1 : so0, tl, (int)(seq_end - tl));
   }
 
-  if (p.final_state && col_ok) {
+  if (p.final_state) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(p.final_state + sbase + (size_t)col * D + dt * 16 + 4 * g4) =
-          make_float4(st[dt][0], st[dt][1], st[dt][2], st[dt][3]);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(p.final_state + sbase + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4)) =
+            make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
   }
+}
+
+// ------------------------------------------------------------------ host
+constexpr int kLdsMax = 160 * 1024;
+// scan workgroup shape: kScanWaves waves, each owning kScanTiles 16-column
+// tiles of the state (64 d_v columns per workgroup)
+#ifndef GDN_SCAN_WAVES
+#define GDN_SCAN_WAVES 4
+#endif
+#ifndef GDN_SCAN_TILES
+#define GDN_SCAN_TILES 1
+#endif
+constexpr int kScanWaves = GDN_SCAN_WAVES;
+constexpr int kScanTiles = GDN_SCAN_TILES;
+
+template <typename T, int D, int C>
+constexpr bool fits() {
+  return PrepLayout<T, D, C>::bytes <= kLdsMax && ScanLayout<T, D, C, kScanWaves, kScanTiles>::bytes <= kLdsMax;
 }
 
 template <typename T, int D, int C>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
-  using L = Layout<T, D, C>;
-  if constexpr (L::bytes > 160 * 1024) {
+  if constexpr (!fits<T, D, C>()) {
     return hipErrorInvalidConfiguration;  // rejected by prefill_supported() first
   } else {
-    auto kern = prefill_kernel<T, D, C>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
+    constexpr int NW = kScanWaves, CT = kScanTiles;
+    using PL = PrepLayout<T, D, C>;
+    using SL = ScanLayout<T, D, C, NW, CT>;
+    unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs,
+                       p.total_tokens, C, reinterpret_cast<int32_t*>(ws));
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nblk = D / kCols > 0 ? D / kCols : 1;
-    const unsigned blocks = (unsigned)((int64_t)p.n_seqs * p.h_v * nblk);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), L::bytes, stream, p);
+    auto prep = prep_kernel<T, D, C>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, PL::bytes);
+    if (e != hipSuccess) return e;
+    if (p.total_tokens > 0) {
+      const int64_t mc = max_chunks(p.total_tokens, p.n_seqs, C);
+      hipLaunchKernelGGL(prep, dim3((unsigned)mc, (unsigned)p.h_qk), dim3(kPrepThreads), PL::bytes,
+                         stream, p, ws);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int nwg = p.n_seqs * p.h_v * (D / SL::cols);
+    const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
+    hipLaunchKernelGGL((scan_kernel<T, D, C, NW, CT>), dim3(grid), dim3(SL::threads), 0, stream, p,
+                       static_cast<const unsigned char*>(ws), nwg);
     return hipGetLastError();
   }
-}
-
-template <typename T, int D>
-constexpr int lds_bytes(int chunk) {
-  return chunk == 16 ? Layout<T, D, 16>::bytes : chunk == 32 ? Layout<T, D, 32>::bytes
-                                                             : Layout<T, D, 64>::bytes;
 }
 
 template <typename T, int D>
@@ -432,14 +910,27 @@ hipError_t launch_c(const PrefillParams& p, hipStream_t stream) {
   }
 }
 
+template <typename T, int D>
+bool fits_c(int chunk) {
+  return chunk == 16 ? fits<T, D, 16>() : chunk == 32 ? fits<T, D, 32>() : fits<T, D, 64>();
+}
+
+template <typename T>
+size_t rec_c(int chunk) {
+  return chunk == 16 ? Rec<T, 16>::bytes : chunk == 32 ? Rec<T, 32>::bytes : Rec<T, 64>::bytes;
+}
+
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t, int, int, int, int, int) { return 0; }
+size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int chunk) {
+  if (n_seqs < 1 || total_tokens < 0 || h_v < 1 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
+  const size_t rec = io_dtype == 1 ? rec_c<__bf16>(chunk) : rec_c<float>(chunk);
+  return off_bytes(n_seqs) + (size_t)max_chunks(total_tokens, n_seqs, chunk) * h_v * rec;
+}
 
 bool prefill_supported(int io_dtype, int d, int chunk) {
-  const int b = io_dtype == 1 ? (d == 128 ? lds_bytes<__bf16, 128>(chunk) : lds_bytes<__bf16, 64>(chunk))
-                              : (d == 128 ? lds_bytes<float, 128>(chunk) : lds_bytes<float, 64>(chunk));
-  return b <= 160 * 1024;
+  if (io_dtype == 1) return d == 128 ? fits_c<__bf16, 128>(chunk) : fits_c<__bf16, 64>(chunk);
+  return d == 128 ? fits_c<float, 128>(chunk) : fits_c<float, 64>(chunk);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream) {

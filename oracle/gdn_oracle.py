@@ -42,6 +42,7 @@ __all__ = [
     "split_qkv",
     "gated_delta_rule",
     "gdn_layer",
+    "layer_channels",
     "decode_step",
     "chunked_gated_delta_rule",
     "unrolled_product_form",
@@ -168,34 +169,45 @@ def gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scal
     return o, S_all
 
 
-def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv_state=None,
-              initial_state=None, cu_seqlens=None, scale=1.0, activation="silu", l2norm_qk=True,
-              v_heads=None):
-    """The whole token mixer for packed sequences: conv(+SiLU) -> split -> recurrence.
-
-    With v_heads given, only the channels those heads read are convolved (the
-    conv is depthwise, so each channel is independent).
-    returns o, final_state, new_conv_state (the latter over the channels used,
-    [N, C_used, W-1], channel order q-heads used | k-heads used | v-heads used).
-    """
-    x = _f64(x)
+def layer_channels(h_qk, d_k, h_v, d_v, v_heads=None):
+    """Indices of the conv channels that the given V heads read, ordered
+    [q of their QK heads | k of their QK heads | v of the heads]."""
     grp = h_v // h_qk
     heads = np.arange(h_v) if v_heads is None else np.asarray(v_heads, dtype=np.int64)
     qks = np.unique(heads // grp)
     nq = h_qk * d_k
-    ch = np.concatenate([
+    return np.concatenate([
         (qks[:, None] * d_k + np.arange(d_k)).reshape(-1),
         nq + (qks[:, None] * d_k + np.arange(d_k)).reshape(-1),
         2 * nq + (heads[:, None] * d_v + np.arange(d_v)).reshape(-1),
     ])
+
+
+def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv_state=None,
+              initial_state=None, cu_seqlens=None, scale=1.0, activation="silu", l2norm_qk=True,
+              v_heads=None, x_is_selected=False):
+    """The whole token mixer for packed sequences: conv(+SiLU) -> split -> recurrence.
+
+    With v_heads given, only the channels those heads read are convolved (the
+    conv is depthwise, so each channel is independent); x_is_selected=True
+    means x, conv_weight, conv_bias and conv_state already hold just those
+    channels, in layer_channels() order.
+    returns o, final_state, new_conv_state (the latter over the channels used,
+    [N, C_used, W-1], in layer_channels() order).
+    """
+    grp = h_v // h_qk
+    heads = np.arange(h_v) if v_heads is None else np.asarray(v_heads, dtype=np.int64)
+    qks = np.unique(heads // grp)
+    ch = slice(None) if x_is_selected else layer_channels(h_qk, d_k, h_v, d_v, v_heads)
+    x = _f64(x)[:, ch]
     cs = None if conv_state is None else _f64(conv_state)[:, ch]
     bias = None if conv_bias is None else _f64(conv_bias)[ch]
-    y, new_cs = causal_conv1d(x[:, ch], _f64(conv_weight)[ch], bias, cs, cu_seqlens, activation)
+    y, new_cs = causal_conv1d(x, _f64(conv_weight)[ch], bias, cs, cu_seqlens, activation)
     nqs = len(qks) * d_k
     q = y[:, :nqs].reshape(-1, len(qks), d_k)
     k = y[:, nqs:2 * nqs].reshape(-1, len(qks), d_k)
     vv = y[:, 2 * nqs:].reshape(-1, len(heads), d_v)
-    # re-index: local V head i reads local QK head position of heads[i]//grp
+    # re-index: local V head i reads the local slot of QK head heads[i] // grp
     local_qk = np.searchsorted(qks, heads // grp)
     qh = q[:, local_qk]
     kh = k[:, local_qk]

@@ -111,8 +111,18 @@ def test_conv_and_decode_validation():
     assert L.gdn_decode_step(ctypes.byref(d), None) == 3
 
 
+def test_prefill_requires_workspace():
+    st, msg = _prefill()
+    assert st == 4 and "workspace" in msg
+    st, msg = _prefill(workspace=0x10000, workspace_bytes=16)
+    assert st == 4
+
+
 def test_workspace_size_query():
     a = gdn.PrefillArgs(struct_size=ctypes.sizeof(gdn.PrefillArgs), n_seqs=1, total_tokens=1024, h_qk=16,
                         h_v=48, d_k=128, d_v=128, chunk=64)
-    assert gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a)) >= 0
+    a.io_dtype = 1
+    n = gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a))
+    # offsets (256 B) + (1024/64 + 1) chunks x 48 heads x (Tb + P bf16 + 4 fp32 rows)
+    assert n == 256 + 17 * 48 * (2 * 64 * 64 * 2 + 16 * 64)
     assert gdn.lib().gdn_status_string(5) == b"GDN_ERR_HIP"

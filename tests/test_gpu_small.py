@@ -112,7 +112,7 @@ def _prefill_case(T, hq, hv, d, io, seed, lens=None, s0=True):
 
 
 @pytest.mark.parametrize("io,d,chunk", [("bf16", 128, 64), ("bf16", 128, 32), ("bf16", 128, 16),
-                                        ("bf16", 64, 64), ("f32", 64, 16), ("f32", 64, 64),
+                                        ("bf16", 64, 64), ("f32", 64, 16), ("f32", 64, 32),
                                         ("f32", 128, 32)])
 def test_prefill_ragged(io, d, chunk):
     T, hq, hv = 201, 2, 6
@@ -143,7 +143,8 @@ def test_prefill_varlen_degenerate_lengths(io):
     T, hq, hv, d = sum(lens), 1, 3, 64
     q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, io, 30, lens)
     cu = gdn_inputs.cu_from_lengths(lens)
-    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0), cu_seqlens=dev(cu), chunk=64)
+    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0), cu_seqlens=dev(cu),
+                       chunk=64 if io == "bf16" else 32)
     ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0),
                                   cu_seqlens=cu.numpy())
     tol = TOL_BF16 if io == "bf16" else TOL_F32
@@ -184,11 +185,11 @@ def test_split_prefill_and_decode_continuation():
     q, k, v, g, b, S0 = _prefill_case(T + 1, hq, hv, d, "f32", 60)
     D = [dev(t) for t in (q, k, v, g, b)]
     S0d = dev(S0)
-    o, S = gdn.prefill(*[t[:T] for t in D], S0d, chunk=64)
-    oa, Sa = gdn.prefill(*[t[:T1] for t in D], S0d, chunk=64)
-    ob, Sb = gdn.prefill(*[t[T1:T] for t in D], Sa, chunk=64)
+    o, S = gdn.prefill(*[t[:T] for t in D], S0d, chunk=32)
+    oa, Sa = gdn.prefill(*[t[:T1] for t in D], S0d, chunk=32)
+    ob, Sb = gdn.prefill(*[t[T1:T] for t in D], Sa, chunk=32)
     assert rel_err(torch.cat([oa, ob]), np64(o)) < 1e-5 and rel_err(Sb, np64(S)) < 1e-5
-    o1, S1 = gdn.prefill(*D, S0d, chunk=64)
+    o1, S1 = gdn.prefill(*D, S0d, chunk=32)
     x = torch.cat([D[0][T].reshape(1, -1), D[1][T].reshape(1, -1), D[2][T].reshape(1, -1)], dim=1)
     Sd = S.clone()
     od = gdn.decode_step(x.contiguous(), D[3][T:].contiguous(), D[4][T:].contiguous(), Sd, hq, hv, d)
