@@ -21,15 +21,22 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // row groups whose loads are in flight together
+#ifndef GDN_DECODE_UNROLL
+#define GDN_DECODE_UNROLL 8
+#endif
+// row groups of 16 rows whose loads a wave keeps in flight together
+constexpr int kConvBatch = 4;  // conv channels per thread whose loads issue together
+template <int D>
+constexpr int kUnroll = GDN_DECODE_UNROLL * 16 <= D ? GDN_DECODE_UNROLL : D / 16;
 
+// State rows are read and written once per step: streaming accesses.
 template <int EPL, typename T>
 __device__ __forceinline__ void load_row(const T* p, float (&v)[EPL]) {
-  if constexpr (EPL == 8) load8(p, v); else load4(p, v);
+  if constexpr (EPL == 8) load8_stream(p, v); else load4_stream(p, v);
 }
 template <int EPL, typename T>
 __device__ __forceinline__ void store_row(T* p, const float (&v)[EPL]) {
-  if constexpr (EPL == 8) store8(p, v); else store4(p, v);
+  if constexpr (EPL == 8) store8_stream(p, v); else store4_stream(p, v);
 }
 
 template <typename IoT, typename StT, int D>
@@ -51,41 +58,89 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   float* s_be = s_al + grp;        // [grp] beta
   float* s_sc = s_be + grp;        // rq, rk, k.q
 
-  // ---- 1. conv step + activation over this workgroup's channels
+  // The state stream does not depend on the conv step: the first pass of
+  // state loads is issued now so that its latency overlaps steps 1 and 2.
+  // A pass covers 16 * U consecutive rows, which divides rows = grp * D:
+  // every row group of a pass exists, so its loads issue back to back with
+  // no branch between them.
+  constexpr int U = kUnroll<D>;
+  static_assert(D % (16 * U) == 0, "rows per pass must divide grp * D");
+  const int rows = grp * D;
+  const int sub = lane & 15;
+  StT* S = reinterpret_cast<StT*>(p.state) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D * D +
+           sub * EPL;
+  int rb = wave * 4 + (lane >> 4);
+  float sv[U][EPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * u) * D, sv[u]);
+
+  // ---- 1. conv step + activation over this workgroup's channels.  A thread
+  // handles up to kConvBatch channels at a time and issues every load of the
+  // batch (input, taps, history, bias) before using any of them; out-of-range
+  // slots and taps load a clamped, valid address and are discarded.
   const int64_t C = (int64_t)(2 * p.h_qk + p.h_v) * D;
   const IoT* x = reinterpret_cast<const IoT*>(p.x) + (int64_t)n * C;
   const int nloc = (2 + grp) * D;
-  const int W = p.width;
-  for (int cl = tid; cl < nloc; cl += kThreads) {
-    int64_t c;
-    if (cl < D) c = (int64_t)hq * D + cl;
-    else if (cl < 2 * D) c = (int64_t)(p.h_qk + hq) * D + (cl - D);
-    else c = (int64_t)2 * p.h_qk * D + (int64_t)hq * grp * D + (cl - 2 * D);
-    const IoT xr = x[c];
-    float y = to_f32(xr);
-    if (p.conv_weight) {
-      const IoT* w = reinterpret_cast<const IoT*>(p.conv_weight) + c * W;
-      IoT* st = reinterpret_cast<IoT*>(p.conv_state) + ((int64_t)n * C + c) * (W - 1);
-      IoT h0 = st[0];
-      IoT h1 = W > 2 ? st[1] : h0;
-      IoT h2 = W > 3 ? st[2] : h0;
-      float acc = p.conv_bias ? to_f32(reinterpret_cast<const IoT*>(p.conv_bias)[c]) : 0.f;
-      acc += to_f32(w[0]) * to_f32(h0);
-      if (W > 2) acc += to_f32(w[1]) * to_f32(h1);
-      if (W > 3) acc += to_f32(w[2]) * to_f32(h2);
-      acc += to_f32(w[W - 1]) * y;
-      // shift the new input in: the state keeps the last W-1 inputs, oldest first
-      if (W == 2) { st[0] = xr; }
-      else if (W == 3) { st[0] = h1; st[1] = xr; }
-      else { st[0] = h1; st[1] = h2; st[2] = xr; }
-      y = p.act ? silu(acc) : acc;
+  const int W = p.width;  // 2..4
+  const int64_t gi = (int64_t)n * p.h_v + (int64_t)hq * grp + min(tid, grp - 1);
+  const float g_in = p.g[gi], b_in = p.beta[gi];  // stored to LDS after the conv loads
+  const IoT* wt = reinterpret_cast<const IoT*>(p.conv_weight);
+  const IoT* bias = reinterpret_cast<const IoT*>(p.conv_bias);
+  IoT* cst = reinterpret_cast<IoT*>(p.conv_state);
+  auto conv_batch = [&](int base) {
+    int64_t cc[kConvBatch];
+    IoT xr[kConvBatch], wv[kConvBatch][4], hv[kConvBatch][3], bv[kConvBatch];
+#pragma unroll
+    for (int j = 0; j < kConvBatch; ++j) {
+      const int cl = min(base + j * kThreads + tid, nloc - 1);
+      int64_t c;
+      if (cl < D) c = (int64_t)hq * D + cl;
+      else if (cl < 2 * D) c = (int64_t)(p.h_qk + hq) * D + (cl - D);
+      else c = (int64_t)2 * p.h_qk * D + (int64_t)hq * grp * D + (cl - 2 * D);
+      cc[j] = c;
+      xr[j] = x[c];
+      // without a conv (or a bias) the loads read x[c] instead and are unused:
+      // no branch separates the loads of a batch
+      const IoT* wp = wt ? wt + c * W : x + c;
+      const IoT* st = wt ? cst + ((int64_t)n * C + c) * (W - 1) : x + c;
+      const int wm = wt ? W - 1 : 0, hm = wt ? W - 2 : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[j][i] = wp[min(i, wm)];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) hv[j][i] = st[min(i, hm)];
+      bv[j] = bias ? bias[c] : x[c];
     }
-    s_q[cl] = y;
-  }
+#pragma unroll
+    for (int j = 0; j < kConvBatch; ++j) {
+      const int cl = base + j * kThreads + tid;
+      if (cl >= nloc) continue;
+      float y = to_f32(xr[j]);
+      if (wt) {
+        // taps 0..W-2 meet the history (oldest first), tap W-1 the new input
+        float acc = bias ? to_f32(bv[j]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xi = i < W - 1 ? to_f32(hv[j][min(i, 2)]) : (i == W - 1 ? y : 0.f);
+          acc += to_f32(wv[j][i]) * xi;
+        }
+        // shift the new input in: the history keeps the last W-1 inputs
+        IoT* st = cst + ((int64_t)n * C + cc[j]) * (W - 1);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (i < W - 1) st[i] = i + 1 < W - 1 ? hv[j][min(i + 1, 2)] : xr[j];
+        y = p.act ? silu(acc) : acc;
+      }
+      s_q[cl] = y;
+    }
+  };
+  // the first batch is peeled off the loop: inside a loop the compiler's wait
+  // counts merge with the previous iteration and would stall on the state
+  // loads issued above
+  conv_batch(0);
+  for (int base = kConvBatch * kThreads; base < nloc; base += kConvBatch * kThreads) conv_batch(base);
   if (tid < grp) {
-    const int64_t gi = (int64_t)n * p.h_v + (int64_t)hq * grp + tid;
-    s_al[tid] = __expf(p.g[gi]);
-    s_be[tid] = p.beta[gi];
+    s_al[tid] = __expf(g_in);
+    s_be[tid] = b_in;
   }
   __syncthreads();
 
@@ -107,42 +162,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   // ---- 3. stream the state rows once
   const float rq = s_sc[0], rk = s_sc[1], kq = s_sc[2];
-  const int sub = lane & 15;
   float kf[EPL], qf[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     kf[e] = s_k[sub * EPL + e] * rk;
     qf[e] = s_q[sub * EPL + e] * rq;
   }
-  StT* S = reinterpret_cast<StT*>(p.state) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D * D +
-           sub * EPL;
-  const int rows = grp * D;  // a multiple of 16
-  for (int rb = wave * 4 + (lane >> 4); rb < rows; rb += 16 * kUnroll) {
-    float sv[kUnroll][EPL];
+  while (true) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int r = rb + 16 * u;
-      if (r < rows) load_row<EPL>(S + (int64_t)r * D, sv[u]);
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) { a += sv[u][e] * kf[e]; b += sv[u][e] * qf[e]; }
+      a = row16_sum(a);
+      b = row16_sum(b);
+      const int hl = r / D;
+      const float al = s_al[hl];
+      const float dl = s_be[hl] * (s_v[r] - al * a);
+      float nv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
+      store_row<EPL>(S + (int64_t)r * D, nv);
+      if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
     }
+    rb += 16 * U;
+    if (rb >= rows) break;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = rb + 16 * u;
-      if (r < rows) {  // uniform across each wave (rows % 16 == 0)
-        float a = 0.f, b = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) { a += sv[u][e] * kf[e]; b += sv[u][e] * qf[e]; }
-        a = row16_sum(a);
-        b = row16_sum(b);
-        const int hl = r / D;
-        const float al = s_al[hl];
-        const float dl = s_be[hl] * (s_v[r] - al * a);
-        float nv[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
-        store_row<EPL>(S + (int64_t)r * D, nv);
-        if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
-      }
-    }
+    for (int u = 0; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * u) * D, sv[u]);
   }
   __syncthreads();
   IoT* o = reinterpret_cast<IoT*>(p.o) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D;

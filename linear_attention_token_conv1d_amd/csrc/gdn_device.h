@@ -76,6 +76,60 @@ __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming variants for data touched once per launch (the decode state):
+// nontemporal loads/stores, so the stream does not evict reusable lines.
+typedef unsigned gdn_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load8_stream(const __bf16* p, float (&v)[8]) {
+  const gdn_u4 w = __builtin_nontemporal_load(reinterpret_cast<const gdn_u4*>(p));
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void load8_stream(const float* p, float (&v)[8]) {
+  const gdn_u4 a = __builtin_nontemporal_load(reinterpret_cast<const gdn_u4*>(p));
+  const gdn_u4 b = __builtin_nontemporal_load(reinterpret_cast<const gdn_u4*>(p) + 1);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+  v[3] = __uint_as_float(a.w); v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+  v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ void store8_stream(__bf16* p, const float (&v)[8]) {
+  gdn_u4 w;
+  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
+  __builtin_nontemporal_store(w, reinterpret_cast<gdn_u4*>(p));
+}
+__device__ __forceinline__ void store8_stream(float* p, const float (&v)[8]) {
+  gdn_u4 a, b;
+  a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]); a.z = __float_as_uint(v[2]);
+  a.w = __float_as_uint(v[3]); b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]);
+  b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
+  __builtin_nontemporal_store(a, reinterpret_cast<gdn_u4*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<gdn_u4*>(p) + 1);
+}
+__device__ __forceinline__ void load4_stream(const __bf16* p, float (&v)[4]) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 w = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+}
+__device__ __forceinline__ void load4_stream(const float* p, float (&v)[4]) {
+  const gdn_u4 a = __builtin_nontemporal_load(reinterpret_cast<const gdn_u4*>(p));
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z);
+  v[3] = __uint_as_float(a.w);
+}
+__device__ __forceinline__ void store4_stream(__bf16* p, const float (&v)[4]) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  u2 w;
+  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+  __builtin_nontemporal_store(w, reinterpret_cast<u2*>(p));
+}
+__device__ __forceinline__ void store4_stream(float* p, const float (&v)[4]) {
+  gdn_u4 a;
+  a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]); a.z = __float_as_uint(v[2]);
+  a.w = __float_as_uint(v[3]);
+  __builtin_nontemporal_store(a, reinterpret_cast<gdn_u4*>(p));
+}
+
 // ---------------------------------------------------------- reductions
 // DPP controls (GCN/CDNA encoding).
 enum : int {

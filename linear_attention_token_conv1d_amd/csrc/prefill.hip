@@ -17,10 +17,10 @@
 //
 // Three launches on the caller's stream:
 //  plan  one workgroup: chunk offsets of every packed sequence (workspace).
-//  prep  one workgroup per (chunk, QK head), all chunks in parallel: row norms,
-//        the two Gram matrices (MFMA) once per QK head, then per V head of the
-//        group the decay masks, the UT solve T = (I + A)^-1 (fp32) and the
-//        chunk operands Tb, P and the per-token scalars, written to workspace.
+//  prep  one workgroup per (chunk, V head), all chunks in parallel: row norms,
+//        the two Gram matrices (MFMA), the decay masks, the UT solve
+//        T = (I + A)^-1 (fp32) and the chunk operands Tb, P and the per-token
+//        scalars, written to workspace.
 //  scan  one workgroup per (sequence, V head, block of 16*NW d_v columns),
 //        walking its chunks in order.  Wave w owns 16 d_v columns of the fp32
 //        state S^T (d_k x 16) in MFMA accumulators for the whole sequence.
@@ -198,6 +198,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
 }
 
 // ------------------------------------------------------------------ prep
+// One workgroup per (chunk, V head).  LDS holds the chunk's K and Q rows
+// while the Gram tiles are formed, then the same bytes hold the fp32 A/T
+// work array, the block-product scratch and the staging tile for the bf16
+// outputs, so four workgroups fit on a CU.
 template <typename T, int D, int C>
 struct PrepLayout {
   static constexpr int NT = C / 16;
@@ -206,13 +210,17 @@ struct PrepLayout {
   static constexpr int LDC = C + PADE;
   static constexpr int LDF = C + 4;
   static constexpr int LDZ = 20;
+  // phase 1: K, Q rows
   static constexpr int oK = 0;
   static constexpr int oQ = oK + C * LDK * (int)sizeof(T);
-  static constexpr int oA = oQ + C * LDK * (int)sizeof(T);
+  static constexpr int kq_bytes = oQ + C * LDK * (int)sizeof(T);
+  // phase 2 (same bytes): A/T work array, scratch, output staging
+  static constexpr int oA = 0;
   static constexpr int oZ = oA + C * LDF * 4;
   static constexpr int oSt = oZ + 4 * 16 * LDZ * 4;
-  static constexpr int oVec = oSt + C * LDC * (int)sizeof(T);
-  static constexpr int bytes = oVec + 6 * C * 4;
+  static constexpr int work_bytes = oSt + C * LDC * (int)sizeof(T);
+  static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
+  static constexpr int bytes = oVec + 5 * C * 4;
 };
 
 // Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
@@ -246,25 +254,46 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
   float* rq_s = g_s + 4 * C;
 
   const int32_t* off = reinterpret_cast<const int32_t*>(ws);
-  const int ci = blockIdx.x, hq = blockIdx.y;
+  const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= off[p.n_seqs]) return;
+  const int hq = h / (p.h_v / p.h_qk);
   const int n = owner(off, p.n_seqs, ci);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
   const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
   const int Lc = (int)min((int64_t)C, seq_end - t0);
-  const int grp = p.h_v / p.h_qk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
 
-  // K, Q rows of this chunk and QK head; rows >= Lc are zero
+  // K, Q rows of this chunk and QK head (rows >= Lc zero); g, beta of this V head
   const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
   const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
-  for (int e = tid; e < C * (D / 8); e += kPrepThreads) {
+  // all loads are issued before any is used (rows past the chunk re-read its
+  // last row and are zeroed afterwards), so the workgroup waits on memory once
+  constexpr int NV = (C * (D / 8) + kPrepThreads - 1) / kPrepThreads;
+  R8 kv[NV], qv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = min(tid + i * kPrepThreads, C * (D / 8) - 1);
+    const int r = min(e / (D / 8), Lc - 1), d0 = (e % (D / 8)) * 8;
+    kv[i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
+    qv[i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
+  }
+  const int ti = min(tid, Lc - 1);
+  const float gv = p.g[(t0 + ti) * p.h_v + h];
+  const float bv = p.beta[(t0 + ti) * p.h_v + h];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + i * kPrepThreads;
     const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
-    const bool ok = r < Lc;
-    (ok ? R8::load(kg + (t0 + r) * p.k_stride + d0) : R8::zero()).store(K_s + r * L::LDK + d0);
-    (ok ? R8::load(qg + (t0 + r) * p.q_stride + d0) : R8::zero()).store(Q_s + r * L::LDK + d0);
+    if (e < C * (D / 8)) {
+      (r < Lc ? kv[i] : R8::zero()).store(K_s + r * L::LDK + d0);
+      (r < Lc ? qv[i] : R8::zero()).store(Q_s + r * L::LDK + d0);
+    }
+  }
+  if (tid < C) {
+    g_s[tid] = tid < Lc ? gv : 0.f;
+    b_s[tid] = tid < Lc ? bv : 0.f;
   }
   __syncthreads();
 
@@ -284,7 +313,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
       rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
     }
   }
-
+  // cumulative log-decay over the chunk
+  if (wave == 0) {
+    float G = lane < C ? g_s[lane] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_up(G, o, 64);
+      if (lane >= o) G += u;
+    }
+    if (lane < C) G_s[lane] = G;
+  }
   // raw Gram tiles (lower triangle): jobs [0, NLT) are K K^T, [NLT, 2 NLT) are Q K^T
   f32x4 gram[NJ];
   int jmt[NJ], jnt[NJ];
@@ -304,146 +342,131 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
         M::mma(gram[jj], M::lds(Arow + 32 * s, g4, false), M::lds(Brow + 32 * s, g4, false), false);
     }
   }
+  __syncthreads();  // norms and G published; K, Q are dead from here on
 
-  const size_t rec_base = off_bytes(p.n_seqs);
-  for (int vh = 0; vh < grp; ++vh) {
-    const int h = hq * grp + vh;
-    unsigned char* rec = ws + rec_base + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
-    T* Tb_g = reinterpret_cast<T*>(rec);
-    T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
-    float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
-
-    if (tid < C) {
-      const bool ok = tid < Lc;
-      g_s[tid] = ok ? p.g[(t0 + tid) * p.h_v + h] : 0.f;
-      b_s[tid] = ok ? p.beta[(t0 + tid) * p.h_v + h] : 0.f;
-    }
-    __syncthreads();  // also publishes the norms (first head)
-    if (wave == 0) {
-      float G = lane < C ? g_s[lane] : 0.f;
+  unsigned char* rec = ws + off_bytes(p.n_seqs) + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
+  T* Tb_g = reinterpret_cast<T*>(rec);
+  T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
+  float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
+  if (tid < C) {
+    const float G = G_s[tid], Gl = G_s[Lc - 1], eg = fexp(G);
+    vec_g[tid] = eg * rk_s[tid];
+    vec_g[C + tid] = p.scale * eg * rq_s[tid];
+    vec_g[2 * C + tid] = fexp(Gl - G) * rk_s[tid];
+    vec_g[3 * C + tid] = fexp(Gl);
+  }
+  // decay-masked Gram tiles: A (strict lower, fp32) and P (lower incl. diagonal)
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(G, o, 64);
-        if (lane >= o) G += u;
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int job = wave + 4 * jj;
+    if (job < 2 * NLT) {
+      const bool isP = job >= NLT;
+      const int j = jnt[jj] * 16 + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = jmt[jj] * 16 + 4 * g4 + i;
+        const float dec = (j <= r) ? fexp(G_s[r] - G_s[j]) : 0.f;
+        if (!isP)
+          A_s[r * L::LDF + j] = (j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f;
+        else
+          St[r * L::LDC + j] = from_f32<T>(p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]);
       }
-      if (lane < C) G_s[lane] = G;
-      const float Gl = __shfl(G, Lc - 1, 64);
-      if (lane < C) {
-        const float eg = fexp(G);
-        vec_g[lane] = eg * rk_s[lane];
-        vec_g[C + lane] = p.scale * eg * rq_s[lane];
-        vec_g[2 * C + lane] = fexp(Gl - G) * rk_s[lane];
-        vec_g[3 * C + lane] = fexp(Gl);
+    }
+  }
+  for (int e = tid; e < C * C; e += kPrepThreads) {
+    const int r = e / C, j = e % C;
+    if ((j >> 4) > (r >> 4)) St[r * L::LDC + j] = from_f32<T>(0.f);
+  }
+  __syncthreads();
+
+  // P -> workspace; diagonal 16x16 blocks of T = (I + A)^-1 in place.  Wave b
+  // solves block b by forward substitution: lane 4c+p owns column c and the
+  // rows r = p (mod 4); each row's sum is split over the 4 lanes of a quad.
+  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+    const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
+    R8::load(St + r * L::LDC + j0).store(P_g + r * C + j0);
+  }
+  if (wave < NT) {
+    const int b = wave, c = lane >> 2, part = lane & 3;
+    float xl[4] = {0.f, 0.f, 0.f, 0.f};  // x_{4m+part} of column c
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int j = 4 * m + part;
+        s += (j < r) ? arow[j] * xl[m] : 0.f;
       }
+      s += dpp_f32<DPP_QUAD_1032>(s);
+      s += dpp_f32<DPP_QUAD_2301>(s);
+      const float xr = ((r == c) ? 1.f : 0.f) - s;
+      if (part == (r & 3)) xl[r >> 2] = xr;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A_s[(16 * b + 4 * m + part) * L::LDF + 16 * b + c] = xl[m];
+  }
+  __syncthreads();
+
+  // off-diagonal blocks, in place (each A block is consumed by the
+  // product that produces the T block in its position)
+  auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
+  auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
+  const int rr = tid >> 4, cc = tid & 15;
+  if constexpr (NT >= 2) {
+    // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
+#pragma unroll
+    for (int b = 0; b < NT / 2; ++b) {
+      float z = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
+      Zel(b, rr, cc) = z;
     }
     __syncthreads();
-
-    // decay-masked Gram tiles: A (strict lower, fp32) and P (lower incl. diagonal)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int job = wave + 4 * jj;
-      if (job < 2 * NLT) {
-        const bool isP = job >= NLT;
-        const int j = jnt[jj] * 16 + l16;
+    for (int b = 0; b < NT / 2; ++b) {
+      float t = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = jmt[jj] * 16 + 4 * g4 + i;
-          const float dec = (j <= r) ? fexp(G_s[r] - G_s[j]) : 0.f;
-          if (!isP)
-            A_s[r * L::LDF + j] = (j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f;
-          else
-            St[r * L::LDC + j] = from_f32<T>(p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]);
-        }
-      }
-    }
-    for (int e = tid; e < C * C; e += kPrepThreads) {
-      const int r = e / C, j = e % C;
-      if ((j >> 4) > (r >> 4)) St[r * L::LDC + j] = from_f32<T>(0.f);
+      for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
+      Ael(2 * b + 1, 2 * b, rr, cc) = t;
     }
     __syncthreads();
-
-    // P -> workspace; diagonal 16x16 blocks of T = (I + A)^-1 in place
-    for (int e = tid; e < C * C / 8; e += kPrepThreads) {
-      const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
-      R8::load(St + r * L::LDC + j0).store(P_g + r * C + j0);
+  }
+  if constexpr (NT == 4) {
+    // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
+    float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
+      z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
+      z21 += Ael(2, 1, rr, m) * t11;
+      z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
+      z31 += Ael(3, 1, rr, m) * t11;
     }
-    if (wave < NT && lane < 16) {
-      const int b = wave, c = lane;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
-        float s = (r == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
-        x[r] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) A_s[(16 * b + r) * L::LDF + 16 * b + c] = x[r];
-    }
+    Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
     __syncthreads();
-
-    // off-diagonal blocks, in place (each A block is consumed by the
-    // product that produces the T block in its position)
-    auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
-    auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
-    const int rr = tid >> 4, cc = tid & 15;
-    if constexpr (NT >= 2) {
-      // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
+    float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
 #pragma unroll
-      for (int b = 0; b < NT / 2; ++b) {
-        float z = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
-        Zel(b, rr, cc) = z;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int b = 0; b < NT / 2; ++b) {
-        float t = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
-        Ael(2 * b + 1, 2 * b, rr, cc) = t;
-      }
-      __syncthreads();
+    for (int m = 0; m < 16; ++m) {
+      const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
+      t20 -= a22 * Zel(0, m, cc);
+      t21 -= a22 * Zel(1, m, cc);
+      t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
+      t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
     }
-    if constexpr (NT == 4) {
-      // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
-      float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
-        z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
-        z21 += Ael(2, 1, rr, m) * t11;
-        z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
-        z31 += Ael(3, 1, rr, m) * t11;
-      }
-      Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
-      __syncthreads();
-      float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
-        t20 -= a22 * Zel(0, m, cc);
-        t21 -= a22 * Zel(1, m, cc);
-        t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
-        t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
-      }
-      Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
-      __syncthreads();
-    }
-
-    // Tb = T diag(beta) (upper blocks zero) -> staging -> workspace
-    for (int e = tid; e < C * C; e += kPrepThreads) {
-      const int r = e / C, j = e % C;
-      St[r * L::LDC + j] = from_f32<T>((j >> 4) > (r >> 4) ? 0.f : A_s[r * L::LDF + j] * b_s[j]);
-    }
+    Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
     __syncthreads();
-    for (int e = tid; e < C * C / 8; e += kPrepThreads) {
-      const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
-      R8::load(St + r * L::LDC + j0).store(Tb_g + r * C + j0);
-    }
-    __syncthreads();  // St, A_s, g_s are rewritten for the next V head
+  }
+
+  // Tb = T diag(beta) (upper blocks zero) -> staging -> workspace
+  for (int e = tid; e < C * C; e += kPrepThreads) {
+    const int r = e / C, j = e % C;
+    St[r * L::LDC + j] = from_f32<T>((j >> 4) > (r >> 4) ? 0.f : A_s[r * L::LDF + j] * b_s[j]);
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+    const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
+    R8::load(St + r * L::LDC + j0).store(Tb_g + r * C + j0);
   }
 }
 
@@ -888,7 +911,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (p.total_tokens > 0) {
       const int64_t mc = max_chunks(p.total_tokens, p.n_seqs, C);
-      hipLaunchKernelGGL(prep, dim3((unsigned)mc, (unsigned)p.h_qk), dim3(kPrepThreads), PL::bytes,
+      hipLaunchKernelGGL(prep, dim3((unsigned)mc, (unsigned)p.h_v), dim3(kPrepThreads), PL::bytes,
                          stream, p, ws);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
