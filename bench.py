@@ -49,6 +49,43 @@ def decode_bytes_per_step(cfg):
             + C * W * 2)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_attention_token_conv1d_amd", "csrc")
+
+
+def measured_traffic(summary, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy of known
+    size reads on the same counter).  None when the summary is missing or was
+    taken on a different version of the kernel source."""
+    import hashlib
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip().lstrip("- ")] = v.strip().strip("`")
+    digest = hashlib.sha256(open(os.path.join(CSRC, source), "rb").read()).hexdigest()
+    if fields.get(f"sha256 {source}") != digest or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
+
+
+def calibrate_copy(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters: profiled with the same counters as the kernels."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": reps}), flush=True)
+
+
 _SHARED = {}  # oracle inputs handed to forked workers without pickling
 
 
@@ -135,8 +172,9 @@ def run_prefill(name, steps, warmup, do_cpu, cpu_tokens):
         "prefill_kernel_ms": k_ms,
         "prefill_only_tokens_per_s": T / (k_ms * 1e-3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<bf16,128,64>",
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(f"prefill_{name}_traffic.md", "prefill.hip"),
+                     "kernel": "gdn_prefill (plan_kernel + prep_kernel + scan_kernel)",
                      "flops_per_launch": flops},
         "config": {"workload": f"{name}: B={inp['n_seqs']} T={T} h_qk={hq} h_v={hv} d={d} "
                                f"chunk={cfg['chunk']} conv{cfg['width']}+SiLU, bf16 io, fp32 state",
@@ -178,7 +216,8 @@ def run_decode(steps, warmup, do_cpu):
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"value": 1e3 / ms, "unit": "steps/s", "tokens_per_s": N * 1e3 / ms, "ms_per_step": ms,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic("decode_qwen35_27b_decode_traffic.md", "decode.hip"),
                         "kernel": "decode_kernel<bf16,bf16,128>", "bytes_per_launch": nbytes},
            "config": {"workload": f"qwen35_27b_decode: {N} sequences x 1 token, h_qk={hq} h_v={hv} d={d}, "
                                   f"bf16 state, conv4+SiLU, {nsteps} consecutive steps"}}
@@ -210,6 +249,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mixer shards by (sequence, V head) with no "
@@ -219,6 +260,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     pre = run_prefill(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_tokens)
     line = {"metric": METRIC, "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s/layer",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

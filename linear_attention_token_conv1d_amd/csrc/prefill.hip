@@ -33,6 +33,8 @@
 //        registers while the current one is computed; K^T fragments for the
 //        state update come straight from the row-major K tile through the
 //        gfx950 LDS transpose read (ds_read_b64_tr_b16).
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -490,27 +492,44 @@ __device__ __forceinline__ int pidx(int t, int m) {
 // and the per-column V reads of a wave on distinct banks.  The layout is
 // dense, so a wave's direct-to-LDS load (64 lanes x 16 B into 1 KiB of
 // consecutive LDS) fills it without a register round trip.
+// Row functions of the swizzles below (slot of chunk j of row r = j ^ f(r)).
+struct RowK {  // token-major K/Q tiles of 16+ chunks: fragment rows in pidx order, transpose reads
+  static __device__ __forceinline__ int f(int r) { return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) | ((r >> 4) & 1); }
+};
+struct RowT {  // narrower tiles (Tb, P; K/Q when d_k = 64)
+  static __device__ __forceinline__ int f(int r) { return ((r >> 1) & 1) | (((r >> 3) & 3) << 1); }
+};
+template <int NT>
+struct RowV {  // V tile read by the transposing loads: rows b..b+3 and b+8..b+11 on distinct banks
+  static __device__ __forceinline__ int f(int r) {
+    if constexpr (NT == 1) return (((r >> 1) & 1) | (((r >> 2) & 1) << 1)) << 1;
+    else return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1;
+  }
+};
 template <int RB>
-struct Swz {
+struct RowSeq {  // 16 consecutive rows read at one chunk: spread over the 256-byte bank window
+  static __device__ __forceinline__ int f(int r) { return r / (RB >= 256 ? 1 : 256 / RB); }
+};
+
+template <int RB, typename F>
+struct SwzT {
   static constexpr int CPR = RB / 16;
   static_assert(CPR >= 1 && (CPR & (CPR - 1)) == 0, "row of 2^k chunks");
-  static __device__ __forceinline__ int f(int r) {
-    if constexpr (CPR >= 16) return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) | ((r >> 4) & 1);
-    else return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);
-  }
-  static __device__ __forceinline__ int slot(int r, int j) { return (j ^ f(r)) & (CPR - 1); }
+  static constexpr int RBYTES = RB;
+  static __device__ __forceinline__ int slot(int r, int j) { return (j ^ F::f(r)) & (CPR - 1); }
   // byte offset of byte b of row r
   static __device__ __forceinline__ int off(int r, int b) { return r * RB + (slot(r, b >> 4) << 4) + (b & 15); }
 };
+template <int RB>
+using Swz = SwzT<RB, std::conditional_t<(RB / 16 >= 16), RowK, RowT>>;
 
 // Direct-to-LDS copy of ROWS rows of RB bytes.  Global row r (clamped to
 // rmax - 1) starts at gbase + r * gstride bytes.  Instruction k of wave w
 // fills LDS chunks [(k * NWAVES + w) * 64, +64): lane l writes chunk q and
 // fetches the global chunk whose swizzled slot is q.
-template <int RB, int ROWS, int NWAVES>
-__device__ __forceinline__ void dma_tile(unsigned char* lds, const unsigned char* gbase, int64_t gstride,
-                                         int rmax, int wave, int lane) {
-  using S = Swz<RB>;
+template <typename S, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile_s(unsigned char* lds, const unsigned char* gbase, int64_t gstride,
+                                           int rmax, int wave, int lane) {
   constexpr int TOTAL = ROWS * S::CPR;
 #pragma unroll
   for (int k = 0; k * NWAVES * 64 < TOTAL; ++k) {
@@ -523,6 +542,11 @@ __device__ __forceinline__ void dma_tile(unsigned char* lds, const unsigned char
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
     }
   }
+}
+template <int RB, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, const unsigned char* gbase, int64_t gstride,
+                                         int rmax, int wave, int lane) {
+  dma_tile_s<Swz<RB>, ROWS, NWAVES>(lds, gbase, gstride, rmax, wave, lane);
 }
 
 // Plain direct-to-LDS copy of NB bytes (a multiple of 16).
@@ -538,11 +562,44 @@ __device__ __forceinline__ void dma_linear(unsigned char* lds, const unsigned ch
   }
 }
 
+// Precomputed form of dma_tile_s for full chunks: the per-lane source offset
+// of each instruction (row r of the tile at r * gstride bytes, chunk slot
+// from the swizzle) does not change from chunk to chunk, so it is computed
+// once and a chunk costs one address add per instruction.  Offsets are 32-bit
+// (the caller checks that ROWS * gstride fits).
+template <typename S, int ROWS, int NWAVES>
+struct DmaPlan {
+  static constexpr int TOTAL = ROWS * S::CPR;
+  static constexpr int NI = (TOTAL + NWAVES * 64 - 1) / (NWAVES * 64);
+  uint32_t off[NI];
+  __device__ __forceinline__ void init(uint32_t gstride, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int q = min((k * NWAVES + wave) * 64 + lane, TOTAL - 1);
+      const int r = q / S::CPR;
+      off[k] = (uint32_t)r * gstride + (uint32_t)S::slot(r, q % S::CPR) * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(unsigned char* lds, const unsigned char* gbase, int wave, int lane) const {
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int q0 = (k * NWAVES + wave) * 64;
+      if (q0 < TOTAL && q0 + lane < TOTAL)
+        __builtin_amdgcn_global_load_lds(gbase + off[k], (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
+    }
+  }
+};
+
 // A fragment: 8 consecutive elements k0..k0+7 of row `row` of a swizzled
 // tile (4 elements and 4 zeros when `half`).
+template <typename T, typename S>
+__device__ __forceinline__ typename Mma<T>::frag frag_row_s(const unsigned char* tile, int row, int k0, bool half);
 template <typename T, int RB>
 __device__ __forceinline__ typename Mma<T>::frag frag_row(const unsigned char* tile, int row, int k0, bool half) {
-  using S = Swz<RB>;
+  return frag_row_s<T, Swz<RB>>(tile, row, k0, half);
+}
+template <typename T, typename S>
+__device__ __forceinline__ typename Mma<T>::frag frag_row_s(const unsigned char* tile, int row, int k0, bool half) {
   if constexpr (sizeof(T) == 2) {
     if (half) {
       const uint2 lo = *reinterpret_cast<const uint2*>(tile + S::off(row, k0 * 2));
@@ -874,6 +931,340 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   }
 }
 
+// ------------------------------------------------------- split-role scan
+// bf16 scan with two wave roles per workgroup (8 waves, two per SIMD), for a
+// block of 64 d_v columns of one (sequence, V head):
+//  chain waves 0-3 own 16 columns each of the fp32 state S^T in accumulator
+//    tiles and run the serial part of a chunk:  X1 = K S^T,
+//    R = V - diag(gamma rk) X1,  U = Tb R,  S^T <- gamma_last S^T + K^T diag(e rk) U;
+//  output waves 4-7 (same 16 columns each) compute the chunk's output
+//    O^T = (S Q^T) diag(scale gamma rq) + U^T P^T  from the state and U that
+//    the chain waves publish in LDS as bf16, and store O straight from their
+//    accumulators (a lane holds 4 consecutive columns of one token).
+// The two roles share each SIMD, so one role's MFMA and LDS work fills the
+// other's dependency stalls.  All eight waves issue the next chunk's
+// direct-to-LDS loads at the start of a chunk.  Per chunk: barrier B1 after U
+// is published (LDS only: the loads stay in flight), and B2 at the end (the
+// next chunk has landed, the new state is published).
+template <int D, int C>
+struct Scan2Layout {
+  static constexpr int NT = C / 16, DT = D / 16;
+  static constexpr int cols = 64;  // d_v columns per workgroup
+  static constexpr int RBK = D * 2, RBC = C * 2, RBV = cols * 2, RBS = D * 2, RBU = C * 2;
+  using SK = Swz<RBK>;
+  using SC = Swz<RBC>;
+  using SV = SwzT<RBV, RowV<NT>>;
+  using SS = SwzT<RBS, RowSeq<RBS>>;
+  using SU = SwzT<RBU, RowSeq<RBU>>;
+  static constexpr int oK = 0;
+  static constexpr int oQ = oK + C * RBK;
+  static constexpr int oTb = oQ + C * RBK;
+  static constexpr int oP = oTb + C * RBC;
+  static constexpr int oV = oP + C * RBC;
+  static constexpr int oVec = oV + C * RBV;
+  static constexpr int buf = oVec + 16 * C;
+  static constexpr int sbytes = cols * RBS;
+  static constexpr int ubytes = cols * RBU;
+  static constexpr int bytes = 2 * buf + sbytes + ubytes;
+};
+
+// s_waitcnt with vmcnt(vm), expcnt untouched, lgkmcnt(0)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier that waits only for what is named: this wave's LDS
+// operations and all but its last VM vector-memory operations.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vm_lgkm0<VM>();
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsigned char* ws, int nwg) {
+  using L = Scan2Layout<D, C>;
+  using T = __bf16;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  using SK = typename L::SK;
+  using SC = typename L::SC;
+  using SV = typename L::SV;
+  using SS = typename L::SS;
+  using SU = typename L::SU;
+  constexpr int NT = L::NT, DT = L::DT, DKS = D / 32;
+  constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
+  constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
+  constexpr int NB = D / L::cols;
+  __shared__ __align__(16) unsigned char sb0[L::buf];
+  __shared__ __align__(16) unsigned char sb1[L::buf];
+  __shared__ __align__(16) unsigned char sS[L::sbytes];
+  __shared__ __align__(16) unsigned char sU[L::ubytes];
+
+  // XCD-aware order, as in the four-wave scan
+  const int per_xcd = (nwg + 7) / 8;
+  const int wid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wid >= nwg) return;
+  const int blk = wid % NB;
+  const int h = (wid / NB) % p.h_v;
+  const int n = wid / (NB * p.h_v);
+  const int hq = h / (p.h_v / p.h_qk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const bool chain = wave < 4;
+  const int cw = wave & 3;           // 16-column slice of this wave
+  const int col = 16 * cw + l16;     // this lane's column in the block
+
+  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
+  const unsigned char* recs = ws + off_bytes(p.n_seqs);
+  const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
+  const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
+  const int c0 = off[n];
+  const int nch = off[n + 1] - c0;
+
+  const unsigned char* qg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + (int64_t)hq * D);
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + (int64_t)hq * D);
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + (int64_t)h * D +
+                                                                   blk * L::cols);
+  auto chunk_t0 = [&](int c) { return seq_start + (int64_t)c * C; };
+  auto chunk_len = [&](int c) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
+  auto chunk_rec = [&](int c) { return recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes; };
+
+  // ---- data movement: every wave issues its share of the next chunk's
+  // direct-to-LDS loads at the start of a chunk.  A full chunk uses per-lane
+  // offsets computed once (DmaPlan); a partial chunk (the last of a
+  // sequence) takes the clamped path, where rows past its end re-read its
+  // last row: they only meet zero columns of Tb and zero rows of U.
+  DmaPlan<SK, C, 8> pk, pq;
+  DmaPlan<SC, C, 8> ptb;
+  DmaPlan<SV, C, 8> pv;
+  const bool fast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) &&
+                    p.v_stride * 2 * C < (1ll << 31);
+  if (fast) {
+    pk.init((uint32_t)(p.k_stride * 2), wave, lane);
+    pq.init((uint32_t)(p.q_stride * 2), wave, lane);
+    ptb.init((uint32_t)L::RBC, wave, lane);
+    pv.init((uint32_t)(p.v_stride * 2), wave, lane);
+  }
+  auto issue = [&](int c, unsigned char* b) {
+    const int64_t t0 = chunk_t0(c);
+    const int Lc = chunk_len(c);
+    const unsigned char* rec = chunk_rec(c);
+    const unsigned char* kc = kg + t0 * p.k_stride * 2;
+    const unsigned char* qc = qg + t0 * p.q_stride * 2;
+    const unsigned char* vc = vg + t0 * p.v_stride * 2;
+    if (fast && Lc == C) {
+      pk.issue(b + L::oK, kc, wave, lane);
+      pq.issue(b + L::oQ, qc, wave, lane);
+      ptb.issue(b + L::oTb, rec, wave, lane);
+      ptb.issue(b + L::oP, rec + Rec<T, C>::mat, wave, lane);
+      pv.issue(b + L::oV, vc, wave, lane);
+    } else {
+      dma_tile_s<SK, C, 8>(b + L::oK, kc, p.k_stride * 2, Lc, wave, lane);
+      dma_tile_s<SK, C, 8>(b + L::oQ, qc, p.q_stride * 2, Lc, wave, lane);
+      dma_tile_s<SC, C, 8>(b + L::oTb, rec, L::RBC, C, wave, lane);
+      dma_tile_s<SC, C, 8>(b + L::oP, rec + Rec<T, C>::mat, L::RBC, C, wave, lane);
+      dma_tile_s<SV, C, 8>(b + L::oV, vc, p.v_stride * 2, Lc, wave, lane);
+    }
+    dma_linear<16 * C, 8>(b + L::oVec, rec + 2 * Rec<T, C>::mat, wave, lane);
+  };
+
+  if (nch > 0) issue(0, sb0);
+
+  if (chain) {
+    // ---------------------------------------------------------- chain waves
+    // state S^T (d_k x 16 columns) in DT accumulator tiles; row 4g+i of tile
+    // dt is d_k index pidx<DT>(dt, 4g+i)
+    f32x4 st[DT];
+    const size_t srow = (((size_t)n * p.h_v + h) * D + (size_t)(blk * L::cols + col)) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      st[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p.initial_state) {
+        const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + srow + pidx<DT>(dt, 4 * g4));
+        st[dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+      }
+    }
+    // the state as bf16 rows [column][d_k] for the output waves: tiles 2u,
+    // 2u+1 give this lane d_k 32u + 8g .. 32u + 8g + 7
+    auto publish_state = [&]() {
+#pragma unroll
+      for (int u = 0; u < DT / 2; ++u)
+        *reinterpret_cast<frag*>(sS + SS::off(col, (32 * u + 8 * g4) * 2)) = M::acc(st[2 * u], st[2 * u + 1]);
+    };
+    publish_state();
+    __syncthreads();  // initial state published; chunk 0 has landed
+
+    auto step = [&](int c, const unsigned char* cur, unsigned char* nxt) {
+      if (c + 1 < nch) issue(c + 1, nxt);
+      const unsigned char* K_t = cur + L::oK;
+      const unsigned char* Tb_t = cur + L::oTb;
+      const unsigned char* V_t = cur + L::oV;
+      const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
+      // operands of R and U that do not depend on the state, read up front:
+      // V[token pidx(mt, 4g) + e][col] (one transposing read per tile) and Tb
+      uint2 vw[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const int r0 = pidx<NT>(mt, 4 * g4);
+        vw[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(
+            __attribute__((address_space(3))) unsigned char*)(V_t + SV::off(r0 + (l16 >> 2), (16 * cw + 4 * (l16 & 3)) * 2))));
+      }
+      frag at[KS][NT];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          at[s][mt] = frag_row_s<T, SC>(Tb_t, pidx<NT>(mt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+      // X1 = K S^T
+      f32x4 x1[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) x1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DKS; ++s) {
+        const frag bs = M::acc(st[2 * s], st[2 * s + 1]);
+        frag ak[NT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) ak[mt] = frag_row_s<T, SK>(K_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) M::mma(x1[mt], ak[mt], bs, false);
+      }
+      // R = V - diag(gamma rk) X1
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const float4 vq = *reinterpret_cast<const float4*>(vec + pidx<NT>(mt, 4 * g4));
+        x1[mt][0] = bf16_lo(vw[mt].x) - vq.x * x1[mt][0];
+        x1[mt][1] = bf16_hi(vw[mt].x) - vq.y * x1[mt][1];
+        x1[mt][2] = bf16_lo(vw[mt].y) - vq.z * x1[mt][2];
+        x1[mt][3] = bf16_hi(vw[mt].y) - vq.w * x1[mt][3];
+      }
+      // U = Tb R
+      f32x4 u[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) u[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const frag bs = M::acc(x1[2 * s], tile_hi<NT>(x1, s));
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) M::mma(u[mt], at[s][mt], bs, HALF);
+      }
+      // publish U as bf16 rows [column][token] (natural token order)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (HALF) {
+          *reinterpret_cast<uint2*>(sU + SU::off(col, 8 * g4)) =
+              make_uint2(pack_bf16x2(u[0][0], u[0][1]), pack_bf16x2(u[0][2], u[0][3]));
+        } else {
+          *reinterpret_cast<frag*>(sU + SU::off(col, (32 * s + 8 * g4) * 2)) = M::acc(u[2 * s], u[2 * s + 1]);
+        }
+      }
+      // U' = diag(e rk) U for the state update
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const float4 vq = *reinterpret_cast<const float4*>(vec + 2 * C + pidx<NT>(mt, 4 * g4));
+        u[mt][0] *= vq.x; u[mt][1] *= vq.y; u[mt][2] *= vq.z; u[mt][3] *= vq.w;
+      }
+      const float gl = vec[3 * C];
+      barrier_vm<63>();  // B1: U is visible; the output waves are done with the old state
+      // S^T <- gamma_last S^T + K^T diag(e rk) U
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) st[dt] *= gl;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const frag bs = M::acc(u[2 * s], tile_hi<NT>(u, s));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const frag ak = frag_kt<T, L::RBK, DT>(K_t, dt, HALF ? 4 * g4 : 32 * s + 8 * g4, l16, HALF);
+          M::mma(st[dt], ak, bs, HALF);
+        }
+      }
+      publish_state();
+      __syncthreads();  // B2: next chunk loaded, new state published
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, sb0, sb1);
+      if (c + 1 < nch) step(c + 1, sb1, sb0);
+    }
+    if (p.final_state) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(p.final_state + srow + pidx<DT>(dt, 4 * g4)) =
+            make_float4(st[dt][0], st[dt][1], st[dt][2], st[dt][3]);
+    }
+  } else {
+    // --------------------------------------------------------- output waves
+    const int64_t o_stride = (int64_t)p.h_v * D;
+    T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols + 16 * cw + 4 * g4;
+    // O^T tile nt: rows 4g+i = columns 16cw + 4g + i, column l16 = token
+    // pidx(nt, l16) of the chunk
+    f32x4 o[NT];
+    int64_t orow[NT];  // element offset of this lane's token row in each tile
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) orow[nt] = (int64_t)pidx<NT>(nt, l16) * o_stride;
+    auto store_o = [&](int64_t t0, int Lc) {
+      T* oc = og + t0 * o_stride;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (pidx<NT>(nt, l16) < Lc)
+          *reinterpret_cast<uint2*>(oc + orow[nt]) =
+              make_uint2(pack_bf16x2(o[nt][0], o[nt][1]), pack_bf16x2(o[nt][2], o[nt][3]));
+      }
+    };
+    __syncthreads();  // chunk 0 has landed; the initial state is published
+
+    auto step = [&](int c, const unsigned char* cur, unsigned char* nxt) {
+      const bool more = c + 1 < nch;
+      if (c > 0) store_o(chunk_t0(c - 1), C);
+      const unsigned char* Q_t = cur + L::oQ;
+      const unsigned char* P_t = cur + L::oP;
+      const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
+      if (more) issue(c + 1, nxt);
+      // Y^T = S Q^T, columns scaled by scale gamma rq
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DKS; ++s) {
+        const frag as = frag_row_s<T, SS>(sS, col, 32 * s + 8 * g4, false);
+        frag bq[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bq[nt] = frag_row_s<T, SK>(Q_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) M::mma(o[nt], as, bq[nt], false);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] *= vec[C + pidx<NT>(nt, l16)];
+      barrier_vm<63>();  // B1
+      // O^T += U^T P^T
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const frag au = frag_row_s<T, SU>(sU, col, HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+        frag bp[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(nt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) M::mma(o[nt], au, bp[nt], HALF);
+      }
+      __syncthreads();  // B2
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, sb0, sb1);
+      if (c + 1 < nch) step(c + 1, sb1, sb0);
+    }
+    if (nch > 0) store_o(chunk_t0(nch - 1), chunk_len(nch - 1));
+  }
+}
+
+// Every launched variant is instantiated explicitly: clang does not always
+// emit the host launch stub of an implicitly instantiated kernel template
+// whose body holds capturing lambdas.
+#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C>(PrefillParams, const unsigned char*, int);
+GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
+#undef GDN_SCAN2
+
 // ------------------------------------------------------------------ host
 constexpr int kLdsMax = 160 * 1024;
 // scan workgroup shape: kScanWaves waves, each owning kScanTiles 16-column
@@ -887,9 +1278,16 @@ constexpr int kLdsMax = 160 * 1024;
 constexpr int kScanWaves = GDN_SCAN_WAVES;
 constexpr int kScanTiles = GDN_SCAN_TILES;
 
+// bf16 runs the split-role scan, fp32 the four-wave scan
+template <typename T, int D, int C>
+constexpr int scan_lds_bytes() {
+  if constexpr (sizeof(T) == 2) return Scan2Layout<D, C>::bytes;
+  else return ScanLayout<T, D, C, kScanWaves, kScanTiles>::bytes;
+}
+
 template <typename T, int D, int C>
 constexpr bool fits() {
-  return PrepLayout<T, D, C>::bytes <= kLdsMax && ScanLayout<T, D, C, kScanWaves, kScanTiles>::bytes <= kLdsMax;
+  return PrepLayout<T, D, C>::bytes <= kLdsMax && scan_lds_bytes<T, D, C>() <= kLdsMax;
 }
 
 template <typename T, int D, int C>
@@ -916,10 +1314,18 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    const int nwg = p.n_seqs * p.h_v * (D / SL::cols);
-    const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
-    hipLaunchKernelGGL((scan_kernel<T, D, C, NW, CT>), dim3(grid), dim3(SL::threads), 0, stream, p,
-                       static_cast<const unsigned char*>(ws), nwg);
+    if constexpr (sizeof(T) == 2) {
+      using S2 = Scan2Layout<D, C>;
+      const int nwg = p.n_seqs * p.h_v * (D / S2::cols);
+      const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
+      hipLaunchKernelGGL((scan2_kernel<D, C>), dim3(grid), dim3(512), 0, stream, p,
+                         static_cast<const unsigned char*>(ws), nwg);
+    } else {
+      const int nwg = p.n_seqs * p.h_v * (D / SL::cols);
+      const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
+      hipLaunchKernelGGL((scan_kernel<T, D, C, NW, CT>), dim3(grid), dim3(SL::threads), 0, stream, p,
+                         static_cast<const unsigned char*>(ws), nwg);
+    }
     return hipGetLastError();
   }
 }
