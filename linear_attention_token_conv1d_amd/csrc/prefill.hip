@@ -199,280 +199,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
   }
 }
 
-// ------------------------------------------------------------------ prep
-// One workgroup per (chunk, V head).  LDS holds the chunk's K and Q rows
-// while the Gram tiles are formed, then the same bytes hold the fp32 A/T
-// work array, the block-product scratch and the staging tile for the bf16
-// outputs, so four workgroups fit on a CU.
-template <typename T, int D, int C>
-struct PrepLayout {
-  static constexpr int NT = C / 16;
-  static constexpr int PADE = 16 / (int)sizeof(T);
-  static constexpr int LDK = D + PADE;
-  static constexpr int LDC = C + PADE;
-  static constexpr int LDF = C + 4;
-  static constexpr int LDZ = 20;
-  // phase 1: K, Q rows
-  static constexpr int oK = 0;
-  static constexpr int oQ = oK + C * LDK * (int)sizeof(T);
-  static constexpr int kq_bytes = oQ + C * LDK * (int)sizeof(T);
-  // phase 2 (same bytes): A/T work array, scratch, output staging
-  static constexpr int oA = 0;
-  static constexpr int oZ = oA + C * LDF * 4;
-  static constexpr int oSt = oZ + 4 * 16 * LDZ * 4;
-  static constexpr int work_bytes = oSt + C * LDC * (int)sizeof(T);
-  static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
-  static constexpr int bytes = oVec + 5 * C * 4;
-};
-
-// Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
-__device__ __forceinline__ int owner(const int32_t* off, int n_seqs, int c) {
-  int lo = 0, hi = n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-template <typename T, int D, int C>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, unsigned char* ws) {
-  using L = PrepLayout<T, D, C>;
-  using M = Mma<T>;
-  using R8 = Raw8<T>;
-  constexpr int NT = L::NT;
-  constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
-  constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* K_s = reinterpret_cast<T*>(smem + L::oK);
-  T* Q_s = reinterpret_cast<T*>(smem + L::oQ);
-  float* A_s = reinterpret_cast<float*>(smem + L::oA);
-  float* Z_s = reinterpret_cast<float*>(smem + L::oZ);
-  T* St = reinterpret_cast<T*>(smem + L::oSt);
-  float* g_s = reinterpret_cast<float*>(smem + L::oVec);
-  float* b_s = g_s + C;
-  float* G_s = g_s + 2 * C;
-  float* rk_s = g_s + 3 * C;
-  float* rq_s = g_s + 4 * C;
-
-  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
-  const int ci = blockIdx.x, h = blockIdx.y;
-  if (ci >= off[p.n_seqs]) return;
-  const int hq = h / (p.h_v / p.h_qk);
-  const int n = owner(off, p.n_seqs, ci);
-  const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
-  const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
-  const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
-  const int Lc = (int)min((int64_t)C, seq_end - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, l16 = lane & 15;
-
-  // K, Q rows of this chunk and QK head (rows >= Lc zero); g, beta of this V head
-  const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
-  const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
-  // all loads are issued before any is used (rows past the chunk re-read its
-  // last row and are zeroed afterwards), so the workgroup waits on memory once
-  constexpr int NV = (C * (D / 8) + kPrepThreads - 1) / kPrepThreads;
-  R8 kv[NV], qv[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = min(tid + i * kPrepThreads, C * (D / 8) - 1);
-    const int r = min(e / (D / 8), Lc - 1), d0 = (e % (D / 8)) * 8;
-    kv[i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
-    qv[i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
-  }
-  const int ti = min(tid, Lc - 1);
-  const float gv = p.g[(t0 + ti) * p.h_v + h];
-  const float bv = p.beta[(t0 + ti) * p.h_v + h];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = tid + i * kPrepThreads;
-    const int r = e / (D / 8), d0 = (e % (D / 8)) * 8;
-    if (e < C * (D / 8)) {
-      (r < Lc ? kv[i] : R8::zero()).store(K_s + r * L::LDK + d0);
-      (r < Lc ? qv[i] : R8::zero()).store(Q_s + r * L::LDK + d0);
-    }
-  }
-  if (tid < C) {
-    g_s[tid] = tid < Lc ? gv : 0.f;
-    b_s[tid] = tid < Lc ? bv : 0.f;
-  }
-  __syncthreads();
-
-  // row norms (4 lanes per row)
-  for (int r = tid >> 2; r < C; r += kPrepThreads / 4) {
-    const int part = tid & 3;
-    float sk = 0.f, sq = 0.f;
-    for (int d = part; d < D; d += 4) {
-      const float a = to_f32(K_s[r * L::LDK + d]);
-      const float b = to_f32(Q_s[r * L::LDK + d]);
-      sk += a * a; sq += b * b;
-    }
-    sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk);
-    sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq);
-    if (part == 0) {
-      rk_s[r] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-      rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-    }
-  }
-  // cumulative log-decay over the chunk
-  if (wave == 0) {
-    float G = lane < C ? g_s[lane] : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float u = __shfl_up(G, o, 64);
-      if (lane >= o) G += u;
-    }
-    if (lane < C) G_s[lane] = G;
-  }
-  // raw Gram tiles (lower triangle): jobs [0, NLT) are K K^T, [NLT, 2 NLT) are Q K^T
-  f32x4 gram[NJ];
-  int jmt[NJ], jnt[NJ];
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int job = wave + 4 * jj;
-    gram[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    jmt[jj] = jnt[jj] = 0;
-    if (job < 2 * NLT) {
-      int tj = job >= NLT ? job - NLT : job, mt = 0;
-      while (tj > mt) { tj -= mt + 1; ++mt; }
-      jmt[jj] = mt; jnt[jj] = tj;
-      const T* Arow = (job >= NLT ? Q_s : K_s) + (mt * 16 + l16) * L::LDK;
-      const T* Brow = K_s + (tj * 16 + l16) * L::LDK;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        M::mma(gram[jj], M::lds(Arow + 32 * s, g4, false), M::lds(Brow + 32 * s, g4, false), false);
-    }
-  }
-  __syncthreads();  // norms and G published; K, Q are dead from here on
-
-  unsigned char* rec = ws + off_bytes(p.n_seqs) + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
-  T* Tb_g = reinterpret_cast<T*>(rec);
-  T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
-  float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
-  if (tid < C) {
-    const float G = G_s[tid], Gl = G_s[Lc - 1], eg = fexp(G);
-    vec_g[tid] = eg * rk_s[tid];
-    vec_g[C + tid] = p.scale * eg * rq_s[tid];
-    vec_g[2 * C + tid] = fexp(Gl - G) * rk_s[tid];
-    vec_g[3 * C + tid] = fexp(Gl);
-  }
-  // decay-masked Gram tiles: A (strict lower, fp32) and P (lower incl. diagonal)
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int job = wave + 4 * jj;
-    if (job < 2 * NLT) {
-      const bool isP = job >= NLT;
-      const int j = jnt[jj] * 16 + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = jmt[jj] * 16 + 4 * g4 + i;
-        const float dec = (j <= r) ? fexp(G_s[r] - G_s[j]) : 0.f;
-        if (!isP)
-          A_s[r * L::LDF + j] = (j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f;
-        else
-          St[r * L::LDC + j] = from_f32<T>(p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]);
-      }
-    }
-  }
-  for (int e = tid; e < C * C; e += kPrepThreads) {
-    const int r = e / C, j = e % C;
-    if ((j >> 4) > (r >> 4)) St[r * L::LDC + j] = from_f32<T>(0.f);
-  }
-  __syncthreads();
-
-  // P -> workspace; diagonal 16x16 blocks of T = (I + A)^-1 in place.  Wave b
-  // solves block b by forward substitution: lane 4c+p owns column c and the
-  // rows r = p (mod 4); each row's sum is split over the 4 lanes of a quad.
-  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
-    const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
-    R8::load(St + r * L::LDC + j0).store(P_g + r * C + j0);
-  }
-  if (wave < NT) {
-    const int b = wave, c = lane >> 2, part = lane & 3;
-    float xl[4] = {0.f, 0.f, 0.f, 0.f};  // x_{4m+part} of column c
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = 4 * m + part;
-        s += (j < r) ? arow[j] * xl[m] : 0.f;
-      }
-      s += dpp_f32<DPP_QUAD_1032>(s);
-      s += dpp_f32<DPP_QUAD_2301>(s);
-      const float xr = ((r == c) ? 1.f : 0.f) - s;
-      if (part == (r & 3)) xl[r >> 2] = xr;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) A_s[(16 * b + 4 * m + part) * L::LDF + 16 * b + c] = xl[m];
-  }
-  __syncthreads();
-
-  // off-diagonal blocks, in place (each A block is consumed by the
-  // product that produces the T block in its position)
-  auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
-  auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
-  const int rr = tid >> 4, cc = tid & 15;
-  if constexpr (NT >= 2) {
-    // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
-#pragma unroll
-    for (int b = 0; b < NT / 2; ++b) {
-      float z = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
-      Zel(b, rr, cc) = z;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < NT / 2; ++b) {
-      float t = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
-      Ael(2 * b + 1, 2 * b, rr, cc) = t;
-    }
-    __syncthreads();
-  }
-  if constexpr (NT == 4) {
-    // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
-    float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
-      z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
-      z21 += Ael(2, 1, rr, m) * t11;
-      z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
-      z31 += Ael(3, 1, rr, m) * t11;
-    }
-    Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
-    __syncthreads();
-    float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
-      t20 -= a22 * Zel(0, m, cc);
-      t21 -= a22 * Zel(1, m, cc);
-      t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
-      t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
-    }
-    Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
-    __syncthreads();
-  }
-
-  // Tb = T diag(beta) (upper blocks zero) -> staging -> workspace
-  for (int e = tid; e < C * C; e += kPrepThreads) {
-    const int r = e / C, j = e % C;
-    St[r * L::LDC + j] = from_f32<T>((j >> 4) > (r >> 4) ? 0.f : A_s[r * L::LDF + j] * b_s[j]);
-  }
-  __syncthreads();
-  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
-    const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
-    R8::load(St + r * L::LDC + j0).store(Tb_g + r * C + j0);
-  }
-}
-
-// ------------------------------------------------------------------ scan
+// ---------------------------------------------------- LDS tile helpers
 // Row order inside a pair of 16-row MFMA tiles.  Row m of tile 2s+b stands
 // for index 32s + 8(m/4) + 4b + m%4 (tokens of a chunk, or d_k of the state).
 // An accumulator tile holds rows 4g+i (g = lane/16) of column lane%16; with
@@ -650,6 +377,318 @@ __device__ __forceinline__ typename Mma<T>::frag frag_kt(const unsigned char* ti
   }
 }
 
+// ------------------------------------------------------------------ prep
+// One workgroup per (chunk, V head).  The chunk's raw K and Q rows are loaded
+// into registers (every load issued before any is used); their L2 norms are
+// reduced there, then the rows go to swizzled LDS tiles for the Gram MFMAs.
+// The Gram tiles are formed transposed (K Q^T, K K^T tile by tile), so a lane
+// holds four consecutive columns of one row of P and of A: P goes straight
+// to the workspace and A to the fp32 work array of the UT solve, which
+// reuses the K/Q bytes.  Tb = T diag(beta) leaves in 16-byte row pieces.
+template <typename T, int D, int C>
+struct PrepLayout {
+  static constexpr int NT = C / 16;
+  static constexpr int E = (int)sizeof(T);
+  static constexpr int RBK = D * E;  // K, Q tile rows (swizzled)
+  static constexpr int LDF = C + 4;
+  static constexpr int LDZ = 20;
+  // phase 1: K, Q tiles
+  static constexpr int oK = 0;
+  static constexpr int oQ = oK + C * RBK;
+  static constexpr int kq_bytes = oQ + C * RBK;
+  // phase 2 (same bytes): A/T work array, block-product scratch
+  static constexpr int oA = 0;
+  static constexpr int oZ = oA + C * LDF * 4;
+  static constexpr int work_bytes = oZ + 4 * 16 * LDZ * 4;
+  static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
+  static constexpr int bytes = oVec + 5 * C * 4;
+};
+
+// Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
+__device__ __forceinline__ int owner(const int32_t* off, int n_seqs, int c) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, unsigned char* ws) {
+  using L = PrepLayout<T, D, C>;
+  using M = Mma<T>;
+  using R8 = Raw8<T>;
+  using SK = Swz<L::RBK>;
+  constexpr int NT = L::NT;
+  constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
+  constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
+  constexpr int RT = D / 8;                    // threads per row in the load layout
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* K_s = smem + L::oK;
+  unsigned char* Q_s = smem + L::oQ;
+  float* A_s = reinterpret_cast<float*>(smem + L::oA);
+  float* Z_s = reinterpret_cast<float*>(smem + L::oZ);
+  float* g_s = reinterpret_cast<float*>(smem + L::oVec);
+  float* b_s = g_s + C;
+  float* G_s = g_s + 2 * C;
+  float* rk_s = g_s + 3 * C;
+  float* rq_s = g_s + 4 * C;
+
+  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
+  const int ci = blockIdx.x, h = blockIdx.y;
+  if (ci >= off[p.n_seqs]) return;
+  const int hq = h / (p.h_v / p.h_qk);
+  const int n = owner(off, p.n_seqs, ci);
+  const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
+  const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
+  const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
+  const int Lc = (int)min((int64_t)C, seq_end - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+
+  // K, Q rows of this chunk and QK head; g, beta of this V head.  Rows past
+  // the chunk re-read its last row and are zeroed below.
+  const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
+  const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
+  constexpr int NV = (C * RT + kPrepThreads - 1) / kPrepThreads;
+  R8 kv[NV], qv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = min(tid + i * kPrepThreads, C * RT - 1);
+    const int r = min(e / RT, Lc - 1), d0 = (e % RT) * 8;
+    kv[i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
+    qv[i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
+  }
+  const int ti = min(tid, Lc - 1);
+  const float gv = p.g[(t0 + ti) * p.h_v + h];
+  const float bv = p.beta[(t0 + ti) * p.h_v + h];
+
+  // row norms: the RT threads of a row are consecutive lanes
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + i * kPrepThreads;
+    const int r = e / RT, d0 = (e % RT) * 8;
+    float fk[8], fq[8];
+    if constexpr (sizeof(T) == 2) {
+      const uint4 a = kv[i].a, b = qv[i].a;
+      fk[0] = bf16_lo(a.x); fk[1] = bf16_hi(a.x); fk[2] = bf16_lo(a.y); fk[3] = bf16_hi(a.y);
+      fk[4] = bf16_lo(a.z); fk[5] = bf16_hi(a.z); fk[6] = bf16_lo(a.w); fk[7] = bf16_hi(a.w);
+      fq[0] = bf16_lo(b.x); fq[1] = bf16_hi(b.x); fq[2] = bf16_lo(b.y); fq[3] = bf16_hi(b.y);
+      fq[4] = bf16_lo(b.z); fq[5] = bf16_hi(b.z); fq[6] = bf16_lo(b.w); fq[7] = bf16_hi(b.w);
+    } else {
+      const uint4 a0 = kv[i].a, a1 = kv[i].b, b0 = qv[i].a, b1 = qv[i].b;
+      fk[0] = __uint_as_float(a0.x); fk[1] = __uint_as_float(a0.y); fk[2] = __uint_as_float(a0.z);
+      fk[3] = __uint_as_float(a0.w); fk[4] = __uint_as_float(a1.x); fk[5] = __uint_as_float(a1.y);
+      fk[6] = __uint_as_float(a1.z); fk[7] = __uint_as_float(a1.w);
+      fq[0] = __uint_as_float(b0.x); fq[1] = __uint_as_float(b0.y); fq[2] = __uint_as_float(b0.z);
+      fq[3] = __uint_as_float(b0.w); fq[4] = __uint_as_float(b1.x); fq[5] = __uint_as_float(b1.y);
+      fq[6] = __uint_as_float(b1.z); fq[7] = __uint_as_float(b1.w);
+    }
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sk += fk[j] * fk[j]; sq += fq[j] * fq[j]; }
+    sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk); sk += dpp_f32<DPP_ROW_HALF_MIRROR>(sk);
+    sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq); sq += dpp_f32<DPP_ROW_HALF_MIRROR>(sq);
+    if constexpr (RT == 16) { sk += dpp_f32<DPP_ROW_MIRROR>(sk); sq += dpp_f32<DPP_ROW_MIRROR>(sq); }
+    if (e >= C * RT) continue;  // a pass wider than the chunk (whole rows per pass)
+    if (d0 == 0) {
+      rk_s[r] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+      rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+    }
+    // raw rows into the swizzled tiles (rows >= Lc zero)
+#pragma unroll
+    for (int part = 0; part < (int)sizeof(R8) / 16; ++part) {
+      const int b = d0 * (int)sizeof(T) + 16 * part;
+      const uint4 zk = r < Lc ? (part ? reinterpret_cast<const uint4*>(&kv[i])[1] : kv[i].a) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 zq = r < Lc ? (part ? reinterpret_cast<const uint4*>(&qv[i])[1] : qv[i].a) : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(K_s + SK::off(r, b)) = zk;
+      *reinterpret_cast<uint4*>(Q_s + SK::off(r, b)) = zq;
+    }
+  }
+  if (tid < C) {
+    g_s[tid] = tid < Lc ? gv : 0.f;
+    b_s[tid] = tid < Lc ? bv : 0.f;
+  }
+  __syncthreads();
+
+  // cumulative log-decay over the chunk
+  if (wave == 0) {
+    float G = lane < C ? g_s[lane] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_up(G, o, 64);
+      if (lane >= o) G += u;
+    }
+    if (lane < C) G_s[lane] = G;
+  }
+  // transposed Gram tiles below the diagonal: job (mt, tj), tj <= mt, holds
+  // rows j = 16 tj + 4g + i, column r = 16 mt + l16 of K K^T (jobs
+  // [0, NLT)) or of K Q^T (jobs [NLT, 2 NLT))
+  f32x4 gram[NJ];
+  int jmt[NJ], jnt[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int job = wave + 4 * jj;
+    gram[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    jmt[jj] = jnt[jj] = 0;
+    if (job < 2 * NLT) {
+      int tj = job >= NLT ? job - NLT : job, mt = 0;
+      while (tj > mt) { tj -= mt + 1; ++mt; }
+      jmt[jj] = mt; jnt[jj] = tj;
+      const unsigned char* Bt = job >= NLT ? Q_s : K_s;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        M::mma(gram[jj], frag_row<T, L::RBK>(K_s, tj * 16 + l16, 32 * s + 8 * g4, false),
+               frag_row<T, L::RBK>(Bt, mt * 16 + l16, 32 * s + 8 * g4, false), false);
+    }
+  }
+  __syncthreads();  // norms and G published; K, Q are dead from here on
+
+  unsigned char* rec = ws + off_bytes(p.n_seqs) + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
+  T* Tb_g = reinterpret_cast<T*>(rec);
+  T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
+  float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
+  if (tid < C) {
+    const float G = G_s[tid], Gl = G_s[Lc - 1], eg = fexp(G);
+    vec_g[tid] = eg * rk_s[tid];
+    vec_g[C + tid] = p.scale * eg * rq_s[tid];
+    vec_g[2 * C + tid] = fexp(Gl - G) * rk_s[tid];
+    vec_g[3 * C + tid] = fexp(Gl);
+  }
+  // decay-masked tiles: A (strict lower, fp32, to LDS) and P (lower incl.
+  // the diagonal, to the workspace); a lane holds row r, columns j0..j0+3
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int job = wave + 4 * jj;
+    if (job < 2 * NLT) {
+      const bool isP = job >= NLT;
+      const int r = jmt[jj] * 16 + l16, j0 = jnt[jj] * 16 + 4 * g4;
+      const float Gr = G_s[r];
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + i;
+        const float dec = (j <= r) ? fexp(Gr - G_s[j]) : 0.f;
+        v[i] = isP ? p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]
+                   : ((j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f);
+      }
+      if (isP) {
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2*>(P_g + r * C + j0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        else
+          *reinterpret_cast<float4*>(P_g + r * C + j0) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<float4*>(A_s + r * L::LDF + j0) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+  // P above the diagonal tiles is zero
+  constexpr int NUP = NT * (NT - 1) / 2 * 16 * 16 / 8;  // 8-element pieces of the upper tiles
+  for (int e = tid; e < NUP; e += kPrepThreads) {
+    int k = e / 32, mt = 0;  // tile k of the upper tiles, row-major (mt, tj > mt)
+    while (k >= NT - 1 - mt) { k -= NT - 1 - mt; ++mt; }
+    const int tj = mt + 1 + k, rr = (e % 32) / 2, half = e % 2;
+    R8::zero().store(P_g + (mt * 16 + rr) * C + tj * 16 + 8 * half);
+  }
+  __syncthreads();
+
+  // diagonal 16x16 blocks of T = (I + A)^-1 in place.  Wave b solves block b
+  // by forward substitution: lane 4c+p owns column c and the rows r = p
+  // (mod 4); each row's sum is split over the 4 lanes of a quad.
+  if (wave < NT) {
+    const int b = wave, c = lane >> 2, part = lane & 3;
+    float xl[4] = {0.f, 0.f, 0.f, 0.f};  // x_{4m+part} of column c
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int j = 4 * m + part;
+        s += (j < r) ? arow[j] * xl[m] : 0.f;
+      }
+      s += dpp_f32<DPP_QUAD_1032>(s);
+      s += dpp_f32<DPP_QUAD_2301>(s);
+      const float xr = ((r == c) ? 1.f : 0.f) - s;
+      if (part == (r & 3)) xl[r >> 2] = xr;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A_s[(16 * b + 4 * m + part) * L::LDF + 16 * b + c] = xl[m];
+  }
+  __syncthreads();
+
+  // off-diagonal blocks, in place (each A block is consumed by the
+  // product that produces the T block in its position)
+  auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
+  auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
+  const int rr = tid >> 4, cc = tid & 15;
+  if constexpr (NT >= 2) {
+    // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
+#pragma unroll
+    for (int b = 0; b < NT / 2; ++b) {
+      float z = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
+      Zel(b, rr, cc) = z;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NT / 2; ++b) {
+      float t = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
+      Ael(2 * b + 1, 2 * b, rr, cc) = t;
+    }
+    __syncthreads();
+  }
+  if constexpr (NT == 4) {
+    // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
+    float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
+      z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
+      z21 += Ael(2, 1, rr, m) * t11;
+      z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
+      z31 += Ael(3, 1, rr, m) * t11;
+    }
+    Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
+    __syncthreads();
+    float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
+      t20 -= a22 * Zel(0, m, cc);
+      t21 -= a22 * Zel(1, m, cc);
+      t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
+      t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
+    }
+    Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
+    __syncthreads();
+  }
+
+  // Tb = T diag(beta) (upper blocks zero), 8 consecutive elements of a row
+  // per thread, straight to the workspace
+  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+    const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
+    float v[8];
+    if ((j0 >> 4) > (r >> 4)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    } else {
+      const float4 a0 = *reinterpret_cast<const float4*>(A_s + r * L::LDF + j0);
+      const float4 a1 = *reinterpret_cast<const float4*>(A_s + r * L::LDF + j0 + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(b_s + j0);
+      const float4 b1 = *reinterpret_cast<const float4*>(b_s + j0 + 4);
+      v[0] = a0.x * b0.x; v[1] = a0.y * b0.y; v[2] = a0.z * b0.z; v[3] = a0.w * b0.w;
+      v[4] = a1.x * b1.x; v[5] = a1.y * b1.y; v[6] = a1.z * b1.z; v[7] = a1.w * b1.w;
+    }
+    store8(Tb_g + r * C + j0, v);
+  }
+}
+
+// ------------------------------------------------------------------ scan
 template <typename T, int D, int C, int NW, int CT>
 struct ScanLayout {
   static constexpr int NT = C / 16;
