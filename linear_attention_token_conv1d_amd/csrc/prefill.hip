@@ -156,7 +156,7 @@ __device__ __forceinline__ f32x4 tile_hi(const f32x4 (&t)[NT], int s) {
 }
 
 // ------------------------------------------------------------- workspace
-// [chunk offsets: n_seqs+1 int32, padded to 256 B]
+// [chunk offsets: n_seqs+1 int32, scan order: n_seqs int32, padded to 256 B]
 // [per (chunk, V head) record: Tb [C][C] T | P [C][C] T | vec [4][C] fp32]
 //  vec rows: gamma*rk, scale*gamma*rq, e*rk, gamma_last (broadcast)
 template <typename T, int C>
@@ -165,15 +165,22 @@ struct Rec {
   static constexpr size_t bytes = 2 * mat + 16 * (size_t)C;
 };
 
-__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs + 1) * 4 + 255) / 256 * 256; }
+// [chunk offsets: n_seqs+1 int32 | scan order: n_seqs int32], padded to 256 B
+__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs * 2 + 1) * 4 + 255) / 256 * 256; }
 
 __host__ __device__ inline int64_t max_chunks(int64_t T, int n_seqs, int C) { return T / C + n_seqs; }
 
 // ------------------------------------------------------------------ plan
+// One workgroup: chunk offsets of every packed sequence (exclusive prefix sum
+// of ceil(len / C)), then the scan order: sequences by chunk count, longest
+// first (ties by index), so that the longest serial chains start first.
+constexpr int kPlanSortMax = 2048;  // longer batches keep their own order
+
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs, int64_t total, int C,
                                                    int32_t* chunk_off) {
   __shared__ int32_t part[256];
   __shared__ int32_t carry;
+  __shared__ int32_t cnt_s[kPlanSortMax];
   const int tid = threadIdx.x;
   if (tid == 0) { carry = 0; chunk_off[0] = 0; }
   __syncthreads();
@@ -183,6 +190,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
     if (i < n_seqs) {
       const int64_t s = cu ? cu[i] : 0, e = cu ? cu[i + 1] : total;
       cnt = (int)((e - s + C - 1) / C);
+      if (i < kPlanSortMax) cnt_s[i] = cnt;
     }
     part[tid] = cnt;
     __syncthreads();
@@ -197,6 +205,46 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
     if (tid == 255) carry += part[255];
     __syncthreads();
   }
+  int32_t* order = chunk_off + n_seqs + 1;
+  for (int i = tid; i < n_seqs; i += 256) {
+    int rank = i;
+    if (n_seqs <= kPlanSortMax) {
+      const int ci = cnt_s[i];
+      rank = 0;
+      for (int j = 0; j < n_seqs; ++j) {
+        const int cj = cnt_s[j];
+        rank += (cj > ci) || (cj == ci && j < i);
+      }
+    }
+    order[rank] = i;
+  }
+}
+
+// Workgroup -> (sequence, V head, column block) for the scans.  The unit of
+// placement is a QK-head group: the grp = h_v / h_qk V heads (times NB column
+// blocks) that read the same K, Q and chunk rows.  Consecutive groups go to
+// consecutive XCDs (the hardware deals workgroups round-robin over the 8
+// XCDs), so one group shares an L2 while long chains spread over all XCDs;
+// groups are numbered in scan order (longest sequence first).
+struct ScanSlot {
+  int n, h, blk;
+  bool valid;
+};
+__device__ __forceinline__ ScanSlot scan_slot(const PrefillParams& p, const int32_t* order, int NB) {
+  const int grp = p.h_v / p.h_qk, gs = grp * NB, ngroups = p.n_seqs * p.h_qk;
+  const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int gi = (k / gs) * 8 + x, j = k % gs;
+  ScanSlot r{0, 0, 0, gi < ngroups};
+  if (r.valid) {
+    r.n = order[gi / p.h_qk];
+    r.h = (gi % p.h_qk) * grp + j / NB;
+    r.blk = j % NB;
+  }
+  return r;
+}
+inline unsigned scan_grid(int n_seqs, int h_qk, int h_v, int NB) {
+  const int ngroups = n_seqs * h_qk;
+  return (unsigned)(8 * ((ngroups + 7) / 8) * (h_v / h_qk) * NB);
 }
 
 // ---------------------------------------------------- LDS tile helpers
@@ -717,7 +765,7 @@ struct ScanLayout {
 };
 
 template <typename T, int D, int C, int NW, int CT>
-__global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const unsigned char* ws, int nwg) {
+__global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const unsigned char* ws) {
   using L = ScanLayout<T, D, C, NW, CT>;
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -731,15 +779,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   __shared__ __align__(16) unsigned char so0[L::stage_o ? L::obuf : 16];
   __shared__ __align__(16) unsigned char so1[L::stage_o ? L::obuf : 16];
 
-  // XCD-aware order: hardware places consecutive workgroups on consecutive
-  // XCDs, so logical neighbours (the blocks and V heads that read the same K
-  // and Q) are spread as (id % 8) * per_xcd + id / 8 to share an L2.
-  const int per_xcd = (nwg + 7) / 8;
-  const int wid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (wid >= nwg) return;
-  const int blk = wid % NB;
-  const int h = (wid / NB) % p.h_v;
-  const int n = wid / (NB * p.h_v);
+  const ScanSlot slot = scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
+  if (!slot.valid) return;
+  const int blk = slot.blk, h = slot.h, n = slot.n;
   const int hq = h / (p.h_v / p.h_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -1024,7 +1066,7 @@ __device__ __forceinline__ void barrier_vm() {
 }
 
 template <int D, int C>
-__global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsigned char* ws, int nwg) {
+__global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
   using L = Scan2Layout<D, C>;
   using T = __bf16;
   using M = Mma<T>;
@@ -1043,13 +1085,9 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
   __shared__ __align__(16) unsigned char sS[L::sbytes];
   __shared__ __align__(16) unsigned char sU[L::ubytes];
 
-  // XCD-aware order, as in the four-wave scan
-  const int per_xcd = (nwg + 7) / 8;
-  const int wid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (wid >= nwg) return;
-  const int blk = wid % NB;
-  const int h = (wid / NB) % p.h_v;
-  const int n = wid / (NB * p.h_v);
+  const ScanSlot slot = scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
+  if (!slot.valid) return;
+  const int blk = slot.blk, h = slot.h, n = slot.n;
   const int hq = h / (p.h_v / p.h_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -1300,7 +1338,7 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
 // Every launched variant is instantiated explicitly: clang does not always
 // emit the host launch stub of an implicitly instantiated kernel template
 // whose body holds capturing lambdas.
-#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C>(PrefillParams, const unsigned char*, int);
+#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C>(PrefillParams, const unsigned char*);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
 
@@ -1355,15 +1393,13 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     }
     if constexpr (sizeof(T) == 2) {
       using S2 = Scan2Layout<D, C>;
-      const int nwg = p.n_seqs * p.h_v * (D / S2::cols);
-      const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
+      const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / S2::cols);
       hipLaunchKernelGGL((scan2_kernel<D, C>), dim3(grid), dim3(512), 0, stream, p,
-                         static_cast<const unsigned char*>(ws), nwg);
+                         static_cast<const unsigned char*>(ws));
     } else {
-      const int nwg = p.n_seqs * p.h_v * (D / SL::cols);
-      const unsigned grid = (unsigned)((nwg + 7) / 8 * 8);
+      const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / SL::cols);
       hipLaunchKernelGGL((scan_kernel<T, D, C, NW, CT>), dim3(grid), dim3(SL::threads), 0, stream, p,
-                         static_cast<const unsigned char*>(ws), nwg);
+                         static_cast<const unsigned char*>(ws));
     }
     return hipGetLastError();
   }
