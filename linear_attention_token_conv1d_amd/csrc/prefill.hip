@@ -433,23 +433,25 @@ __device__ __forceinline__ typename Mma<T>::frag frag_kt(const unsigned char* ti
 // holds four consecutive columns of one row of P and of A: P goes straight
 // to the workspace and A to the fp32 work array of the UT solve, which
 // reuses the K/Q bytes.  Tb = T diag(beta) leaves in 16-byte row pieces.
-template <typename T, int D, int C>
+template <typename T, int D, int C, int VPW>
 struct PrepLayout {
   static constexpr int NT = C / 16;
   static constexpr int E = (int)sizeof(T);
   static constexpr int RBK = D * E;  // K, Q tile rows (swizzled)
   static constexpr int LDF = C + 4;
   static constexpr int LDZ = 20;
-  // phase 1: K, Q tiles
+  // phase 1 (shared by the V-head teams): K, Q tiles
   static constexpr int oK = 0;
   static constexpr int oQ = oK + C * RBK;
   static constexpr int kq_bytes = oQ + C * RBK;
-  // phase 2 (same bytes): A/T work array, block-product scratch
+  // phase 2 (same bytes): per team, the A/T work array and block-product scratch
   static constexpr int oA = 0;
   static constexpr int oZ = oA + C * LDF * 4;
-  static constexpr int work_bytes = oZ + 4 * 16 * LDZ * 4;
+  static constexpr int team_bytes = oZ + 4 * 16 * LDZ * 4;
+  static constexpr int work_bytes = VPW * team_bytes;
+  // row scalars: rk, rq (shared), then g, beta, G per team
   static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
-  static constexpr int bytes = oVec + 5 * C * 4;
+  static constexpr int bytes = oVec + (2 + 3 * VPW) * C * 4;
 };
 
 // Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
@@ -462,9 +464,9 @@ __device__ __forceinline__ int owner(const int32_t* off, int n_seqs, int c) {
   return lo;
 }
 
-template <typename T, int D, int C>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, unsigned char* ws) {
-  using L = PrepLayout<T, D, C>;
+template <typename T, int D, int C, int VPW>
+__global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams p, unsigned char* ws) {
+  using L = PrepLayout<T, D, C, VPW>;
   using M = Mma<T>;
   using R8 = Raw8<T>;
   using SK = Swz<L::RBK>;
@@ -472,50 +474,54 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
   constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
   constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
   constexpr int RT = D / 8;                    // threads per row in the load layout
+  constexpr int NTH = kPrepThreads * VPW;
   extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // four waves (one team) per V head: the teams share the K, Q load, the
+  // norms and the K, Q tiles, and run the per-V-head steps side by side
+  const int team = tid / kPrepThreads, ttid = tid % kPrepThreads, wave = ttid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
   unsigned char* K_s = smem + L::oK;
   unsigned char* Q_s = smem + L::oQ;
-  float* A_s = reinterpret_cast<float*>(smem + L::oA);
-  float* Z_s = reinterpret_cast<float*>(smem + L::oZ);
-  float* g_s = reinterpret_cast<float*>(smem + L::oVec);
+  float* A_s = reinterpret_cast<float*>(smem + team * L::team_bytes + L::oA);
+  float* Z_s = reinterpret_cast<float*>(smem + team * L::team_bytes + L::oZ);
+  float* rk_s = reinterpret_cast<float*>(smem + L::oVec);
+  float* rq_s = rk_s + C;
+  float* g_s = rk_s + (2 + 3 * team) * C;
   float* b_s = g_s + C;
   float* G_s = g_s + 2 * C;
-  float* rk_s = g_s + 3 * C;
-  float* rq_s = g_s + 4 * C;
 
   const int32_t* off = reinterpret_cast<const int32_t*>(ws);
-  const int ci = blockIdx.x, h = blockIdx.y;
+  const int ci = blockIdx.x, h = blockIdx.y * VPW + team;
   if (ci >= off[p.n_seqs]) return;
-  const int hq = h / (p.h_v / p.h_qk);
+  const int hq = h / (p.h_v / p.h_qk);  // the same for every team (VPW divides h_v / h_qk)
   const int n = owner(off, p.n_seqs, ci);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
   const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
   const int Lc = (int)min((int64_t)C, seq_end - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, l16 = lane & 15;
 
   // K, Q rows of this chunk and QK head; g, beta of this V head.  Rows past
   // the chunk re-read its last row and are zeroed below.
   const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
   const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
-  constexpr int NV = (C * RT + kPrepThreads - 1) / kPrepThreads;
+  constexpr int NV = (C * RT + NTH - 1) / NTH;
   R8 kv[NV], qv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = min(tid + i * kPrepThreads, C * RT - 1);
+    const int e = min(tid + i * NTH, C * RT - 1);
     const int r = min(e / RT, Lc - 1), d0 = (e % RT) * 8;
     kv[i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
     qv[i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
   }
-  const int ti = min(tid, Lc - 1);
+  const int ti = min(ttid, Lc - 1);
   const float gv = p.g[(t0 + ti) * p.h_v + h];
   const float bv = p.beta[(t0 + ti) * p.h_v + h];
 
   // row norms: the RT threads of a row are consecutive lanes
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = tid + i * kPrepThreads;
+    const int e = tid + i * NTH;
     const int r = e / RT, d0 = (e % RT) * 8;
     float fk[8], fq[8];
     if constexpr (sizeof(T) == 2) {
@@ -554,9 +560,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
       *reinterpret_cast<uint4*>(Q_s + SK::off(r, b)) = zq;
     }
   }
-  if (tid < C) {
-    g_s[tid] = tid < Lc ? gv : 0.f;
-    b_s[tid] = tid < Lc ? bv : 0.f;
+  if (ttid < C) {
+    g_s[ttid] = ttid < Lc ? gv : 0.f;
+    b_s[ttid] = ttid < Lc ? bv : 0.f;
   }
   __syncthreads();
 
@@ -597,12 +603,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
   T* Tb_g = reinterpret_cast<T*>(rec);
   T* P_g = reinterpret_cast<T*>(rec + Rec<T, C>::mat);
   float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
-  if (tid < C) {
-    const float G = G_s[tid], Gl = G_s[Lc - 1], eg = fexp(G);
-    vec_g[tid] = eg * rk_s[tid];
-    vec_g[C + tid] = p.scale * eg * rq_s[tid];
-    vec_g[2 * C + tid] = fexp(Gl - G) * rk_s[tid];
-    vec_g[3 * C + tid] = fexp(Gl);
+  if (ttid < C) {
+    const float G = G_s[ttid], Gl = G_s[Lc - 1], eg = fexp(G);
+    vec_g[ttid] = eg * rk_s[ttid];
+    vec_g[C + ttid] = p.scale * eg * rq_s[ttid];
+    vec_g[2 * C + ttid] = fexp(Gl - G) * rk_s[ttid];
+    vec_g[3 * C + ttid] = fexp(Gl);
   }
   // decay-masked tiles: A (strict lower, fp32, to LDS) and P (lower incl.
   // the diagonal, to the workspace); a lane holds row r, columns j0..j0+3
@@ -633,7 +639,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
   }
   // P above the diagonal tiles is zero
   constexpr int NUP = NT * (NT - 1) / 2 * 16 * 16 / 8;  // 8-element pieces of the upper tiles
-  for (int e = tid; e < NUP; e += kPrepThreads) {
+  for (int e = ttid; e < NUP; e += kPrepThreads) {
     int k = e / 32, mt = 0;  // tile k of the upper tiles, row-major (mt, tj > mt)
     while (k >= NT - 1 - mt) { k -= NT - 1 - mt; ++mt; }
     const int tj = mt + 1 + k, rr = (e % 32) / 2, half = e % 2;
@@ -670,7 +676,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
   // product that produces the T block in its position)
   auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
   auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
-  const int rr = tid >> 4, cc = tid & 15;
+  const int rr = ttid >> 4, cc = ttid & 15;
   if constexpr (NT >= 2) {
     // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
 #pragma unroll
@@ -718,7 +724,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrefillParams p, uns
 
   // Tb = T diag(beta) (upper blocks zero), 8 consecutive elements of a row
   // per thread, straight to the workspace
-  for (int e = tid; e < C * C / 8; e += kPrepThreads) {
+  for (int e = ttid; e < C * C / 8; e += kPrepThreads) {
     const int r = e / (C / 8), j0 = (e % (C / 8)) * 8;
     float v[8];
     if ((j0 >> 4) > (r >> 4)) {
@@ -1364,7 +1370,23 @@ constexpr int scan_lds_bytes() {
 
 template <typename T, int D, int C>
 constexpr bool fits() {
-  return PrepLayout<T, D, C>::bytes <= kLdsMax && scan_lds_bytes<T, D, C>() <= kLdsMax;
+  return PrepLayout<T, D, C, 1>::bytes <= kLdsMax && scan_lds_bytes<T, D, C>() <= kLdsMax;
+}
+
+template <typename T, int D, int C, int VPW>
+hipError_t launch_prep(const PrefillParams& p, unsigned char* ws, int64_t mc, hipStream_t stream) {
+  using PL = PrepLayout<T, D, C, VPW>;
+  if constexpr (PL::bytes > kLdsMax) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    auto prep = prep_kernel<T, D, C, VPW>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, PL::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep, dim3((unsigned)mc, (unsigned)(p.h_v / VPW)), dim3(kPrepThreads * VPW), PL::bytes,
+                       stream, p, ws);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int D, int C>
@@ -1373,22 +1395,20 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     return hipErrorInvalidConfiguration;  // rejected by prefill_supported() first
   } else {
     constexpr int NW = kScanWaves, CT = kScanTiles;
-    using PL = PrepLayout<T, D, C>;
     using SL = ScanLayout<T, D, C, NW, CT>;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs,
                        p.total_tokens, C, reinterpret_cast<int32_t*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto prep = prep_kernel<T, D, C>;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, PL::bytes);
-    if (e != hipSuccess) return e;
+    const int grp = p.h_v / p.h_qk;
+    const int vpw = sizeof(T) != 2 ? 1 : grp % 4 == 0 ? 4 : grp % 3 == 0 ? 3 : grp % 2 == 0 ? 2 : 1;
     if (p.total_tokens > 0) {
       const int64_t mc = max_chunks(p.total_tokens, p.n_seqs, C);
-      hipLaunchKernelGGL(prep, dim3((unsigned)mc, (unsigned)p.h_v), dim3(kPrepThreads), PL::bytes,
-                         stream, p, ws);
-      e = hipGetLastError();
+      e = vpw == 4 ? launch_prep<T, D, C, 4>(p, ws, mc, stream)
+        : vpw == 3 ? launch_prep<T, D, C, 3>(p, ws, mc, stream)
+        : vpw == 2 ? launch_prep<T, D, C, 2>(p, ws, mc, stream)
+                   : launch_prep<T, D, C, 1>(p, ws, mc, stream);
       if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(T) == 2) {
