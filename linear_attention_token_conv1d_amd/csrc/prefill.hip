@@ -355,13 +355,16 @@ struct DmaPlan {
       off[k] = (uint32_t)r * gstride + (uint32_t)S::slot(r, q % S::CPR) * 16u;
     }
   }
+  // instruction k of this wave (no-op past the tile)
+  __device__ __forceinline__ void issue_one(int k, unsigned char* lds, const unsigned char* gbase, int wave,
+                                            int lane) const {
+    const int q0 = (k * NWAVES + wave) * 64;
+    if (q0 < TOTAL && q0 + lane < TOTAL)
+      __builtin_amdgcn_global_load_lds(gbase + off[k], (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
+  }
   __device__ __forceinline__ void issue(unsigned char* lds, const unsigned char* gbase, int wave, int lane) const {
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int q0 = (k * NWAVES + wave) * 64;
-      if (q0 < TOTAL && q0 + lane < TOTAL)
-        __builtin_amdgcn_global_load_lds(gbase + off[k], (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, 0);
-    }
+    for (int k = 0; k < NI; ++k) issue_one(k, lds, gbase, wave, lane);
   }
 };
 
@@ -1116,46 +1119,47 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
   auto chunk_len = [&](int c) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
   auto chunk_rec = [&](int c) { return recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes; };
 
-  // ---- data movement: every wave issues its share of the next chunk's
-  // direct-to-LDS loads at the start of a chunk.  A full chunk uses per-lane
-  // offsets computed once (DmaPlan); a partial chunk (the last of a
-  // sequence) takes the clamped path, where rows past its end re-read its
-  // last row: they only meet zero columns of Tb and zero rows of U.
-  DmaPlan<SK, C, 8> pk, pq;
-  DmaPlan<SC, C, 8> ptb;
-  DmaPlan<SV, C, 8> pv;
+  // ---- data movement.  Chunk 0 is loaded by all eight waves before the
+  // roles split; after that only the output waves move data, in pieces
+  // between their own products, so that no wave ever waits long to issue
+  // and the chain waves issue nothing.  A full chunk uses per-lane offsets
+  // computed once (DmaPlan); a partial chunk (the last of a sequence) takes
+  // the clamped path, where rows past its end re-read its last row: they
+  // only meet zero columns of Tb and zero rows of U.
+  DmaPlan<SK, C, 4> pk, pq;
+  DmaPlan<SC, C, 4> ptb;
+  DmaPlan<SV, C, 4> pv;
   const bool fast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) &&
                     p.v_stride * 2 * C < (1ll << 31);
-  if (fast) {
-    pk.init((uint32_t)(p.k_stride * 2), wave, lane);
-    pq.init((uint32_t)(p.q_stride * 2), wave, lane);
-    ptb.init((uint32_t)L::RBC, wave, lane);
-    pv.init((uint32_t)(p.v_stride * 2), wave, lane);
+  if (fast && !chain) {
+    pk.init((uint32_t)(p.k_stride * 2), cw, lane);
+    pq.init((uint32_t)(p.q_stride * 2), cw, lane);
+    ptb.init((uint32_t)L::RBC, cw, lane);
+    pv.init((uint32_t)(p.v_stride * 2), cw, lane);
   }
-  auto issue = [&](int c, unsigned char* b) {
+  auto chunk_ptrs = [&](int c, const unsigned char*& kc, const unsigned char*& qc, const unsigned char*& vc,
+                        const unsigned char*& rec) {
     const int64_t t0 = chunk_t0(c);
+    kc = kg + t0 * p.k_stride * 2;
+    qc = qg + t0 * p.q_stride * 2;
+    vc = vg + t0 * p.v_stride * 2;
+    rec = chunk_rec(c);
+  };
+  // clamped (any chunk), over NW waves with wave index w
+  auto issue_slow = [&](int c, unsigned char* b, auto nw, int w) {
+    constexpr int NW = decltype(nw)::value;
+    const unsigned char *kc, *qc, *vc, *rec;
+    chunk_ptrs(c, kc, qc, vc, rec);
     const int Lc = chunk_len(c);
-    const unsigned char* rec = chunk_rec(c);
-    const unsigned char* kc = kg + t0 * p.k_stride * 2;
-    const unsigned char* qc = qg + t0 * p.q_stride * 2;
-    const unsigned char* vc = vg + t0 * p.v_stride * 2;
-    if (fast && Lc == C) {
-      pk.issue(b + L::oK, kc, wave, lane);
-      pq.issue(b + L::oQ, qc, wave, lane);
-      ptb.issue(b + L::oTb, rec, wave, lane);
-      ptb.issue(b + L::oP, rec + Rec<T, C>::mat, wave, lane);
-      pv.issue(b + L::oV, vc, wave, lane);
-    } else {
-      dma_tile_s<SK, C, 8>(b + L::oK, kc, p.k_stride * 2, Lc, wave, lane);
-      dma_tile_s<SK, C, 8>(b + L::oQ, qc, p.q_stride * 2, Lc, wave, lane);
-      dma_tile_s<SC, C, 8>(b + L::oTb, rec, L::RBC, C, wave, lane);
-      dma_tile_s<SC, C, 8>(b + L::oP, rec + Rec<T, C>::mat, L::RBC, C, wave, lane);
-      dma_tile_s<SV, C, 8>(b + L::oV, vc, p.v_stride * 2, Lc, wave, lane);
-    }
-    dma_linear<16 * C, 8>(b + L::oVec, rec + 2 * Rec<T, C>::mat, wave, lane);
+    dma_tile_s<SK, C, NW>(b + L::oK, kc, p.k_stride * 2, Lc, w, lane);
+    dma_tile_s<SK, C, NW>(b + L::oQ, qc, p.q_stride * 2, Lc, w, lane);
+    dma_tile_s<SC, C, NW>(b + L::oTb, rec, L::RBC, C, w, lane);
+    dma_tile_s<SC, C, NW>(b + L::oP, rec + Rec<T, C>::mat, L::RBC, C, w, lane);
+    dma_tile_s<SV, C, NW>(b + L::oV, vc, p.v_stride * 2, Lc, w, lane);
+    dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, w, lane);
   };
 
-  if (nch > 0) issue(0, sb0);
+  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, 8>{}, wave);
 
   if (chain) {
     // ---------------------------------------------------------- chain waves
@@ -1181,8 +1185,7 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
     publish_state();
     __syncthreads();  // initial state published; chunk 0 has landed
 
-    auto step = [&](int c, const unsigned char* cur, unsigned char* nxt) {
-      if (c + 1 < nch) issue(c + 1, nxt);
+    auto step = [&](const unsigned char* cur) {
       const unsigned char* K_t = cur + L::oK;
       const unsigned char* Tb_t = cur + L::oTb;
       const unsigned char* V_t = cur + L::oV;
@@ -1268,8 +1271,8 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
       __syncthreads();  // B2: next chunk loaded, new state published
     };
     for (int c = 0; c < nch; c += 2) {
-      step(c, sb0, sb1);
-      if (c + 1 < nch) step(c + 1, sb1, sb0);
+      step(sb0);
+      if (c + 1 < nch) step(sb1);
     }
     if (p.final_state) {
 #pragma unroll
@@ -1299,17 +1302,29 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
     __syncthreads();  // chunk 0 has landed; the initial state is published
 
     auto step = [&](int c, const unsigned char* cur, unsigned char* nxt) {
-      const bool more = c + 1 < nch;
       if (c > 0) store_o(chunk_t0(c - 1), C);
+      // the next chunk: full ones in pieces, a partial one at once
+      const bool more = c + 1 < nch;
+      const bool pieces = more && fast && chunk_len(c + 1) == C;
+      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, 4>{}, cw);
+      const unsigned char *kc, *qc, *vc, *rec;
+      chunk_ptrs(more ? c + 1 : c, kc, qc, vc, rec);
       const unsigned char* Q_t = cur + L::oQ;
       const unsigned char* P_t = cur + L::oP;
       const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
-      if (more) issue(c + 1, nxt);
-      // Y^T = S Q^T, columns scaled by scale gamma rq
+      // Y^T = S Q^T, columns scaled by scale gamma rq; K and Q of the next
+      // chunk go out one instruction each per k-step
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DKS; ++s) {
+      for (int s = 0; s < D / 32; ++s) {
+        if (pieces) {
+#pragma unroll
+          for (int k = s * decltype(pk)::NI / (D / 32); k < (s + 1) * decltype(pk)::NI / (D / 32); ++k) {
+            pk.issue_one(k, nxt + L::oK, kc, cw, lane);
+            pq.issue_one(k, nxt + L::oQ, qc, cw, lane);
+          }
+        }
         const frag as = frag_row_s<T, SS>(sS, col, 32 * s + 8 * g4, false);
         frag bq[NT];
 #pragma unroll
@@ -1320,6 +1335,12 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt] *= vec[C + pidx<NT>(nt, l16)];
       barrier_vm<63>();  // B1
+      if (pieces) {
+        ptb.issue(nxt + L::oTb, rec, cw, lane);
+        ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, cw, lane);
+        pv.issue(nxt + L::oV, vc, cw, lane);
+        dma_linear<16 * C, 4>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, cw, lane);
+      }
       // O^T += U^T P^T
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -1331,7 +1352,7 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) M::mma(o[nt], au, bp[nt], HALF);
       }
-      __syncthreads();  // B2
+      __syncthreads();  // B2: the next chunk has landed
     };
     for (int c = 0; c < nch; c += 2) {
       step(c, sb0, sb1);
