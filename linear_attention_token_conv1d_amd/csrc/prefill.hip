@@ -1074,8 +1074,8 @@ __device__ __forceinline__ void barrier_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int C>
-__global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
+template <int D, int C, int CT>
+__global__ __launch_bounds__(128 * (4 / CT)) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
   using L = Scan2Layout<D, C>;
   using T = __bf16;
   using M = Mma<T>;
@@ -1089,6 +1089,8 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
   constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
   constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
   constexpr int NB = D / L::cols;
+  constexpr int NWR = 4 / CT;       // waves per role
+  constexpr int SW = 16 * CT;       // columns per wave
   __shared__ __align__(16) unsigned char sb0[L::buf];
   __shared__ __align__(16) unsigned char sb1[L::buf];
   __shared__ __align__(16) unsigned char sS[L::sbytes];
@@ -1100,9 +1102,9 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
   const int hq = h / (p.h_v / p.h_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const bool chain = wave < 4;
-  const int cw = wave & 3;           // 16-column slice of this wave
-  const int col = 16 * cw + l16;     // this lane's column in the block
+  const bool chain = wave < NWR;
+  const int cw = wave % NWR;  // column slice of this wave: columns SW cw .. SW cw + SW - 1
+  auto colof = [&](int ct) { return SW * cw + 16 * ct + l16; };  // this lane's column in tile ct
 
   const int32_t* off = reinterpret_cast<const int32_t*>(ws);
   const unsigned char* recs = ws + off_bytes(p.n_seqs);
@@ -1119,16 +1121,16 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
   auto chunk_len = [&](int c) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
   auto chunk_rec = [&](int c) { return recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes; };
 
-  // ---- data movement.  Chunk 0 is loaded by all eight waves before the
-  // roles split; after that only the output waves move data, in pieces
-  // between their own products, so that no wave ever waits long to issue
-  // and the chain waves issue nothing.  A full chunk uses per-lane offsets
-  // computed once (DmaPlan); a partial chunk (the last of a sequence) takes
-  // the clamped path, where rows past its end re-read its last row: they
-  // only meet zero columns of Tb and zero rows of U.
-  DmaPlan<SK, C, 4> pk, pq;
-  DmaPlan<SC, C, 4> ptb;
-  DmaPlan<SV, C, 4> pv;
+  // ---- data movement.  Chunk 0 is loaded by all waves before the roles
+  // split; after that only the output waves move data, in pieces between
+  // their own products, so that no wave ever waits long to issue and the
+  // chain waves issue nothing.  A full chunk uses per-lane offsets computed
+  // once (DmaPlan); a partial chunk (the last of a sequence) takes the
+  // clamped path, where rows past its end re-read its last row: they only
+  // meet zero columns of Tb and zero rows of U.
+  DmaPlan<SK, C, NWR> pk, pq;
+  DmaPlan<SC, C, NWR> ptb;
+  DmaPlan<SV, C, NWR> pv;
   const bool fast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) &&
                     p.v_stride * 2 * C < (1ll << 31);
   if (fast && !chain) {
@@ -1159,28 +1161,33 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
     dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, w, lane);
   };
 
-  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, 8>{}, wave);
+  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, 2 * NWR>{}, wave);
 
   if (chain) {
     // ---------------------------------------------------------- chain waves
-    // state S^T (d_k x 16 columns) in DT accumulator tiles; row 4g+i of tile
-    // dt is d_k index pidx<DT>(dt, 4g+i)
-    f32x4 st[DT];
-    const size_t srow = (((size_t)n * p.h_v + h) * D + (size_t)(blk * L::cols + col)) * D;
+    // state S^T (d_k x 16 columns) of column tile ct in DT accumulator
+    // tiles; row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
+    f32x4 st[CT][DT];
+    auto srow = [&](int ct) { return (((size_t)n * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D; };
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      st[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (p.initial_state) {
-        const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + srow + pidx<DT>(dt, 4 * g4));
-        st[dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        st[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.initial_state) {
+          const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + srow(ct) + pidx<DT>(dt, 4 * g4));
+          st[ct][dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+        }
       }
-    }
     // the state as bf16 rows [column][d_k] for the output waves: tiles 2u,
     // 2u+1 give this lane d_k 32u + 8g .. 32u + 8g + 7
     auto publish_state = [&]() {
 #pragma unroll
-      for (int u = 0; u < DT / 2; ++u)
-        *reinterpret_cast<frag*>(sS + SS::off(col, (32 * u + 8 * g4) * 2)) = M::acc(st[2 * u], st[2 * u + 1]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int u = 0; u < DT / 2; ++u)
+          *reinterpret_cast<frag*>(sS + SS::off(colof(ct), (32 * u + 8 * g4) * 2)) =
+              M::acc(st[ct][2 * u], st[ct][2 * u + 1]);
     };
     publish_state();
     __syncthreads();  // initial state published; chunk 0 has landed
@@ -1191,80 +1198,108 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
       const unsigned char* V_t = cur + L::oV;
       const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
       // operands of R and U that do not depend on the state, read up front:
-      // V[token pidx(mt, 4g) + e][col] (one transposing read per tile) and Tb
-      uint2 vw[NT];
+      // V[token pidx(mt, 4g) + e][column] (one transposing read per tile) and Tb
+      uint2 vw[CT][NT];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        const int r0 = pidx<NT>(mt, 4 * g4);
-        vw[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(
-            __attribute__((address_space(3))) unsigned char*)(V_t + SV::off(r0 + (l16 >> 2), (16 * cw + 4 * (l16 & 3)) * 2))));
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          const int r0 = pidx<NT>(mt, 4 * g4);
+          vw[ct][mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(
+              __attribute__((address_space(3))) unsigned char*)(V_t + SV::off(r0 + (l16 >> 2),
+                                                                               (SW * cw + 16 * ct + 4 * (l16 & 3)) * 2))));
+        }
       frag at[KS][NT];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
           at[s][mt] = frag_row_s<T, SC>(Tb_t, pidx<NT>(mt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
-      // X1 = K S^T
-      f32x4 x1[NT];
+      // X1 = K S^T: each K fragment feeds every column tile
+      f32x4 x1[CT][NT];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) x1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) x1[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DKS; ++s) {
-        const frag bs = M::acc(st[2 * s], st[2 * s + 1]);
-        frag ak[NT];
+        frag bs[CT], ak[NT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(st[ct][2 * s], st[ct][2 * s + 1]);
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) ak[mt] = frag_row_s<T, SK>(K_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) M::mma(x1[mt], ak[mt], bs, false);
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(x1[ct][mt], ak[mt], bs[ct], false);
       }
       // R = V - diag(gamma rk) X1
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
         const float4 vq = *reinterpret_cast<const float4*>(vec + pidx<NT>(mt, 4 * g4));
-        x1[mt][0] = bf16_lo(vw[mt].x) - vq.x * x1[mt][0];
-        x1[mt][1] = bf16_hi(vw[mt].x) - vq.y * x1[mt][1];
-        x1[mt][2] = bf16_lo(vw[mt].y) - vq.z * x1[mt][2];
-        x1[mt][3] = bf16_hi(vw[mt].y) - vq.w * x1[mt][3];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          x1[ct][mt][0] = bf16_lo(vw[ct][mt].x) - vq.x * x1[ct][mt][0];
+          x1[ct][mt][1] = bf16_hi(vw[ct][mt].x) - vq.y * x1[ct][mt][1];
+          x1[ct][mt][2] = bf16_lo(vw[ct][mt].y) - vq.z * x1[ct][mt][2];
+          x1[ct][mt][3] = bf16_hi(vw[ct][mt].y) - vq.w * x1[ct][mt][3];
+        }
       }
       // U = Tb R
-      f32x4 u[NT];
+      f32x4 u[CT][NT];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) u[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) u[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const frag bs = M::acc(x1[2 * s], tile_hi<NT>(x1, s));
+        frag bs[CT];
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) M::mma(u[mt], at[s][mt], bs, HALF);
+        for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(x1[ct][2 * s], tile_hi<NT>(x1[ct], s));
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(u[ct][mt], at[s][mt], bs[ct], HALF);
       }
       // publish U as bf16 rows [column][token] (natural token order)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (HALF) {
-          *reinterpret_cast<uint2*>(sU + SU::off(col, 8 * g4)) =
-              make_uint2(pack_bf16x2(u[0][0], u[0][1]), pack_bf16x2(u[0][2], u[0][3]));
-        } else {
-          *reinterpret_cast<frag*>(sU + SU::off(col, (32 * s + 8 * g4) * 2)) = M::acc(u[2 * s], u[2 * s + 1]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if constexpr (HALF) {
+            *reinterpret_cast<uint2*>(sU + SU::off(colof(ct), 8 * g4)) =
+                make_uint2(pack_bf16x2(u[ct][0][0], u[ct][0][1]), pack_bf16x2(u[ct][0][2], u[ct][0][3]));
+          } else {
+            *reinterpret_cast<frag*>(sU + SU::off(colof(ct), (32 * s + 8 * g4) * 2)) =
+                M::acc(u[ct][2 * s], u[ct][2 * s + 1]);
+          }
         }
-      }
       // U' = diag(e rk) U for the state update
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
         const float4 vq = *reinterpret_cast<const float4*>(vec + 2 * C + pidx<NT>(mt, 4 * g4));
-        u[mt][0] *= vq.x; u[mt][1] *= vq.y; u[mt][2] *= vq.z; u[mt][3] *= vq.w;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          u[ct][mt][0] *= vq.x; u[ct][mt][1] *= vq.y; u[ct][mt][2] *= vq.z; u[ct][mt][3] *= vq.w;
+        }
       }
       const float gl = vec[3 * C];
       barrier_vm<63>();  // B1: U is visible; the output waves are done with the old state
-      // S^T <- gamma_last S^T + K^T diag(e rk) U
+      // S^T <- gamma_last S^T + K^T diag(e rk) U: each K^T fragment feeds every column tile
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st[dt] *= gl;
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st[ct][dt] *= gl;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const frag bs = M::acc(u[2 * s], tile_hi<NT>(u, s));
+        frag bs[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(u[ct][2 * s], tile_hi<NT>(u[ct], s));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const frag ak = frag_kt<T, L::RBK, DT>(K_t, dt, HALF ? 4 * g4 : 32 * s + 8 * g4, l16, HALF);
-          M::mma(st[dt], ak, bs, HALF);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], ak, bs[ct], HALF);
         }
       }
       publish_state();
@@ -1276,28 +1311,32 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
     }
     if (p.final_state) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(p.final_state + srow + pidx<DT>(dt, 4 * g4)) =
-            make_float4(st[dt][0], st[dt][1], st[dt][2], st[dt][3]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(p.final_state + srow(ct) + pidx<DT>(dt, 4 * g4)) =
+              make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
   } else {
     // --------------------------------------------------------- output waves
     const int64_t o_stride = (int64_t)p.h_v * D;
-    T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols + 16 * cw + 4 * g4;
-    // O^T tile nt: rows 4g+i = columns 16cw + 4g + i, column l16 = token
-    // pidx(nt, l16) of the chunk
-    f32x4 o[NT];
+    T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols + SW * cw + 4 * g4;
+    // O^T tile (ct, nt): rows 4g+i = columns SW cw + 16 ct + 4g + i, column
+    // l16 = token pidx(nt, l16) of the chunk
+    f32x4 o[CT][NT];
     int64_t orow[NT];  // element offset of this lane's token row in each tile
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) orow[nt] = (int64_t)pidx<NT>(nt, l16) * o_stride;
     auto store_o = [&](int64_t t0, int Lc) {
       T* oc = og + t0 * o_stride;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (pidx<NT>(nt, l16) < Lc)
-          *reinterpret_cast<uint2*>(oc + orow[nt]) =
-              make_uint2(pack_bf16x2(o[nt][0], o[nt][1]), pack_bf16x2(o[nt][2], o[nt][3]));
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (pidx<NT>(nt, l16) < Lc)
+            *reinterpret_cast<uint2*>(oc + orow[nt] + 16 * ct) =
+                make_uint2(pack_bf16x2(o[ct][nt][0], o[ct][nt][1]), pack_bf16x2(o[ct][nt][2], o[ct][nt][3]));
+        }
     };
     __syncthreads();  // chunk 0 has landed; the initial state is published
 
@@ -1306,16 +1345,18 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
       // the next chunk: full ones in pieces, a partial one at once
       const bool more = c + 1 < nch;
       const bool pieces = more && fast && chunk_len(c + 1) == C;
-      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, 4>{}, cw);
+      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, NWR>{}, cw);
       const unsigned char *kc, *qc, *vc, *rec;
       chunk_ptrs(more ? c + 1 : c, kc, qc, vc, rec);
       const unsigned char* Q_t = cur + L::oQ;
       const unsigned char* P_t = cur + L::oP;
       const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
       // Y^T = S Q^T, columns scaled by scale gamma rq; K and Q of the next
-      // chunk go out one instruction each per k-step
+      // chunk go out a few instructions per k-step
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         if (pieces) {
@@ -1325,32 +1366,42 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
             pq.issue_one(k, nxt + L::oQ, qc, cw, lane);
           }
         }
-        const frag as = frag_row_s<T, SS>(sS, col, 32 * s + 8 * g4, false);
-        frag bq[NT];
+        frag as[CT], bq[NT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) as[ct] = frag_row_s<T, SS>(sS, colof(ct), 32 * s + 8 * g4, false);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) bq[nt] = frag_row_s<T, SK>(Q_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) M::mma(o[nt], as, bq[nt], false);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], as[ct], bq[nt], false);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt] *= vec[C + pidx<NT>(nt, l16)];
+      for (int nt = 0; nt < NT; ++nt) {
+        const float sc = vec[C + pidx<NT>(nt, l16)];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= sc;
+      }
       barrier_vm<63>();  // B1
       if (pieces) {
         ptb.issue(nxt + L::oTb, rec, cw, lane);
         ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, cw, lane);
         pv.issue(nxt + L::oV, vc, cw, lane);
-        dma_linear<16 * C, 4>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, cw, lane);
+        dma_linear<16 * C, NWR>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, cw, lane);
       }
       // O^T += U^T P^T
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const frag au = frag_row_s<T, SU>(sU, col, HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
-        frag bp[NT];
+        frag au[CT], bp[NT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) au[ct] = frag_row_s<T, SU>(sU, colof(ct), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(nt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) M::mma(o[nt], au, bp[nt], HALF);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], au[ct], bp[nt], HALF);
       }
       __syncthreads();  // B2: the next chunk has landed
     };
@@ -1365,7 +1416,11 @@ __global__ __launch_bounds__(512) void scan2_kernel(PrefillParams p, const unsig
 // Every launched variant is instantiated explicitly: clang does not always
 // emit the host launch stub of an implicitly instantiated kernel template
 // whose body holds capturing lambdas.
-#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C>(PrefillParams, const unsigned char*);
+#ifndef GDN_SCAN2_CT
+#define GDN_SCAN2_CT 1
+#endif
+constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave (1: 8 waves, 2: 4 waves)
+#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C, kScan2Tiles>(PrefillParams, const unsigned char*);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
 
@@ -1435,7 +1490,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
       using S2 = Scan2Layout<D, C>;
       const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / S2::cols);
-      hipLaunchKernelGGL((scan2_kernel<D, C>), dim3(grid), dim3(512), 0, stream, p,
+      hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles>), dim3(grid), dim3(128 * (4 / kScan2Tiles)), 0, stream, p,
                          static_cast<const unsigned char*>(ws));
     } else {
       const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / SL::cols);
