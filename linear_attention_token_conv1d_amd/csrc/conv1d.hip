@@ -124,6 +124,38 @@ __global__ __launch_bounds__(kThreads) void conv1d_kernel(ConvParams p) {
     }
   }
 
+  // fast path: a full tile inside one sequence.  Every load of a batch is
+  // issued with no branch around it, so the batch's loads are in flight
+  // together.
+  if (t1 - t0 == kTile && seq_end >= t1) {
+    for (int64_t tb = t0; tb < t1; tb += kBatch) {
+      typename Vec8<T>::type raw[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) raw[i] = ld8raw(x + (tb + i) * C + c0);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        float xv[8];
+        unpack8(raw[i], xv);
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = bias[e];
+#pragma unroll
+          for (int j = 0; j < W - 1; ++j) acc += w[j][e] * win[j][e];
+          acc += w[W - 1][e] * xv[e];
+          out[e] = p.act ? silu(acc) : acc;
+        }
+        store8(y + (tb + i) * C + c0, out);
+#pragma unroll
+        for (int j = 0; j + 1 < W - 1; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) win[j][e] = win[j + 1][e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) win[W - 2][e] = xv[e];
+      }
+    }
+    return;
+  }
   for (int64_t tb = t0; tb < t1; tb += kBatch) {
     typename Vec8<T>::type raw[kBatch];
 #pragma unroll

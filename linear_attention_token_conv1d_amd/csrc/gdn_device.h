@@ -161,6 +161,8 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+// y * sigmoid(y) with a reciprocal-based divide (within a few ulp; 0 for
+// very negative y, where 1 + e^-y overflows and the reciprocal is 0)
+__device__ __forceinline__ float silu(float y) { return __fdividef(y, 1.0f + __expf(-y)); }
 
 }  // namespace gdn
