@@ -274,11 +274,16 @@ struct RowK {  // token-major K/Q tiles of 16+ chunks: fragment rows in pidx ord
 struct RowT {  // narrower tiles (Tb, P; K/Q when d_k = 64)
   static __device__ __forceinline__ int f(int r) { return ((r >> 1) & 1) | (((r >> 3) & 3) << 1); }
 };
-template <int NT>
-struct RowV {  // V tile read by the transposing loads: rows b..b+3 and b+8..b+11 on distinct banks
+template <int NT, int CPR>
+struct RowV {  // V tile read by the transposing loads: the rows a 32-lane pass reads on distinct banks
   static __device__ __forceinline__ int f(int r) {
-    if constexpr (NT == 1) return (((r >> 1) & 1) | (((r >> 2) & 1) << 1)) << 1;
-    else return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1;
+    if constexpr (CPR >= 8) {
+      if constexpr (NT == 1) return (((r >> 1) & 1) | (((r >> 2) & 1) << 1)) << 1;
+      else return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1;
+    } else {
+      if constexpr (NT == 1) return ((r >> 2) & 1) << 1;
+      else return ((r >> 3) & 1) << 1;
+    }
   }
 };
 template <int RB>
@@ -1036,14 +1041,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 // direct-to-LDS loads at the start of a chunk.  Per chunk: barrier B1 after U
 // is published (LDS only: the loads stay in flight), and B2 at the end (the
 // next chunk has landed, the new state is published).
-template <int D, int C>
+template <int D, int C, int COLS>
 struct Scan2Layout {
   static constexpr int NT = C / 16, DT = D / 16;
-  static constexpr int cols = 64;  // d_v columns per workgroup
+  static constexpr int cols = COLS;  // d_v columns per workgroup
   static constexpr int RBK = D * 2, RBC = C * 2, RBV = cols * 2, RBS = D * 2, RBU = C * 2;
   using SK = Swz<RBK>;
   using SC = Swz<RBC>;
-  using SV = SwzT<RBV, RowV<NT>>;
+  using SV = SwzT<RBV, RowV<NT, RBV / 16>>;
   using SS = SwzT<RBS, RowSeq<RBS>>;
   using SU = SwzT<RBU, RowSeq<RBU>>;
   static constexpr int oK = 0;
@@ -1074,9 +1079,9 @@ __device__ __forceinline__ void barrier_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int C, int CT>
-__global__ __launch_bounds__(128 * (4 / CT)) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
-  using L = Scan2Layout<D, C>;
+template <int D, int C, int CT, int NWR>
+__global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
+  using L = Scan2Layout<D, C, 16 * CT * NWR>;
   using T = __bf16;
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -1089,7 +1094,7 @@ __global__ __launch_bounds__(128 * (4 / CT)) void scan2_kernel(PrefillParams p, 
   constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
   constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
   constexpr int NB = D / L::cols;
-  constexpr int NWR = 4 / CT;       // waves per role
+  // NWR waves per role
   constexpr int SW = 16 * CT;       // columns per wave
   __shared__ __align__(16) unsigned char sb0[L::buf];
   __shared__ __align__(16) unsigned char sb1[L::buf];
@@ -1419,8 +1424,13 @@ __global__ __launch_bounds__(128 * (4 / CT)) void scan2_kernel(PrefillParams p, 
 #ifndef GDN_SCAN2_CT
 #define GDN_SCAN2_CT 1
 #endif
-constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave (1: 8 waves, 2: 4 waves)
-#define GDN_SCAN2(D, C) template __global__ void scan2_kernel<D, C, kScan2Tiles>(PrefillParams, const unsigned char*);
+constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave
+// Two workgroup widths: 64 columns (four waves per role, two waves per SIMD)
+// for launches that fill the chip, 32 columns (two waves per role) to spread
+// a few long chains over twice as many CUs.
+#define GDN_SCAN2(D, C) \
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>(PrefillParams, const unsigned char*); \
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>(PrefillParams, const unsigned char*);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
 
@@ -1440,7 +1450,7 @@ constexpr int kScanTiles = GDN_SCAN_TILES;
 // bf16 runs the split-role scan, fp32 the four-wave scan
 template <typename T, int D, int C>
 constexpr int scan_lds_bytes() {
-  if constexpr (sizeof(T) == 2) return Scan2Layout<D, C>::bytes;
+  if constexpr (sizeof(T) == 2) return Scan2Layout<D, C, 64>::bytes;
   else return ScanLayout<T, D, C, kScanWaves, kScanTiles>::bytes;
 }
 
@@ -1488,10 +1498,18 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(T) == 2) {
-      using S2 = Scan2Layout<D, C>;
-      const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / S2::cols);
-      hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles>), dim3(grid), dim3(128 * (4 / kScan2Tiles)), 0, stream, p,
-                         static_cast<const unsigned char*>(ws));
+      // narrow workgroups when even they leave CUs idle
+      constexpr int kCUs = 256;
+      const bool narrow = (int64_t)p.n_seqs * p.h_v * (D / 32) <= kCUs;
+      if (narrow) {
+        const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 32);
+        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>), dim3(grid), dim3(128 * (2 / kScan2Tiles)),
+                           0, stream, p, static_cast<const unsigned char*>(ws));
+      } else {
+        const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 64);
+        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3(grid), dim3(128 * (4 / kScan2Tiles)),
+                           0, stream, p, static_cast<const unsigned char*>(ws));
+      }
     } else {
       const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / SL::cols);
       hipLaunchKernelGGL((scan_kernel<T, D, C, NW, CT>), dim3(grid), dim3(SL::threads), 0, stream, p,
