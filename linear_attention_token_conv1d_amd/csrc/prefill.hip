@@ -626,14 +626,19 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
     if (job < 2 * NLT) {
       const bool isP = job >= NLT;
       const int r = jmt[jj] * 16 + l16, j0 = jnt[jj] * 16 + 4 * g4;
+      // row factor (scale rq_r for P, beta_r rk_r for A) and the four
+      // columns' G and rk, each read once
       const float Gr = G_s[r];
+      const float fr = isP ? p.scale * rq_s[r] : b_s[r] * rk_s[r];
+      const float4 Gj = *reinterpret_cast<const float4*>(G_s + j0);
+      const float4 kj = *reinterpret_cast<const float4*>(rk_s + j0);
+      const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w}, rkj[4] = {kj.x, kj.y, kj.z, kj.w};
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + i;
-        const float dec = (j <= r) ? fexp(Gr - G_s[j]) : 0.f;
-        v[i] = isP ? p.scale * dec * rq_s[r] * rk_s[j] * gram[jj][i]
-                   : ((j < r) ? b_s[r] * dec * rk_s[r] * rk_s[j] * gram[jj][i] : 0.f);
+        const bool keep = isP ? j <= r : j < r;
+        v[i] = keep ? fr * fexp(Gr - gj[i]) * rkj[i] * gram[jj][i] : 0.f;
       }
       if (isP) {
         if constexpr (sizeof(T) == 2)
