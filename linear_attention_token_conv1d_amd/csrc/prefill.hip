@@ -155,6 +155,16 @@ __device__ __forceinline__ f32x4 tile_hi(const f32x4 (&t)[NT], int s) {
   return i < NT ? t[i < NT ? i : 0] : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Y^T W + acc for 16x16 fp32 tiles held in the accumulator layout (lane
+// (g, c) holds rows 4g..4g+3 of column c): MFMA s sums over k = 4g + s, its
+// A operand being register s of Y's tile (Y[4g+s][c] = Y^T[c][4g+s]) and its
+// B operand register s of W's tile.
+__device__ __forceinline__ f32x4 mfma_tn(const f32x4& y, const f32x4& w, f32x4 acc) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(y[s], w[s], acc, 0, 0, 0);
+  return acc;
+}
+
 // ------------------------------------------------------------- workspace
 // [chunk offsets: n_seqs+1 int32, scan order: n_seqs int32, padded to 256 B]
 // [per (chunk, V head) record: Tb [C][C] T | P [C][C] T | vec [4][C] fp32]
@@ -447,15 +457,13 @@ struct PrepLayout {
   static constexpr int E = (int)sizeof(T);
   static constexpr int RBK = D * E;  // K, Q tile rows (swizzled)
   static constexpr int LDF = C + 4;
-  static constexpr int LDZ = 20;
   // phase 1 (shared by the V-head teams): K, Q tiles
   static constexpr int oK = 0;
   static constexpr int oQ = oK + C * RBK;
   static constexpr int kq_bytes = oQ + C * RBK;
-  // phase 2 (same bytes): per team, the A/T work array and block-product scratch
+  // phase 2 (same bytes): per team, the A/T work array
   static constexpr int oA = 0;
-  static constexpr int oZ = oA + C * LDF * 4;
-  static constexpr int team_bytes = oZ + 4 * 16 * LDZ * 4;
+  static constexpr int team_bytes = oA + C * LDF * 4;
   static constexpr int work_bytes = VPW * team_bytes;
   // row scalars: rk, rq (shared), then g, beta, G per team
   static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
@@ -492,7 +500,6 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   unsigned char* K_s = smem + L::oK;
   unsigned char* Q_s = smem + L::oQ;
   float* A_s = reinterpret_cast<float*>(smem + team * L::team_bytes + L::oA);
-  float* Z_s = reinterpret_cast<float*>(smem + team * L::team_bytes + L::oZ);
   float* rk_s = reinterpret_cast<float*>(smem + L::oVec);
   float* rq_s = rk_s + C;
   float* g_s = rk_s + (2 + 3 * team) * C;
@@ -660,78 +667,76 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   }
   __syncthreads();
 
-  // diagonal 16x16 blocks of T = (I + A)^-1 in place.  Wave b solves block b
-  // by forward substitution: lane 4c+p owns column c and the rows r = p
-  // (mod 4); each row's sum is split over the 4 lanes of a quad.
+  // T = (I + A)^-1 by 16x16 blocks on fp32 MFMA, in place.  A block X of
+  // A_s is read as the accumulator layout of X (col: lane (g, c) holds
+  // X[4g+i][c]) or of X^T (row: X[c][4g+i], one 16-byte read); tn(Y, W)
+  // forms Y^T W from two such tiles.
+  const int c16 = lane & 15;
+  auto col = [&](int bi, int bj) {
+    const float* a = A_s + (16 * bi + 4 * g4) * L::LDF + 16 * bj + c16;
+    return f32x4{a[0], a[L::LDF], a[2 * L::LDF], a[3 * L::LDF]};
+  };
+  auto row = [&](int bi, int bj) {
+    const float4 v = *reinterpret_cast<const float4*>(A_s + (16 * bi + c16) * L::LDF + 16 * bj + 4 * g4);
+    return f32x4{v.x, v.y, v.z, v.w};
+  };
+  auto put = [&](int bi, int bj, const f32x4& t, float sgn) {
+    float* a = A_s + (16 * bi + 4 * g4) * L::LDF + 16 * bj + c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i * L::LDF] = sgn * t[i];
+  };
+  // diagonal blocks: wave b inverts the unit lower-triangular I + N (N the
+  // strictly lower block, nilpotent) as (I - N)(I + N^2)(I + N^4)(I + N^8);
+  // M = N^T runs alongside so every product is a tn() of held tiles
+  f32x4 Tdiag = {0.f, 0.f, 0.f, 0.f}, Z1 = {0.f, 0.f, 0.f, 0.f};
   if (wave < NT) {
-    const int b = wave, c = lane >> 2, part = lane & 3;
-    float xl[4] = {0.f, 0.f, 0.f, 0.f};  // x_{4m+part} of column c
+    const int b = wave;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 N1 = col(b, b), M1 = row(b, b);
+    const f32x4 M2 = mfma_tn(N1, M1, zero), N2 = mfma_tn(M1, N1, zero);
+    const f32x4 M4 = mfma_tn(N2, M2, zero), N4 = mfma_tn(M2, N2, zero);
+    const f32x4 M8 = mfma_tn(N4, M4, zero);
+    f32x4 X;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* arow = A_s + (16 * b + r) * L::LDF + 16 * b;
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int j = 4 * m + part;
-        s += (j < r) ? arow[j] * xl[m] : 0.f;
-      }
-      s += dpp_f32<DPP_QUAD_1032>(s);
-      s += dpp_f32<DPP_QUAD_2301>(s);
-      const float xr = ((r == c) ? 1.f : 0.f) - s;
-      if (part == (r & 3)) xl[r >> 2] = xr;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) A_s[(16 * b + 4 * m + part) * L::LDF + 16 * b + c] = xl[m];
+    for (int i = 0; i < 4; ++i) X[i] = (4 * g4 + i == c16 ? 1.f : 0.f) - N1[i];
+    X = mfma_tn(M2, X, X);  // (I + N^2) X
+    X = mfma_tn(M4, X, X);
+    X = mfma_tn(M8, X, X);
+    Tdiag = X;
+    // level 1 starts at once in the wave that holds T_{2b,2b}
+    if constexpr (NT >= 2)
+      if ((b & 1) == 0) Z1 = mfma_tn(row(b + 1, b), X, zero);  // A_{2b+1,2b} T_{2b,2b}
   }
+  if (wave < NT) put(wave, wave, Tdiag, 1.f);
   __syncthreads();
-
-  // off-diagonal blocks, in place (each A block is consumed by the
-  // product that produces the T block in its position)
-  auto Ael = [&](int bi, int bj, int rr, int cc) -> float& { return A_s[(16 * bi + rr) * L::LDF + 16 * bj + cc]; };
-  auto Zel = [&](int z, int rr, int cc) -> float& { return Z_s[(z * 16 + rr) * L::LDZ + cc]; };
-  const int rr = ttid >> 4, cc = ttid & 15;
   if constexpr (NT >= 2) {
-    // level 1: blocks (2b+1, 2b): Z = A_{2b+1,2b} T_{2b,2b};  T = -T_{2b+1,2b+1} Z
-#pragma unroll
-    for (int b = 0; b < NT / 2; ++b) {
-      float z = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) z += Ael(2 * b + 1, 2 * b, rr, m) * Ael(2 * b, 2 * b, m, cc);
-      Zel(b, rr, cc) = z;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < NT / 2; ++b) {
-      float t = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) t -= Ael(2 * b + 1, 2 * b + 1, rr, m) * Zel(b, m, cc);
-      Ael(2 * b + 1, 2 * b, rr, cc) = t;
-    }
+    // level 1: T_{2b+1,2b} = -T_{2b+1,2b+1} A_{2b+1,2b} T_{2b,2b}
+    if (wave < NT && (wave & 1) == 0)
+      put(wave + 1, wave, mfma_tn(row(wave + 1, wave + 1), Z1, f32x4{0.f, 0.f, 0.f, 0.f}), -1.f);
     __syncthreads();
   }
   if constexpr (NT == 4) {
-    // level 2: the lower-left 32x32 block T_[23][01] = -T_[23][23] A_[23][01] T_[01][01]
-    float z20 = 0.f, z21 = 0.f, z30 = 0.f, z31 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float t00 = Ael(0, 0, m, cc), t10 = Ael(1, 0, m, cc), t11 = Ael(1, 1, m, cc);
-      z20 += Ael(2, 0, rr, m) * t00 + Ael(2, 1, rr, m) * t10;
-      z21 += Ael(2, 1, rr, m) * t11;
-      z30 += Ael(3, 0, rr, m) * t00 + Ael(3, 1, rr, m) * t10;
-      z31 += Ael(3, 1, rr, m) * t11;
+    // level 2: T_[23][01] = -T_[23][23] Z with Z = A_[23][01] T_[01][01];
+    // wave (i, j) = (2 + wave/2, wave%2) forms block (i, j), the i = 3 waves
+    // recomputing the Z_2j they share
+    const int j = wave & 1, i = 2 + (wave >> 1);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 t = zero;
+    if (wave < 4) {
+      const f32x4 T1j = col(1, j);
+      f32x4 z2 = mfma_tn(row(2, 1), T1j, zero);
+      if (j == 0) z2 = mfma_tn(row(2, 0), col(0, 0), z2);
+      if (i == 2) {
+        t = mfma_tn(row(2, 2), z2, zero);
+      } else {
+        f32x4 z3 = mfma_tn(row(3, 1), T1j, zero);
+        if (j == 0) z3 = mfma_tn(row(3, 0), col(0, 0), z3);
+        t = mfma_tn(row(3, 2), z2, zero);
+        t = mfma_tn(row(3, 3), z3, t);
+      }
     }
-    Zel(0, rr, cc) = z20; Zel(1, rr, cc) = z21; Zel(2, rr, cc) = z30; Zel(3, rr, cc) = z31;
-    __syncthreads();
-    float t20 = 0.f, t21 = 0.f, t30 = 0.f, t31 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float a22 = Ael(2, 2, rr, m), a32 = Ael(3, 2, rr, m), a33 = Ael(3, 3, rr, m);
-      t20 -= a22 * Zel(0, m, cc);
-      t21 -= a22 * Zel(1, m, cc);
-      t30 -= a32 * Zel(0, m, cc) + a33 * Zel(2, m, cc);
-      t31 -= a32 * Zel(1, m, cc) + a33 * Zel(3, m, cc);
-    }
-    Ael(2, 0, rr, cc) = t20; Ael(2, 1, rr, cc) = t21; Ael(3, 0, rr, cc) = t30; Ael(3, 1, rr, cc) = t31;
+    __syncthreads();  // every A_[23][01] block read before any is replaced
+    if (wave < 4) put(i, j, t, -1.f);
     __syncthreads();
   }
 
