@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // no branch between them.
   constexpr int U = kUnroll<D>;
   static_assert(D % (16 * U) == 0, "rows per pass must divide grp * D");
+  static_assert(U % 2 == 0, "a pass is streamed in two halves");
   const int rows = grp * D;
   const int sub = lane & 15;
   StT* S = reinterpret_cast<StT*>(p.state) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D * D +
@@ -168,28 +169,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     kf[e] = s_k[sub * EPL + e] * rk;
     qf[e] = s_q[sub * EPL + e] * rq;
   }
+  auto row_step = [&](int u) {
+    const int r = rb + 16 * u;
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) { a += sv[u][e] * kf[e]; b += sv[u][e] * qf[e]; }
+    a = row16_sum(a);
+    b = row16_sum(b);
+    const int hl = r / D;
+    const float al = s_al[hl];
+    const float dl = s_be[hl] * (s_v[r] - al * a);
+    float nv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
+    store_row<EPL>(S + (int64_t)r * D, nv);
+    if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
+  };
+  // The row groups of a pass are processed in two halves; once a half is
+  // written back its registers load the same half of the next pass, so loads
+  // stay in flight while the other half is computed.  The last pass has its
+  // own copy of the second half, which keeps every load outside a branch.
+  constexpr int H = U / 2;
   while (true) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = rb + 16 * u;
-      float a = 0.f, b = 0.f;
+    for (int u = 0; u < H; ++u) row_step(u);
+    if (rb + 16 * U >= rows) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) { a += sv[u][e] * kf[e]; b += sv[u][e] * qf[e]; }
-      a = row16_sum(a);
-      b = row16_sum(b);
-      const int hl = r / D;
-      const float al = s_al[hl];
-      const float dl = s_be[hl] * (s_v[r] - al * a);
-      float nv[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
-      store_row<EPL>(S + (int64_t)r * D, nv);
-      if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
+      for (int u = H; u < U; ++u) row_step(u);
+      break;
     }
-    rb += 16 * U;
-    if (rb >= rows) break;
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * u) * D, sv[u]);
+    for (int u = 0; u < H; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sv[u]);
+#pragma unroll
+    for (int u = H; u < U; ++u) row_step(u);
+#pragma unroll
+    for (int u = H; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sv[u]);
+    rb += 16 * U;
   }
   __syncthreads();
   IoT* o = reinterpret_cast<IoT*>(p.o) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D;

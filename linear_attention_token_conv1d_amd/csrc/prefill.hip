@@ -470,8 +470,14 @@ struct PrepLayout {
   static constexpr int bytes = oVec + (2 + 3 * VPW) * C * 4;
 };
 
+// The chunk offsets and cu_seqlens are never written while prep and scan
+// run; reading them through the constant address space lets loads at
+// uniform indices go through the scalar cache.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)p; }
+
 // Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
-__device__ __forceinline__ int owner(const int32_t* off, int n_seqs, int c) {
+__device__ __forceinline__ int owner(cint32* off, int n_seqs, int c) {
   int lo = 0, hi = n_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -506,13 +512,14 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   float* b_s = g_s + C;
   float* G_s = g_s + 2 * C;
 
-  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
+  cint32* off = as_const(reinterpret_cast<const int32_t*>(ws));
+  cint32* cu = as_const(p.cu_seqlens);
   const int ci = blockIdx.x, h = blockIdx.y * VPW + team;
   if (ci >= off[p.n_seqs]) return;
   const int hq = h / (p.h_v / p.h_qk);  // the same for every team (VPW divides h_v / h_qk)
   const int n = owner(off, p.n_seqs, ci);
-  const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
-  const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
+  const int64_t seq_start = cu ? cu[n] : 0;
+  const int64_t seq_end = cu ? cu[n + 1] : p.total_tokens;
   const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
   const int Lc = (int)min((int64_t)C, seq_end - t0);
 
