@@ -1211,10 +1211,54 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
           *reinterpret_cast<frag*>(sS + SS::off(colof(ct), (32 * u + 8 * g4) * 2)) =
               M::acc(st[ct][2 * u], st[ct][2 * u + 1]);
     };
+    // L2 prefetch PFD chunks ahead, by the chain waves (the output waves
+    // move the next chunk into LDS): one 4-byte load per 128-byte line of
+    // the chunk's K, Q and V rows and of its record, issued while the chain
+    // waits at B1 and consumed a chunk later, so nothing waits for it.  The
+    // K, Q and record lines, which the NB column blocks of a head share, are
+    // split between the blocks.  Only the 32-column workgroups prefetch:
+    // they run when the launch leaves CUs idle and the scan waits on HBM
+    // latency; with every CU busy the extra requests cost more than they save.
+    constexpr int PFD = L::cols == 32 ? 3 : 0;
+    constexpr int LPR = (D * 2 + 127) / 128;  // lines per K or Q row
+    constexpr int NKL = C * LPR;
+    constexpr int NSH = 2 * NKL + (int)(Rec<T, C>::bytes / 128);
+    constexpr int NTOUCH = ((NSH + NB - 1) / NB + C + 64 * NWR - 1) / (64 * NWR);
+    // touch i of chunk c reads tbase[i] + c * tstep[i]
+    const unsigned char* tbase[NTOUCH];
+    uint32_t tstep[NTOUCH];
+    uint32_t tv[NTOUCH];
+    const unsigned char* rec0 = chunk_rec(0);  // always a whole record
+    {
+      const int nsw = (NSH - blk + NB - 1) / NB;  // shared lines of this block
+      const int64_t ks = p.k_stride * 2, qs = p.q_stride * 2, vs = p.v_stride * 2;
+#pragma unroll
+      for (int i = 0; i < NTOUCH; ++i) {
+        const int sl = (i * NWR + cw) * 64 + lane;
+        tv[i] = 0u;
+        tbase[i] = rec0;
+        tstep[i] = (uint32_t)(p.h_v * Rec<T, C>::bytes);
+        if (sl < nsw) {
+          const int l = blk + NB * sl;
+          if (l < 2 * NKL) {
+            const bool isq = l >= NKL;
+            const int lk = isq ? l - NKL : l;
+            const int64_t st = isq ? qs : ks;
+            tbase[i] = (isq ? qg : kg) + seq_start * st + (lk / LPR) * st + (lk % LPR) * 128;
+            tstep[i] = (uint32_t)(C * st);
+          } else {
+            tbase[i] = rec0 + (l - 2 * NKL) * 128;
+          }
+        } else if (sl < nsw + C) {
+          tbase[i] = vg + seq_start * vs + (sl - nsw) * vs;
+          tstep[i] = (uint32_t)(C * vs);
+        }
+      }
+    }
     publish_state();
     __syncthreads();  // initial state published; chunk 0 has landed
 
-    auto step = [&](const unsigned char* cur) {
+    auto step = [&](int c, const unsigned char* cur) {
       const unsigned char* K_t = cur + L::oK;
       const unsigned char* Tb_t = cur + L::oTb;
       const unsigned char* V_t = cur + L::oV;
@@ -1306,6 +1350,16 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
         }
       }
       const float gl = vec[3 * C];
+      // the previous touches have landed; chunk c + PFD is touched (without
+      // a full chunk c + PFD, every touch re-reads the sequence's first record)
+      if constexpr (PFD > 0) {
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
+        const bool ok = fast && c + PFD < nch && chunk_len(c + PFD) == C;
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i)
+          tv[i] = *reinterpret_cast<const uint32_t*>(ok ? tbase[i] + (uint64_t)(c + PFD) * tstep[i] : rec0);
+      }
       barrier_vm<63>();  // B1: U is visible; the output waves are done with the old state
       // S^T <- gamma_last S^T + K^T diag(e rk) U: each K^T fragment feeds every column tile
 #pragma unroll
@@ -1328,8 +1382,12 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
       __syncthreads();  // B2: next chunk loaded, new state published
     };
     for (int c = 0; c < nch; c += 2) {
-      step(sb0);
-      if (c + 1 < nch) step(sb1);
+      step(c, sb0);
+      if (c + 1 < nch) step(c + 1, sb1);
+    }
+    if constexpr (PFD > 0) {
+#pragma unroll
+      for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
     }
     if (p.final_state) {
 #pragma unroll
