@@ -85,7 +85,7 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
   if (!aligned(a->g, 4) || !aligned(a->beta, 4) || !aligned(a->cu_seqlens, 4))
     return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: g, beta, cu_seqlens must be 4-byte aligned");
   const size_t need = gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v,
-                                                   a->chunk);
+                                                   a->d_k, a->chunk);
   if (need && (!a->workspace || a->workspace_bytes < need))
     return fail(GDN_ERR_WORKSPACE, "gdn_prefill: workspace of %zu bytes required", need);
   if (need && !aligned(a->workspace, 256))
@@ -154,7 +154,7 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* a, void* stream) {
 
 size_t gdn_prefill_workspace_size(const gdn_prefill_args* a) {
   if (!a || a->struct_size < sizeof(gdn_prefill_args)) return 0;
-  return gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v, a->chunk);
+  return gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v, a->d_k, a->chunk);
 }
 
 gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {

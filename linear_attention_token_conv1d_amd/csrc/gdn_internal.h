@@ -68,7 +68,7 @@ struct PrefillParams {
 };
 // Workspace of gdn_prefill: chunk offsets plus, per (chunk, V head), the
 // chunk operands Tb, P and four per-token scalar rows.
-size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int chunk);
+size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk);
 bool prefill_supported(int io_dtype, int d, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream);
 

@@ -180,6 +180,49 @@ __host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seq
 
 __host__ __device__ inline int64_t max_chunks(int64_t T, int n_seqs, int C) { return T / C + n_seqs; }
 
+// Sequence split of the bf16 scan.  When one sequence's heads leave most CUs
+// idle, its chunks [0, m) are scanned from the initial state (ending in S_m)
+// while chunks [m, nch) are scanned twice at the same time: from a zero state
+// (outputs o0, final state S0) and as the transition Phi of that segment
+// (basis initial state, zero values: outputs w_t = scale Phi_{m,t} q^_t, final
+// state Phi).  Every state update is linear in the state, so on the second
+// segment o_t = o0_t + S_m w_t and the final state is S_m Phi + S0; a join
+// launch forms both.  Workspace after the records, 256-byte aligned:
+// [S_m | S0 | Phi: h_v d d fp32 each][w: tokens of the second segment x h_v x d, bf16]
+constexpr int kSplitMinChunks = 32;  // shorter sequences keep one pass
+constexpr int kScanCUs = 256;
+struct SplitPlan {
+  bool on;
+  int m;             // chunks in the first segment
+  int64_t t_b;       // first token of the second segment
+  size_t o_state, o_w, bytes;  // workspace offsets (after the records) and total
+};
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d, int C, size_t base) {
+  SplitPlan s{false, 0, 0, 0, 0, base};
+  const int64_t nch = (T + C - 1) / C;
+  if (io_dtype != 1 || n_seqs != 1 || nch < kSplitMinChunks || 3 * h_v * (d / 64) > kScanCUs) return s;
+  s.on = true;
+  s.m = (int)(nch / 2);
+  s.t_b = (int64_t)s.m * C;
+  s.o_state = align256(base);
+  s.o_w = s.o_state + 3 * (size_t)h_v * d * d * 4;
+  s.bytes = align256(s.o_w + (size_t)(T - s.t_b) * h_v * d * 2);
+  return s;
+}
+// What a split scan's workgroups find: role 0 = first segment, 1 = second
+// segment from zero, 2 = the transition of the second segment.
+struct ScanSplit {
+  int on, m;
+  float* s_mid;  // [h_v][d][d] state after chunk m
+  float* s_zero; // [h_v][d][d] second segment's final state from zero
+  float* phi;    // [h_v][d][d] transition of the second segment (row i = basis row i)
+  __bf16* w;     // [tokens after t_b][h_v][d]
+};
+
+// 256 zero bytes: the V rows of the transition role of a split scan
+__device__ __align__(256) unsigned char g_zero_line[256] = {};
+
 // ------------------------------------------------------------------ plan
 // One workgroup: chunk offsets of every packed sequence (exclusive prefix sum
 // of ceil(len / C)), then the scan order: sequences by chunk count, longest
@@ -237,20 +280,36 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
 // XCDs), so one group shares an L2 while long chains spread over all XCDs;
 // groups are numbered in scan order (longest sequence first).
 struct ScanSlot {
-  int n, h, blk;
+  int n, h, blk, role;
   bool valid;
 };
 __device__ __forceinline__ ScanSlot scan_slot(const PrefillParams& p, const int32_t* order, int NB) {
   const int grp = p.h_v / p.h_qk, gs = grp * NB, ngroups = p.n_seqs * p.h_qk;
   const int x = blockIdx.x % 8, k = blockIdx.x / 8;
   const int gi = (k / gs) * 8 + x, j = k % gs;
-  ScanSlot r{0, 0, 0, gi < ngroups};
+  ScanSlot r{0, 0, 0, 0, gi < ngroups};
   if (r.valid) {
     r.n = order[gi / p.h_qk];
     r.h = (gi % p.h_qk) * grp + j / NB;
     r.blk = j % NB;
   }
   return r;
+}
+// Split scan of one sequence: 3 NB workgroups per V head (roles x column
+// blocks), the heads dealt over the XCDs in runs so that the second-segment
+// and transition workgroups of a head, which read the same chunks, share L2.
+__device__ __forceinline__ ScanSlot split_slot(const PrefillParams& p, int NB) {
+  const int per = 3 * NB;
+  int h, j;
+  if (p.h_v % 8 == 0) {
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8, hx = p.h_v / 8;
+    h = x * hx + k / per;
+    j = k % per;
+  } else {
+    h = blockIdx.x / per;
+    j = blockIdx.x % per;
+  }
+  return ScanSlot{0, h, j % NB, j / NB, h < p.h_v};
 }
 inline unsigned scan_grid(int n_seqs, int h_qk, int h_v, int NB) {
   const int ngroups = n_seqs * h_qk;
@@ -1097,7 +1156,7 @@ __device__ __forceinline__ void barrier_vm() {
 }
 
 template <int D, int C, int CT, int NWR>
-__global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const unsigned char* ws) {
+__global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const unsigned char* ws, ScanSplit sp) {
   using L = Scan2Layout<D, C, 16 * CT * NWR>;
   using T = __bf16;
   using M = Mma<T>;
@@ -1118,9 +1177,10 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
   __shared__ __align__(16) unsigned char sS[L::sbytes];
   __shared__ __align__(16) unsigned char sU[L::ubytes];
 
-  const ScanSlot slot = scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
+  const ScanSlot slot =
+      sp.on ? split_slot(p, NB) : scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
   if (!slot.valid) return;
-  const int blk = slot.blk, h = slot.h, n = slot.n;
+  const int blk = slot.blk, h = slot.h, n = slot.n, role = slot.role;
   const int hq = h / (p.h_v / p.h_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -1132,14 +1192,21 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
   const unsigned char* recs = ws + off_bytes(p.n_seqs);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
-  const int c0 = off[n];
-  const int nch = off[n + 1] - c0;
+  // this workgroup's chunks: the whole sequence, or one segment of a split
+  const int cseq = off[n], nch_seq = off[n + 1] - cseq;
+  const int cbeg = role == 0 ? 0 : sp.m;
+  const int nch = sp.on ? (role == 0 ? sp.m : nch_seq - sp.m) : nch_seq;
+  const int c0 = cseq + cbeg;
+  const int64_t seg_start = seq_start + (int64_t)cbeg * C;
 
   const unsigned char* qg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + (int64_t)hq * D);
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + (int64_t)hq * D);
-  const unsigned char* vg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + (int64_t)h * D +
-                                                                   blk * L::cols);
-  auto chunk_t0 = [&](int c) { return seq_start + (int64_t)c * C; };
+  // the transition role scans zero values: every V row reads the zero line
+  const int64_t vrow = role == 2 ? 0 : p.v_stride * 2;
+  const unsigned char* vg =
+      role == 2 ? g_zero_line
+                : reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + (int64_t)h * D + blk * L::cols);
+  auto chunk_t0 = [&](int c) { return seg_start + (int64_t)c * C; };
   auto chunk_len = [&](int c) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
   auto chunk_rec = [&](int c) { return recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes; };
 
@@ -1159,14 +1226,14 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     pk.init((uint32_t)(p.k_stride * 2), cw, lane);
     pq.init((uint32_t)(p.q_stride * 2), cw, lane);
     ptb.init((uint32_t)L::RBC, cw, lane);
-    pv.init((uint32_t)(p.v_stride * 2), cw, lane);
+    pv.init((uint32_t)vrow, cw, lane);
   }
   auto chunk_ptrs = [&](int c, const unsigned char*& kc, const unsigned char*& qc, const unsigned char*& vc,
                         const unsigned char*& rec) {
     const int64_t t0 = chunk_t0(c);
     kc = kg + t0 * p.k_stride * 2;
     qc = qg + t0 * p.q_stride * 2;
-    vc = vg + t0 * p.v_stride * 2;
+    vc = vg + t0 * vrow;
     rec = chunk_rec(c);
   };
   // clamped (any chunk), over NW waves with wave index w
@@ -1179,7 +1246,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     dma_tile_s<SK, C, NW>(b + L::oQ, qc, p.q_stride * 2, Lc, w, lane);
     dma_tile_s<SC, C, NW>(b + L::oTb, rec, L::RBC, C, w, lane);
     dma_tile_s<SC, C, NW>(b + L::oP, rec + Rec<T, C>::mat, L::RBC, C, w, lane);
-    dma_tile_s<SV, C, NW>(b + L::oV, vc, p.v_stride * 2, Lc, w, lane);
+    dma_tile_s<SV, C, NW>(b + L::oV, vc, vrow, Lc, w, lane);
     dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, w, lane);
   };
 
@@ -1191,14 +1258,22 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     // tiles; row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
     f32x4 st[CT][DT];
     auto srow = [&](int ct) { return (((size_t)n * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D; };
+    // initial state: the caller's (or zero) for a whole sequence or a first
+    // segment, zero for a second segment, the identity for the transition
+    const float* s_init = role == 0 ? p.initial_state : nullptr;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         st[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (p.initial_state) {
-          const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + srow(ct) + pidx<DT>(dt, 4 * g4));
+        if (s_init) {
+          const float4 v4 = *reinterpret_cast<const float4*>(s_init + srow(ct) + pidx<DT>(dt, 4 * g4));
           st[ct][dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+        }
+        if (role == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st[ct][dt][i] = pidx<DT>(dt, 4 * g4 + i) == blk * L::cols + colof(ct) ? 1.f : 0.f;
         }
       }
     // the state as bf16 rows [column][d_k] for the output waves: tiles 2u,
@@ -1231,7 +1306,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     const unsigned char* rec0 = chunk_rec(0);  // always a whole record
     {
       const int nsw = (NSH - blk + NB - 1) / NB;  // shared lines of this block
-      const int64_t ks = p.k_stride * 2, qs = p.q_stride * 2, vs = p.v_stride * 2;
+      const int64_t ks = p.k_stride * 2, qs = p.q_stride * 2, vs = vrow;
 #pragma unroll
       for (int i = 0; i < NTOUCH; ++i) {
         const int sl = (i * NWR + cw) * 64 + lane;
@@ -1244,13 +1319,13 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
             const bool isq = l >= NKL;
             const int lk = isq ? l - NKL : l;
             const int64_t st = isq ? qs : ks;
-            tbase[i] = (isq ? qg : kg) + seq_start * st + (lk / LPR) * st + (lk % LPR) * 128;
+            tbase[i] = (isq ? qg : kg) + seg_start * st + (lk / LPR) * st + (lk % LPR) * 128;
             tstep[i] = (uint32_t)(C * st);
           } else {
             tbase[i] = rec0 + (l - 2 * NKL) * 128;
           }
         } else if (sl < nsw + C) {
-          tbase[i] = vg + seq_start * vs + (sl - nsw) * vs;
+          tbase[i] = vg + seg_start * vs + (sl - nsw) * vs;
           tstep[i] = (uint32_t)(C * vs);
         }
       }
@@ -1389,18 +1464,26 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
 #pragma unroll
       for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
     }
-    if (p.final_state) {
+    // final state: the caller's, or the split's S_m (always: the join needs
+    // it), S0 and Phi (only when the caller wants a final state)
+    float* s_fin = !sp.on ? p.final_state
+                 : role == 0 ? sp.s_mid
+                 : !p.final_state ? nullptr
+                 : role == 1 ? sp.s_zero : sp.phi;
+    if (s_fin) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(p.final_state + srow(ct) + pidx<DT>(dt, 4 * g4)) =
+          *reinterpret_cast<float4*>(s_fin + srow(ct) + pidx<DT>(dt, 4 * g4)) =
               make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
   } else {
     // --------------------------------------------------------- output waves
     const int64_t o_stride = (int64_t)p.h_v * D;
-    T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols + SW * cw + 4 * g4;
+    // outputs go to o, except the transition's (w, from token seg_start on)
+    T* og = (role == 2 ? sp.w : reinterpret_cast<T*>(p.o)) + (int64_t)h * D + blk * L::cols + SW * cw + 4 * g4;
+    const int64_t otok = role == 2 ? seg_start : 0;
     // O^T tile (ct, nt): rows 4g+i = columns SW cw + 16 ct + 4g + i, column
     // l16 = token pidx(nt, l16) of the chunk
     f32x4 o[CT][NT];
@@ -1408,7 +1491,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) orow[nt] = (int64_t)pidx<NT>(nt, l16) * o_stride;
     auto store_o = [&](int64_t t0, int Lc) {
-      T* oc = og + t0 * o_stride;
+      T* oc = og + (t0 - otok) * o_stride;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1504,10 +1587,155 @@ constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave
 // for launches that fill the chip, 32 columns (two waves per role) to spread
 // a few long chains over twice as many CUs.
 #define GDN_SCAN2(D, C) \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>(PrefillParams, const unsigned char*); \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>(PrefillParams, const unsigned char*);
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>(PrefillParams, const unsigned char*, \
+                                                                           ScanSplit); \
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>(PrefillParams, const unsigned char*, \
+                                                                           ScanSplit);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
+
+// ------------------------------------------------------------------ join
+// After a split scan, on the second segment: o_t += S_m w_t, as
+// O^T[j][t] = sum_i S_m[j][i] w[t][i] on MFMA (bf16 operands, fp32 sums; o
+// is read and rounded once more), and the final state S_m Phi + S0 in fp32.
+// Blocks [0, nstate): with a final state, h_v D/16 blocks of 16 state rows
+// each, first so that their dependent sums overlap the rest.  Then blocks of
+// kJoinTok tokens of V head h = block % h_v (a head's blocks share an XCD,
+// and its S_m that L2): S_m (as bf16) and the w rows go to LDS through
+// coalesced 16-byte loads, issued with the o rows they correct before any
+// is used; wave w forms tokens [32 w, 32 w + 32) for every j, and the
+// correction returns through LDS (fp32) so that o is read and written as
+// whole 16-byte row pieces.
+constexpr int kJoinTok = 128;
+template <int D>
+struct JoinLayout {
+  static constexpr int RB = D * 2;  // bf16 rows of S_m and w
+  static constexpr int oA = 0, oB = D * RB;
+  static constexpr int in_bytes = oB + kJoinTok * RB;
+  static constexpr int out_bytes = kJoinTok * D * 4;  // fp32 correction [t][j]
+  static constexpr int bytes = in_bytes > out_bytes ? in_bytes : out_bytes;
+};
+template <int D>
+__global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp, int64_t t_b, int nstate) {
+  using M = Mma<__bf16>;
+  using L = JoinLayout<D>;
+  using SW = Swz<L::RB>;
+  __shared__ __align__(16) unsigned char sm[L::bytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, l16 = lane & 15;
+  const int64_t o_stride = (int64_t)p.h_v * D;
+  const int64_t ntok = p.total_tokens - t_b;
+  if ((int)blockIdx.x < nstate) {
+    // final state rows j = 16 jb + tid / 16, columns cb .. cb + D/16 - 1
+    constexpr int NC = D / 16;
+    const int h = blockIdx.x / (D / 16), j = 16 * (blockIdx.x % (D / 16)) + tid / 16, cb = (tid % 16) * NC;
+    const size_t hs = (size_t)h * D * D;
+    const float* smr = sp.s_mid + hs + (size_t)j * D;
+    const float* ph = sp.phi + hs + cb;
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; c += 4) {
+      const float4 z = *reinterpret_cast<const float4*>(sp.s_zero + hs + (size_t)j * D + cb + c);
+      acc[c] = z.x; acc[c + 1] = z.y; acc[c + 2] = z.z; acc[c + 3] = z.w;
+    }
+    // eight rows of Phi per batch, all loads of a batch issued together
+    for (int i0 = 0; i0 < D; i0 += 8) {
+      const float4 a0 = *reinterpret_cast<const float4*>(smr + i0), a1 = *reinterpret_cast<const float4*>(smr + i0 + 4);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      float4 r[8][NC / 4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < NC / 4; ++c) r[i][c] = *reinterpret_cast<const float4*>(ph + (size_t)(i0 + i) * D + 4 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < NC / 4; ++c) {
+          acc[4 * c] += a[i] * r[i][c].x;
+          acc[4 * c + 1] += a[i] * r[i][c].y;
+          acc[4 * c + 2] += a[i] * r[i][c].z;
+          acc[4 * c + 3] += a[i] * r[i][c].w;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; c += 4)
+      *reinterpret_cast<float4*>(p.final_state + hs + (size_t)j * D + cb + c) =
+          make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+    return;
+  }
+  const int bo = blockIdx.x - nstate;
+  const int h = bo % p.h_v;
+  const int64_t tb0 = (int64_t)(bo / p.h_v) * kJoinTok;  // relative to t_b
+  // ---- loads: S_m (fp32, D/4 float4 per row), w and o rows (D/8 16-byte
+  // pieces per token); rows past the segment re-read its last token
+  constexpr int NSQ = D * D / 4 / 256, NWQ = kJoinTok * D / 8 / 256;
+  const float* Sm = sp.s_mid + (size_t)h * D * D;
+  float4 sv[NSQ];
+  uint4 wv[NWQ], ov[NWQ];
+#pragma unroll
+  for (int q = 0; q < NSQ; ++q) sv[q] = reinterpret_cast<const float4*>(Sm)[tid + 256 * q];
+#pragma unroll
+  for (int q = 0; q < NWQ; ++q) {
+    const int e = tid + 256 * q, t = e / (D / 8), pc = e % (D / 8);
+    const int64_t tt = min(tb0 + t, ntok - 1);
+    wv[q] = *reinterpret_cast<const uint4*>(sp.w + tt * o_stride + (int64_t)h * D + 8 * pc);
+    ov[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(p.o) + (t_b + tt) * o_stride +
+                                            (int64_t)h * D + 8 * pc);
+  }
+#pragma unroll
+  for (int q = 0; q < NSQ; ++q) {
+    const int e = tid + 256 * q, j = e / (D / 4), c4 = e % (D / 4);
+    *reinterpret_cast<uint2*>(sm + L::oA + SW::off(j, 8 * c4)) =
+        make_uint2(pack_bf16x2(sv[q].x, sv[q].y), pack_bf16x2(sv[q].z, sv[q].w));
+  }
+#pragma unroll
+  for (int q = 0; q < NWQ; ++q) {
+    const int e = tid + 256 * q, t = e / (D / 8), pc = e % (D / 8);
+    *reinterpret_cast<uint4*>(sm + L::oB + SW::off(t, 16 * pc)) = wv[q];
+  }
+  __syncthreads();
+  // ---- O^T tiles (jt, tt): rows j = 16 jt + 4g + i, column t = 32 wave + 16 tt + l16
+  constexpr int JTN = D / 16, KS = D / 32;
+  f32x4 acc[JTN][2];
+#pragma unroll
+  for (int jt = 0; jt < JTN; ++jt) acc[jt][0] = acc[jt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    typename M::frag bw[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      bw[tt] = frag_row_s<__bf16, SW>(sm + L::oB, 32 * wave + 16 * tt + l16, 32 * s + 8 * g4, false);
+#pragma unroll
+    for (int jt = 0; jt < JTN; ++jt) {
+      const typename M::frag a = frag_row_s<__bf16, SW>(sm + L::oA, 16 * jt + l16, 32 * s + 8 * g4, false);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) M::mma(acc[jt][tt], a, bw[tt], false);
+    }
+  }
+  __syncthreads();  // S_m and w are dead: the bytes take the fp32 correction
+  // [t][j] fp32, float4 column slots xor-swizzled by t so that the 16 lanes
+  // of a group (16 tokens, one j slot) write 16 different bank groups
+  auto cor = [&](int t, int j4) -> float4* {
+    return reinterpret_cast<float4*>(sm) + t * (D / 4) + (j4 ^ (t % (D / 4)));
+  };
+#pragma unroll
+  for (int jt = 0; jt < JTN; ++jt)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      *cor(32 * wave + 16 * tt + l16, 4 * jt + g4) = make_float4(acc[jt][tt][0], acc[jt][tt][1], acc[jt][tt][2], acc[jt][tt][3]);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NWQ; ++q) {
+    const int e = tid + 256 * q, t = e / (D / 8), pc = e % (D / 8);
+    if (tb0 + t >= ntok) continue;
+    const float4 c0 = *cor(t, 2 * pc), c1 = *cor(t, 2 * pc + 1);
+    const uint4 o = ov[q];
+    const uint4 r = make_uint4(pack_bf16x2(bf16_lo(o.x) + c0.x, bf16_hi(o.x) + c0.y),
+                               pack_bf16x2(bf16_lo(o.y) + c0.z, bf16_hi(o.y) + c0.w),
+                               pack_bf16x2(bf16_lo(o.z) + c1.x, bf16_hi(o.z) + c1.y),
+                               pack_bf16x2(bf16_lo(o.w) + c1.z, bf16_hi(o.w) + c1.w));
+    *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(p.o) + (t_b + tb0 + t) * o_stride + (int64_t)h * D + 8 * pc) = r;
+  }
+}
 
 // ------------------------------------------------------------------ host
 constexpr int kLdsMax = 160 * 1024;
@@ -1573,17 +1801,30 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(T) == 2) {
-      // narrow workgroups when even they leave CUs idle
-      constexpr int kCUs = 256;
-      const bool narrow = (int64_t)p.n_seqs * p.h_v * (D / 32) <= kCUs;
-      if (narrow) {
+      const size_t recs_end = off_bytes(p.n_seqs) + (size_t)max_chunks(p.total_tokens, p.n_seqs, C) * p.h_v * Rec<T, C>::bytes;
+      const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, recs_end);
+      ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr};
+      if (sp.on) {
+        // one long sequence: two segments side by side on 64-column workgroups
+        float* st = reinterpret_cast<float*>(ws + sp.o_state);
+        const size_t hs = (size_t)p.h_v * D * D;
+        ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w)};
+        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3((unsigned)(3 * p.h_v * (D / 64))),
+                           dim3(128 * (4 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int ntile = (int)((p.total_tokens - sp.t_b + kJoinTok - 1) / kJoinTok);
+        const int nstate = p.final_state ? p.h_v * (D / 16) : 0;
+        hipLaunchKernelGGL(join_kernel<D>, dim3((unsigned)(nstate + ntile * p.h_v)), dim3(256), 0, stream, p, ss,
+                           sp.t_b, nstate);
+      } else if ((int64_t)p.n_seqs * p.h_v * (D / 32) <= kScanCUs) {
+        // narrow workgroups when even they leave CUs idle
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 32);
         hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>), dim3(grid), dim3(128 * (2 / kScan2Tiles)),
-                           0, stream, p, static_cast<const unsigned char*>(ws));
+                           0, stream, p, static_cast<const unsigned char*>(ws), ss);
       } else {
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 64);
         hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3(grid), dim3(128 * (4 / kScan2Tiles)),
-                           0, stream, p, static_cast<const unsigned char*>(ws));
+                           0, stream, p, static_cast<const unsigned char*>(ws), ss);
       }
     } else {
       const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / SL::cols);
@@ -1615,10 +1856,11 @@ size_t rec_c(int chunk) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int chunk) {
+size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk) {
   if (n_seqs < 1 || total_tokens < 0 || h_v < 1 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
   const size_t rec = io_dtype == 1 ? rec_c<__bf16>(chunk) : rec_c<float>(chunk);
-  return off_bytes(n_seqs) + (size_t)max_chunks(total_tokens, n_seqs, chunk) * h_v * rec;
+  const size_t recs_end = off_bytes(n_seqs) + (size_t)max_chunks(total_tokens, n_seqs, chunk) * h_v * rec;
+  return split_plan(io_dtype, total_tokens, n_seqs, h_v, d, chunk, recs_end).bytes;
 }
 
 bool prefill_supported(int io_dtype, int d, int chunk) {

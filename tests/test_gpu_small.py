@@ -125,6 +125,33 @@ def test_prefill_ragged(io, d, chunk):
     assert e["o"] < tol and e["state"] < tol
 
 
+@pytest.mark.parametrize("T,hq,hv,d,chunk,s0,fin", [
+    (2500, 2, 4, 128, 64, True, True),   # ragged last chunk, grouped heads
+    (2048, 1, 1, 128, 64, False, True),  # whole chunks, one head, zero initial state
+    (2113, 2, 2, 64, 64, True, True),    # d = 64: one 64-column block per head
+    (1100, 2, 2, 128, 32, True, True),   # chunk 32
+    (600, 1, 3, 128, 16, True, False),   # chunk 16, no final state asked for
+])
+def test_prefill_one_long_sequence_split(T, hq, hv, d, chunk, s0, fin):
+    """One sequence of 32+ chunks whose heads leave most CUs idle: the scan runs
+    the two halves side by side (the second from a zero state and as its own
+    transition) and joins them.  Outputs and final state must match the
+    token-by-token oracle as on the one-pass path."""
+    q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, "bf16", 90, s0=s0)
+    # the split is in use: its workspace holds the extra states and outputs
+    assert gdn.prefill_workspace_size(dev(q), dev(v), 1, chunk) > gdn.prefill_workspace_size(dev(q), dev(v), 2, chunk)
+    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0) if s0 else None, chunk=chunk,
+                       output_final_state=fin)
+    ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0) if s0 else None)
+    e = dict(o=rel_err(o, ro))
+    if fin:
+        e["state"] = rel_err(S, rS)
+    else:
+        assert S is None
+    report(f"prefill_split[T={T},h={hq}/{hv},d={d},C={chunk}]", **e)
+    assert all(x < TOL_BF16 for x in e.values())
+
+
 def test_prefill_tiny_fp32_config():
     """The tiny fp32 layer: T=256, 4 heads, d=64, chunk 16, zero initial state."""
     inp = gdn_inputs.prefill_inputs("tiny_fp32")
