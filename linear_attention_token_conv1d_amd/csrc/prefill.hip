@@ -15,24 +15,27 @@
 // o_t = scale S_t q_t ("Inside Qwen3.5", sections 4-5) unrolled over one
 // chunk; only e^{x} with x <= 0 is ever formed.
 //
-// Three launches on the caller's stream:
-//  plan  one workgroup: chunk offsets of every packed sequence (workspace).
-//  prep  one workgroup per (chunk, V head), all chunks in parallel: row norms,
-//        the two Gram matrices (MFMA), the decay masks, the UT solve
-//        T = (I + A)^-1 (fp32) and the chunk operands Tb, P and the per-token
-//        scalars, written to workspace.
-//  scan  one workgroup per (sequence, V head, block of 16*NW d_v columns),
-//        walking its chunks in order.  Wave w owns 16 d_v columns of the fp32
-//        state S^T (d_k x 16) in MFMA accumulators for the whole sequence.
-//        Every state-dependent product uses the previous result's accumulator
-//        tiles directly as the B operand of the next MFMA (a 16x16 accumulator
-//        holds rows 4g+i, g = lane/16, of column lane%16: a valid B fragment
-//        once the A operand reads its k index in the same order), so the
-//        serial chain never leaves registers.  The chunk's K, Q, Tb, P are
-//        double-buffered in LDS and the next chunk is prefetched into
-//        registers while the current one is computed; K^T fragments for the
-//        state update come straight from the row-major K tile through the
-//        gfx950 LDS transpose read (ds_read_b64_tr_b16).
+// Launches on the caller's stream:
+//  plan  one workgroup: chunk offsets of every packed sequence and the scan
+//        order (longest sequence first), in the workspace.
+//  prep  one workgroup per (chunk, group of V heads sharing a QK head), all
+//        chunks in parallel: row norms, the two Gram matrices (MFMA), the
+//        decay masks, the UT solve T = (I + A)^-1 (fp32 MFMA) and the chunk
+//        operands Tb, P and the per-token scalars, written to workspace.
+//  scan  bf16: scan2_kernel, one workgroup per (sequence, V head, block of
+//        32 or 64 d_v columns) walking its chunks in order.  Chain waves own
+//        16 columns of the fp32 state S^T each in MFMA accumulators for the
+//        whole sequence; every state-dependent product uses the previous
+//        result's accumulator tiles directly as the B operand of the next
+//        MFMA (a 16x16 accumulator holds rows 4g+i, g = lane/16, of column
+//        lane%16: a valid B fragment once the A operand reads its k index in
+//        the same order), so the serial chain never leaves registers.  Output
+//        waves form O^T from the published state and U and move the next
+//        chunk into the second LDS buffer by direct-to-LDS loads.  fp32:
+//        scan_kernel, the same math in four waves.
+//  join  only after a split scan of one long sequence (see split_plan):
+//        adds S_m w_t to the second segment's outputs and forms the final
+//        state.
 #include <type_traits>
 
 #include "gdn_device.h"
