@@ -56,6 +56,10 @@ typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activatio
 
 /* flags */
 #define GDN_FLAG_L2NORM_QK 1u /* L2-normalise q and k per head (eps 1e-6 inside the sqrt) */
+/* Erase-off variant: S_t = a_t S_{t-1} + b_t v_t k_t^T, the additive linear
+ * attention of "Inside Qwen3.5", section 2 (S = sum v k^T, o = S q) with the
+ * decay gate of section 5 kept and its error-correcting write dropped. */
+#define GDN_FLAG_NO_ERASE 2u
 
 /* ------------------------------------------------------------------------
  * gdn_conv1d -- causal depthwise convolution (+ optional SiLU) over packed
@@ -116,7 +120,9 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  *                always fp32; accumulation is fp32.  With GDN_BF16 the dense
  *                chunk contractions run on bf16 MFMA; with GDN_F32 on fp32
  *                MFMA.
- *   flags        GDN_FLAG_L2NORM_QK to normalise q and k inside the call.
+ *   flags        GDN_FLAG_L2NORM_QK to normalise q and k inside the call;
+ *                GDN_FLAG_NO_ERASE for the erase-off variant (same chunked
+ *                machinery with A = 0, i.e. T = I, and U = diag(beta) V).
  *   n_seqs       >= 1.    total_tokens T >= 0.
  *   h_qk, h_v    head counts, h_v % h_qk == 0.
  *   d_k, d_v     head widths: both 64 or both 128.
@@ -185,7 +191,9 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  *                conv_state and o.
  *   state_dtype  GDN_BF16 (stored with round-to-nearest-even, accumulated in
  *                fp32) or GDN_F32.
- *   flags        GDN_FLAG_L2NORM_QK.
+ *   flags        GDN_FLAG_L2NORM_QK; GDN_FLAG_NO_ERASE for the erase-off
+ *                variant (delta_i = beta v_i: the state is still read and
+ *                written once).
  *   n_seqs       >= 0.   h_qk, h_v (h_v % h_qk == 0), d_k = d_v in {64, 128}.
  *   width        conv width W in 2..4 (ignored without conv_weight).
  *   activation   GDN_ACT_SILU or GDN_ACT_NONE.

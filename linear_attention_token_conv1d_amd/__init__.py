@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 F32, BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 FLAG_L2NORM_QK = 1
+FLAG_NO_ERASE = 2
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _c_void_p = ctypes.c_void_p
 
@@ -154,10 +155,11 @@ def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="s
 
 
 def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
-                  workspace=None):
+                  workspace=None, erase=True):
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
-    a = PrefillArgs(ctypes.sizeof(PrefillArgs), FLAG_L2NORM_QK if l2norm else 0, _DT[q.dtype], N, T,
+    flags = (FLAG_L2NORM_QK if l2norm else 0) | (0 if erase else FLAG_NO_ERASE)
+    a = PrefillArgs(ctypes.sizeof(PrefillArgs), flags, _DT[q.dtype], N, T,
                     h_qk, h_v, d_k, d_v, chunk, scale, _ptr(q), _ptr(k), _ptr(v), q.stride(0),
                     k.stride(0), v.stride(0), _ptr(g), _ptr(beta), _ptr(initial_state),
                     _ptr(final_state), _ptr(o), _ptr(cu), _ptr(workspace),
@@ -181,9 +183,11 @@ def _head_view(t, name, heads_dim_ok=True):
 
 
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, scale=1.0,
-            l2norm=True, output_final_state=True, o=None, final_state=None, workspace=None):
+            l2norm=True, output_final_state=True, o=None, final_state=None, workspace=None,
+            erase=True):
     """Chunked gated delta rule.  q, k [T, H_qk, d], v [T, H_v, d] (bf16 or fp32,
     token stride free), g, beta [T, H_v] fp32, initial_state [N, H_v, d, d] fp32.
+    erase=False runs the erase-off variant S_t = a_t S_{t-1} + b_t v_t k_t^T.
 
     Returns (o [T, H_v, d], final_state [N, H_v, d, d] fp32 or None)."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -205,7 +209,7 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, sca
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
-                      workspace if need else None)
+                      workspace if need else None, erase)
     _check(lib().gdn_prefill(ctypes.byref(a), _stream(q.device)), "gdn_prefill")
     return o, final_state
 
@@ -221,20 +225,22 @@ def split_qkv(y, h_qk, d_k, h_v, d_v):
 
 
 def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv_state=None,
-              initial_state=None, cu_seqlens=None, chunk=64, scale=1.0, l2norm=True, y=None):
+              initial_state=None, cu_seqlens=None, chunk=64, scale=1.0, l2norm=True, y=None,
+              erase=True):
     """The whole mixer: conv1d(+SiLU) over [q|k|v], then the chunked recurrence
     reading q, k, v as column slices of the conv output (no copies)."""
     y = conv1d(x, conv_weight, conv_bias, conv_state, cu_seqlens, "silu", out=y)
     q, k, v = split_qkv(y, h_qk, d_k, h_v, d_v)
-    o, S = prefill(q, k, v, g, beta, initial_state, cu_seqlens, chunk, scale, l2norm)
+    o, S = prefill(q, k, v, g, beta, initial_state, cu_seqlens, chunk, scale, l2norm, erase=erase)
     return o, S
 
 
 def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=None, conv_bias=None,
-                activation="silu", l2norm=True, scale=1.0, o=None):
+                activation="silu", l2norm=True, scale=1.0, o=None, erase=True):
     """One token for each of N sequences.  x [N, C] (pre-conv, or q|k|v when
     conv_weight is None); state [N, H_v, d, d] (bf16 or fp32) and conv_state
-    [N, C, W-1] are updated in place.  Returns o [N, H_v, d]."""
+    [N, C, W-1] are updated in place.  Returns o [N, H_v, d].  erase=False runs
+    the erase-off variant."""
     _contig(x, "x")
     N = x.shape[0]
     _contig(g, "g", torch.float32)
@@ -248,7 +254,8 @@ def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=No
     if o is None:
         o = torch.empty((N, h_v, d), dtype=x.dtype, device=x.device)
     W = conv_weight.shape[1] if conv_weight is not None else 4
-    a = DecodeArgs(ctypes.sizeof(DecodeArgs), FLAG_L2NORM_QK if l2norm else 0, _DT[x.dtype],
+    flags = (FLAG_L2NORM_QK if l2norm else 0) | (0 if erase else FLAG_NO_ERASE)
+    a = DecodeArgs(ctypes.sizeof(DecodeArgs), flags, _DT[x.dtype],
                    _DT[state.dtype], N, h_qk, h_v, d, d, W,
                    ACT_SILU if activation == "silu" else ACT_NONE, scale, _ptr(x), _ptr(conv_weight),
                    _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), _ptr(o))

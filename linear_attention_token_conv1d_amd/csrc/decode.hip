@@ -8,7 +8,8 @@
 //   2. L2-normalises q and k (one wave, fp32);
 //   3. streams the grp*d_v state rows once: each row S_i (d_k values) is
 //      loaded by 16 lanes, reduced against k and q with DPP row sums, then
-//        a_i = S_i.k,  b_i = S_i.q,  d_i = beta (v_i - alpha a_i)
+//        a_i = S_i.k,  b_i = S_i.q,  d_i = beta (v_i - alpha a_i)  (beta v_i
+//        without the erase)
 //        S_i <- alpha S_i + d_i k^T,  o_i = scale (alpha b_i + d_i (k.q))
 //      and written back.  Rows are independent, so one pass suffices: the
 //      kernel reads and writes each state byte exactly once.
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     b = row16_sum(b);
     const int hl = r / D;
     const float al = s_al[hl];
-    const float dl = s_be[hl] * (s_v[r] - al * a);
+    const float dl = s_be[hl] * (s_v[r] - (p.erase ? al * a : 0.f));
     float nv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];

@@ -56,7 +56,8 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
     return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: struct_size %u < %zu", a->struct_size,
                 sizeof(gdn_prefill_args));
   if (!is_dtype(a->io_dtype)) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: bad io_dtype %d", a->io_dtype);
-  if (a->flags & ~GDN_FLAG_L2NORM_QK) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: unknown flags 0x%x", a->flags);
+  if (a->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_NO_ERASE))
+    return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: unknown flags 0x%x", a->flags);
   if (a->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: n_seqs %d < 1", a->n_seqs);
   if (a->total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: total_tokens < 0");
   if (a->h_qk < 1 || a->h_v < 1 || a->h_v % a->h_qk)
@@ -165,7 +166,7 @@ gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
                          a->g, a->beta, a->initial_state, a->final_state, a->o, a->cu_seqlens,
                          a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
                          (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale, a->workspace,
-                         a->workspace_bytes};
+                         a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_prefill(p, a->io_dtype, a->d_k, s), s, "gdn_prefill");
   } catch (...) {
@@ -181,7 +182,7 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
                   sizeof(gdn_decode_args));
     if (!is_dtype(a->io_dtype) || !is_dtype(a->state_dtype))
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: bad io_dtype/state_dtype");
-    if (a->flags & ~GDN_FLAG_L2NORM_QK)
+    if (a->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_NO_ERASE))
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: unknown flags 0x%x", a->flags);
     if (a->n_seqs < 0) return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: n_seqs < 0");
     if (a->h_qk < 1 || a->h_v < 1 || a->h_v % a->h_qk)
@@ -209,7 +210,8 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
     if (a->n_seqs == 0) { g_last_error.clear(); return GDN_OK; }
     gdn::DecodeParams p{a->x, a->conv_weight, a->conv_bias, a->conv_state, a->g, a->beta,
                         a->state, a->o, a->n_seqs, a->h_qk, a->h_v, a->conv_weight ? a->width : 4,
-                        a->activation, (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale};
+                        a->activation, (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale,
+                        (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_decode(p, a->io_dtype, a->state_dtype, a->d_k, s), s, "gdn_decode_step");
   } catch (...) {

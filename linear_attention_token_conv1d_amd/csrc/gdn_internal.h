@@ -39,6 +39,7 @@ struct DecodeParams {
   int32_t act;
   int32_t l2norm;
   float scale;
+  int32_t erase;  // 0: erase-off variant, S_t = a_t S_{t-1} + b_t v_t k_t^T
 };
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, int state_dtype, int d,
                          hipStream_t stream);
@@ -65,6 +66,7 @@ struct PrefillParams {
   float scale;
   void* workspace;
   size_t workspace_bytes;
+  int32_t erase;  // 0: erase-off variant (A = 0, U = diag(beta) V)
 };
 // Workspace of gdn_prefill: chunk offsets plus, per (chunk, V head), the
 // chunk operands Tb, P and four per-token scalar rows.

@@ -689,7 +689,7 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   float* vec_g = reinterpret_cast<float*>(rec + 2 * Rec<T, C>::mat);
   if (ttid < C) {
     const float G = G_s[ttid], Gl = G_s[Lc - 1], eg = fexp(G);
-    vec_g[ttid] = eg * rk_s[ttid];
+    vec_g[ttid] = p.erase ? eg * rk_s[ttid] : 0.f;  // no erase: R = V
     vec_g[C + ttid] = p.scale * eg * rq_s[ttid];
     vec_g[2 * C + ttid] = fexp(Gl - G) * rk_s[ttid];
     vec_g[3 * C + ttid] = fexp(Gl);
@@ -702,10 +702,10 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
     if (job < 2 * NLT) {
       const bool isP = job >= NLT;
       const int r = jmt[jj] * 16 + l16, j0 = jnt[jj] * 16 + 4 * g4;
-      // row factor (scale rq_r for P, beta_r rk_r for A) and the four
-      // columns' G and rk, each read once
+      // row factor (scale rq_r for P, beta_r rk_r for A, or 0 for A without
+      // the erase: T = I) and the four columns' G and rk, each read once
       const float Gr = G_s[r];
-      const float fr = isP ? p.scale * rq_s[r] : b_s[r] * rk_s[r];
+      const float fr = isP ? p.scale * rq_s[r] : p.erase ? b_s[r] * rk_s[r] : 0.f;
       const float4 Gj = *reinterpret_cast<const float4*>(G_s + j0);
       const float4 kj = *reinterpret_cast<const float4*>(rk_s + j0);
       const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w}, rkj[4] = {kj.x, kj.y, kj.z, kj.w};

@@ -18,9 +18,13 @@ the method is stated:
 * the gated delta rule ("Inside Qwen3.5", sections 4-5: the update
   S <- a*S + b*(v - S*k)*k^T with per-token, per-head a and b), read with the
   decay applied first, i.e. S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T
-  and o_t = S_t q_t.  V head h reads QK head h // (H_v / H_qk).
+  and o_t = S_t q_t.  V head h reads QK head h // (H_v / H_qk);
+* with erase=False, the same recurrence without the error-correcting write:
+  S_t = a_t S_{t-1} + b_t v_t k_t^T, the additive linear attention of
+  "Inside Qwen3.5", section 2 (S = sum v k^T, o = S q) with the decay gate of
+  section 5 kept and the correction term dropped.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * eps = 1e-6 inside the square root of the L2 norm;
   * conv tap W-1 multiplies the current token; the conv state holds the last
     W-1 inputs in chronological order (oldest first); positions before a
@@ -123,7 +127,7 @@ def split_qkv(y, h_qk, d_k, h_v, d_v):
 
 
 def gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
-                     l2norm_qk=True, eps=1e-6, v_heads=None):
+                     l2norm_qk=True, eps=1e-6, v_heads=None, erase=True):
     """Sequential gated delta rule, one token at a time, in fp64.
 
     q, k  [T, H_qk, d_k];  v [T, H_v, d_v];  g, beta [T, H_v]
@@ -137,6 +141,7 @@ def gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scal
         S  <- S + beta_t * (v_t - S k_t) k_t^T   (delta write against the decayed S)
         o_t = scale * S q_t
     which equals S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T.
+    erase=False drops the S k_t term: S_t = a_t S_{t-1} + b_t v_t k_t^T.
     """
     q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
     T, h_qk, d_k = q.shape
@@ -161,7 +166,7 @@ def gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scal
             kt = k[t, qk_of]                      # [H, d_k]
             qt = q[t, qk_of]                      # [H, d_k]
             S = np.exp(g[t, heads])[:, None, None] * S
-            pred = np.matmul(S, kt[:, :, None])[:, :, 0]          # S k   [H, d_v]
+            pred = np.matmul(S, kt[:, :, None])[:, :, 0] if erase else 0.0  # S k   [H, d_v]
             err = beta[t, heads][:, None] * (v[t, heads] - pred)  # b (v - S k)
             S = S + err[:, :, None] * kt[:, None, :]
             o[t] = scale * np.matmul(S, qt[:, :, None])[:, :, 0]
@@ -185,7 +190,7 @@ def layer_channels(h_qk, d_k, h_v, d_v, v_heads=None):
 
 def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv_state=None,
               initial_state=None, cu_seqlens=None, scale=1.0, activation="silu", l2norm_qk=True,
-              v_heads=None, x_is_selected=False):
+              v_heads=None, x_is_selected=False, erase=True):
     """The whole token mixer for packed sequences: conv(+SiLU) -> split -> recurrence.
 
     With v_heads given, only the channels those heads read are convolved (the
@@ -215,12 +220,12 @@ def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv
     bh = _f64(beta)[:, heads]
     s0 = None if initial_state is None else _f64(initial_state)[:, heads]
     # one QK slot per V head (explicitly repeated), so the grouping is trivial
-    o, S = gated_delta_rule(qh, kh, vv, gh, bh, s0, cu_seqlens, scale, l2norm_qk)
+    o, S = gated_delta_rule(qh, kh, vv, gh, bh, s0, cu_seqlens, scale, l2norm_qk, erase=erase)
     return o, S, new_cs
 
 
 def decode_step(x, conv_weight, g, beta, state, conv_state, h_qk, d_k, h_v, d_v, conv_bias=None,
-                scale=1.0, activation="silu", l2norm_qk=True, round_state_bf16=False):
+                scale=1.0, activation="silu", l2norm_qk=True, round_state_bf16=False, erase=True):
     """One new token for each of N independent sequences.
 
     x [N, C] pre-conv inputs; conv_state [N, C, W-1]; state [N, H_v, d_v, d_k];
@@ -239,14 +244,14 @@ def decode_step(x, conv_weight, g, beta, state, conv_state, h_qk, d_k, h_v, d_v,
     else:
         y, new_cs = causal_conv1d(x, conv_weight, conv_bias, conv_state, cu, activation)
     q, k, v = split_qkv(y, h_qk, d_k, h_v, d_v)
-    o, S = gated_delta_rule(q, k, v, g, beta, state, cu, scale, l2norm_qk)
+    o, S = gated_delta_rule(q, k, v, g, beta, state, cu, scale, l2norm_qk, erase=erase)
     if round_state_bf16:
         S = round_to_bf16(S)
     return o, S, new_cs
 
 
 def chunked_gated_delta_rule(q, k, v, g, beta, initial_state, chunk, scale=1.0, l2norm_qk=True,
-                             eps=1e-6):
+                             eps=1e-6, erase=True):
     """The chunked (WY / UT-transform) rearrangement of the same recurrence, fp64.
 
     Used only to pin the algebra of the chunked prefill in tests; it is never
@@ -256,6 +261,7 @@ def chunked_gated_delta_rule(q, k, v, g, beta, initial_state, chunk, scale=1.0, 
         U   = Tm diag(beta) (V - diag(gamma) K S^T)
         O   = diag(gamma) Q S^T + (lower_incl(e^{G_r-G_j}) * Q K^T) U
         S'  = gamma_last S + U^T diag(e^{G_last - G}) K
+    With erase=False there is no correction: A = 0 (Tm = I) and U = diag(beta) V.
     """
     q, k, v, g, beta = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta)
     T, h_qk, d_k = q.shape
@@ -279,9 +285,12 @@ def chunked_gated_delta_rule(q, k, v, g, beta, initial_state, chunk, scale=1.0, 
             incl = np.tril(np.ones((n, n), dtype=bool))
             D = np.where(incl, G[:, None] - G[None, :], 0.0)
             Gam = np.where(incl, np.exp(D), 0.0)
-            A = np.tril(b[:, None] * Gam * (K @ K.T), -1)
-            Tm = np.linalg.inv(np.eye(n) + A)
-            U = Tm @ (b[:, None] * (V - gam[:, None] * (K @ S.T)))
+            if erase:
+                A = np.tril(b[:, None] * Gam * (K @ K.T), -1)
+                Tm = np.linalg.inv(np.eye(n) + A)
+                U = Tm @ (b[:, None] * (V - gam[:, None] * (K @ S.T)))
+            else:
+                U = b[:, None] * V
             o[c0:c1, h] = scale * (gam[:, None] * (Q @ S.T) + (Gam * (Q @ K.T)) @ U)
             S = gam[-1] * S + (U * np.exp(G[-1] - G)[:, None]).T @ K
         S_all[h] = S

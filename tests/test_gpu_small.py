@@ -83,6 +83,28 @@ def test_decode_step_matches_oracle(io, state_dt, d):
     assert e["o"] < tol and e["state"] < tol and e["conv_state"] == 0.0
 
 
+@pytest.mark.parametrize("io,state_dt,d", [("bf16", "bf16", 128), ("f32", "f32", 64)])
+def test_decode_step_erase_off(io, state_dt, d):
+    """The erase-off variant (delta_i = beta v_i) against the oracle's additive
+    recurrence, with the conv step."""
+    N, hq, hv = 4, 2, 6
+    C = 2 * hq * d + hv * d
+    x = _rand((N, C), DT[io], seed=17)
+    w = _rand((C, 4), DT[io], 0.5, seed=18)
+    cs = _rand((N, C, 3), DT[io], seed=19)
+    S = _rand((N, hv, d, d), DT[state_dt], 0.1, seed=20)
+    g, b = _gates(N, hv, 21)
+    S_d, cs_d = dev(S.clone()), dev(cs.clone())
+    o = gdn.decode_step(dev(x), dev(g), dev(b), S_d, hq, hv, d, conv_weight=dev(w), conv_state=cs_d,
+                        erase=False)
+    ro, rS, rcs = orc.decode_step(np64(x), np64(w), np64(g), np64(b), np64(S), np64(cs), hq, d, hv, d,
+                                  erase=False)
+    tol = TOL_BF16 if "bf16" in (io, state_dt) else TOL_F32
+    e = dict(o=rel_err(o, ro), state=rel_err(S_d, rS), conv_state=rel_err(cs_d, rcs))
+    report(f"decode_erase_off[{io},{state_dt},d={d}]", **e)
+    assert e["o"] < tol and e["state"] < tol and e["conv_state"] == 0.0
+
+
 def test_decode_step_without_conv_64_steps():
     """No conv (x already holds q|k|v), 64 steps, fp32 io/state, 1e-4."""
     N, hq, hv, d = 3, 1, 2, 64
@@ -150,6 +172,30 @@ def test_prefill_one_long_sequence_split(T, hq, hv, d, chunk, s0, fin):
         assert S is None
     report(f"prefill_split[T={T},h={hq}/{hv},d={d},C={chunk}]", **e)
     assert all(x < TOL_BF16 for x in e.values())
+
+
+@pytest.mark.parametrize("io,d,chunk,T,lens", [
+    ("bf16", 128, 64, 201, None),          # ragged tail, grouped heads
+    ("f32", 64, 16, 150, None),            # fp32 path
+    ("bf16", 64, 32, None, [40, 0, 130, 7]),  # varlen pack with an empty sequence
+    ("bf16", 128, 64, 2500, None),         # one long sequence: split scan
+])
+def test_prefill_erase_off(io, d, chunk, T, lens):
+    """The erase-off variant S_t = a_t S_{t-1} + b_t v_t k_t^T (same chunked
+    path with A = 0, U = diag(beta) V) against the oracle's additive recurrence."""
+    hq, hv = 2, 4
+    if lens is not None:
+        T = sum(lens)
+    q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, io, 110, lens)
+    cu = None if lens is None else gdn_inputs.cu_from_lengths(lens)
+    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0), cu_seqlens=dev(cu), chunk=chunk,
+                       erase=False)
+    ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0),
+                                  cu_seqlens=None if cu is None else cu.numpy(), erase=False)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    e = dict(o=rel_err(o, ro), state=rel_err(S, rS))
+    report(f"prefill_erase_off[{io},d={d},C={chunk},T={T}]", **e)
+    assert e["o"] < tol and e["state"] < tol
 
 
 def test_prefill_tiny_fp32_config():

@@ -321,6 +321,92 @@ def test_layer_and_decode_handoff():
     assert np.allclose(o2, o[:, [3, 0]], atol=1e-14) and np.allclose(S2, S[:, [3, 0]], atol=1e-14)
 
 
+# ------------------------------------------------------- erase-off variant
+
+def test_erase_off_closed_form_any_keys():
+    """Without the correcting write the recurrence is additive: for any keys
+    S_t = (prod_{r<=t} a_r) S_0 + sum_{s<=t} (prod_{s<r<=t} a_r) b_s v_s k_s^T
+    and o_t = scale S_t q_t -- the linear attention S = sum v k^T, o = S q of
+    "Inside Qwen3.5", section 2, with the decay gate of section 5."""
+    rng = np.random.default_rng(40)
+    T = 8
+    q, k, v, g, beta, s0 = _rand_case(rng, T=T, h_qk=1, h_v=1)
+    o, S = orc.gated_delta_rule(q, k, v, g, beta, s0, scale=0.7, erase=False)
+    kn = k[:, 0] / np.sqrt((k[:, 0] ** 2).sum(-1, keepdims=True) + 1e-6)
+    qn = q[:, 0] / np.sqrt((q[:, 0] ** 2).sum(-1, keepdims=True) + 1e-6)
+    G = np.cumsum(g[:, 0])
+    for t in range(T):
+        St = np.exp(G[t]) * s0[0, 0] + sum(np.exp(G[t] - G[s]) * beta[s, 0] * np.outer(v[s, 0], kn[s])
+                                           for s in range(t + 1))
+        assert np.allclose(o[t, 0], 0.7 * St @ qn[t], atol=1e-13)
+    assert np.allclose(S[0, 0], St, atol=1e-13)
+
+
+def test_erase_off_plain_linear_attention():
+    """a = b = 1 and S_0 = 0: S_t = sum_{s<=t} v_s k_s^T and o_t = S_t q_t,
+    as printed in "Inside Qwen3.5", section 2 (prefix sums by torch.cumsum)."""
+    rng = np.random.default_rng(41)
+    T, d = 7, 5
+    q, k, v = rng.standard_normal((T, 1, d)), rng.standard_normal((T, 1, d)), rng.standard_normal((T, 1, 3))
+    o, S = orc.gated_delta_rule(q, k, v, np.zeros((T, 1)), np.ones((T, 1)), None, l2norm_qk=False,
+                                erase=False)
+    outer = torch.from_numpy(np.einsum("ti,tj->tij", v[:, 0], k[:, 0]))
+    St = torch.cumsum(outer, dim=0).numpy()
+    assert np.allclose(S[0, 0], St[-1], atol=1e-14)
+    assert np.allclose(o[:, 0], np.einsum("tij,tj->ti", St, q[:, 0]), atol=1e-13)
+
+
+def test_erase_off_equals_erase_on_for_orthogonal_keys():
+    """Mutually orthogonal unit keys and S_0 = 0: S_{t-1} k_t = 0, so the
+    correcting term vanishes and the two forms agree."""
+    rng = np.random.default_rng(42)
+    T, d = 6, 8
+    k = np.eye(d)[rng.permutation(d)[:T]][:, None, :]
+    q = rng.standard_normal((T, 1, d))
+    v = rng.standard_normal((T, 1, 3))
+    g = -np.logaddexp(0, -rng.standard_normal((T, 1)))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, 1))))
+    o1, S1 = orc.gated_delta_rule(q, k, v, g, beta, None, l2norm_qk=False)
+    o0, S0 = orc.gated_delta_rule(q, k, v, g, beta, None, l2norm_qk=False, erase=False)
+    assert np.allclose(o1, o0, atol=1e-14) and np.allclose(S1, S0, atol=1e-14)
+    # with a repeated key they differ: the erase-on form replaces, the other adds
+    k2 = k.copy()
+    k2[3] = k2[1]
+    _, Sa = orc.gated_delta_rule(q, k2, v, g, beta, None, l2norm_qk=False)
+    _, Sb = orc.gated_delta_rule(q, k2, v, g, beta, None, l2norm_qk=False, erase=False)
+    assert np.abs(Sa - Sb).max() > 1e-3
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64])
+def test_erase_off_chunked_equals_sequential(chunk):
+    """Brute force: the chunked form with no correction (A = 0, U = diag(b) V)
+    equals the sequential additive recurrence, partial chunks and S_0 != 0."""
+    rng = np.random.default_rng(43)
+    q, k, v, g, beta, s0 = _rand_case(rng, T=37, h_qk=2, h_v=6, d_k=8, d_v=5)
+    o, S = orc.gated_delta_rule(q, k, v, g, beta, s0, erase=False)
+    oc, Sc = orc.chunked_gated_delta_rule(q, k, v, g, beta, s0[0], chunk, erase=False)
+    assert np.abs(o - oc).max() < 1e-12
+    assert np.abs(S[0] - Sc).max() < 1e-12
+
+
+def test_erase_off_layer_and_decode_handoff():
+    """Erase off: the layer over T tokens, then one decode step from its
+    states, equals the layer over T + 1 tokens."""
+    rng = np.random.default_rng(44)
+    hq, hv, d = 1, 3, 8
+    C = 2 * hq * d + hv * d
+    T = 9
+    x = rng.standard_normal((T + 1, C))
+    w = 0.5 * rng.standard_normal((C, 4))
+    g = -np.logaddexp(0, -rng.standard_normal((T + 1, hv)))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T + 1, hv))))
+    s0 = 0.1 * rng.standard_normal((1, hv, d, d))
+    o, S, cs = orc.gdn_layer(x, w, g, beta, hq, d, hv, d, initial_state=s0, erase=False)
+    oa, Sa, csa = orc.gdn_layer(x[:T], w, g[:T], beta[:T], hq, d, hv, d, initial_state=s0, erase=False)
+    od, Sd, _ = orc.decode_step(x[T:], w, g[T:], beta[T:], Sa, csa, hq, d, hv, d, erase=False)
+    assert np.allclose(od[0], o[T], atol=1e-13) and np.allclose(Sd, S, atol=1e-13)
+
+
 def test_bf16_rounding_is_nearest_even():
     vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1e-3, 3.0e38])
     ref = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).float().numpy()
