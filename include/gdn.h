@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -141,6 +141,22 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  *   cu_seqlens   as in gdn_conv1d.
  *   workspace    device scratch of at least gdn_prefill_workspace_size()
  *                bytes, 256-byte aligned.  Contents on entry are ignored.
+ *   emit_every   K >= 0.  With K > 0 the state after every K-th whole chunk
+ *                of a sequence that ends before the sequence does (tokens
+ *                j K chunk, j = 1, 2, ..., strictly inside the sequence) is
+ *                written to chunk_states, for prefix caching: the chunk
+ *                boundary states already exist on chip, and a recurrent cache
+ *                can be reused only from states stored at block boundaries
+ *                ("Mamba hybrid model selection", adoption checklist).
+ *   chunk_states [R, h_v, d_v, d_k] fp32, R = sum_n E_n with
+ *                E_n = floor(max(len_n - 1, 0) / (K chunk)); sequence n's
+ *                states are rows sum_{m<n} E_m + j - 1.  NULL when K = 0.
+ *   state_idx    [n_seqs] int32 or NULL: sequence n reads initial_state and
+ *                writes final_state at slot state_idx[n] of [slots, h_v, d_v,
+ *                d_k] pools (NULL: slot n), for caches that keep states in
+ *                slots across requests ("Mamba hybrid model selection",
+ *                concurrent-requests section).  Slots must be distinct and
+ *                inside both pools; they are not read on the host.
  * ---------------------------------------------------------------------- */
 typedef struct gdn_prefill_args {
   uint32_t struct_size;
@@ -168,6 +184,9 @@ typedef struct gdn_prefill_args {
   const int32_t* cu_seqlens;
   void* workspace;
   size_t workspace_bytes;
+  int32_t emit_every;
+  float* chunk_states;
+  const int32_t* state_idx;
 } gdn_prefill_args;
 
 /* Bytes of workspace gdn_prefill needs for these arguments (pointers are not
@@ -206,6 +225,10 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  *   g, beta      [n_seqs, h_v] fp32.
  *   state        [n_seqs, h_v, d_v, d_k] in/out, in state_dtype.
  *   o            [n_seqs, h_v, d_v] in io_dtype.
+ *   state_idx    [n_seqs] int32 or NULL: sequence n's state and conv_state
+ *                are slot state_idx[n] of [slots, ...] pools (NULL: slot n);
+ *                x, g, beta and o stay indexed by n.  Slots must be distinct
+ *                and inside both pools; they are not read on the host.
  * ---------------------------------------------------------------------- */
 typedef struct gdn_decode_args {
   uint32_t struct_size;
@@ -228,6 +251,7 @@ typedef struct gdn_decode_args {
   const float* beta;
   void* state;
   void* o;
+  const int32_t* state_idx;
 } gdn_decode_args;
 
 gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);

@@ -28,6 +28,7 @@ F32, BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 FLAG_L2NORM_QK = 1
 FLAG_NO_ERASE = 2
+ABI_VERSION = 2  # the gdn.h this binding matches
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _c_void_p = ctypes.c_void_p
 
@@ -55,7 +56,8 @@ class PrefillArgs(ctypes.Structure):
                 ("k_stride", ctypes.c_int64), ("v_stride", ctypes.c_int64), ("g", _c_void_p),
                 ("beta", _c_void_p), ("initial_state", _c_void_p), ("final_state", _c_void_p),
                 ("o", _c_void_p), ("cu_seqlens", _c_void_p), ("workspace", _c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("emit_every", ctypes.c_int32),
+                ("chunk_states", _c_void_p), ("state_idx", _c_void_p)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -65,7 +67,8 @@ class DecodeArgs(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("width", ctypes.c_int32),
                 ("activation", ctypes.c_int32), ("scale", ctypes.c_float), ("x", _c_void_p),
                 ("conv_weight", _c_void_p), ("conv_bias", _c_void_p), ("conv_state", _c_void_p),
-                ("g", _c_void_p), ("beta", _c_void_p), ("state", _c_void_p), ("o", _c_void_p)]
+                ("g", _c_void_p), ("beta", _c_void_p), ("state", _c_void_p), ("o", _c_void_p),
+                ("state_idx", _c_void_p)]
 
 
 _lib = None
@@ -91,7 +94,7 @@ def lib():
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
-        if L.gdn_abi_version() != 1:
+        if L.gdn_abi_version() != ABI_VERSION:
             raise GdnError("libgdn.so ABI version mismatch")
         _lib = L
     return _lib
@@ -155,7 +158,7 @@ def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="s
 
 
 def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
-                  workspace=None, erase=True):
+                  workspace=None, erase=True, emit_every=0, chunk_states=None, state_idx=None):
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     flags = (FLAG_L2NORM_QK if l2norm else 0) | (0 if erase else FLAG_NO_ERASE)
@@ -163,15 +166,25 @@ def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk,
                     h_qk, h_v, d_k, d_v, chunk, scale, _ptr(q), _ptr(k), _ptr(v), q.stride(0),
                     k.stride(0), v.stride(0), _ptr(g), _ptr(beta), _ptr(initial_state),
                     _ptr(final_state), _ptr(o), _ptr(cu), _ptr(workspace),
-                    0 if workspace is None else workspace.numel())
+                    0 if workspace is None else workspace.numel(), emit_every, _ptr(chunk_states),
+                    _ptr(state_idx))
     return a
 
 
-def prefill_workspace_size(q, v, n_seqs=1, chunk=64):
+def prefill_workspace_size(q, v, n_seqs=1, chunk=64, emit_every=0):
     T, h_qk, d_k = q.shape
     a = PrefillArgs(struct_size=ctypes.sizeof(PrefillArgs), io_dtype=_DT[q.dtype], n_seqs=n_seqs,
-                    total_tokens=T, h_qk=h_qk, h_v=v.shape[1], d_k=d_k, d_v=v.shape[2], chunk=chunk)
+                    total_tokens=T, h_qk=h_qk, h_v=v.shape[1], d_k=d_k, d_v=v.shape[2], chunk=chunk,
+                    emit_every=emit_every)
     return lib().gdn_prefill_workspace_size(ctypes.byref(a))
+
+
+def chunk_state_rows(lengths, chunk, emit_every):
+    """Rows of chunk_states for sequences of these lengths: each sequence
+    emits the state after every emit_every-th whole chunk that ends inside it
+    (floor((len - 1) / (emit_every chunk)) states), in sequence order."""
+    every = emit_every * chunk
+    return sum((int(L) - 1) // every for L in lengths if int(L) > 0)
 
 
 def _head_view(t, name, heads_dim_ok=True):
@@ -184,10 +197,14 @@ def _head_view(t, name, heads_dim_ok=True):
 
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, scale=1.0,
             l2norm=True, output_final_state=True, o=None, final_state=None, workspace=None,
-            erase=True):
+            erase=True, emit_every=0, chunk_states=None, state_idx=None):
     """Chunked gated delta rule.  q, k [T, H_qk, d], v [T, H_v, d] (bf16 or fp32,
     token stride free), g, beta [T, H_v] fp32, initial_state [N, H_v, d, d] fp32.
     erase=False runs the erase-off variant S_t = a_t S_{t-1} + b_t v_t k_t^T.
+    emit_every=K > 0 also returns the chunk-boundary states [rows, H_v, d, d]
+    (see chunk_state_rows) as a third result.  state_idx [N] int32 maps each
+    sequence to a slot of the initial_state / final_state pools (both then
+    given by the caller).
 
     Returns (o [T, H_v, d], final_state [N, H_v, d, d] fp32 or None)."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -203,14 +220,25 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, sca
         _contig(initial_state, "initial_state", torch.float32)
     if o is None:
         o = torch.empty((T, h_v, d_v), dtype=q.dtype, device=q.device)
+    if state_idx is not None:
+        _contig(state_idx, "state_idx", torch.int32)
+        if output_final_state and final_state is None:
+            raise GdnError("with state_idx, pass the final_state pool")
     if output_final_state and final_state is None:
         final_state = torch.empty((N, h_v, d_v, q.shape[2]), dtype=torch.float32, device=q.device)
-    need = prefill_workspace_size(q, v, N, chunk)
+    if emit_every > 0 and chunk_states is None:
+        lengths = [T] if cu is None else (cu[1:] - cu[:-1]).tolist()
+        rows = chunk_state_rows(lengths, chunk, emit_every)
+        chunk_states = torch.empty((max(rows, 1), h_v, d_v, q.shape[2]), dtype=torch.float32, device=q.device)
+    need = prefill_workspace_size(q, v, N, chunk, emit_every)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
-                      workspace if need else None, erase)
+                      workspace if need else None, erase, emit_every, chunk_states if emit_every > 0 else None,
+                      state_idx)
     _check(lib().gdn_prefill(ctypes.byref(a), _stream(q.device)), "gdn_prefill")
+    if emit_every > 0:
+        return o, final_state, chunk_states
     return o, final_state
 
 
@@ -236,11 +264,12 @@ def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv
 
 
 def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=None, conv_bias=None,
-                activation="silu", l2norm=True, scale=1.0, o=None, erase=True):
+                activation="silu", l2norm=True, scale=1.0, o=None, erase=True, state_idx=None):
     """One token for each of N sequences.  x [N, C] (pre-conv, or q|k|v when
     conv_weight is None); state [N, H_v, d, d] (bf16 or fp32) and conv_state
     [N, C, W-1] are updated in place.  Returns o [N, H_v, d].  erase=False runs
-    the erase-off variant."""
+    the erase-off variant; state_idx [N] int32 picks each sequence's slot of
+    the state and conv_state pools."""
     _contig(x, "x")
     N = x.shape[0]
     _contig(g, "g", torch.float32)
@@ -251,6 +280,8 @@ def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=No
         _contig(conv_state, "conv_state", x.dtype)
     if conv_bias is not None:
         _contig(conv_bias, "conv_bias", x.dtype)
+    if state_idx is not None:
+        _contig(state_idx, "state_idx", torch.int32)
     if o is None:
         o = torch.empty((N, h_v, d), dtype=x.dtype, device=x.device)
     W = conv_weight.shape[1] if conv_weight is not None else 4
@@ -258,6 +289,7 @@ def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=No
     a = DecodeArgs(ctypes.sizeof(DecodeArgs), flags, _DT[x.dtype],
                    _DT[state.dtype], N, h_qk, h_v, d, d, W,
                    ACT_SILU if activation == "silu" else ACT_NONE, scale, _ptr(x), _ptr(conv_weight),
-                   _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), _ptr(o))
+                   _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                   _ptr(state_idx))
     _check(lib().gdn_decode_step(ctypes.byref(a), _stream(x.device)), "gdn_decode_step")
     return o

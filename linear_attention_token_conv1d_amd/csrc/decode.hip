@@ -69,8 +69,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   static_assert(U % 2 == 0, "a pass is streamed in two halves");
   const int rows = grp * D;
   const int sub = lane & 15;
-  StT* S = reinterpret_cast<StT*>(p.state) + ((int64_t)n * p.h_v + (int64_t)hq * grp) * D * D +
-           sub * EPL;
+  // state and conv-state slot of sequence n
+  const int64_t slot = p.state_idx ? as_const(p.state_idx)[n] : n;
+  StT* S = reinterpret_cast<StT*>(p.state) + (slot * p.h_v + (int64_t)hq * grp) * D * D + sub * EPL;
   int rb = wave * 4 + (lane >> 4);
   float sv[U][EPL];
 #pragma unroll
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // without a conv (or a bias) the loads read x[c] instead and are unused:
       // no branch separates the loads of a batch
       const IoT* wp = wt ? wt + c * W : x + c;
-      const IoT* st = wt ? cst + ((int64_t)n * C + c) * (W - 1) : x + c;
+      const IoT* st = wt ? cst + (slot * C + c) * (W - 1) : x + c;
       const int wm = wt ? W - 1 : 0, hm = wt ? W - 2 : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[j][i] = wp[min(i, wm)];
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           acc += to_f32(wv[j][i]) * xi;
         }
         // shift the new input in: the history keeps the last W-1 inputs
-        IoT* st = cst + ((int64_t)n * C + cc[j]) * (W - 1);
+        IoT* st = cst + (slot * C + cc[j]) * (W - 1);
 #pragma unroll
         for (int i = 0; i < 3; ++i)
           if (i < W - 1) st[i] = i + 1 < W - 1 ? hv[j][min(i + 1, 2)] : xr[j];

@@ -85,8 +85,13 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
     if (!aligned(p, 16)) return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: tensors must be 16-byte aligned");
   if (!aligned(a->g, 4) || !aligned(a->beta, 4) || !aligned(a->cu_seqlens, 4))
     return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: g, beta, cu_seqlens must be 4-byte aligned");
+  if (a->emit_every < 0) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: emit_every %d < 0", a->emit_every);
+  if (a->emit_every > 0 && a->total_tokens > 0 && !a->chunk_states)
+    return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: chunk_states is required when emit_every > 0");
+  if (!aligned(a->chunk_states, 16) || !aligned(a->state_idx, 4))
+    return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: chunk_states must be 16-byte, state_idx 4-byte aligned");
   const size_t need = gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v,
-                                                   a->d_k, a->chunk);
+                                                   a->d_k, a->chunk, a->emit_every);
   if (need && (!a->workspace || a->workspace_bytes < need))
     return fail(GDN_ERR_WORKSPACE, "gdn_prefill: workspace of %zu bytes required", need);
   if (need && !aligned(a->workspace, 256))
@@ -155,7 +160,8 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* a, void* stream) {
 
 size_t gdn_prefill_workspace_size(const gdn_prefill_args* a) {
   if (!a || a->struct_size < sizeof(gdn_prefill_args)) return 0;
-  return gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v, a->d_k, a->chunk);
+  return gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v, a->d_k, a->chunk,
+                                      a->emit_every > 0 ? a->emit_every : 0);
 }
 
 gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
@@ -166,7 +172,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
                          a->g, a->beta, a->initial_state, a->final_state, a->o, a->cu_seqlens,
                          a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
                          (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale, a->workspace,
-                         a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1};
+                         a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->emit_every,
+                         a->chunk_states, a->state_idx};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_prefill(p, a->io_dtype, a->d_k, s), s, "gdn_prefill");
   } catch (...) {
@@ -202,6 +209,8 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: conv_state is required with a conv");
     if (!aligned(a->state, 16))
       return fail(GDN_ERR_ALIGNMENT, "gdn_decode_step: state must be 16-byte aligned");
+    if (!aligned(a->state_idx, 4))
+      return fail(GDN_ERR_ALIGNMENT, "gdn_decode_step: state_idx must be 4-byte aligned");
     const size_t es = esize(a->io_dtype);
     if (!aligned(a->x, es) || !aligned(a->o, es) || !aligned(a->conv_weight, es) ||
         !aligned(a->conv_bias, es) || !aligned(a->conv_state, es) || !aligned(a->g, 4) ||
@@ -211,7 +220,7 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
     gdn::DecodeParams p{a->x, a->conv_weight, a->conv_bias, a->conv_state, a->g, a->beta,
                         a->state, a->o, a->n_seqs, a->h_qk, a->h_v, a->conv_weight ? a->width : 4,
                         a->activation, (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale,
-                        (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1};
+                        (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->state_idx};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_decode(p, a->io_dtype, a->state_dtype, a->d_k, s), s, "gdn_decode_step");
   } catch (...) {

@@ -165,4 +165,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // very negative y, where 1 + e^-y overflows and the reciprocal is 0)
 __device__ __forceinline__ float silu(float y) { return __fdividef(y, 1.0f + __expf(-y)); }
 
+// Index arrays a kernel only reads (chunk offsets, cu_seqlens, state slots)
+// are never written while it runs; reading them through the constant
+// address space lets loads at uniform indices go through the scalar cache.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)p; }
+
 }  // namespace gdn

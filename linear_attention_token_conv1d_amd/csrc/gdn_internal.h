@@ -40,6 +40,7 @@ struct DecodeParams {
   int32_t l2norm;
   float scale;
   int32_t erase;  // 0: erase-off variant, S_t = a_t S_{t-1} + b_t v_t k_t^T
+  const int32_t* state_idx;  // [n_seqs] state and conv-state slots, or null (slot n)
 };
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, int state_dtype, int d,
                          hipStream_t stream);
@@ -67,10 +68,14 @@ struct PrefillParams {
   void* workspace;
   size_t workspace_bytes;
   int32_t erase;  // 0: erase-off variant (A = 0, U = diag(beta) V)
+  int32_t emit_every;        // > 0: the state after every emit_every-th whole chunk
+  float* chunk_states;       // [rows, h_v, d_v, d_k] (rows from the plan)
+  const int32_t* state_idx;  // [n_seqs] state slots, or null (slot n)
 };
 // Workspace of gdn_prefill: chunk offsets plus, per (chunk, V head), the
 // chunk operands Tb, P and four per-token scalar rows.
-size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk);
+size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk,
+                               int emit_every);
 bool prefill_supported(int io_dtype, int d, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream);
 

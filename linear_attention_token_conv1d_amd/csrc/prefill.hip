@@ -178,8 +178,9 @@ struct Rec {
   static constexpr size_t bytes = 2 * mat + 16 * (size_t)C;
 };
 
-// [chunk offsets: n_seqs+1 int32 | scan order: n_seqs int32], padded to 256 B
-__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs * 2 + 1) * 4 + 255) / 256 * 256; }
+// [chunk offsets: n_seqs+1 int32 | scan order: n_seqs int32 | rows of the
+//  emitted chunk-boundary states: n_seqs+1 int32], padded to 256 B
+__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs * 3 + 2) * 4 + 255) / 256 * 256; }
 
 __host__ __device__ inline int64_t max_chunks(int64_t T, int n_seqs, int C) { return T / C + n_seqs; }
 
@@ -201,10 +202,13 @@ struct SplitPlan {
   size_t o_state, o_w, bytes;  // workspace offsets (after the records) and total
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d, int C, size_t base) {
+inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d, int C, int emit_every,
+                            size_t base) {
   SplitPlan s{false, 0, 0, 0, 0, base};
   const int64_t nch = (T + C - 1) / C;
-  if (io_dtype != 1 || n_seqs != 1 || nch < kSplitMinChunks || 3 * h_v * (d / 64) > kScanCUs) return s;
+  // chunk-boundary states are not formed on the second segment: no split then
+  if (io_dtype != 1 || n_seqs != 1 || emit_every > 0 || nch < kSplitMinChunks || 3 * h_v * (d / 64) > kScanCUs)
+    return s;
   s.on = true;
   s.m = (int)(nch / 2);
   s.t_b = (int64_t)s.m * C;
@@ -233,33 +237,42 @@ __device__ __align__(256) unsigned char g_zero_line[256] = {};
 constexpr int kPlanSortMax = 2048;  // longer batches keep their own order
 
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs, int64_t total, int C,
-                                                   int32_t* chunk_off) {
+                                                   int emit_every, int32_t* chunk_off) {
   __shared__ int32_t part[256];
   __shared__ int32_t carry;
   __shared__ int32_t cnt_s[kPlanSortMax];
   const int tid = threadIdx.x;
-  if (tid == 0) { carry = 0; chunk_off[0] = 0; }
-  __syncthreads();
-  for (int base = 0; base < n_seqs; base += 256) {
-    const int i = base + tid;
-    int cnt = 0;
-    if (i < n_seqs) {
-      const int64_t s = cu ? cu[i] : 0, e = cu ? cu[i + 1] : total;
-      cnt = (int)((e - s + C - 1) / C);
-      if (i < kPlanSortMax) cnt_s[i] = cnt;
-    }
-    part[tid] = cnt;
+  // out[0] = 0, out[i + 1] = sum of count(m) over m <= i
+  auto prefix = [&](auto count, int32_t* out) {
+    if (tid == 0) { carry = 0; out[0] = 0; }
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const int v = tid >= o ? part[tid - o] : 0;
+    for (int base = 0; base < n_seqs; base += 256) {
+      const int i = base + tid;
+      part[tid] = i < n_seqs ? count(i) : 0;
       __syncthreads();
-      part[tid] += v;
+      for (int o = 1; o < 256; o <<= 1) {
+        const int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+      }
+      if (i < n_seqs) out[i + 1] = carry + part[tid];
+      __syncthreads();
+      if (tid == 255) carry += part[255];
       __syncthreads();
     }
-    if (i < n_seqs) chunk_off[i + 1] = carry + part[tid];
-    __syncthreads();
-    if (tid == 255) carry += part[255];
-    __syncthreads();
+  };
+  auto len = [&](int i) { return cu ? (int64_t)cu[i + 1] - cu[i] : total; };
+  // chunks per sequence (kept for the scan order)
+  prefix([&](int i) {
+    const int cnt = (int)((len(i) + C - 1) / C);
+    if (i < kPlanSortMax) cnt_s[i] = cnt;
+    return cnt;
+  }, chunk_off);
+  // emitted chunk-boundary states per sequence: boundaries j K C < len
+  if (emit_every > 0) {
+    const int64_t every = (int64_t)emit_every * C;
+    prefix([&](int i) { return (int)(len(i) > 0 ? (len(i) - 1) / every : 0); }, chunk_off + 2 * n_seqs + 1);
   }
   int32_t* order = chunk_off + n_seqs + 1;
   for (int i = tid; i < n_seqs; i += 256) {
@@ -531,12 +544,6 @@ struct PrepLayout {
   static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
   static constexpr int bytes = oVec + (2 + 3 * VPW) * C * 4;
 };
-
-// The chunk offsets and cu_seqlens are never written while prep and scan
-// run; reading them through the constant address space lets loads at
-// uniform indices go through the scalar cache.
-typedef const __attribute__((address_space(4))) int32_t cint32;
-__device__ __forceinline__ cint32* as_const(const int32_t* p) { return (cint32*)p; }
 
 // Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
 __device__ __forceinline__ int owner(cint32* off, int n_seqs, int c) {
@@ -926,7 +933,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   // state S^T (d_k x 16 columns per column tile) in DT accumulator tiles;
   // row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
   f32x4 st[CT][DT];
-  const size_t sbase = ((size_t)n * p.h_v + h) * D * D + (size_t)(blk * L::cols) * D;
+  const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
+  const size_t sbase = ((size_t)sslot * p.h_v + h) * D * D + (size_t)(blk * L::cols) * D;
+  // rows of this sequence's emitted chunk-boundary states
+  const int erow = p.emit_every > 0 ? as_const(reinterpret_cast<const int32_t*>(ws))[2 * p.n_seqs + 1 + n] : 0;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1080,6 +1090,17 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], ak, bs[ct], HALF);
       }
+    }
+    // the state after every emit_every-th whole chunk inside the sequence
+    if (p.emit_every > 0 && (c + 1) % p.emit_every == 0 && t0 + C < seq_end) {
+      float* dst = p.chunk_states + ((size_t)(erow + (c + 1) / p.emit_every - 1) * p.h_v + h) * D * D +
+                   (size_t)(blk * L::cols) * D;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(dst + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4)) =
+              make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
     __syncthreads();  // waits for the next chunk's loads; frees `cur`
   };
@@ -1260,7 +1281,12 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     // state S^T (d_k x 16 columns) of column tile ct in DT accumulator
     // tiles; row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
     f32x4 st[CT][DT];
-    auto srow = [&](int ct) { return (((size_t)n * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D; };
+    // row of this lane's column in the caller's state pools (slot of
+    // sequence n) and in the split's workspace states (one sequence)
+    const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
+    auto srow = [&](int ct) { return (((size_t)sslot * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D; };
+    auto wrow = [&](int ct) { return ((size_t)h * D + (size_t)(blk * L::cols + colof(ct))) * D; };
+    const int erow = p.emit_every > 0 ? as_const(reinterpret_cast<const int32_t*>(ws))[2 * p.n_seqs + 1 + n] : 0;
     // initial state: the caller's (or zero) for a whole sequence or a first
     // segment, zero for a second segment, the identity for the transition
     const float* s_init = role == 0 ? p.initial_state : nullptr;
@@ -1456,6 +1482,17 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
           for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], ak, bs[ct], HALF);
         }
       }
+      // the state after every emit_every-th whole chunk inside the sequence
+      // (a split scan never emits: its second segment does not hold S)
+      if (p.emit_every > 0 && (cbeg + c + 1) % p.emit_every == 0 && chunk_t0(c) + C < seq_end) {
+        float* dst = p.chunk_states + (size_t)(erow + (cbeg + c + 1) / p.emit_every - 1) * p.h_v * D * D;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<float4*>(dst + wrow(ct) + pidx<DT>(dt, 4 * g4)) =
+                make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
+      }
       publish_state();
       __syncthreads();  // B2: next chunk loaded, new state published
     };
@@ -1478,7 +1515,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(s_fin + srow(ct) + pidx<DT>(dt, 4 * g4)) =
+          *reinterpret_cast<float4*>(s_fin + (sp.on ? wrow(ct) : srow(ct)) + pidx<DT>(dt, 4 * g4)) =
               make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
   } else {
@@ -1632,6 +1669,8 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
     constexpr int NC = D / 16;
     const int h = blockIdx.x / (D / 16), j = 16 * (blockIdx.x % (D / 16)) + tid / 16, cb = (tid % 16) * NC;
     const size_t hs = (size_t)h * D * D;
+    // the caller's final state: slot of the one sequence
+    const size_t fs = ((size_t)(p.state_idx ? as_const(p.state_idx)[0] : 0) * p.h_v + h) * D * D;
     const float* smr = sp.s_mid + hs + (size_t)j * D;
     const float* ph = sp.phi + hs + cb;
     float acc[NC];
@@ -1661,7 +1700,7 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
     }
 #pragma unroll
     for (int c = 0; c < NC; c += 4)
-      *reinterpret_cast<float4*>(p.final_state + hs + (size_t)j * D + cb + c) =
+      *reinterpret_cast<float4*>(p.final_state + fs + (size_t)j * D + cb + c) =
           make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
     return;
   }
@@ -1790,7 +1829,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     using SL = ScanLayout<T, D, C, NW, CT>;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs,
-                       p.total_tokens, C, reinterpret_cast<int32_t*>(ws));
+                       p.total_tokens, C, p.emit_every, reinterpret_cast<int32_t*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grp = p.h_v / p.h_qk;
@@ -1805,7 +1844,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     }
     if constexpr (sizeof(T) == 2) {
       const size_t recs_end = off_bytes(p.n_seqs) + (size_t)max_chunks(p.total_tokens, p.n_seqs, C) * p.h_v * Rec<T, C>::bytes;
-      const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, recs_end);
+      const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, p.emit_every, recs_end);
       ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr};
       if (sp.on) {
         // one long sequence: two segments side by side on 64-column workgroups
@@ -1859,11 +1898,12 @@ size_t rec_c(int chunk) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk) {
+size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk,
+                               int emit_every) {
   if (n_seqs < 1 || total_tokens < 0 || h_v < 1 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
   const size_t rec = io_dtype == 1 ? rec_c<__bf16>(chunk) : rec_c<float>(chunk);
   const size_t recs_end = off_bytes(n_seqs) + (size_t)max_chunks(total_tokens, n_seqs, chunk) * h_v * rec;
-  return split_plan(io_dtype, total_tokens, n_seqs, h_v, d, chunk, recs_end).bytes;
+  return split_plan(io_dtype, total_tokens, n_seqs, h_v, d, chunk, emit_every, recs_end).bytes;
 }
 
 bool prefill_supported(int io_dtype, int d, int chunk) {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
     for n in names:
         assert re.search(rf"\bT {n}$", out, flags=re.M), n
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == gdn.ABI_VERSION == 2
 
 
 def test_struct_layout_matches_header():
@@ -83,6 +83,8 @@ def _prefill(**kw):
     (dict(q_stride=100), 1), (dict(q_stride=260), 3), (dict(q=0x1001), 3), (dict(flags=8), 1),
     (dict(struct_size=8), 1), (dict(total_tokens=-1), 1),
     (dict(io_dtype=0, d_k=128, d_v=128, chunk=64), 2),
+    (dict(emit_every=-1), 1), (dict(emit_every=2), 1), (dict(emit_every=2, chunk_states=0x7008), 3),
+    (dict(state_idx=0x7002), 3),
 ])
 def test_prefill_validation(kw, code):
     st, msg = _prefill(**kw)

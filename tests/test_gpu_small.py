@@ -198,6 +198,85 @@ def test_prefill_erase_off(io, d, chunk, T, lens):
     assert e["o"] < tol and e["state"] < tol
 
 
+@pytest.mark.parametrize("io,d,chunk,K,lens", [
+    ("bf16", 128, 64, 1, [200, 0, 300, 64, 65]),  # every chunk; empty and exact-chunk sequences
+    ("f32", 64, 16, 3, [250]),                     # fp32 scan, every third chunk
+    ("bf16", 128, 64, 2, [2500]),                  # one long sequence: the split is off when emitting
+])
+def test_prefill_chunk_state_emission(io, d, chunk, K, lens):
+    """emit_every = K: the state after every K-th whole chunk that ends inside
+    its sequence equals the oracle's final state over that prefix."""
+    hq, hv = 2, 4
+    T = sum(lens)
+    q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, io, 120, lens)
+    cu = gdn_inputs.cu_from_lengths(lens)
+    o, S, E = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0), cu_seqlens=dev(cu), chunk=chunk,
+                          emit_every=K)
+    rows = gdn.chunk_state_rows(lens, chunk, K)
+    assert rows == sum((L - 1) // (K * chunk) for L in lens if L > 0)
+    ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0), cu_seqlens=cu.numpy())
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    assert rel_err(o, ro) < tol and rel_err(S, rS) < tol
+    r, worst = 0, 0.0
+    for n, L in enumerate(lens):
+        s0 = int(cu[n])
+        for j in range(1, (L - 1) // (K * chunk) + 1 if L > 0 else 1):
+            e = s0 + j * K * chunk
+            _, rSj = orc.gated_delta_rule(np64(q[s0:e]), np64(k[s0:e]), np64(v[s0:e]), np64(g[s0:e]),
+                                          np64(b[s0:e]), np64(S0[n:n + 1]))
+            worst = max(worst, rel_err(E[r:r + 1], rSj))
+            r += 1
+    assert r == rows
+    report(f"chunk_states[{io},d={d},C={chunk},K={K}]", states=worst)
+    assert worst < tol
+
+
+@pytest.mark.parametrize("lens,slots,pool", [([70, 130, 5], [2, 0, 3], 4), ([2500], [3], 4)])
+def test_prefill_state_slots(lens, slots, pool):
+    """state_idx: sequence n starts from initial pool slot state_idx[n] and
+    writes final pool slot state_idx[n]; other slots are left alone.  The
+    single long sequence takes the split scan."""
+    hq, hv, d = 2, 4, 128
+    T = sum(lens)
+    q, k, v, g, b, _ = _prefill_case(T, hq, hv, d, "bf16", 130, lens)
+    P0 = _rand((pool, hv, d, d), torch.float32, 0.1, seed=131)
+    cu = gdn_inputs.cu_from_lengths(lens)
+    idx = torch.tensor(slots, dtype=torch.int32)
+    fin = torch.full((pool, hv, d, d), 7.0, device="cuda")
+    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(P0), cu_seqlens=dev(cu), chunk=64,
+                       final_state=fin, state_idx=dev(idx))
+    ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(P0[idx.long()]),
+                                  cu_seqlens=cu.numpy())
+    e = dict(o=rel_err(o, ro), state=rel_err(fin[idx.long()], rS))
+    report(f"state_slots[{lens}]", **e)
+    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16
+    untouched = [i for i in range(pool) if i not in slots]
+    assert bool((fin[untouched] == 7.0).all())
+
+
+def test_decode_step_state_slots():
+    """state_idx: the state and conv-state pools are addressed by slot; x, g,
+    beta and o by sequence; slots no sequence names are left alone."""
+    N, hq, hv, d, pool = 3, 2, 6, 128, 5
+    C = 2 * hq * d + hv * d
+    slots = [4, 1, 2]
+    x = _rand((N, C), torch.bfloat16, seed=140)
+    w = _rand((C, 4), torch.bfloat16, 0.5, seed=141)
+    cs = _rand((pool, C, 3), torch.bfloat16, seed=142)
+    S = _rand((pool, hv, d, d), torch.bfloat16, 0.1, seed=143)
+    g, b = _gates(N, hv, 144)
+    idx = torch.tensor(slots, dtype=torch.long)
+    S_d, cs_d = dev(S.clone()), dev(cs.clone())
+    o = gdn.decode_step(dev(x), dev(g), dev(b), S_d, hq, hv, d, conv_weight=dev(w), conv_state=cs_d,
+                        state_idx=dev(idx.int()))
+    ro, rS, rcs = orc.decode_step(np64(x), np64(w), np64(g), np64(b), np64(S[idx]), np64(cs[idx]), hq, d, hv, d)
+    e = dict(o=rel_err(o, ro), state=rel_err(S_d[idx.cuda()], rS), conv_state=rel_err(cs_d[idx.cuda()], rcs))
+    report("decode_state_slots", **e)
+    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+    for i in (0, 3):
+        assert torch.equal(S_d[i].cpu(), S[i]) and torch.equal(cs_d[i].cpu(), cs[i])
+
+
 def test_prefill_tiny_fp32_config():
     """The tiny fp32 layer: T=256, 4 heads, d=64, chunk 16, zero initial state."""
     inp = gdn_inputs.prefill_inputs("tiny_fp32")
