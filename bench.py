@@ -201,7 +201,9 @@ def run_decode(steps, warmup, do_cpu):
     N, hq, hv, d = cfg["n_seqs"], cfg["h_qk"], cfg["h_v"], cfg["d_k"]
     o = torch.empty((N, hv, d), dtype=torch.bfloat16, device=dev)
     nsteps = xs.shape[0]
-    for i in range(warmup):
+    # untimed: at least one full pass of the 64 steps (the clocks settle over
+    # the first few dozen launches)
+    for i in range(max(warmup, nsteps)):
         gdn.decode_step(xs[i % nsteps], gs[i % nsteps], bs[i % nsteps], S, hq, hv, d, conv_weight=w,
                         conv_state=cs, o=o)
     torch.cuda.synchronize()

@@ -197,6 +197,7 @@ constexpr int kSplitMinChunks = 32;  // shorter sequences keep one pass
 constexpr int kScanCUs = 256;
 struct SplitPlan {
   bool on;
+  int cols;          // columns per scan workgroup (32 or 64)
   int m;             // chunks in the first segment
   int64_t t_b;       // first token of the second segment
   size_t o_state, o_w, bytes;  // workspace offsets (after the records) and total
@@ -204,13 +205,30 @@ struct SplitPlan {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d, int C, int emit_every,
                             size_t base) {
-  SplitPlan s{false, 0, 0, 0, 0, base};
+  SplitPlan s{false, 0, 0, 0, 0, 0, base};
   const int64_t nch = (T + C - 1) / C;
   // chunk-boundary states are not formed on the second segment: no split then
-  if (io_dtype != 1 || n_seqs != 1 || emit_every > 0 || nch < kSplitMinChunks || 3 * h_v * (d / 64) > kScanCUs)
+  if (io_dtype != 1 || n_seqs != 1 || emit_every > 0 || nch < kSplitMinChunks) return s;
+  // Workgroups of one role (first segment, second from zero, transition):
+  // gn with 32 columns, gw with 64.  The first segment's go first in the
+  // grid.  If all three roles fit on the CUs, the halves are even.  If only
+  // the first segment and part of the second fit, the rest of the second
+  // segment starts as its first workgroups finish: the second segment then
+  // runs in two waves and gets a third of the chunks.
+  const int gn = h_v * (d / 32), gw = h_v * (d / 64);
+  if (3 * gn <= kScanCUs) {
+    s.cols = 32;
+    s.m = (int)(nch / 2);
+  } else if (2 * gn <= kScanCUs) {
+    s.cols = 32;
+    s.m = (int)((2 * nch + 1) / 3);
+  } else if (3 * gw <= kScanCUs) {
+    s.cols = 64;
+    s.m = (int)(nch / 2);
+  } else {
     return s;
+  }
   s.on = true;
-  s.m = (int)(nch / 2);
   s.t_b = (int64_t)s.m * C;
   s.o_state = align256(base);
   s.o_w = s.o_state + 3 * (size_t)h_v * d * d * 4;
@@ -311,21 +329,25 @@ __device__ __forceinline__ ScanSlot scan_slot(const PrefillParams& p, const int3
   }
   return r;
 }
-// Split scan of one sequence: 3 NB workgroups per V head (roles x column
-// blocks), the heads dealt over the XCDs in runs so that the second-segment
-// and transition workgroups of a head, which read the same chunks, share L2.
+// Split scan of one sequence: the h_v NB first-segment workgroups come first
+// in the grid (they must all start at once), then per V head the NB
+// second-segment and NB transition workgroups, which read the same chunks.
+// With h_v a multiple of 8 the heads go to the XCDs in runs (blockIdx mod 8
+// is the XCD), so the workgroups of a head share one L2.
 __device__ __forceinline__ ScanSlot split_slot(const PrefillParams& p, int NB) {
-  const int per = 3 * NB;
+  const int G = p.h_v * NB, b = blockIdx.x;
+  const bool first = b < G;
+  const int per = first ? NB : 2 * NB, bb = first ? b : b - G;
   int h, j;
   if (p.h_v % 8 == 0) {
-    const int x = blockIdx.x % 8, k = blockIdx.x / 8, hx = p.h_v / 8;
-    h = x * hx + k / per;
+    const int x = bb % 8, k = bb / 8;
+    h = x * (p.h_v / 8) + k / per;
     j = k % per;
   } else {
-    h = blockIdx.x / per;
-    j = blockIdx.x % per;
+    h = bb / per;
+    j = bb % per;
   }
-  return ScanSlot{0, h, j % NB, j / NB, h < p.h_v};
+  return ScanSlot{0, h, j % NB, first ? 0 : 1 + j / NB, h < p.h_v};
 }
 inline unsigned scan_grid(int n_seqs, int h_qk, int h_v, int NB) {
   const int ngroups = n_seqs * h_qk;
@@ -1847,12 +1869,17 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, p.emit_every, recs_end);
       ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr};
       if (sp.on) {
-        // one long sequence: two segments side by side on 64-column workgroups
+        // one long sequence: two segments side by side
         float* st = reinterpret_cast<float*>(ws + sp.o_state);
         const size_t hs = (size_t)p.h_v * D * D;
         ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w)};
-        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3((unsigned)(3 * p.h_v * (D / 64))),
-                           dim3(128 * (4 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        const unsigned grid = (unsigned)(3 * p.h_v * (D / sp.cols));
+        if (sp.cols == 32)
+          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>), dim3(grid),
+                             dim3(128 * (2 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        else
+          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3(grid),
+                             dim3(128 * (4 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int ntile = (int)((p.total_tokens - sp.t_b + kJoinTok - 1) / kJoinTok);
         const int nstate = p.final_state ? p.h_v * (D / 16) : 0;

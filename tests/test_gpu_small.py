@@ -153,6 +153,8 @@ def test_prefill_ragged(io, d, chunk):
     (2113, 2, 2, 64, 64, True, True),    # d = 64: one 64-column block per head
     (1100, 2, 2, 128, 32, True, True),   # chunk 32
     (600, 1, 3, 128, 16, True, False),   # chunk 16, no final state asked for
+    (2100, 8, 24, 128, 64, True, True),  # 32-column split with the second segment in two waves
+    (2048, 8, 40, 128, 64, True, True),  # 64-column split
 ])
 def test_prefill_one_long_sequence_split(T, hq, hv, d, chunk, s0, fin):
     """One sequence of 32+ chunks whose heads leave most CUs idle: the scan runs
