@@ -1201,8 +1201,9 @@ __device__ __forceinline__ void barrier_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int C, int CT, int NWR>
-__global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const unsigned char* ws, ScanSplit sp) {
+template <int D, int C, int CT, int NWR, int OS>
+__global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParams p, const unsigned char* ws,
+                                                                   ScanSplit sp) {
   using L = Scan2Layout<D, C, 16 * CT * NWR>;
   using T = __bf16;
   using M = Mma<T>;
@@ -1216,8 +1217,11 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
   constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
   constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
   constexpr int NB = D / L::cols;
-  // NWR waves per role
+  // NWR chain waves; OS output waves per chain wave's column slice, each
+  // forming NT / OS of the chunk's 16-token tiles
   constexpr int SW = 16 * CT;       // columns per wave
+  constexpr int NO = NWR * OS, NTO = NT / OS;
+  static_assert(NT % OS == 0, "token tiles split evenly over the output waves of a slice");
   __shared__ __align__(16) unsigned char sb0[L::buf];
   __shared__ __align__(16) unsigned char sb1[L::buf];
   __shared__ __align__(16) unsigned char sS[L::sbytes];
@@ -1231,7 +1235,9 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   const bool chain = wave < NWR;
-  const int cw = wave % NWR;  // column slice of this wave: columns SW cw .. SW cw + SW - 1
+  const int ow = chain ? 0 : wave - NWR;  // index among the output waves
+  const int cw = chain ? wave : ow % NWR;  // column slice: columns SW cw .. SW cw + SW - 1
+  const int th = chain ? 0 : ow / NWR;     // output waves: token tiles [th NTO, (th + 1) NTO)
   auto colof = [&](int ct) { return SW * cw + 16 * ct + l16; };  // this lane's column in tile ct
 
   const int32_t* off = reinterpret_cast<const int32_t*>(ws);
@@ -1263,16 +1269,16 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
   // once (DmaPlan); a partial chunk (the last of a sequence) takes the
   // clamped path, where rows past its end re-read its last row: they only
   // meet zero columns of Tb and zero rows of U.
-  DmaPlan<SK, C, NWR> pk, pq;
-  DmaPlan<SC, C, NWR> ptb;
-  DmaPlan<SV, C, NWR> pv;
+  DmaPlan<SK, C, NO> pk, pq;
+  DmaPlan<SC, C, NO> ptb;
+  DmaPlan<SV, C, NO> pv;
   const bool fast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) &&
                     p.v_stride * 2 * C < (1ll << 31);
   if (fast && !chain) {
-    pk.init((uint32_t)(p.k_stride * 2), cw, lane);
-    pq.init((uint32_t)(p.q_stride * 2), cw, lane);
-    ptb.init((uint32_t)L::RBC, cw, lane);
-    pv.init((uint32_t)vrow, cw, lane);
+    pk.init((uint32_t)(p.k_stride * 2), ow, lane);
+    pq.init((uint32_t)(p.q_stride * 2), ow, lane);
+    ptb.init((uint32_t)L::RBC, ow, lane);
+    pv.init((uint32_t)vrow, ow, lane);
   }
   auto chunk_ptrs = [&](int c, const unsigned char*& kc, const unsigned char*& qc, const unsigned char*& vc,
                         const unsigned char*& rec) {
@@ -1296,7 +1302,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, w, lane);
   };
 
-  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, 2 * NWR>{}, wave);
+  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, NWR + NO>{}, wave);
 
   if (chain) {
     // ---------------------------------------------------------- chain waves
@@ -1547,18 +1553,18 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
     T* og = (role == 2 ? sp.w : reinterpret_cast<T*>(p.o)) + (int64_t)h * D + blk * L::cols + SW * cw + 4 * g4;
     const int64_t otok = role == 2 ? seg_start : 0;
     // O^T tile (ct, nt): rows 4g+i = columns SW cw + 16 ct + 4g + i, column
-    // l16 = token pidx(nt, l16) of the chunk
-    f32x4 o[CT][NT];
-    int64_t orow[NT];  // element offset of this lane's token row in each tile
+    // l16 = token pidx(th NTO + nt, l16) of the chunk
+    f32x4 o[CT][NTO];
+    int64_t orow[NTO];  // element offset of this lane's token row in each tile
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) orow[nt] = (int64_t)pidx<NT>(nt, l16) * o_stride;
+    for (int nt = 0; nt < NTO; ++nt) orow[nt] = (int64_t)pidx<NT>(th * NTO + nt, l16) * o_stride;
     auto store_o = [&](int64_t t0, int Lc) {
       T* oc = og + (t0 - otok) * o_stride;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (pidx<NT>(nt, l16) < Lc)
+        for (int nt = 0; nt < NTO; ++nt) {
+          if (pidx<NT>(th * NTO + nt, l16) < Lc)
             *reinterpret_cast<uint2*>(oc + orow[nt] + 16 * ct) =
                 make_uint2(pack_bf16x2(o[ct][nt][0], o[ct][nt][1]), pack_bf16x2(o[ct][nt][2], o[ct][nt][3]));
         }
@@ -1570,7 +1576,7 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
       // the next chunk: full ones in pieces, a partial one at once
       const bool more = c + 1 < nch;
       const bool pieces = more && fast && chunk_len(c + 1) == C;
-      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, NWR>{}, cw);
+      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, NO>{}, ow);
       const unsigned char *kc, *qc, *vc, *rec;
       chunk_ptrs(more ? c + 1 : c, kc, qc, vc, rec);
       const unsigned char* Q_t = cur + L::oQ;
@@ -1581,50 +1587,51 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NTO; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         if (pieces) {
 #pragma unroll
           for (int k = s * decltype(pk)::NI / (D / 32); k < (s + 1) * decltype(pk)::NI / (D / 32); ++k) {
-            pk.issue_one(k, nxt + L::oK, kc, cw, lane);
-            pq.issue_one(k, nxt + L::oQ, qc, cw, lane);
+            pk.issue_one(k, nxt + L::oK, kc, ow, lane);
+            pq.issue_one(k, nxt + L::oQ, qc, ow, lane);
           }
         }
-        frag as[CT], bq[NT];
+        frag as[CT], bq[NTO];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) as[ct] = frag_row_s<T, SS>(sS, colof(ct), 32 * s + 8 * g4, false);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bq[nt] = frag_row_s<T, SK>(Q_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
+        for (int nt = 0; nt < NTO; ++nt)
+          bq[nt] = frag_row_s<T, SK>(Q_t, pidx<NT>(th * NTO + nt, l16), 32 * s + 8 * g4, false);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTO; ++nt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], as[ct], bq[nt], false);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float sc = vec[C + pidx<NT>(nt, l16)];
+      for (int nt = 0; nt < NTO; ++nt) {
+        const float sc = vec[C + pidx<NT>(th * NTO + nt, l16)];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= sc;
       }
       barrier_vm<63>();  // B1
       if (pieces) {
-        ptb.issue(nxt + L::oTb, rec, cw, lane);
-        ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, cw, lane);
-        pv.issue(nxt + L::oV, vc, cw, lane);
-        dma_linear<16 * C, NWR>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, cw, lane);
+        ptb.issue(nxt + L::oTb, rec, ow, lane);
+        ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, ow, lane);
+        pv.issue(nxt + L::oV, vc, ow, lane);
+        dma_linear<16 * C, NO>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, ow, lane);
       }
       // O^T += U^T P^T
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        frag au[CT], bp[NT];
+        frag au[CT], bp[NTO];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) au[ct] = frag_row_s<T, SU>(sU, colof(ct), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(nt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
+        for (int nt = 0; nt < NTO; ++nt)
+          bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(th * NTO + nt, l16), HALF ? 4 * g4 : 32 * s + 8 * g4, HALF);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTO; ++nt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], au[ct], bp[nt], HALF);
       }
@@ -1645,14 +1652,21 @@ __global__ __launch_bounds__(128 * NWR) void scan2_kernel(PrefillParams p, const
 #define GDN_SCAN2_CT 1
 #endif
 constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave
+// output waves per column slice (each forms half of the chunk's tokens);
+// one when the chunk has a single 16-token tile
+#ifndef GDN_SCAN2_OS
+#define GDN_SCAN2_OS 2
+#endif
+template <int C>
+constexpr int kOutSplit = C >= 32 ? GDN_SCAN2_OS : 1;
 // Two workgroup widths: 64 columns (four waves per role, two waves per SIMD)
 // for launches that fill the chip, 32 columns (two waves per role) to spread
 // a few long chains over twice as many CUs.
 #define GDN_SCAN2(D, C) \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>(PrefillParams, const unsigned char*, \
-                                                                           ScanSplit); \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>(PrefillParams, const unsigned char*, \
-                                                                           ScanSplit);
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>(PrefillParams, \
+                                                                                          const unsigned char*, ScanSplit); \
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>(PrefillParams, \
+                                                                                          const unsigned char*, ScanSplit);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
 
@@ -1875,11 +1889,11 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
         ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w)};
         const unsigned grid = (unsigned)(3 * p.h_v * (D / sp.cols));
         if (sp.cols == 32)
-          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>), dim3(grid),
-                             dim3(128 * (2 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>), dim3(grid),
+                             dim3(64 * (2 / kScan2Tiles) * (1 + kOutSplit<C>)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
         else
-          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3(grid),
-                             dim3(128 * (4 / kScan2Tiles)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>), dim3(grid),
+                             dim3(64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int ntile = (int)((p.total_tokens - sp.t_b + kJoinTok - 1) / kJoinTok);
         const int nstate = p.final_state ? p.h_v * (D / 16) : 0;
@@ -1888,11 +1902,11 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       } else if ((int64_t)p.n_seqs * p.h_v * (D / 32) <= kScanCUs) {
         // narrow workgroups when even they leave CUs idle
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 32);
-        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles>), dim3(grid), dim3(128 * (2 / kScan2Tiles)),
+        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>), dim3(grid), dim3(64 * (2 / kScan2Tiles) * (1 + kOutSplit<C>)),
                            0, stream, p, static_cast<const unsigned char*>(ws), ss);
       } else {
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 64);
-        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles>), dim3(grid), dim3(128 * (4 / kScan2Tiles)),
+        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>), dim3(grid), dim3(64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>)),
                            0, stream, p, static_cast<const unsigned char*>(ws), ss);
       }
     } else {
