@@ -1149,17 +1149,18 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 }
 
 // ------------------------------------------------------- split-role scan
-// bf16 scan with two wave roles per workgroup (8 waves, two per SIMD), for a
-// block of 64 d_v columns of one (sequence, V head):
-//  chain waves 0-3 own 16 columns each of the fp32 state S^T in accumulator
-//    tiles and run the serial part of a chunk:  X1 = K S^T,
+// bf16 scan with two wave roles per workgroup, for a block of 32 or 64 d_v
+// columns of one (sequence, V head):
+//  chain waves (one per 16 columns) own their columns of the fp32 state S^T
+//    in accumulator tiles and run the serial part of a chunk:  X1 = K S^T,
 //    R = V - diag(gamma rk) X1,  U = Tb R,  S^T <- gamma_last S^T + K^T diag(e rk) U;
-//  output waves 4-7 (same 16 columns each) compute the chunk's output
-//    O^T = (S Q^T) diag(scale gamma rq) + U^T P^T  from the state and U that
-//    the chain waves publish in LDS as bf16, and store O straight from their
-//    accumulators (a lane holds 4 consecutive columns of one token).
-// The two roles share each SIMD, so one role's MFMA and LDS work fills the
-// other's dependency stalls.  All eight waves issue the next chunk's
+//  output waves (two per 16 columns, each on half of the chunk's tokens)
+//    compute the chunk's output O^T = (S Q^T) diag(scale gamma rq) + U^T P^T
+//    from the state and U that the chain waves publish in LDS as bf16, and
+//    store O straight from their accumulators (a lane holds 4 consecutive
+//    columns of one token).
+// The roles share the SIMDs, so one role's MFMA and LDS work fills the
+// other's dependency stalls.  The output waves issue all of the next chunk's
 // direct-to-LDS loads at the start of a chunk.  Per chunk: barrier B1 after U
 // is published (LDS only: the loads stay in flight), and B2 at the end (the
 // next chunk has landed, the new state is published).
@@ -1201,9 +1202,9 @@ __device__ __forceinline__ void barrier_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int C, int CT, int NWR, int OS>
-__global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParams p, const unsigned char* ws,
-                                                                   ScanSplit sp) {
+template <int D, int C, int CT, int NWR, int OS, int NM>
+__global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(PrefillParams p, const unsigned char* ws,
+                                                                          ScanSplit sp) {
   using L = Scan2Layout<D, C, 16 * CT * NWR>;
   using T = __bf16;
   using M = Mma<T>;
@@ -1222,6 +1223,9 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
   constexpr int SW = 16 * CT;       // columns per wave
   constexpr int NO = NWR * OS, NTO = NT / OS;
   static_assert(NT % OS == 0, "token tiles split evenly over the output waves of a slice");
+  // NM mover waves (if any) issue the next chunk's loads; without them the
+  // output waves do
+  constexpr int NX = NM > 0 ? NM : NO;
   __shared__ __align__(16) unsigned char sb0[L::buf];
   __shared__ __align__(16) unsigned char sb1[L::buf];
   __shared__ __align__(16) unsigned char sS[L::sbytes];
@@ -1234,10 +1238,20 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
   const int hq = h / (p.h_v / p.h_qk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const bool chain = wave < NWR;
-  const int ow = chain ? 0 : wave - NWR;  // index among the output waves
-  const int cw = chain ? wave : ow % NWR;  // column slice: columns SW cw .. SW cw + SW - 1
-  const int th = chain ? 0 : ow / NWR;     // output waves: token tiles [th NTO, (th + 1) NTO)
+  // Waves w and w + 4 of a workgroup share a SIMD.  With movers (eight
+  // waves) the chain waves 0 .. NWR-1 share their SIMDs only with the movers
+  // 4 .. 4+NWR-1, which issue loads and little else; the output waves take
+  // the other two slots of the remaining SIMDs.  Without movers the output
+  // waves follow the chain waves.
+  static_assert(NM == 0 || (NM == NWR && NWR + NO / 2 == 4), "mover layout: eight waves, two per SIMD");
+  const int slot4 = wave & 3, hi4 = wave >> 2;
+  const bool chain = NM > 0 ? (slot4 < NWR && hi4 == 0) : wave < NWR;
+  const bool mover = NM > 0 && slot4 < NWR && hi4 == 1;
+  const int ow = chain || mover ? 0 : NM > 0 ? slot4 - NWR + (4 - NWR) * hi4 : wave - NWR;  // index among the output waves
+  const int cw = chain ? slot4 : ow % NWR;           // column slice: columns SW cw .. SW cw + SW - 1
+  const int th = chain ? 0 : ow / NWR;               // output waves: token tiles [th NTO, (th + 1) NTO)
+  const bool moves = NM > 0 ? mover : !chain;        // issues the loads of chunks 1, 2, ...
+  const int xw = NM > 0 ? (mover ? slot4 : 0) : ow;  // index among the moving waves
   auto colof = [&](int ct) { return SW * cw + 16 * ct + l16; };  // this lane's column in tile ct
 
   const int32_t* off = reinterpret_cast<const int32_t*>(ws);
@@ -1263,22 +1277,23 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
   auto chunk_rec = [&](int c) { return recs + ((size_t)(c0 + c) * p.h_v + h) * Rec<T, C>::bytes; };
 
   // ---- data movement.  Chunk 0 is loaded by all waves before the roles
-  // split; after that only the output waves move data, in pieces between
-  // their own products, so that no wave ever waits long to issue and the
-  // chain waves issue nothing.  A full chunk uses per-lane offsets computed
+  // split; after that the mover waves (else the output waves) issue the next
+  // chunk at the start of a chunk, so the loads have the whole chunk to land.
+  // A wave that issues them stalls until the CU's load path has room, so with
+  // movers neither the chain nor the output waves issue any load.  A full chunk uses per-lane offsets computed
   // once (DmaPlan); a partial chunk (the last of a sequence) takes the
   // clamped path, where rows past its end re-read its last row: they only
   // meet zero columns of Tb and zero rows of U.
-  DmaPlan<SK, C, NO> pk, pq;
-  DmaPlan<SC, C, NO> ptb;
-  DmaPlan<SV, C, NO> pv;
+  DmaPlan<SK, C, NX> pk, pq;
+  DmaPlan<SC, C, NX> ptb;
+  DmaPlan<SV, C, NX> pv;
   const bool fast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) &&
                     p.v_stride * 2 * C < (1ll << 31);
-  if (fast && !chain) {
-    pk.init((uint32_t)(p.k_stride * 2), ow, lane);
-    pq.init((uint32_t)(p.q_stride * 2), ow, lane);
-    ptb.init((uint32_t)L::RBC, ow, lane);
-    pv.init((uint32_t)vrow, ow, lane);
+  if (fast && moves) {
+    pk.init((uint32_t)(p.k_stride * 2), xw, lane);
+    pq.init((uint32_t)(p.q_stride * 2), xw, lane);
+    ptb.init((uint32_t)L::RBC, xw, lane);
+    pv.init((uint32_t)vrow, xw, lane);
   }
   auto chunk_ptrs = [&](int c, const unsigned char*& kc, const unsigned char*& qc, const unsigned char*& vc,
                         const unsigned char*& rec) {
@@ -1302,7 +1317,80 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
     dma_linear<16 * C, NW>(b + L::oVec, rec + 2 * Rec<T, C>::mat, w, lane);
   };
 
-  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, NWR + NO>{}, wave);
+  // the next chunk, c + 1, into nxt, by the moving waves
+  auto issue_next = [&](int c, unsigned char* nxt) {
+    if (c + 1 >= nch) return;
+    if (fast && chunk_len(c + 1) == C) {
+      const unsigned char *kc, *qc, *vc, *rec;
+      chunk_ptrs(c + 1, kc, qc, vc, rec);
+      pk.issue(nxt + L::oK, kc, xw, lane);
+      pq.issue(nxt + L::oQ, qc, xw, lane);
+      ptb.issue(nxt + L::oTb, rec, xw, lane);
+      ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, xw, lane);
+      pv.issue(nxt + L::oV, vc, xw, lane);
+      dma_linear<16 * C, NX>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, xw, lane);
+    } else {
+      issue_slow(c + 1, nxt, std::integral_constant<int, NX>{}, xw);
+    }
+  };
+  if (nch > 0) issue_slow(0, sb0, std::integral_constant<int, NWR + NO + NM>{}, wave);
+
+  // L2 prefetch PFD chunks ahead, by the chain waves or the movers: one
+  // 4-byte load per 128-byte line of the chunk's K, Q and V rows and of its
+  // record, consumed a chunk later, so nothing waits for it.  The K, Q and
+  // record lines, which the NB column blocks of a head share, are split
+  // between the blocks.  Only the 32-column workgroups prefetch: they run
+  // when the launch leaves CUs idle and the scan waits on HBM latency; with
+  // every CU busy the extra requests cost more than they save.
+  constexpr int PFD = L::cols == 32 ? 3 : 0;
+  constexpr int TW = NM > 0 ? NM : NWR;  // touching waves
+  constexpr int LPR = (D * 2 + 127) / 128;  // lines per K or Q row
+  constexpr int NKL = C * LPR;
+  constexpr int NSH = 2 * NKL + (int)(Rec<T, C>::bytes / 128);
+  constexpr int NTOUCH = PFD > 0 ? ((NSH + NB - 1) / NB + C + 64 * TW - 1) / (64 * TW) : 0;
+  const bool touches = PFD > 0 && (NM > 0 ? mover : chain);
+  const int tw = NM > 0 ? xw : cw;
+  // touch i of chunk c reads tbase[i] + c * tstep[i]
+  const unsigned char* tbase[NTOUCH > 0 ? NTOUCH : 1];
+  uint32_t tstep[NTOUCH > 0 ? NTOUCH : 1];
+  uint32_t tv[NTOUCH > 0 ? NTOUCH : 1];
+  const unsigned char* rec0 = chunk_rec(0);  // always a whole record
+  if (touches) {
+    const int nsw = (NSH - blk + NB - 1) / NB;  // shared lines of this block
+    const int64_t ks = p.k_stride * 2, qs = p.q_stride * 2, vs = vrow;
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i) {
+      const int sl = (i * TW + tw) * 64 + lane;
+      tv[i] = 0u;
+      tbase[i] = rec0;
+      tstep[i] = (uint32_t)(p.h_v * Rec<T, C>::bytes);
+      if (sl < nsw) {
+        const int l = blk + NB * sl;
+        if (l < 2 * NKL) {
+          const bool isq = l >= NKL;
+          const int lk = isq ? l - NKL : l;
+          const int64_t st = isq ? qs : ks;
+          tbase[i] = (isq ? qg : kg) + seg_start * st + (lk / LPR) * st + (lk % LPR) * 128;
+          tstep[i] = (uint32_t)(C * st);
+        } else {
+          tbase[i] = rec0 + (l - 2 * NKL) * 128;
+        }
+      } else if (sl < nsw + C) {
+        tbase[i] = vg + seg_start * vs + (sl - nsw) * vs;
+        tstep[i] = (uint32_t)(C * vs);
+      }
+    }
+  }
+  // the previous touches have landed; chunk c + PFD is touched (without a
+  // full chunk c + PFD, every touch re-reads the sequence's first record)
+  auto touch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
+    const bool ok = fast && c + PFD < nch && chunk_len(c + PFD) == C;
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i)
+      tv[i] = *reinterpret_cast<const uint32_t*>(ok ? tbase[i] + (uint64_t)(c + PFD) * tstep[i] : rec0);
+  };
 
   if (chain) {
     // ---------------------------------------------------------- chain waves
@@ -1343,50 +1431,6 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
           *reinterpret_cast<frag*>(sS + SS::off(colof(ct), (32 * u + 8 * g4) * 2)) =
               M::acc(st[ct][2 * u], st[ct][2 * u + 1]);
     };
-    // L2 prefetch PFD chunks ahead, by the chain waves (the output waves
-    // move the next chunk into LDS): one 4-byte load per 128-byte line of
-    // the chunk's K, Q and V rows and of its record, issued while the chain
-    // waits at B1 and consumed a chunk later, so nothing waits for it.  The
-    // K, Q and record lines, which the NB column blocks of a head share, are
-    // split between the blocks.  Only the 32-column workgroups prefetch:
-    // they run when the launch leaves CUs idle and the scan waits on HBM
-    // latency; with every CU busy the extra requests cost more than they save.
-    constexpr int PFD = L::cols == 32 ? 3 : 0;
-    constexpr int LPR = (D * 2 + 127) / 128;  // lines per K or Q row
-    constexpr int NKL = C * LPR;
-    constexpr int NSH = 2 * NKL + (int)(Rec<T, C>::bytes / 128);
-    constexpr int NTOUCH = ((NSH + NB - 1) / NB + C + 64 * NWR - 1) / (64 * NWR);
-    // touch i of chunk c reads tbase[i] + c * tstep[i]
-    const unsigned char* tbase[NTOUCH];
-    uint32_t tstep[NTOUCH];
-    uint32_t tv[NTOUCH];
-    const unsigned char* rec0 = chunk_rec(0);  // always a whole record
-    {
-      const int nsw = (NSH - blk + NB - 1) / NB;  // shared lines of this block
-      const int64_t ks = p.k_stride * 2, qs = p.q_stride * 2, vs = vrow;
-#pragma unroll
-      for (int i = 0; i < NTOUCH; ++i) {
-        const int sl = (i * NWR + cw) * 64 + lane;
-        tv[i] = 0u;
-        tbase[i] = rec0;
-        tstep[i] = (uint32_t)(p.h_v * Rec<T, C>::bytes);
-        if (sl < nsw) {
-          const int l = blk + NB * sl;
-          if (l < 2 * NKL) {
-            const bool isq = l >= NKL;
-            const int lk = isq ? l - NKL : l;
-            const int64_t st = isq ? qs : ks;
-            tbase[i] = (isq ? qg : kg) + seg_start * st + (lk / LPR) * st + (lk % LPR) * 128;
-            tstep[i] = (uint32_t)(C * st);
-          } else {
-            tbase[i] = rec0 + (l - 2 * NKL) * 128;
-          }
-        } else if (sl < nsw + C) {
-          tbase[i] = vg + seg_start * vs + (sl - nsw) * vs;
-          tstep[i] = (uint32_t)(C * vs);
-        }
-      }
-    }
     publish_state();
     __syncthreads();  // initial state published; chunk 0 has landed
 
@@ -1431,6 +1475,13 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) M::mma(x1[ct][mt], ak[mt], bs[ct], false);
       }
+      // K^T fragments of the state update, read while X1 drains
+      frag kt[KS][DT];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          kt[s][dt] = frag_kt<T, L::RBK, DT>(K_t, dt, HALF ? 4 * g4 : 32 * s + 8 * g4, l16, HALF);
       // R = V - diag(gamma rk) X1
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
@@ -1482,18 +1533,9 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
         }
       }
       const float gl = vec[3 * C];
-      // the previous touches have landed; chunk c + PFD is touched (without
-      // a full chunk c + PFD, every touch re-reads the sequence's first record)
-      if constexpr (PFD > 0) {
-#pragma unroll
-        for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
-        const bool ok = fast && c + PFD < nch && chunk_len(c + PFD) == C;
-#pragma unroll
-        for (int i = 0; i < NTOUCH; ++i)
-          tv[i] = *reinterpret_cast<const uint32_t*>(ok ? tbase[i] + (uint64_t)(c + PFD) * tstep[i] : rec0);
-      }
-      barrier_vm<63>();  // B1: U is visible; the output waves are done with the old state
-      // S^T <- gamma_last S^T + K^T diag(e rk) U: each K^T fragment feeds every column tile
+      if (NM == 0 && touches) touch(c);
+      // S^T <- gamma_last S^T + K^T diag(e rk) U in registers, before B1: the
+      // state in LDS changes only after it
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1504,12 +1546,11 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(u[ct][2 * s], tile_hi<NT>(u[ct], s));
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const frag ak = frag_kt<T, L::RBK, DT>(K_t, dt, HALF ? 4 * g4 : 32 * s + 8 * g4, l16, HALF);
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], ak, bs[ct], HALF);
-        }
+          for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], kt[s][dt], bs[ct], HALF);
       }
+      barrier_vm<63>();  // B1: U is visible; the output waves are done with the old state
       // the state after every emit_every-th whole chunk inside the sequence
       // (a split scan never emits: its second segment does not hold S)
       if (p.emit_every > 0 && (cbeg + c + 1) % p.emit_every == 0 && chunk_t0(c) + C < seq_end) {
@@ -1528,7 +1569,7 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
       step(c, sb0);
       if (c + 1 < nch) step(c + 1, sb1);
     }
-    if constexpr (PFD > 0) {
+    if (NM == 0 && touches) {
 #pragma unroll
       for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
     }
@@ -1546,7 +1587,7 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
           *reinterpret_cast<float4*>(s_fin + (sp.on ? wrow(ct) : srow(ct)) + pidx<DT>(dt, 4 * g4)) =
               make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
-  } else {
+  } else if (!mover) {
     // --------------------------------------------------------- output waves
     const int64_t o_stride = (int64_t)p.h_v * D;
     // outputs go to o, except the transition's (w, from token seg_start on)
@@ -1573,30 +1614,17 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
 
     auto step = [&](int c, const unsigned char* cur, unsigned char* nxt) {
       if (c > 0) store_o(chunk_t0(c - 1), C);
-      // the next chunk: full ones in pieces, a partial one at once
-      const bool more = c + 1 < nch;
-      const bool pieces = more && fast && chunk_len(c + 1) == C;
-      if (more && !pieces) issue_slow(c + 1, nxt, std::integral_constant<int, NO>{}, ow);
-      const unsigned char *kc, *qc, *vc, *rec;
-      chunk_ptrs(more ? c + 1 : c, kc, qc, vc, rec);
+      if constexpr (NM == 0) issue_next(c, nxt);
       const unsigned char* Q_t = cur + L::oQ;
       const unsigned char* P_t = cur + L::oP;
       const float* vec = reinterpret_cast<const float*>(cur + L::oVec);
-      // Y^T = S Q^T, columns scaled by scale gamma rq; K and Q of the next
-      // chunk go out a few instructions per k-step
+      // Y^T = S Q^T, columns scaled by scale gamma rq
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int nt = 0; nt < NTO; ++nt) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        if (pieces) {
-#pragma unroll
-          for (int k = s * decltype(pk)::NI / (D / 32); k < (s + 1) * decltype(pk)::NI / (D / 32); ++k) {
-            pk.issue_one(k, nxt + L::oK, kc, ow, lane);
-            pq.issue_one(k, nxt + L::oQ, qc, ow, lane);
-          }
-        }
         frag as[CT], bq[NTO];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) as[ct] = frag_row_s<T, SS>(sS, colof(ct), 32 * s + 8 * g4, false);
@@ -1615,12 +1643,6 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
         for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= sc;
       }
       barrier_vm<63>();  // B1
-      if (pieces) {
-        ptb.issue(nxt + L::oTb, rec, ow, lane);
-        ptb.issue(nxt + L::oP, rec + Rec<T, C>::mat, ow, lane);
-        pv.issue(nxt + L::oV, vc, ow, lane);
-        dma_linear<16 * C, NO>(nxt + L::oVec, rec + 2 * Rec<T, C>::mat, ow, lane);
-      }
       // O^T += U^T P^T
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -1642,6 +1664,20 @@ __global__ __launch_bounds__(64 * NWR * (1 + OS)) void scan2_kernel(PrefillParam
       if (c + 1 < nch) step(c + 1, sb1, sb0);
     }
     if (nch > 0) store_o(chunk_t0(nch - 1), chunk_len(nch - 1));
+  } else {
+    // ---------------------------------------------------------- mover waves
+    // per chunk: the next chunk's loads, then the touches, which stay in
+    // flight across B2 (only the loads before them are waited for)
+    __syncthreads();  // chunk 0 has landed; the initial state is published
+    for (int c = 0; c < nch; ++c) {
+      issue_next(c, (c & 1) ? sb0 : sb1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (touches) touch(c);
+      barrier_vm<63>();      // B1 (nothing to wait for)
+      barrier_vm<NTOUCH>();  // B2: this wave's loads of the next chunk have landed
+    }
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(tv[i]));
   }
 }
 
@@ -1659,14 +1695,23 @@ constexpr int kScan2Tiles = GDN_SCAN2_CT;  // 16-column tiles per wave
 #endif
 template <int C>
 constexpr int kOutSplit = C >= 32 ? GDN_SCAN2_OS : 1;
+// mover waves of the 32-column workgroups (the 64-column ones have no VGPR
+// room for more waves: their output waves move the data)
+#ifndef GDN_SCAN2_MOVERS
+#define GDN_SCAN2_MOVERS 2
+#endif
+// (the layout needs two output waves per column slice: chunks of 32 tokens
+// or more)
+template <int C>
+constexpr int kMovers = kOutSplit<C> == 2 ? GDN_SCAN2_MOVERS : 0;
 // Two workgroup widths: 64 columns (four waves per role, two waves per SIMD)
 // for launches that fill the chip, 32 columns (two waves per role) to spread
 // a few long chains over twice as many CUs.
 #define GDN_SCAN2(D, C) \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>(PrefillParams, \
-                                                                                          const unsigned char*, ScanSplit); \
-  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>(PrefillParams, \
-                                                                                          const unsigned char*, ScanSplit);
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>, 0>( \
+      PrefillParams, const unsigned char*, ScanSplit); \
+  template __global__ void scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>, kMovers<C>>( \
+      PrefillParams, const unsigned char*, ScanSplit);
 GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCAN2(128, 32) GDN_SCAN2(128, 64)
 #undef GDN_SCAN2
 
@@ -1882,18 +1927,19 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       const size_t recs_end = off_bytes(p.n_seqs) + (size_t)max_chunks(p.total_tokens, p.n_seqs, C) * p.h_v * Rec<T, C>::bytes;
       const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, p.emit_every, recs_end);
       ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr};
+      // 32- and 64-column workgroups: chain, output and mover waves
+      constexpr unsigned narrow_threads = 64 * ((2 / kScan2Tiles) * (1 + kOutSplit<C>) + kMovers<C>);
+      constexpr unsigned wide_threads = 64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>);
+      const auto narrow = scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>, kMovers<C>>;
+      const auto wide = scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>, 0>;
       if (sp.on) {
         // one long sequence: two segments side by side
         float* st = reinterpret_cast<float*>(ws + sp.o_state);
         const size_t hs = (size_t)p.h_v * D * D;
         ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w)};
         const unsigned grid = (unsigned)(3 * p.h_v * (D / sp.cols));
-        if (sp.cols == 32)
-          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>), dim3(grid),
-                             dim3(64 * (2 / kScan2Tiles) * (1 + kOutSplit<C>)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
-        else
-          hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>), dim3(grid),
-                             dim3(64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>)), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        hipLaunchKernelGGL(sp.cols == 32 ? narrow : wide, dim3(grid), dim3(sp.cols == 32 ? narrow_threads : wide_threads),
+                           0, stream, p, static_cast<const unsigned char*>(ws), ss);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int ntile = (int)((p.total_tokens - sp.t_b + kJoinTok - 1) / kJoinTok);
         const int nstate = p.final_state ? p.h_v * (D / 16) : 0;
@@ -1902,12 +1948,11 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
       } else if ((int64_t)p.n_seqs * p.h_v * (D / 32) <= kScanCUs) {
         // narrow workgroups when even they leave CUs idle
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 32);
-        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 2 / kScan2Tiles, kOutSplit<C>>), dim3(grid), dim3(64 * (2 / kScan2Tiles) * (1 + kOutSplit<C>)),
-                           0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        hipLaunchKernelGGL(narrow, dim3(grid), dim3(narrow_threads), 0, stream, p,
+                           static_cast<const unsigned char*>(ws), ss);
       } else {
         const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / 64);
-        hipLaunchKernelGGL((scan2_kernel<D, C, kScan2Tiles, 4 / kScan2Tiles, kOutSplit<C>>), dim3(grid), dim3(64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>)),
-                           0, stream, p, static_cast<const unsigned char*>(ws), ss);
+        hipLaunchKernelGGL(wide, dim3(grid), dim3(wide_threads), 0, stream, p, static_cast<const unsigned char*>(ws), ss);
       }
     } else {
       const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / SL::cols);
