@@ -765,7 +765,8 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   }
   __syncthreads();
 
-  // T = (I + A)^-1 by 16x16 blocks on fp32 MFMA, in place.  A block X of
+  // T = (I + A)^-1 by 16x16 blocks, in place: the diagonal blocks by forward
+  // substitution, the blocks below them on fp32 MFMA.  A block X of
   // A_s is read as the accumulator layout of X (col: lane (g, c) holds
   // X[4g+i][c]) or of X^T (row: X[c][4g+i], one 16-byte read); tn(Y, W)
   // forms Y^T W from two such tiles.
@@ -783,34 +784,40 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i * L::LDF] = sgn * t[i];
   };
-  // diagonal blocks: wave b inverts the unit lower-triangular I + N (N the
-  // strictly lower block, nilpotent) as (I - N)(I + N^2)(I + N^4)(I + N^8);
-  // M = N^T runs alongside so every product is a tn() of held tiles
-  f32x4 Tdiag = {0.f, 0.f, 0.f, 0.f}, Z1 = {0.f, 0.f, 0.f, 0.f};
-  if (wave < NT) {
-    const int b = wave;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 N1 = col(b, b), M1 = row(b, b);
-    const f32x4 M2 = mfma_tn(N1, M1, zero), N2 = mfma_tn(M1, N1, zero);
-    const f32x4 M4 = mfma_tn(N2, M2, zero), N4 = mfma_tn(M2, N2, zero);
-    const f32x4 M8 = mfma_tn(N4, M4, zero);
-    f32x4 X;
+  // diagonal blocks: wave 0 inverts each unit lower-triangular I + N (N the
+  // strictly lower 16x16 block) by forward substitution in fp32, lane
+  // (b, k) = (lane / 16, lane % 16) forming column k of block b:
+  // t_i = [i == k] - sum_{j < i} N_ij t_j (zero above k, one at k).  Rows of
+  // N are read as broadcasts (the 16 lanes of a block share each address).
+  if (wave == 0 && (lane >> 4) < NT) {
+    const int b = lane >> 4, k = lane & 15;
+    const float* nb = A_s + 16 * b * L::LDF + 16 * b;  // block (b, b)
+    float t[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) X[i] = (4 * g4 + i == c16 ? 1.f : 0.f) - N1[i];
-    X = mfma_tn(M2, X, X);  // (I + N^2) X
-    X = mfma_tn(M4, X, X);
-    X = mfma_tn(M8, X, X);
-    Tdiag = X;
-    // level 1 starts at once in the wave that holds T_{2b,2b}
-    if constexpr (NT >= 2)
-      if ((b & 1) == 0) Z1 = mfma_tn(row(b + 1, b), X, zero);  // A_{2b+1,2b} T_{2b,2b}
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == k ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; q < (i + 3) / 4; ++q) {
+        const float4 n4 = *reinterpret_cast<const float4*>(nb + i * L::LDF + 4 * q);
+        const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e < i) acc -= nv[e] * t[4 * q + e];
+      }
+      t[i] = acc;
+    }
+    float* out = A_s + 16 * b * L::LDF + 16 * b + k;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i * L::LDF] = t[i];
   }
-  if (wave < NT) put(wave, wave, Tdiag, 1.f);
   __syncthreads();
   if constexpr (NT >= 2) {
     // level 1: T_{2b+1,2b} = -T_{2b+1,2b+1} A_{2b+1,2b} T_{2b,2b}
-    if (wave < NT && (wave & 1) == 0)
-      put(wave + 1, wave, mfma_tn(row(wave + 1, wave + 1), Z1, f32x4{0.f, 0.f, 0.f, 0.f}), -1.f);
+    if (wave < NT && (wave & 1) == 0) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 z1 = mfma_tn(row(wave + 1, wave), col(wave, wave), zero);  // A_{2b+1,2b} T_{2b,2b}
+      put(wave + 1, wave, mfma_tn(row(wave + 1, wave + 1), z1, zero), -1.f);
+    }
     __syncthreads();
   }
   if constexpr (NT == 4) {
