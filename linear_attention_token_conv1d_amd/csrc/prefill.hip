@@ -552,12 +552,16 @@ template <typename T, int D, int C, int VPW>
 struct PrepLayout {
   static constexpr int NT = C / 16;
   static constexpr int E = (int)sizeof(T);
-  static constexpr int RBK = D * E;  // K, Q tile rows (swizzled)
   static constexpr int LDF = C + 4;
+  // the K, Q tiles hold d_k in NH passes: two when they would otherwise be
+  // the largest LDS user (one V head per workgroup)
+  static constexpr int NH = 2 * C * D * E > VPW * C * LDF * 4 ? 2 : 1;
+  static constexpr int DH = D / NH;
+  static constexpr int RBH = DH * E;  // K, Q tile rows (swizzled)
   // phase 1 (shared by the V-head teams): K, Q tiles
   static constexpr int oK = 0;
-  static constexpr int oQ = oK + C * RBK;
-  static constexpr int kq_bytes = oQ + C * RBK;
+  static constexpr int oQ = oK + C * RBH;
+  static constexpr int kq_bytes = oQ + C * RBH;
   // phase 2 (same bytes): per team, the A/T work array
   static constexpr int oA = 0;
   static constexpr int team_bytes = oA + C * LDF * 4;
@@ -565,6 +569,10 @@ struct PrepLayout {
   // row scalars: rk, rq (shared), then g, beta, G per team
   static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
   static constexpr int bytes = oVec + (2 + 3 * VPW) * C * 4;
+  // with split tiles, the waves per SIMD that LDS allows (at most 6) set the
+  // register budget; otherwise the compiler's own choice stands
+  static constexpr int wgs = 160 * 1024 / bytes;
+  static constexpr int waves_per_eu = NH == 1 ? 1 : wgs * VPW > 6 ? 6 : wgs * VPW < 1 ? 1 : wgs * VPW;
 };
 
 // Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
@@ -578,11 +586,13 @@ __device__ __forceinline__ int owner(cint32* off, int n_seqs, int c) {
 }
 
 template <typename T, int D, int C, int VPW>
-__global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams p, unsigned char* ws) {
+__global__ __launch_bounds__(kPrepThreads * VPW)
+__attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) void prep_kernel(PrefillParams p,
+                                                                                             unsigned char* ws) {
   using L = PrepLayout<T, D, C, VPW>;
   using M = Mma<T>;
   using R8 = Raw8<T>;
-  using SK = Swz<L::RBK>;
+  using SK = Swz<L::RBH>;
   constexpr int NT = L::NT;
   constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
   constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
@@ -618,61 +628,83 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
   // the chunk re-read its last row and are zeroed below.
   const T* kg = reinterpret_cast<const T*>(p.k) + (int64_t)hq * D;
   const T* qg = reinterpret_cast<const T*>(p.q) + (int64_t)hq * D;
-  constexpr int NV = (C * RT + NTH - 1) / NTH;
-  R8 kv[NV], qv[NV];
+  // piece (hf, e) of a pass: row e / RTH, d_k 8 (e % RTH) of part hf
+  constexpr int RTH = RT / L::NH;                 // threads per row and part
+  constexpr int NV = (C * RTH + NTH - 1) / NTH;   // pieces per thread and part
+  R8 kv[L::NH][NV], qv[L::NH][NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = min(tid + i * NTH, C * RT - 1);
-    const int r = min(e / RT, Lc - 1), d0 = (e % RT) * 8;
-    kv[i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
-    qv[i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
-  }
+  for (int hf = 0; hf < L::NH; ++hf)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = min(tid + i * NTH, C * RTH - 1);
+      const int r = min(e / RTH, Lc - 1), d0 = hf * L::DH + (e % RTH) * 8;
+      kv[hf][i] = R8::load(kg + (t0 + r) * p.k_stride + d0);
+      qv[hf][i] = R8::load(qg + (t0 + r) * p.q_stride + d0);
+    }
   const int ti = min(ttid, Lc - 1);
   const float gv = p.g[(t0 + ti) * p.h_v + h];
   const float bv = p.beta[(t0 + ti) * p.h_v + h];
 
-  // row norms: the RT threads of a row are consecutive lanes
+  // row norms: the RTH threads of a row are consecutive lanes; a thread
+  // holds the same rows in every part
+  float skr[NV], sqr[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) skr[i] = sqr[i] = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < L::NH; ++hf)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float fk[8], fq[8];
+      if constexpr (sizeof(T) == 2) {
+        const uint4 a = kv[hf][i].a, b = qv[hf][i].a;
+        fk[0] = bf16_lo(a.x); fk[1] = bf16_hi(a.x); fk[2] = bf16_lo(a.y); fk[3] = bf16_hi(a.y);
+        fk[4] = bf16_lo(a.z); fk[5] = bf16_hi(a.z); fk[6] = bf16_lo(a.w); fk[7] = bf16_hi(a.w);
+        fq[0] = bf16_lo(b.x); fq[1] = bf16_hi(b.x); fq[2] = bf16_lo(b.y); fq[3] = bf16_hi(b.y);
+        fq[4] = bf16_lo(b.z); fq[5] = bf16_hi(b.z); fq[6] = bf16_lo(b.w); fq[7] = bf16_hi(b.w);
+      } else {
+        const uint4 a0 = kv[hf][i].a, a1 = kv[hf][i].b, b0 = qv[hf][i].a, b1 = qv[hf][i].b;
+        fk[0] = __uint_as_float(a0.x); fk[1] = __uint_as_float(a0.y); fk[2] = __uint_as_float(a0.z);
+        fk[3] = __uint_as_float(a0.w); fk[4] = __uint_as_float(a1.x); fk[5] = __uint_as_float(a1.y);
+        fk[6] = __uint_as_float(a1.z); fk[7] = __uint_as_float(a1.w);
+        fq[0] = __uint_as_float(b0.x); fq[1] = __uint_as_float(b0.y); fq[2] = __uint_as_float(b0.z);
+        fq[3] = __uint_as_float(b0.w); fq[4] = __uint_as_float(b1.x); fq[5] = __uint_as_float(b1.y);
+        fq[6] = __uint_as_float(b1.z); fq[7] = __uint_as_float(b1.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { skr[i] += fk[j] * fk[j]; sqr[i] += fq[j] * fq[j]; }
+    }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    float sk = skr[i], sq = sqr[i];
+    sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk);
+    sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq);
+    if constexpr (RTH >= 8) { sk += dpp_f32<DPP_ROW_HALF_MIRROR>(sk); sq += dpp_f32<DPP_ROW_HALF_MIRROR>(sq); }
+    if constexpr (RTH == 16) { sk += dpp_f32<DPP_ROW_MIRROR>(sk); sq += dpp_f32<DPP_ROW_MIRROR>(sq); }
     const int e = tid + i * NTH;
-    const int r = e / RT, d0 = (e % RT) * 8;
-    float fk[8], fq[8];
-    if constexpr (sizeof(T) == 2) {
-      const uint4 a = kv[i].a, b = qv[i].a;
-      fk[0] = bf16_lo(a.x); fk[1] = bf16_hi(a.x); fk[2] = bf16_lo(a.y); fk[3] = bf16_hi(a.y);
-      fk[4] = bf16_lo(a.z); fk[5] = bf16_hi(a.z); fk[6] = bf16_lo(a.w); fk[7] = bf16_hi(a.w);
-      fq[0] = bf16_lo(b.x); fq[1] = bf16_hi(b.x); fq[2] = bf16_lo(b.y); fq[3] = bf16_hi(b.y);
-      fq[4] = bf16_lo(b.z); fq[5] = bf16_hi(b.z); fq[6] = bf16_lo(b.w); fq[7] = bf16_hi(b.w);
-    } else {
-      const uint4 a0 = kv[i].a, a1 = kv[i].b, b0 = qv[i].a, b1 = qv[i].b;
-      fk[0] = __uint_as_float(a0.x); fk[1] = __uint_as_float(a0.y); fk[2] = __uint_as_float(a0.z);
-      fk[3] = __uint_as_float(a0.w); fk[4] = __uint_as_float(a1.x); fk[5] = __uint_as_float(a1.y);
-      fk[6] = __uint_as_float(a1.z); fk[7] = __uint_as_float(a1.w);
-      fq[0] = __uint_as_float(b0.x); fq[1] = __uint_as_float(b0.y); fq[2] = __uint_as_float(b0.z);
-      fq[3] = __uint_as_float(b0.w); fq[4] = __uint_as_float(b1.x); fq[5] = __uint_as_float(b1.y);
-      fq[6] = __uint_as_float(b1.z); fq[7] = __uint_as_float(b1.w);
-    }
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { sk += fk[j] * fk[j]; sq += fq[j] * fq[j]; }
-    sk += dpp_f32<DPP_QUAD_1032>(sk); sk += dpp_f32<DPP_QUAD_2301>(sk); sk += dpp_f32<DPP_ROW_HALF_MIRROR>(sk);
-    sq += dpp_f32<DPP_QUAD_1032>(sq); sq += dpp_f32<DPP_QUAD_2301>(sq); sq += dpp_f32<DPP_ROW_HALF_MIRROR>(sq);
-    if constexpr (RT == 16) { sk += dpp_f32<DPP_ROW_MIRROR>(sk); sq += dpp_f32<DPP_ROW_MIRROR>(sq); }
-    if (e >= C * RT) continue;  // a pass wider than the chunk (whole rows per pass)
-    if (d0 == 0) {
-      rk_s[r] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-      rq_s[r] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-    }
-    // raw rows into the swizzled tiles (rows >= Lc zero)
-#pragma unroll
-    for (int part = 0; part < (int)sizeof(R8) / 16; ++part) {
-      const int b = d0 * (int)sizeof(T) + 16 * part;
-      const uint4 zk = r < Lc ? (part ? reinterpret_cast<const uint4*>(&kv[i])[1] : kv[i].a) : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 zq = r < Lc ? (part ? reinterpret_cast<const uint4*>(&qv[i])[1] : qv[i].a) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(K_s + SK::off(r, b)) = zk;
-      *reinterpret_cast<uint4*>(Q_s + SK::off(r, b)) = zq;
+    if (e >= C * RTH) continue;  // a pass wider than the chunk (whole rows per pass)
+    if (e % RTH == 0) {
+      rk_s[e / RTH] = p.l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+      rq_s[e / RTH] = p.l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
     }
   }
+  // raw rows into the swizzled tiles, d_k part hf of NH (rows >= Lc zero)
+  auto stage = [&](int hf) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * NTH;
+      const int r = e / RTH, c0 = (e % RTH) * 8;
+      if (e >= C * RTH) continue;
+#pragma unroll
+      for (int part = 0; part < (int)sizeof(R8) / 16; ++part) {
+        const int b = c0 * (int)sizeof(T) + 16 * part;
+        const uint4 zk = r < Lc ? (part ? reinterpret_cast<const uint4*>(&kv[hf][i])[1] : kv[hf][i].a) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 zq = r < Lc ? (part ? reinterpret_cast<const uint4*>(&qv[hf][i])[1] : qv[hf][i].a) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(K_s + SK::off(r, b)) = zk;
+        *reinterpret_cast<uint4*>(Q_s + SK::off(r, b)) = zq;
+      }
+    }
+  };
+  stage(0);
   if (ttid < C) {
     g_s[ttid] = ttid < Lc ? gv : 0.f;
     b_s[ttid] = ttid < Lc ? bv : 0.f;
@@ -703,12 +735,28 @@ __global__ __launch_bounds__(kPrepThreads * VPW) void prep_kernel(PrefillParams 
       int tj = job >= NLT ? job - NLT : job, mt = 0;
       while (tj > mt) { tj -= mt + 1; ++mt; }
       jmt[jj] = mt; jnt[jj] = tj;
-      const unsigned char* Bt = job >= NLT ? Q_s : K_s;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        M::mma(gram[jj], frag_row<T, L::RBK>(K_s, tj * 16 + l16, 32 * s + 8 * g4, false),
-               frag_row<T, L::RBK>(Bt, mt * 16 + l16, 32 * s + 8 * g4, false), false);
     }
+  }
+  // the k-steps over the staged part of d_k
+  auto gram_pass = [&]() {
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int job = wave + 4 * jj;
+      if (job < 2 * NLT) {
+        const unsigned char* Bt = job >= NLT ? Q_s : K_s;
+#pragma unroll
+        for (int s = 0; s < L::DH / 32; ++s)
+          M::mma(gram[jj], frag_row<T, L::RBH>(K_s, jnt[jj] * 16 + l16, 32 * s + 8 * g4, false),
+                 frag_row<T, L::RBH>(Bt, jmt[jj] * 16 + l16, 32 * s + 8 * g4, false), false);
+      }
+    }
+  };
+  gram_pass();
+  if constexpr (L::NH == 2) {
+    __syncthreads();  // the first half is read
+    stage(1);
+    __syncthreads();
+    gram_pass();
   }
   __syncthreads();  // norms and G published; K, Q are dead from here on
 
