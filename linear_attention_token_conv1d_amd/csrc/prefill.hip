@@ -307,6 +307,21 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* cu, int n_seqs
   }
 }
 
+// The plan's arrays as the kernels read them.  A call with one sequence and
+// no cu_seqlens launches no plan: each value follows from the token count.
+struct PlanView {
+  cint32* a;  // chunk offsets | scan order | emission rows, or null
+  int n_seqs;
+  int nch1;   // chunks of the one sequence when a is null
+  __device__ __forceinline__ int off(int i) const { return a ? a[i] : i == 0 ? 0 : nch1; }
+  __device__ __forceinline__ int order(int i) const { return a ? a[n_seqs + 1 + i] : 0; }
+  __device__ __forceinline__ int erow(int n) const { return a ? a[2 * n_seqs + 1 + n] : 0; }
+};
+__device__ __forceinline__ PlanView plan_view(const PrefillParams& p, const unsigned char* ws, int C) {
+  return PlanView{p.cu_seqlens ? as_const(reinterpret_cast<const int32_t*>(ws)) : nullptr, p.n_seqs,
+                  (int)((p.total_tokens + C - 1) / C)};
+}
+
 // Workgroup -> (sequence, V head, column block) for the scans.  The unit of
 // placement is a QK-head group: the grp = h_v / h_qk V heads (times NB column
 // blocks) that read the same K, Q and chunk rows.  Consecutive groups go to
@@ -317,13 +332,13 @@ struct ScanSlot {
   int n, h, blk, role;
   bool valid;
 };
-__device__ __forceinline__ ScanSlot scan_slot(const PrefillParams& p, const int32_t* order, int NB) {
+__device__ __forceinline__ ScanSlot scan_slot(const PrefillParams& p, const PlanView& pv, int NB) {
   const int grp = p.h_v / p.h_qk, gs = grp * NB, ngroups = p.n_seqs * p.h_qk;
   const int x = blockIdx.x % 8, k = blockIdx.x / 8;
   const int gi = (k / gs) * 8 + x, j = k % gs;
   ScanSlot r{0, 0, 0, 0, gi < ngroups};
   if (r.valid) {
-    r.n = order[gi / p.h_qk];
+    r.n = pv.order(gi / p.h_qk);
     r.h = (gi % p.h_qk) * grp + j / NB;
     r.blk = j % NB;
   }
@@ -575,12 +590,12 @@ struct PrepLayout {
   static constexpr int waves_per_eu = NH == 1 ? 1 : wgs * VPW > 6 ? 6 : wgs * VPW < 1 ? 1 : wgs * VPW;
 };
 
-// Largest n in [0, n_seqs) with off[n] <= c (the sequence owning chunk c).
-__device__ __forceinline__ int owner(cint32* off, int n_seqs, int c) {
-  int lo = 0, hi = n_seqs - 1;
+// Largest n in [0, n_seqs) with off(n) <= c (the sequence owning chunk c).
+__device__ __forceinline__ int owner(const PlanView& pv, int c) {
+  int lo = 0, hi = pv.a ? pv.n_seqs - 1 : 0;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= c) lo = mid; else hi = mid - 1;
+    if (pv.off(mid) <= c) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -613,15 +628,15 @@ __attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) voi
   float* b_s = g_s + C;
   float* G_s = g_s + 2 * C;
 
-  cint32* off = as_const(reinterpret_cast<const int32_t*>(ws));
+  const PlanView pv = plan_view(p, ws, C);
   cint32* cu = as_const(p.cu_seqlens);
   const int ci = blockIdx.x, h = blockIdx.y * VPW + team;
-  if (ci >= off[p.n_seqs]) return;
+  if (ci >= pv.off(p.n_seqs)) return;
   const int hq = h / (p.h_v / p.h_qk);  // the same for every team (VPW divides h_v / h_qk)
-  const int n = owner(off, p.n_seqs, ci);
+  const int n = owner(pv, ci);
   const int64_t seq_start = cu ? cu[n] : 0;
   const int64_t seq_end = cu ? cu[n + 1] : p.total_tokens;
-  const int64_t t0 = seq_start + (int64_t)(ci - off[n]) * C;
+  const int64_t t0 = seq_start + (int64_t)(ci - pv.off(n)) * C;
   const int Lc = (int)min((int64_t)C, seq_end - t0);
 
   // K, Q rows of this chunk and QK head; g, beta of this V head.  Rows past
@@ -956,7 +971,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   __shared__ __align__(16) unsigned char so0[L::stage_o ? L::obuf : 16];
   __shared__ __align__(16) unsigned char so1[L::stage_o ? L::obuf : 16];
 
-  const ScanSlot slot = scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
+  const PlanView pv = plan_view(p, ws, C);
+  const ScanSlot slot = scan_slot(p, pv, NB);
   if (!slot.valid) return;
   const int blk = slot.blk, h = slot.h, n = slot.n;
   const int hq = h / (p.h_v / p.h_qk);
@@ -965,12 +981,11 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   // this lane's column in the workgroup block for column tile ct
   auto lcol = [&](int ct) { return (wave * CT + ct) * 16 + l16; };
 
-  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
   const unsigned char* recs = ws + off_bytes(p.n_seqs);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
-  const int c0 = off[n];
-  const int nch = off[n + 1] - c0;
+  const int c0 = pv.off(n);
+  const int nch = pv.off(n + 1) - c0;
 
   const unsigned char* qg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + (int64_t)hq * D);
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + (int64_t)hq * D);
@@ -1013,7 +1028,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
   const size_t sbase = ((size_t)sslot * p.h_v + h) * D * D + (size_t)(blk * L::cols) * D;
   // rows of this sequence's emitted chunk-boundary states
-  const int erow = p.emit_every > 0 ? as_const(reinterpret_cast<const int32_t*>(ws))[2 * p.n_seqs + 1 + n] : 0;
+  const int erow = p.emit_every > 0 ? pv.erow(n) : 0;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1286,8 +1301,8 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
   __shared__ __align__(16) unsigned char sS[L::sbytes];
   __shared__ __align__(16) unsigned char sU[L::ubytes];
 
-  const ScanSlot slot =
-      sp.on ? split_slot(p, NB) : scan_slot(p, reinterpret_cast<const int32_t*>(ws) + p.n_seqs + 1, NB);
+  const PlanView plan = plan_view(p, ws, C);
+  const ScanSlot slot = sp.on ? split_slot(p, NB) : scan_slot(p, plan, NB);
   if (!slot.valid) return;
   const int blk = slot.blk, h = slot.h, n = slot.n, role = slot.role;
   const int hq = h / (p.h_v / p.h_qk);
@@ -1309,12 +1324,11 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
   const int xw = NM > 0 ? (mover ? slot4 : 0) : ow;  // index among the moving waves
   auto colof = [&](int ct) { return SW * cw + 16 * ct + l16; };  // this lane's column in tile ct
 
-  const int32_t* off = reinterpret_cast<const int32_t*>(ws);
   const unsigned char* recs = ws + off_bytes(p.n_seqs);
   const int64_t seq_start = p.cu_seqlens ? p.cu_seqlens[n] : 0;
   const int64_t seq_end = p.cu_seqlens ? p.cu_seqlens[n + 1] : p.total_tokens;
   // this workgroup's chunks: the whole sequence, or one segment of a split
-  const int cseq = off[n], nch_seq = off[n + 1] - cseq;
+  const int cseq = plan.off(n), nch_seq = plan.off(n + 1) - cseq;
   const int cbeg = role == 0 ? 0 : sp.m;
   const int nch = sp.on ? (role == 0 ? sp.m : nch_seq - sp.m) : nch_seq;
   const int c0 = cseq + cbeg;
@@ -1457,7 +1471,7 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
     const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
     auto srow = [&](int ct) { return (((size_t)sslot * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D; };
     auto wrow = [&](int ct) { return ((size_t)h * D + (size_t)(blk * L::cols + colof(ct))) * D; };
-    const int erow = p.emit_every > 0 ? as_const(reinterpret_cast<const int32_t*>(ws))[2 * p.n_seqs + 1 + n] : 0;
+    const int erow = p.emit_every > 0 ? plan.erow(n) : 0;
     // initial state: the caller's (or zero) for a whole sequence or a first
     // segment, zero for a second segment, the identity for the transition
     const float* s_init = role == 0 ? p.initial_state : nullptr;
@@ -1964,10 +1978,12 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     constexpr int NW = kScanWaves, CT = kScanTiles;
     using SL = ScanLayout<T, D, C, NW, CT>;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs,
-                       p.total_tokens, C, p.emit_every, reinterpret_cast<int32_t*>(ws));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (p.cu_seqlens) {  // one sequence needs no plan (PlanView)
+      hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs, p.total_tokens, C,
+                         p.emit_every, reinterpret_cast<int32_t*>(ws));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int grp = p.h_v / p.h_qk;
     const int vpw = sizeof(T) != 2 ? 1 : grp % 4 == 0 ? 4 : grp % 3 == 0 ? 3 : grp % 2 == 0 ? 2 : 1;
     if (p.total_tokens > 0) {
