@@ -1789,7 +1789,7 @@ GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCA
 // O^T[j][t] = sum_i S_m[j][i] w[t][i] on MFMA (bf16 operands, fp32 sums; o
 // is read and rounded once more), and the final state S_m Phi + S0 in fp32.
 // Blocks [0, nstate): with a final state, h_v D/16 blocks of 16 state rows
-// each, first so that their dependent sums overlap the rest.  Then blocks of
+// each (fp32 MFMA), first so that they overlap the rest.  Then blocks of
 // kJoinTok tokens of V head h = block % h_v (a head's blocks share an XCD,
 // and its S_m that L2): S_m (as bf16) and the w rows go to LDS through
 // coalesced 16-byte loads, issued with the o rows they correct before any
@@ -1815,43 +1815,42 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
   const int64_t o_stride = (int64_t)p.h_v * D;
   const int64_t ntok = p.total_tokens - t_b;
   if ((int)blockIdx.x < nstate) {
-    // final state rows j = 16 jb + tid / 16, columns cb .. cb + D/16 - 1
-    constexpr int NC = D / 16;
-    const int h = blockIdx.x / (D / 16), j = 16 * (blockIdx.x % (D / 16)) + tid / 16, cb = (tid % 16) * NC;
+    // final state rows 16 jb .. 16 jb + 15 of head h on fp32 MFMA: wave w
+    // forms the 16x16 tiles nb = NPW w .. of S_m Phi + S0 as sums over kb of
+    // (S_m block (jb, kb)) (Phi block (kb, nb)), every operand load issued
+    // before the products
+    constexpr int NB = D / 16, NPW = (NB + 3) / 4;
+    const int h = blockIdx.x / NB, jb = blockIdx.x % NB;
     const size_t hs = (size_t)h * D * D;
     // the caller's final state: slot of the one sequence
     const size_t fs = ((size_t)(p.state_idx ? as_const(p.state_idx)[0] : 0) * p.h_v + h) * D * D;
-    const float* smr = sp.s_mid + hs + (size_t)j * D;
-    const float* ph = sp.phi + hs + cb;
-    float acc[NC];
+    // y[kb]: the transposed S_m block in the accumulator layout, lane (g, c)
+    // holding S_m[16 jb + c][16 kb + 4 g + i]
+    f32x4 y[NB];
 #pragma unroll
-    for (int c = 0; c < NC; c += 4) {
-      const float4 z = *reinterpret_cast<const float4*>(sp.s_zero + hs + (size_t)j * D + cb + c);
-      acc[c] = z.x; acc[c + 1] = z.y; acc[c + 2] = z.z; acc[c + 3] = z.w;
-    }
-    // eight rows of Phi per batch, all loads of a batch issued together
-    for (int i0 = 0; i0 < D; i0 += 8) {
-      const float4 a0 = *reinterpret_cast<const float4*>(smr + i0), a1 = *reinterpret_cast<const float4*>(smr + i0 + 4);
-      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      float4 r[8][NC / 4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int c = 0; c < NC / 4; ++c) r[i][c] = *reinterpret_cast<const float4*>(ph + (size_t)(i0 + i) * D + 4 * c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int c = 0; c < NC / 4; ++c) {
-          acc[4 * c] += a[i] * r[i][c].x;
-          acc[4 * c + 1] += a[i] * r[i][c].y;
-          acc[4 * c + 2] += a[i] * r[i][c].z;
-          acc[4 * c + 3] += a[i] * r[i][c].w;
-        }
+    for (int kb = 0; kb < NB; ++kb) {
+      const float4 v = *reinterpret_cast<const float4*>(sp.s_mid + hs + (size_t)(16 * jb + l16) * D + 16 * kb + 4 * g4);
+      y[kb] = f32x4{v.x, v.y, v.z, v.w};
     }
 #pragma unroll
-    for (int c = 0; c < NC; c += 4)
-      *reinterpret_cast<float4*>(p.final_state + fs + (size_t)j * D + cb + c) =
-          make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]);
+    for (int t = 0; t < NPW; ++t) {
+      const int nb = wave * NPW + t;
+      if (nb >= NB) break;
+      // lane (g, c): element (4 g + i, c) of block (., nb)
+      auto at = [&](const float* m, int rb, int i) { return m + hs + (size_t)(16 * rb + 4 * g4 + i) * D + 16 * nb + l16; };
+      f32x4 acc, w[NB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = *at(sp.s_zero, jb, i);
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[kb][i] = *at(sp.phi, kb, i);
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) acc = mfma_tn(y[kb], w[kb], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.final_state[fs + (size_t)(16 * jb + 4 * g4 + i) * D + 16 * nb + l16] = acc[i];
+    }
     return;
   }
   const int bo = blockIdx.x - nstate;
