@@ -200,12 +200,12 @@ struct SplitPlan {
   int cols;          // columns per scan workgroup (32 or 64)
   int m;             // chunks in the first segment
   int64_t t_b;       // first token of the second segment
-  size_t o_state, o_w, bytes;  // workspace offsets (after the records) and total
+  size_t o_state, o_w, o_smb, bytes;  // workspace offsets (after the records) and total
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d, int C, int emit_every,
                             size_t base) {
-  SplitPlan s{false, 0, 0, 0, 0, 0, base};
+  SplitPlan s{false, 0, 0, 0, 0, 0, 0, base};
   const int64_t nch = (T + C - 1) / C;
   // chunk-boundary states are not formed on the second segment: no split then
   if (io_dtype != 1 || n_seqs != 1 || emit_every > 0 || nch < kSplitMinChunks) return s;
@@ -232,7 +232,8 @@ inline SplitPlan split_plan(int io_dtype, int64_t T, int n_seqs, int h_v, int d,
   s.t_b = (int64_t)s.m * C;
   s.o_state = align256(base);
   s.o_w = s.o_state + 3 * (size_t)h_v * d * d * 4;
-  s.bytes = align256(s.o_w + (size_t)(T - s.t_b) * h_v * d * 2);
+  s.o_smb = align256(s.o_w + (size_t)(T - s.t_b) * h_v * d * 2);
+  s.bytes = align256(s.o_smb + (size_t)h_v * d * d * 2);
   return s;
 }
 // What a split scan's workgroups find: role 0 = first segment, 1 = second
@@ -243,6 +244,7 @@ struct ScanSplit {
   float* s_zero; // [h_v][d][d] second segment's final state from zero
   float* phi;    // [h_v][d][d] transition of the second segment (row i = basis row i)
   __bf16* w;     // [tokens after t_b][h_v][d]
+  __bf16* s_mid_bf;  // [h_v][d][d] S_m rounded to bf16 (the join's MFMA operand)
 };
 
 // 256 zero bytes: the V rows of the transition role of a split scan
@@ -1656,6 +1658,14 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
           *reinterpret_cast<float4*>(s_fin + (sp.on ? wrow(ct) : srow(ct)) + pidx<DT>(dt, 4 * g4)) =
               make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
     }
+    if (sp.on && role == 0) {  // S_m once more, as the join's bf16 operand
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(sp.s_mid_bf + wrow(ct) + pidx<DT>(dt, 4 * g4)) =
+              make_uint2(pack_bf16x2(st[ct][dt][0], st[ct][dt][1]), pack_bf16x2(st[ct][dt][2], st[ct][dt][3]));
+    }
   } else if (!mover) {
     // --------------------------------------------------------- output waves
     const int64_t o_stride = (int64_t)p.h_v * D;
@@ -1791,7 +1801,8 @@ GDN_SCAN2(64, 16) GDN_SCAN2(64, 32) GDN_SCAN2(64, 64) GDN_SCAN2(128, 16) GDN_SCA
 // Blocks [0, nstate): with a final state, h_v D/16 blocks of 16 state rows
 // each (fp32 MFMA), first so that they overlap the rest.  Then blocks of
 // kJoinTok tokens of V head h = block % h_v (a head's blocks share an XCD,
-// and its S_m that L2): S_m (as bf16) and the w rows go to LDS through
+// and its S_m that L2): S_m (the bf16 copy the first segment wrote) and the
+// w rows go to LDS through
 // coalesced 16-byte loads, issued with the o rows they correct before any
 // is used; wave w forms tokens [32 w, 32 w + 32) for every j, and the
 // correction returns through LDS (fp32) so that o is read and written as
@@ -1856,14 +1867,14 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
   const int bo = blockIdx.x - nstate;
   const int h = bo % p.h_v;
   const int64_t tb0 = (int64_t)(bo / p.h_v) * kJoinTok;  // relative to t_b
-  // ---- loads: S_m (fp32, D/4 float4 per row), w and o rows (D/8 16-byte
-  // pieces per token); rows past the segment re-read its last token
-  constexpr int NSQ = D * D / 4 / 256, NWQ = kJoinTok * D / 8 / 256;
-  const float* Sm = sp.s_mid + (size_t)h * D * D;
-  float4 sv[NSQ];
+  // ---- loads: S_m (bf16), w and o rows (D/8 16-byte pieces per row);
+  // rows past the segment re-read its last token
+  constexpr int NSQ = D * D / 8 / 256, NWQ = kJoinTok * D / 8 / 256;
+  const uint4* Sm = reinterpret_cast<const uint4*>(sp.s_mid_bf + (size_t)h * D * D);
+  uint4 sv[NSQ];
   uint4 wv[NWQ], ov[NWQ];
 #pragma unroll
-  for (int q = 0; q < NSQ; ++q) sv[q] = reinterpret_cast<const float4*>(Sm)[tid + 256 * q];
+  for (int q = 0; q < NSQ; ++q) sv[q] = Sm[tid + 256 * q];
 #pragma unroll
   for (int q = 0; q < NWQ; ++q) {
     const int e = tid + 256 * q, t = e / (D / 8), pc = e % (D / 8);
@@ -1874,9 +1885,8 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
   }
 #pragma unroll
   for (int q = 0; q < NSQ; ++q) {
-    const int e = tid + 256 * q, j = e / (D / 4), c4 = e % (D / 4);
-    *reinterpret_cast<uint2*>(sm + L::oA + SW::off(j, 8 * c4)) =
-        make_uint2(pack_bf16x2(sv[q].x, sv[q].y), pack_bf16x2(sv[q].z, sv[q].w));
+    const int e = tid + 256 * q, j = e / (D / 8), c8 = e % (D / 8);
+    *reinterpret_cast<uint4*>(sm + L::oA + SW::off(j, 16 * c8)) = sv[q];
   }
 #pragma unroll
   for (int q = 0; q < NWQ; ++q) {
@@ -1996,7 +2006,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
       const size_t recs_end = off_bytes(p.n_seqs) + (size_t)max_chunks(p.total_tokens, p.n_seqs, C) * p.h_v * Rec<T, C>::bytes;
       const SplitPlan sp = split_plan(1, p.total_tokens, p.n_seqs, p.h_v, D, C, p.emit_every, recs_end);
-      ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr};
+      ScanSplit ss{0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
       // 32- and 64-column workgroups: chain, output and mover waves
       constexpr unsigned narrow_threads = 64 * ((2 / kScan2Tiles) * (1 + kOutSplit<C>) + kMovers<C>);
       constexpr unsigned wide_threads = 64 * (4 / kScan2Tiles) * (1 + kOutSplit<C>);
@@ -2006,7 +2016,8 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
         // one long sequence: two segments side by side
         float* st = reinterpret_cast<float*>(ws + sp.o_state);
         const size_t hs = (size_t)p.h_v * D * D;
-        ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w)};
+        ss = ScanSplit{1, sp.m, st, st + hs, st + 2 * hs, reinterpret_cast<__bf16*>(ws + sp.o_w),
+                       reinterpret_cast<__bf16*>(ws + sp.o_smb)};
         const unsigned grid = (unsigned)(3 * p.h_v * (D / sp.cols));
         hipLaunchKernelGGL(sp.cols == 32 ? narrow : wide, dim3(grid), dim3(sp.cols == 32 ? narrow_threads : wide_threads),
                            0, stream, p, static_cast<const unsigned char*>(ws), ss);
