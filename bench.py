@@ -174,7 +174,7 @@ def run_prefill(name, steps, warmup, do_cpu, cpu_tokens):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(f"prefill_{name}_traffic.md", "prefill.hip"),
-                     "kernel": "gdn_prefill (plan_kernel, prep_kernel, scan2_kernel; join_kernel after a split scan)",
+                     "kernel": "gdn_prefill (prep_kernel, scan2_kernel; plan_kernel with cu_seqlens, join_kernel after a split scan)",
                      "flops_per_launch": flops},
         "config": {"workload": f"{name}: B={inp['n_seqs']} T={T} h_qk={hq} h_v={hv} d={d} "
                                f"chunk={cfg['chunk']} conv{cfg['width']}+SiLU, bf16 io, fp32 state",
