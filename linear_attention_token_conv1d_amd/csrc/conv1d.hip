@@ -4,8 +4,8 @@
 // bf16 vector) by kTile consecutive tokens of the packed array.  Each thread
 // walks its tokens in order keeping the last W-1 inputs of its 8 channels in
 // registers, so every input is read once from HBM (plus a W-1 token halo per
-// tile) and every output written once.  x loads for 8 tokens are issued
-// together before their use.  Sequence starts inside a tile reset the window
+// tile) and every output written once.  x loads for kBatch tokens are
+// issued together before their use.  Sequence starts inside a tile reset the window
 // from that sequence's conv state (or zeros), so nothing leaks across
 // sequences.
 //
@@ -19,8 +19,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;   // tokens per workgroup
-constexpr int kBatch = 8;   // tokens whose loads are issued together
+constexpr int kTile = 16;   // tokens per workgroup (many workgroups keep more loads in flight)
+constexpr int kBatch = 4;   // tokens whose loads are issued together
 
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> { using type = uint4; };
