@@ -16,12 +16,14 @@
 // chunk; only e^{x} with x <= 0 is ever formed.
 //
 // Launches on the caller's stream:
-//  plan  one workgroup: chunk offsets of every packed sequence and the scan
-//        order (longest sequence first), in the workspace.
+//  plan  with cu_seqlens only, one workgroup: chunk offsets of every packed
+//        sequence and the scan order (longest sequence first), in the
+//        workspace (one sequence needs none: PlanView).
 //  prep  one workgroup per (chunk, group of V heads sharing a QK head), all
 //        chunks in parallel: row norms, the two Gram matrices (MFMA), the
-//        decay masks, the UT solve T = (I + A)^-1 (fp32 MFMA) and the chunk
-//        operands Tb, P and the per-token scalars, written to workspace.
+//        decay masks, the UT solve T = (I + A)^-1 (forward substitution on
+//        the diagonal blocks, fp32 MFMA below them) and the chunk operands
+//        Tb, P and the per-token scalars, written to workspace.
 //  scan  bf16: scan2_kernel, one workgroup per (sequence, V head, block of
 //        32 or 64 d_v columns) walking its chunks in order.  Chain waves own
 //        16 columns of the fp32 state S^T each in MFMA accumulators for the
@@ -30,9 +32,10 @@
 //        MFMA (a 16x16 accumulator holds rows 4g+i, g = lane/16, of column
 //        lane%16: a valid B fragment once the A operand reads its k index in
 //        the same order), so the serial chain never leaves registers.  Output
-//        waves form O^T from the published state and U and move the next
-//        chunk into the second LDS buffer by direct-to-LDS loads.  fp32:
-//        scan_kernel, the same math in four waves.
+//        waves form O^T from the published state and U; mover waves (else
+//        the output waves) bring the next chunk into the second LDS buffer
+//        by direct-to-LDS loads.  fp32: scan_kernel, the same math in four
+//        waves.
 //  join  only after a split scan of one long sequence (see split_plan):
 //        adds S_m w_t to the second segment's outputs and forms the final
 //        state.
@@ -1221,7 +1224,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 }
 
 // ------------------------------------------------------- split-role scan
-// bf16 scan with two wave roles per workgroup, for a block of 32 or 64 d_v
+// bf16 scan with three wave roles per workgroup, for a block of 32 or 64 d_v
 // columns of one (sequence, V head):
 //  chain waves (one per 16 columns) own their columns of the fp32 state S^T
 //    in accumulator tiles and run the serial part of a chunk:  X1 = K S^T,
@@ -1230,12 +1233,14 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 //    compute the chunk's output O^T = (S Q^T) diag(scale gamma rq) + U^T P^T
 //    from the state and U that the chain waves publish in LDS as bf16, and
 //    store O straight from their accumulators (a lane holds 4 consecutive
-//    columns of one token).
-// The roles share the SIMDs, so one role's MFMA and LDS work fills the
-// other's dependency stalls.  The output waves issue all of the next chunk's
-// direct-to-LDS loads at the start of a chunk.  Per chunk: barrier B1 after U
-// is published (LDS only: the loads stay in flight), and B2 at the end (the
-// next chunk has landed, the new state is published).
+//    columns of one token);
+//  mover waves (32-column workgroups only) issue the next chunk's
+//    direct-to-LDS loads and the L2 prefetch; without them the output waves
+//    issue the loads.
+// Waves are placed on SIMDs by role (see the kernel).  Per chunk: barrier B1
+// once U is published and the chain has updated its registers (LDS only: the
+// loads stay in flight), and B2 at the end (the next chunk has landed, the
+// new state is published).
 template <int D, int C, int COLS>
 struct Scan2Layout {
   static constexpr int NT = C / 16, DT = D / 16;
