@@ -33,7 +33,13 @@ Readings where the pages are silent:
   * g is log(alpha) and beta is the write strength, both given per token and
     per V head.
 
-Parity pins for every function live in tests/test_oracle_pins.py.
+The *_backward functions are reverse-mode differentiation of the same
+definitions, written out step by step (each forward step taken back in the
+opposite order), for the training row: gradients of a scalar loss with
+respect to every input, given its gradients with respect to every output.
+
+Parity pins for every function live in tests/test_oracle_pins.py and
+tests/test_oracle_backward_pins.py.
 """
 from __future__ import annotations
 
@@ -51,6 +57,9 @@ __all__ = [
     "chunked_gated_delta_rule",
     "unrolled_product_form",
     "round_to_bf16",
+    "l2_normalize_backward",
+    "gated_delta_rule_backward",
+    "causal_conv1d_backward",
 ]
 
 
@@ -323,3 +332,157 @@ def round_to_bf16(a):
     u = a32.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ backward
+
+def l2_normalize_backward(x, d_xhat, eps=1e-6):
+    """Gradient through xhat = x / n, n = sqrt(sum(x^2) + eps), over the last
+    axis: dx = d_xhat / n - x (x . d_xhat) / n^3."""
+    x, d_xhat = _f64(x), _f64(d_xhat)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+    return d_xhat / n - x * np.sum(x * d_xhat, axis=-1, keepdims=True) / n ** 3
+
+
+def gated_delta_rule_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
+                              cu_seqlens=None, scale=1.0, l2norm_qk=True, eps=1e-6, erase=True,
+                              segment=16):
+    """Reverse-mode gradients of gated_delta_rule, token by token, in fp64.
+
+    Inputs as gated_delta_rule, plus d_o [T, H_v, d_v] (gradient of the loss
+    with respect to o) and d_final_state [N, H_v, d_v, d_k] or None (zero).
+    Returns dq, dk [T, H_qk, d_k], dv [T, H_v, d_v], dg, dbeta [T, H_v],
+    d_initial_state [N, H_v, d_v, d_k].
+
+    Each token's forward step, per V head with a = e^{g_t}:
+        Sd = a S_prev;  p = Sd k;  e = b (v - p);  S = Sd + e k^T;  o = scale S q
+    is taken back in the opposite order, with dS the gradient of S:
+        dS += scale do q^T;           dq = scale S^T do
+        de = dS k;  dk = dS^T e;      dSd = dS
+        dv = b de;  db = (v - p).de;  dp = -b de
+        dSd += dp k^T;                dk += Sd^T dp
+        da = <dSd, S_prev>;  dg = a da;  dS_prev = a dSd
+    (without erase, p = 0 and its two lines drop out).  The gradients of a QK
+    head add up over the V heads that read it, then pass through the L2 norm.
+    The states S_prev are recomputed from checkpoints every `segment` tokens.
+    """
+    q, k, v, g, beta, d_o = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta), _f64(d_o)
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    grp = h_v // h_qk
+    qk_of = np.arange(h_v) // grp
+    qn, kn = (l2_normalize(q, eps), l2_normalize(k, eps)) if l2norm_qk else (q, k)
+    b = _bounds(T, cu_seqlens)
+    N = len(b) - 1
+    S0 = np.zeros((N, h_v, d_v, d_k)) if initial_state is None else _f64(initial_state).copy()
+    dSf = np.zeros((N, h_v, d_v, d_k)) if d_final_state is None else _f64(d_final_state)
+    dqn = np.zeros((T, h_v, d_k))
+    dkn = np.zeros((T, h_v, d_k))
+    dv = np.zeros((T, h_v, d_v))
+    dg = np.zeros((T, h_v))
+    db = np.zeros((T, h_v))
+    dS0 = np.zeros((N, h_v, d_v, d_k))
+
+    def step(S, t):
+        kt, a = kn[t, qk_of], np.exp(g[t])[:, None, None]
+        Sd = a * S
+        p = np.matmul(Sd, kt[:, :, None])[:, :, 0] if erase else np.zeros((h_v, d_v))
+        e = beta[t][:, None] * (v[t] - p)
+        return Sd, p, e, Sd + e[:, :, None] * kt[:, None, :]
+
+    for n in range(N):
+        s0, s1 = b[n], b[n + 1]
+        # forward sweep: the state before each segment's first token
+        starts = list(range(s0, s1, segment))
+        ckpt = []
+        S = S0[n].copy()
+        for st in starts:
+            ckpt.append(S.copy())
+            for t in range(st, min(st + segment, s1)):
+                S = step(S, t)[3]
+        dS = dSf[n].copy()
+        for st, Sst in reversed(list(zip(starts, ckpt))):
+            prev = [Sst]
+            for t in range(st, min(st + segment, s1)):
+                prev.append(step(prev[-1], t)[3])
+            for t in reversed(range(st, min(st + segment, s1))):
+                Sp = prev[t - st]
+                Sd, p, e, S = step(Sp, t)
+                kt, qt = kn[t, qk_of], qn[t, qk_of]
+                a = np.exp(g[t])
+                dS = dS + scale * d_o[t][:, :, None] * qt[:, None, :]
+                dqn[t] = scale * np.matmul(np.swapaxes(S, 1, 2), d_o[t][:, :, None])[:, :, 0]
+                de = np.matmul(dS, kt[:, :, None])[:, :, 0]
+                dk_t = np.matmul(np.swapaxes(dS, 1, 2), e[:, :, None])[:, :, 0]
+                dSd = dS
+                dv[t] = beta[t][:, None] * de
+                db[t] = np.sum((v[t] - p) * de, axis=1)
+                if erase:
+                    dp = -beta[t][:, None] * de
+                    dSd = dSd + dp[:, :, None] * kt[:, None, :]
+                    dk_t = dk_t + np.matmul(np.swapaxes(Sd, 1, 2), dp[:, :, None])[:, :, 0]
+                dkn[t] = dk_t
+                da = np.sum(dSd * Sp, axis=(1, 2))
+                dg[t] = a * da
+                dS = a[:, None, None] * dSd
+        dS0[n] = dS
+    # each QK head collects the gradients of the V heads that read it
+    dq = np.zeros((T, h_qk, d_k))
+    dk = np.zeros((T, h_qk, d_k))
+    for h in range(h_v):
+        dq[:, qk_of[h]] += dqn[:, h]
+        dk[:, qk_of[h]] += dkn[:, h]
+    if l2norm_qk:
+        dq = l2_normalize_backward(q, dq, eps)
+        dk = l2_normalize_backward(k, dk, eps)
+    return dq, dk, dv, dg, db, dS0
+
+
+def causal_conv1d_backward(x, weight, dy, bias=None, conv_state=None, cu_seqlens=None,
+                           activation="silu", d_new_state=None):
+    """Gradients of causal_conv1d: returns dx [T, C], dweight [C, W], dbias [C]
+    (None without bias) and d_conv_state [N, C, W-1].
+
+    Per sequence the padded history xp = (state ++ x) gives z = sum_j w_j
+    xp[j : j+L] (+ bias) and y = SiLU(z); new_state = the last W-1 rows of xp.
+    Back: dz = dy SiLU'(z), SiLU'(z) = s (1 + z (1 - s)) with s = sigmoid(z);
+    dxp[j : j+L] += w_j dz, dw_j = sum over tokens of dz xp[j : j+L],
+    dbias = sum of dz, and the new-state gradient adds onto the rows of xp it
+    copied.  dx and d_conv_state are the two parts of dxp.
+    """
+    x, weight, dy = _f64(x), _f64(weight), _f64(dy)
+    bias = _f64(bias)
+    T, C = x.shape
+    W = weight.shape[1]
+    b = _bounds(T, cu_seqlens)
+    N = len(b) - 1
+    state = np.zeros((N, C, W - 1)) if conv_state is None else _f64(conv_state)
+    dx = np.zeros((T, C))
+    dw = np.zeros((C, W))
+    dbias = np.zeros(C)
+    dstate = np.zeros((N, C, W - 1))
+    for n in range(N):
+        s, e = b[n], b[n + 1]
+        L = e - s
+        xp = np.concatenate([state[n].T, x[s:e]], axis=0)
+        z = np.zeros((L, C))
+        for j in range(W):
+            z += weight[:, j] * xp[j:j + L]
+        if bias is not None:
+            z += bias
+        if activation == "silu":
+            sg = 1.0 / (1.0 + np.exp(-z))
+            dz = dy[s:e] * sg * (1.0 + z * (1.0 - sg))
+        else:
+            assert activation in (None, "none")
+            dz = dy[s:e].copy()
+        dxp = np.zeros((W - 1 + L, C))
+        for j in range(W):
+            dxp[j:j + L] += weight[:, j] * dz
+            dw[:, j] += np.sum(dz * xp[j:j + L], axis=0)
+        dbias += np.sum(dz, axis=0)
+        if d_new_state is not None:
+            dxp[L:] += _f64(d_new_state)[n].T
+        dx[s:e] = dxp[W - 1:]
+        dstate[n] = dxp[:W - 1].T
+    return dx, dw, (dbias if bias is not None else None), dstate
