@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -255,6 +255,128 @@ typedef struct gdn_decode_args {
 } gdn_decode_args;
 
 gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_prefill_backward -- gradients of gdn_prefill, for training through the
+ * chunked form ("Inside Qwen3.5", section 5: the gated delta rule layer is
+ * trained at scale; "DeltaNet explained", the chunkwise training form).
+ *
+ * Given the forward call's inputs and the gradients of a loss with respect to
+ * its outputs (d_o, d_final_state), writes the gradients with respect to q,
+ * k, v (before the in-call L2 norm when GDN_FLAG_L2NORM_QK is set), g, beta
+ * and the initial state.  It is reverse-mode differentiation of the same
+ * recurrence: per chunk the state-independent quantities are recomputed, the
+ * chunk-start states are rebuilt by a forward chain over the chunks, the
+ * state gradients run back over the chunks, and each chunk's own gradients
+ * follow from both.  Arithmetic is fp32 throughout (fp32 inputs are used as
+ * given, bf16 inputs are widened exactly).
+ *
+ *   flags, io_dtype, n_seqs, total_tokens, h_qk, h_v, d_k, d_v, chunk,
+ *   scale, q, k, v (with their strides), g, beta, initial_state, cu_seqlens:
+ *                exactly as passed to the forward gdn_prefill call.
+ *                chunk in {16, 32, 64}: the gradients do not depend on it
+ *                beyond rounding.
+ *   d_o          [T, h_v, d_v] in io_dtype, contiguous.
+ *   d_final_state [n_seqs, h_v, d_v, d_k] fp32, or NULL for zero.
+ *   dq, dk       [T, h_qk, d_k] in io_dtype with token strides dq_stride and
+ *                dk_stride; dv [T, h_v, d_v] with dv_stride.  They may be
+ *                column slices of one [T, C] buffer (the conv output's
+ *                gradient) and must not overlap any input.
+ *   dg, dbeta    [T, h_v] fp32.
+ *   d_initial_state [n_seqs, h_v, d_v, d_k] fp32, or NULL (not formed).
+ *   workspace    at least gdn_prefill_backward_workspace_size() bytes,
+ *                256-byte aligned; contents on entry are ignored.
+ * Errors as gdn_prefill; every output is written in full on success.
+ * ---------------------------------------------------------------------- */
+typedef struct gdn_prefill_backward_args {
+  uint32_t struct_size;
+  uint32_t flags;
+  int32_t io_dtype;
+  int32_t n_seqs;
+  int64_t total_tokens;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t chunk;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_stride;
+  int64_t k_stride;
+  int64_t v_stride;
+  const float* g;
+  const float* beta;
+  const float* initial_state;
+  const int32_t* cu_seqlens;
+  const void* d_o;
+  const float* d_final_state;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t dq_stride;
+  int64_t dk_stride;
+  int64_t dv_stride;
+  float* dg;
+  float* dbeta;
+  float* d_initial_state;
+  void* workspace;
+  size_t workspace_bytes;
+} gdn_prefill_backward_args;
+
+/* Bytes of workspace gdn_prefill_backward needs (pointers are not read);
+ * 0 when the arguments are invalid. */
+size_t gdn_prefill_backward_workspace_size(const gdn_prefill_backward_args* args);
+
+gdn_status gdn_prefill_backward(const gdn_prefill_backward_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gdn_conv1d_backward -- gradients of gdn_conv1d (same definition, "Inside
+ * Qwen3.5", section 5, and the conv state of "Mamba hybrid model selection",
+ * per-request memory section).
+ *
+ *   dtype, n_seqs, total_tokens, channels, width, activation, x, weight,
+ *   bias, cu_seqlens: as passed to the forward call.
+ *   conv_state   [n_seqs, C, W-1] in dtype: the state the forward call READ
+ *                (the forward overwrites its buffer, so keep a copy), or NULL
+ *                for zeros.
+ *   dy           [T, C] in dtype: gradient of the loss with respect to y.
+ *   d_new_state  [n_seqs, C, W-1] fp32 gradient with respect to the state the
+ *                forward call wrote, or NULL for zero.
+ *   dx           [T, C] in dtype; must not overlap any input.
+ *   dweight      [C, W] fp32;  dbias [C] fp32 or NULL (only with bias).
+ *   d_conv_state [n_seqs, C, W-1] fp32, or NULL (not formed).
+ *   workspace    at least gdn_conv1d_backward_workspace_size() bytes,
+ *                256-byte aligned (partial weight sums over token tiles,
+ *                added in a fixed order, so results are deterministic).
+ * ---------------------------------------------------------------------- */
+typedef struct gdn_conv1d_backward_args {
+  uint32_t struct_size;
+  int32_t dtype;
+  int32_t n_seqs;
+  int32_t channels;
+  int64_t total_tokens;
+  int32_t width;
+  int32_t activation;
+  const void* x;
+  const void* weight;
+  const void* bias;
+  const void* conv_state;
+  const int32_t* cu_seqlens;
+  const void* dy;
+  const float* d_new_state;
+  void* dx;
+  float* dweight;
+  float* dbias;
+  float* d_conv_state;
+  void* workspace;
+  size_t workspace_bytes;
+} gdn_conv1d_backward_args;
+
+size_t gdn_conv1d_backward_workspace_size(const gdn_conv1d_backward_args* args);
+
+gdn_status gdn_conv1d_backward(const gdn_conv1d_backward_args* args, void* stream);
 
 /* Diagnostics. */
 const char* gdn_status_string(gdn_status status);

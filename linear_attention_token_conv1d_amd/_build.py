@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libgdn.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.cpp", "conv1d.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["gdn_api.cpp", "conv1d.hip", "decode.hip", "prefill.hip", "backward.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

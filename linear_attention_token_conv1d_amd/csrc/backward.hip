@@ -1,0 +1,847 @@
+// Backward pass of the token mixer, for training: gradients of the chunked
+// gated delta rule (gdn_prefill) and of the causal conv (gdn_conv1d).
+//
+// Per chunk of one sequence and one V head (K^, Q^ the normalised keys and
+// queries, rows past the chunk's end padded with zeros and beta = g = 0, so
+// every chunk is a full C rows), the forward is ("Inside Qwen3.5", sections
+// 4-5; "DeltaNet explained", the chunkwise WY form):
+//   G = cumsum(g), gam = e^G, e_j = e^{G_{C-1} - G_j}, Gam_rj = e^{G_r - G_j}
+//   A = strict_lower(beta_r Gam_rj K^_r.K^_j),  T = (I + A)^-1
+//   W = T diag(beta gam) K^,  Ut = T diag(beta) V,  U = Ut - W X
+//   Pm = scale lower_incl(Gam o Q^K^T),  O = scale diag(gam) Q^ X + Pm U
+//   X' = gam_{C-1} X + (diag(e) K^)^T U
+// with X = S^T (d_k x d_v) the state at the chunk start.  The backward takes
+// these steps back in the opposite order:
+//   1. recompute everything that does not depend on the state (batched
+//      products over (chunk, head));
+//   2. rebuild the chunk-start states X_c by running the chain forward;
+//   3. run the state gradient back over the chunks:
+//        dU = Pm^T dO + diag(e) K^ dX',  dX = gam dX' + (scale diag(gam) Q^)^T dO - W^T dU
+//   4. per chunk, the gradients of every chunk-local quantity, down to
+//      dK^, dQ^, dV, dbeta and dG (then dg is the reverse cumulative sum of dG);
+//   5. dK^ and dQ^ of a QK head add up over the V heads that read it and
+//      pass back through the L2 norm.
+// Every product runs in fp32.  The design favours simple, independently
+// checkable stages: a batched fp32 GEMM with LDS tiles, two chain launches,
+// and elementwise kernels that combine the pieces.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+// ------------------------------------------------------------- workspace
+// Header: [0] number of chunks in use, then chunk offsets per sequence
+// (n_seqs + 1), then one (sequence, first token, rows) record per chunk.
+// Then fp32 arrays, each [max_chunks][heads][rows][cols]:
+//   per QK head: Kn, Qn (C x D), KK, QK (C x C)
+//   per V head:  vec (8 x C), five C x C, sixteen C x D and three D x D
+enum { kVecG = 0, kVecGam, kVecE, kVecBeta, kVecDGx, kVecDBx, kNVec = 8 };
+enum { cT = 0, cPm, cDPm, cDT, cM1, kNCC };
+enum { mBK = 0, mEK, mGQ, mBV, mDO, mW, mUt, mU, mDU, mPdO, mDW, mDOX, mUdX, mTdW, mDKn, mDQn, kNCD };
+enum { xXs = 0, xDXs, xZ, kNDD };
+
+struct ChunkRec {
+  int n, t0, len, pad;
+};
+
+struct BwdWs {
+  int* nc;
+  int* co;
+  ChunkRec* ct;
+  float *Kn, *Qn, *KK, *QK;
+  float* vec;
+  float* cc[kNCC];
+  float* cd[kNCD];
+  float* dd[kNDD];
+};
+
+__host__ __device__ inline size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct BwdSizes {
+  int64_t ncm;
+  size_t o_ct, hdr, total;
+};
+
+inline BwdSizes bwd_sizes(int64_t T, int n_seqs, int h_qk, int h_v, int D, int C) {
+  BwdSizes s;
+  s.ncm = T / C + n_seqs;
+  s.o_ct = (4 * (4 + (size_t)n_seqs + 1) + 15) / 16 * 16;
+  s.hdr = a256(s.o_ct + sizeof(ChunkRec) * (size_t)s.ncm);
+  const size_t cq = (size_t)s.ncm * h_qk, cv = (size_t)s.ncm * h_v;
+  size_t f = 0;
+  f += a256(cq * C * D * 4) * 2 + a256(cq * C * C * 4) * 2;
+  f += a256(cv * kNVec * C * 4);
+  f += a256(cv * C * C * 4) * kNCC;
+  f += a256(cv * C * D * 4) * kNCD;
+  f += a256(cv * D * D * 4) * kNDD;
+  s.total = s.hdr + f;
+  return s;
+}
+
+inline BwdWs bwd_carve(void* ws, int64_t T, int n_seqs, int h_qk, int h_v, int D, int C) {
+  const BwdSizes s = bwd_sizes(T, n_seqs, h_qk, h_v, D, C);
+  char* b = static_cast<char*>(ws);
+  BwdWs w;
+  w.nc = reinterpret_cast<int*>(b);
+  w.co = w.nc + 4;
+  w.ct = reinterpret_cast<ChunkRec*>(b + s.o_ct);
+  size_t o = s.hdr;
+  const size_t cq = (size_t)s.ncm * h_qk, cv = (size_t)s.ncm * h_v;
+  auto take = [&](size_t bytes) {
+    float* p = reinterpret_cast<float*>(b + o);
+    o += a256(bytes);
+    return p;
+  };
+  w.Kn = take(cq * C * D * 4);
+  w.Qn = take(cq * C * D * 4);
+  w.KK = take(cq * C * C * 4);
+  w.QK = take(cq * C * C * 4);
+  w.vec = take(cv * kNVec * C * 4);
+  for (int i = 0; i < kNCC; ++i) w.cc[i] = take(cv * C * C * 4);
+  for (int i = 0; i < kNCD; ++i) w.cd[i] = take(cv * C * D * 4);
+  for (int i = 0; i < kNDD; ++i) w.dd[i] = take(cv * D * D * 4);
+  return w;
+}
+
+// Sequence of packed token t: the last n with cu[n] <= t (which skips empty
+// sequences that start at t, and has cu[n + 1] > t since t < cu[n_seqs]).
+__device__ inline int seq_index(const int32_t* cu, int n_seqs, int64_t t) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ plan
+// One workgroup: chunk offsets of every sequence (exclusive prefix sum of
+// ceil(len / C)), then one record per chunk.
+__global__ __launch_bounds__(256) void bwd_plan_kernel(BwdWs w, const int32_t* cu, int n_seqs, int64_t T,
+                                                       int C, int64_t ncm) {
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int n = 0; n < n_seqs; ++n) {
+      w.co[n] = acc;
+      const int len = cu ? cu[n + 1] - cu[n] : (int)T;
+      acc += (len + C - 1) / C;
+    }
+    w.co[n_seqs] = acc;
+    w.nc[0] = acc;
+  }
+  __syncthreads();
+  for (int n = threadIdx.x; n < n_seqs; n += blockDim.x) {
+    const int s = cu ? cu[n] : 0, len = cu ? cu[n + 1] - s : (int)T;
+    for (int c = 0, gc = w.co[n]; c * C < len; ++c, ++gc) w.ct[gc] = ChunkRec{n, s + c * C, min(C, len - c * C), 0};
+  }
+  for (int64_t gc = w.co[n_seqs] + threadIdx.x; gc < ncm; gc += blockDim.x) w.ct[gc] = ChunkRec{0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------- batched GEMM
+// C[b] = alpha op(A[b]) op(B[b]) (+ C[b] when accum), fp32, for every chunk
+// b = (chunk, head) in use.  op(A) is M x K (A row-major M x K, or K x M when
+// ta), op(B) is K x N (B row-major K x N, or N x K when tb).  A QK-head
+// operand is shared by the V heads of its group (head index / hdiv).
+struct BG {
+  const float* A;
+  const float* B;
+  float* Cm;
+  int M, N, K, lda, ldb, ldc;
+  int64_t a_sc, a_sh, b_sc, b_sh, c_sc, c_sh;
+  int a_hdiv, b_hdiv, H, ta, tb, accum;
+  float alpha;
+  const int* nc;
+};
+
+__global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
+  const int z = blockIdx.x, gc = z / p.H, h = z % p.H;
+  if (gc >= *p.nc) return;
+  const int tiles_n = (p.N + 63) / 64;
+  const int m0 = (blockIdx.y / tiles_n) * 64, n0 = (blockIdx.y % tiles_n) * 64;
+  const float* A = p.A + gc * p.a_sc + (int64_t)(h / p.a_hdiv) * p.a_sh;
+  const float* B = p.B + gc * p.b_sc + (int64_t)(h / p.b_hdiv) * p.b_sh;
+  float* Cm = p.Cm + gc * p.c_sc + (int64_t)h * p.c_sh;
+  __shared__ float As[16][68], Bs[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    for (int e = tid; e < 1024; e += 256) {
+      const int mm = p.ta ? (e & 63) : (e >> 4), kk = p.ta ? (e >> 6) : (e & 15);
+      const int m = m0 + mm, k = k0 + kk;
+      float v = 0.f;
+      if (m < p.M && k < p.K) v = p.ta ? A[(int64_t)k * p.lda + m] : A[(int64_t)m * p.lda + k];
+      As[kk][mm] = v;
+    }
+    for (int e = tid; e < 1024; e += 256) {
+      const int nn = p.tb ? (e >> 4) : (e & 63), kk = p.tb ? (e & 15) : (e >> 6);
+      const int n = n0 + nn, k = k0 + kk;
+      float v = 0.f;
+      if (n < p.N && k < p.K) v = p.tb ? B[(int64_t)n * p.ldb + k] : B[(int64_t)k * p.ldb + n];
+      Bs[kk][nn] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < p.M && n < p.N) {
+        float* c = Cm + (int64_t)m * p.ldc + n;
+        const float v = p.alpha * acc[i][j];
+        *c = p.accum ? *c + v : v;
+      }
+    }
+}
+
+// ------------------------------------------------------- stage: Kn, Qn
+// Per (chunk, QK head): the normalised key and query rows, zero past the end.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, const T* k, int64_t qs,
+                                                           int64_t ks, int h_qk, int D, int C, int l2norm) {
+  const int gc = blockIdx.x / h_qk, hq = blockIdx.x % h_qk;
+  if (gc >= *w.nc) return;
+  const ChunkRec cr = w.ct[gc];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* Kn = w.Kn + ((int64_t)gc * h_qk + hq) * C * D;
+  float* Qn = w.Qn + ((int64_t)gc * h_qk + hq) * C * D;
+  for (int r = wave; r < C; r += 4) {
+    for (int which = 0; which < 2; ++which) {
+      const T* src = which ? q : k;
+      float* dst = which ? Qn : Kn;
+      float v[2] = {0.f, 0.f};
+      if (r < cr.len)
+        for (int i = 0; i < D / 64; ++i)
+          v[i] = to_f32(src[(int64_t)(cr.t0 + r) * (which ? qs : ks) + (int64_t)hq * D + lane + 64 * i]);
+      float ss = 0.f;
+      for (int i = 0; i < D / 64; ++i) ss += v[i] * v[i];
+      ss = wave_sum(ss);
+      const float rn = (l2norm && r < cr.len) ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+      for (int i = 0; i < D / 64; ++i) dst[(int64_t)r * D + lane + 64 * i] = v[i] * rn;
+    }
+  }
+}
+
+// ----------------------------------------- prep: gates, T, Pm, scaled rows
+// Per (chunk, V head): G, gam, e, beta; T = (I + A)^-1 by forward
+// substitution; Pm; and the row-scaled operands BK, EK, GQ, BV and dO.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, const float* beta, const T* v,
+                                                       int64_t vs, const T* d_o, int h_qk, int h_v, int D,
+                                                       int C, float scale, int erase) {
+  const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v;
+  if (gc >= *w.nc) return;
+  const ChunkRec cr = w.ct[gc];
+  const int hq = h / (h_v / h_qk), tid = threadIdx.x;
+  const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
+  __shared__ float sG[64], sGam[64], sE[64], sB[64];
+  __shared__ float sA[64][65];
+  __shared__ float sT[64][65];
+  if (tid == 0) {
+    float G = 0.f;
+    for (int r = 0; r < C; ++r) {
+      const bool in = r < cr.len;
+      G += in ? g[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+      sG[r] = G;
+      sB[r] = in ? beta[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+    }
+  }
+  __syncthreads();
+  float* vec = w.vec + bv * kNVec * C;
+  for (int r = tid; r < C; r += blockDim.x) {
+    sGam[r] = expf(sG[r]);
+    sE[r] = expf(sG[C - 1] - sG[r]);
+    vec[kVecG * C + r] = sG[r];
+    vec[kVecGam * C + r] = sGam[r];
+    vec[kVecE * C + r] = sE[r];
+    vec[kVecBeta * C + r] = sB[r];
+  }
+  const float* KK = w.KK + bq * C * C;
+  const float* QK = w.QK + bq * C * C;
+  float* Pm = w.cc[cPm] + bv * C * C;
+  for (int e = tid; e < C * C; e += blockDim.x) {
+    const int r = e / C, j = e % C;
+    sA[r][j] = (erase && j < r) ? sB[r] * expf(sG[r] - sG[j]) * KK[e] : 0.f;
+    Pm[e] = j <= r ? scale * expf(sG[r] - sG[j]) * QK[e] : 0.f;
+  }
+  __syncthreads();
+  // (I + A) T = I, A strictly lower: row i of T is e_i - sum_{j<i} A_ij T_j
+  for (int i = 0; i < C; ++i) {
+    if (tid < C) {
+      float s = i == tid ? 1.f : 0.f;
+      for (int j = 0; j < i; ++j) s -= sA[i][j] * sT[j][tid];
+      sT[i][tid] = s;
+    }
+    __syncthreads();
+  }
+  float* Tm = w.cc[cT] + bv * C * C;
+  for (int e = tid; e < C * C; e += blockDim.x) Tm[e] = sT[e / C][e % C];
+  const float* Kn = w.Kn + bq * C * D;
+  const float* Qn = w.Qn + bq * C * D;
+  float* BK = w.cd[mBK] + bv * C * D;
+  float* EK = w.cd[mEK] + bv * C * D;
+  float* GQ = w.cd[mGQ] + bv * C * D;
+  float* BV = w.cd[mBV] + bv * C * D;
+  float* DO = w.cd[mDO] + bv * C * D;
+  for (int e = tid; e < C * D; e += blockDim.x) {
+    const int r = e / D, c = e % D;
+    const bool in = r < cr.len;
+    const float kn = Kn[e];
+    BK[e] = erase ? sB[r] * sGam[r] * kn : 0.f;
+    EK[e] = sE[r] * kn;
+    GQ[e] = scale * sGam[r] * Qn[e];
+    const int64_t tok = (int64_t)(cr.t0 + r);
+    BV[e] = in ? sB[r] * to_f32(v[tok * vs + (int64_t)h * D + c]) : 0.f;
+    DO[e] = in ? to_f32(d_o[(tok * h_v + h) * D + c]) : 0.f;
+  }
+}
+
+// ----------------------------------------------------------------- chain
+// One workgroup per (sequence, V head, 16 state columns).  Per chunk, with Y
+// the D x 16 state slice:
+//   forward: store Y as X_c;   U  = Ut  - W Y;         Y = gam Y + EK^T U
+//   reverse: store Y as dX'_c; dU = PdO + EK Y;        Y = gam Y + Z - W^T dU
+// (chunks in reverse order).  Y starts from the initial state (forward) or
+// the final-state gradient (reverse); the reverse chain's last Y is the
+// initial-state gradient.
+constexpr int kCW = 16;
+template <bool REV, int D>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdWs w, const float* s_in, float* s_out, int h_v,
+                                                        int C) {
+  const int n = blockIdx.x / h_v, h = blockIdx.x % h_v, col0 = blockIdx.y * kCW, tid = threadIdx.x;
+  extern __shared__ float lds[];
+  float* P1 = lds;             // C x D
+  float* P2 = P1 + C * D;      // C x D
+  float* Y = P2 + C * D;       // D x 16
+  float* Uv = Y + D * kCW;     // C x 16
+  for (int e = tid; e < D * kCW; e += 256) {
+    const int k = e / kCW, c = e % kCW;
+    Y[e] = s_in ? s_in[(((int64_t)n * h_v + h) * D + col0 + c) * D + k] : 0.f;
+  }
+  const int c_lo = w.co[n], c_hi = w.co[n + 1];
+  constexpr int NPT = D / 16;             // state outputs per thread
+  constexpr int TPR = kCW / NPT;          // threads per state row
+  const int yk = tid / TPR, yc = (tid % TPR) * NPT;
+  for (int i = 0; i < c_hi - c_lo; ++i) {
+    const int gc = REV ? c_hi - 1 - i : c_lo + i;
+    const int64_t b = (int64_t)gc * h_v + h;
+    const float4* p1 = reinterpret_cast<const float4*>(w.cd[REV ? mEK : mW] + b * C * D);
+    const float4* p2 = reinterpret_cast<const float4*>(w.cd[REV ? mW : mEK] + b * C * D);
+    __syncthreads();  // the previous chunk is done with P1, P2, Uv and Y
+    for (int e = tid; e < C * D / 4; e += 256) {
+      reinterpret_cast<float4*>(P1)[e] = p1[e];
+      reinterpret_cast<float4*>(P2)[e] = p2[e];
+    }
+    float* ys = w.dd[REV ? xDXs : xXs] + b * D * D;
+    for (int e = tid; e < D * kCW; e += 256) ys[(int64_t)(e / kCW) * D + col0 + e % kCW] = Y[e];
+    __syncthreads();
+    // R1 = P1 Y, then U = Vb -/+ R1 (C x 16)
+    const float* vb = w.cd[REV ? mPdO : mUt] + b * C * D;
+    float* uo = w.cd[REV ? mDU : mU] + b * C * D;
+    for (int e = tid; e < C * (kCW / 4); e += 256) {
+      const int r = e / (kCW / 4), c4 = (e % (kCW / 4)) * 4;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int k = 0; k < D; ++k) {
+        const float pk = P1[r * D + k];
+        const float4 y = *reinterpret_cast<const float4*>(&Y[k * kCW + c4]);
+        a0 = fmaf(pk, y.x, a0);
+        a1 = fmaf(pk, y.y, a1);
+        a2 = fmaf(pk, y.z, a2);
+        a3 = fmaf(pk, y.w, a3);
+      }
+      const float4 v = *reinterpret_cast<const float4*>(vb + (int64_t)r * D + col0 + c4);
+      const float4 u = REV ? make_float4(v.x + a0, v.y + a1, v.z + a2, v.w + a3)
+                           : make_float4(v.x - a0, v.y - a1, v.z - a2, v.w - a3);
+      *reinterpret_cast<float4*>(&Uv[r * kCW + c4]) = u;
+      *reinterpret_cast<float4*>(uo + (int64_t)r * D + col0 + c4) = u;
+    }
+    __syncthreads();
+    // Y = gam Y +/- P2^T U (+ Z)
+    const float gam = w.vec[b * kNVec * C + kVecGam * C + C - 1];
+    float acc[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) acc[j] = 0.f;
+    for (int r = 0; r < C; ++r) {
+      const float pk = P2[r * D + yk];
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) acc[j] = fmaf(pk, Uv[r * kCW + yc + j], acc[j]);
+    }
+    if constexpr (REV) {
+      const float* z = w.dd[xZ] + b * D * D + (int64_t)yk * D + col0 + yc;
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) Y[yk * kCW + yc + j] = gam * Y[yk * kCW + yc + j] + z[j] - acc[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) Y[yk * kCW + yc + j] = gam * Y[yk * kCW + yc + j] + acc[j];
+    }
+  }
+  if (REV && s_out) {
+    __syncthreads();
+    for (int e = tid; e < D * kCW; e += 256) {
+      const int k = e / kCW, c = e % kCW;
+      s_out[(((int64_t)n * h_v + h) * D + col0 + c) * D + k] = Y[e];
+    }
+  }
+}
+
+// ------------------------------------------- C x C gradient combination
+// Per (chunk, V head), from dPm and dA = -T^T dT T^T:
+//   dQK  = scale Gam o dPm (lower incl.)            -> written over dPm
+//   dKK  = beta_r Gam o dA (strict lower), stored as dKK + dKK^T -> over M1
+//   Gam_rj dGam_rj (from Pm and A) summed into dG: + over rows, - over columns
+//   dbeta_r from A: sum_j Gam_rj KK_rj dA_rj
+__global__ __launch_bounds__(256) void bwd_cc_kernel(BwdWs w, int h_qk, int h_v, int C, float scale, int erase) {
+  const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
+  if (gc >= *w.nc) return;
+  const int hq = h / (h_v / h_qk);
+  const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
+  __shared__ float sGG[64][65], sDK[64][65], sG[64], sB[64];
+  float* vec = w.vec + bv * kNVec * C;
+  for (int r = tid; r < C; r += 256) {
+    sG[r] = vec[kVecG * C + r];
+    sB[r] = vec[kVecBeta * C + r];
+  }
+  __syncthreads();
+  const float* KK = w.KK + bq * C * C;
+  const float* QK = w.QK + bq * C * C;
+  float* dPm = w.cc[cDPm] + bv * C * C;
+  const float* dA = w.cc[cDT] + bv * C * C;
+  for (int e = tid; e < C * C; e += 256) {
+    const int r = e / C, j = e % C;
+    const float gm = j <= r ? expf(sG[r] - sG[j]) : 0.f;
+    const float dp = dPm[e];
+    float gg = scale * gm * QK[e] * dp, dk = 0.f;
+    if (erase && j < r) {
+      const float da = dA[e];
+      dk = sB[r] * gm * da;
+      gg += dk * KK[e];
+    }
+    sGG[r][j] = gg;
+    sDK[r][j] = dk;
+    dPm[e] = scale * gm * dp;
+  }
+  __syncthreads();
+  float* sym = w.cc[cM1] + bv * C * C;
+  for (int e = tid; e < C * C; e += 256) sym[e] = sDK[e / C][e % C] + sDK[e % C][e / C];
+  for (int r = tid; r < C; r += 256) {
+    float row = 0.f, col = 0.f, db = 0.f;
+    for (int j = 0; j < C; ++j) {
+      row += sGG[r][j];
+      col += sGG[j][r];
+      if (erase && j < r) db += expf(sG[r] - sG[j]) * KK[(int64_t)r * C + j] * dA[(int64_t)r * C + j];
+    }
+    vec[kVecDGx * C + r] = row - col;
+    vec[kVecDBx * C + r] = db;
+  }
+}
+
+// --------------------------------------------------------- final, V head
+// Per (chunk, V head): dG, its reverse cumulative sum dg, dbeta, dv, and
+// the per-V-head parts of dK^ and dQ^ completed in place.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
+                                                          float* dg, float* dbeta, int h_qk, int h_v, int D, int C,
+                                                          float scale, int erase) {
+  const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
+  if (gc >= *w.nc) return;
+  const ChunkRec cr = w.ct[gc];
+  const int hq = h / (h_v / h_qk), lane = tid & 63, wave = tid >> 6;
+  const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
+  const float* vec = w.vec + bv * kNVec * C;
+  __shared__ float sDG[64], sDB[64], sU[64], sRed[4];
+  const float* GQ = w.cd[mGQ] + bv * C * D;
+  const float* DOX = w.cd[mDOX] + bv * C * D;
+  const float* TdW = w.cd[mTdW] + bv * C * D;
+  const float* Kn = w.Kn + bq * C * D;
+  const float* U = w.cd[mU] + bv * C * D;
+  const float* DU = w.cd[mDU] + bv * C * D;
+  const float* PdO = w.cd[mPdO] + bv * C * D;
+  const float* TdU = w.cd[mUt] + bv * C * D;  // T^T dU was written over Ut
+  for (int r = wave; r < C; r += 4) {
+    float a = 0.f, s = 0.f, u = 0.f, b1 = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      const int64_t e = (int64_t)r * D + c;
+      a += GQ[e] * DOX[e];
+      s += TdW[e] * Kn[e];
+      u += U[e] * (DU[e] - PdO[e]);
+      if (r < cr.len) b1 += to_f32(v[(int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c]) * TdU[e];
+    }
+    a = wave_sum(a);
+    s = wave_sum(s);
+    u = wave_sum(u);
+    b1 = wave_sum(b1);
+    if (lane == 0) {
+      const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r];
+      sDG[r] = a + (erase ? be * gm * s : 0.f) + vec[kVecDGx * C + r] - u;
+      sDB[r] = b1 + vec[kVecDBx * C + r] + (erase ? gm * s : 0.f);
+      sU[r] = u;
+    }
+  }
+  // <X, dX'> for the decay of the whole chunk
+  const float* Xs = w.dd[xXs] + bv * D * D;
+  const float* dXs = w.dd[xDXs] + bv * D * D;
+  float xd = 0.f;
+  for (int e = tid; e < D * D; e += 256) xd += Xs[e] * dXs[e];
+  xd = wave_sum(xd);
+  if (lane == 0) sRed[wave] = xd;
+  __syncthreads();
+  if (tid == 0) {
+    float us = 0.f;
+    for (int r = 0; r < C; ++r) us += sU[r];
+    sDG[C - 1] += us + vec[kVecGam * C + C - 1] * (sRed[0] + sRed[1] + sRed[2] + sRed[3]);
+    float run = 0.f;
+    for (int r = C - 1; r >= 0; --r) {
+      run += sDG[r];
+      sDG[r] = run;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < cr.len; r += 256) {
+    dg[(int64_t)(cr.t0 + r) * h_v + h] = sDG[r];
+    dbeta[(int64_t)(cr.t0 + r) * h_v + h] = sDB[r];
+  }
+  float* dKn = w.cd[mDKn] + bv * C * D;
+  float* dQn = w.cd[mDQn] + bv * C * D;
+  const float* UdX = w.cd[mUdX] + bv * C * D;
+  for (int e = tid; e < C * D; e += 256) {
+    const int r = e / D, c = e % D;
+    const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r];
+    dKn[e] += (erase ? be * gm * TdW[e] : 0.f) + vec[kVecE * C + r] * UdX[e];
+    dQn[e] += scale * gm * DOX[e];
+    if (r < cr.len) dv[(int64_t)(cr.t0 + r) * dvs + (int64_t)h * D + c] = from_f32<T>(be * TdU[e]);
+  }
+}
+
+// -------------------------------------------------------- final, QK head
+// Per (token, QK head): sum dK^ and dQ^ over the V heads of the group, then
+// back through x^ = x / sqrt(|x|^2 + eps): dx = dx^/n - x (x.dx^)/n^3.
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_final_qk_kernel(BwdWs w, const int32_t* cu, int n_seqs, const T* q,
+                                                          const T* k, int64_t qs, int64_t ks, T* dq, T* dk,
+                                                          int64_t dqs, int64_t dks, int h_qk, int h_v, int D,
+                                                          int C, int l2norm) {
+  const int64_t t = blockIdx.x;
+  const int hq = blockIdx.y, lane = threadIdx.x, grp = h_v / h_qk;
+  const int n = cu ? seq_index(cu, n_seqs, t) : 0;
+  const int64_t s = cu ? cu[n] : 0;
+  const int gc = w.co[n] + (int)((t - s) / C), r = (int)((t - s) % C);
+  for (int which = 0; which < 2; ++which) {
+    const float* src = which ? w.cd[mDQn] : w.cd[mDKn];
+    float d[2] = {0.f, 0.f}, x[2] = {0.f, 0.f};
+    for (int i = 0; i < D / 64; ++i) {
+      for (int j = 0; j < grp; ++j)
+        d[i] += src[(((int64_t)gc * h_v + hq * grp + j) * C + r) * D + lane + 64 * i];
+      x[i] = to_f32((which ? q : k)[t * (which ? qs : ks) + (int64_t)hq * D + lane + 64 * i]);
+    }
+    if (l2norm) {
+      float ss = 0.f, xd = 0.f;
+      for (int i = 0; i < D / 64; ++i) {
+        ss += x[i] * x[i];
+        xd += x[i] * d[i];
+      }
+      ss = wave_sum(ss);
+      xd = wave_sum(xd);
+      const float rn = 1.0f / sqrtf(ss + 1e-6f);
+      for (int i = 0; i < D / 64; ++i) d[i] = d[i] * rn - x[i] * xd * rn * rn * rn;
+    }
+    T* dst = which ? dq : dk;
+    const int64_t st = which ? dqs : dks;
+    for (int i = 0; i < D / 64; ++i) dst[t * st + (int64_t)hq * D + lane + 64 * i] = from_f32<T>(d[i]);
+  }
+}
+
+// ------------------------------------------------------------ conv backward
+// z = sum_j w_j xp[t + j] (+ b) over the padded history xp = (state ++ x) of
+// the token's sequence, y = act(z).  dz = dy act'(z); per token tile the
+// partial sums of dz xp[t + j] (weight) and dz (bias) go to the workspace.
+constexpr int kConvTT = 64;
+
+__device__ inline void seq_of(const int32_t* cu, int n_seqs, int64_t T, int64_t t, int& n, int64_t& s,
+                              int64_t& e) {
+  n = cu ? seq_index(cu, n_seqs, t) : 0;
+  s = cu ? cu[n] : 0;
+  e = cu ? cu[n + 1] : T;
+}
+
+template <typename T>
+__device__ inline float conv_xp(const T* x, const T* state, int64_t s, int n, int C, int W, int c, int64_t i) {
+  // padded-history entry i of sequence n (starting at token s), channel c
+  if (i < W - 1) return state ? to_f32(state[((int64_t)n * C + c) * (W - 1) + i]) : 0.f;
+  return to_f32(x[(s + i - (W - 1)) * C + c]);
+}
+
+template <typename T>
+__device__ inline float conv_dz(const T* x, const T* w, const T* bias, const T* state, const T* dy, int64_t s,
+                                int n, int C, int W, int c, int64_t u, int act) {
+  // gradient at pre-activation z of local token u of sequence n
+  float z = bias ? to_f32(bias[c]) : 0.f;
+  for (int j = 0; j < W; ++j) z = fmaf(to_f32(w[c * W + j]), conv_xp(x, state, s, n, C, W, c, u + j), z);
+  const float d = to_f32(dy[(s + u) * C + c]);
+  if (!act) return d;
+  const float sg = 1.0f / (1.0f + expf(-z));
+  return d * sg * (1.0f + z * (1.0f - sg));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* x, const T* w, const T* bias, const T* state,
+                                                          const T* dy, const int32_t* cu, int n_seqs, int64_t Tt,
+                                                          int C, int W, int act, float* part) {
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kConvTT, t1 = min(t0 + kConvTT, Tt);
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  int n = 0;
+  int64_t s = 0, e = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t == t0 || t >= e) seq_of(cu, n_seqs, Tt, t, n, s, e);
+    const int64_t u = t - s;
+    const float dz = conv_dz(x, w, bias, state, dy, s, n, C, W, c, u, act);
+    for (int j = 0; j < W; ++j) acc[j] = fmaf(dz, conv_xp(x, state, s, n, C, W, c, u + j), acc[j]);
+    acc[4] += dz;
+  }
+  float* p = part + ((int64_t)blockIdx.x * C + c) * 5;
+  for (int j = 0; j < 5; ++j) p[j] = acc[j];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const T* x, const T* w, const T* bias, const T* state,
+                                                          const T* dy, const float* dns, const int32_t* cu,
+                                                          int n_seqs, int64_t Tt, int C, int W, int act, T* dx) {
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kConvTT, t1 = min(t0 + kConvTT, Tt);
+  int n = 0;
+  int64_t s = 0, e = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t == t0 || t >= e) seq_of(cu, n_seqs, Tt, t, n, s, e);
+    const int64_t L = e - s, i = t - s + (W - 1);  // padded index of this token
+    float acc = 0.f;
+    for (int j = 0; j < W; ++j) {
+      const int64_t u = i - j;
+      if (u >= 0 && u < L) acc = fmaf(to_f32(w[c * W + j]), conv_dz(x, w, bias, state, dy, s, n, C, W, c, u, act), acc);
+    }
+    if (dns && i >= L) acc += dns[((int64_t)n * C + c) * (W - 1) + (i - L)];
+    dx[t * C + c] = from_f32<T>(acc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv_bwd_state_kernel(const T* x, const T* w, const T* bias, const T* state,
+                                                             const T* dy, const float* dns, const int32_t* cu,
+                                                             int n_seqs, int64_t Tt, int C, int W, int act,
+                                                             float* dstate) {
+  const int c = blockIdx.y * 256 + threadIdx.x, n = blockIdx.x;
+  if (c >= C) return;
+  const int64_t s = cu ? cu[n] : 0, L = (cu ? cu[n + 1] : Tt) - s;
+  for (int i = 0; i < W - 1; ++i) {
+    float acc = 0.f;
+    for (int j = 0; j < W; ++j) {
+      const int64_t u = i - j;
+      if (u >= 0 && u < L) acc = fmaf(to_f32(w[c * W + j]), conv_dz(x, w, bias, state, dy, s, n, C, W, c, u, act), acc);
+    }
+    if (dns && i >= L) acc += dns[((int64_t)n * C + c) * (W - 1) + (i - L)];
+    dstate[((int64_t)n * C + c) * (W - 1) + i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* part, int ntiles, int C, int W,
+                                                              float* dweight, float* dbias) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < ntiles; ++t)
+    for (int j = 0; j < 5; ++j) acc[j] += part[((int64_t)t * C + c) * 5 + j];
+  for (int j = 0; j < W; ++j) dweight[c * W + j] = acc[j];
+  if (dbias) dbias[c] = acc[4];
+}
+
+// ------------------------------------------------------------------ host
+struct Launcher {
+  hipStream_t st;
+  hipError_t err = hipSuccess;
+  void check() {
+    if (err == hipSuccess) err = hipGetLastError();
+  }
+};
+
+BG gemm(const float* A, const float* B, float* Cm, int M, int N, int K, int lda, int ldb, int ldc, int ta, int tb,
+        int64_t a_sc, int64_t a_sh, int a_hdiv, int64_t b_sc, int64_t b_sh, int b_hdiv, int64_t c_sc, int64_t c_sh,
+        int H, float alpha, int accum, const int* nc) {
+  return BG{A, B, Cm, M, N, K, lda, ldb, ldc, a_sc, a_sh, b_sc, b_sh, c_sc, c_sh, a_hdiv, b_hdiv, H, ta, tb,
+            accum, alpha, nc};
+}
+
+void run_gemm(Launcher& L, const BG& p, int64_t ncm) {
+  if (L.err != hipSuccess) return;
+  const dim3 grid((unsigned)(ncm * p.H), (unsigned)(((p.M + 63) / 64) * ((p.N + 63) / 64)));
+  hipLaunchKernelGGL(bgemm_kernel, grid, dim3(256), 0, L.st, p);
+  L.check();
+}
+
+template <typename T>
+hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t stream) {
+  const int C = p.chunk, hq = p.h_qk, hv = p.h_v, grp = hv / hq;
+  const BwdSizes sz = bwd_sizes(p.total_tokens, p.n_seqs, hq, hv, D, C);
+  const int64_t ncm = sz.ncm;
+  BwdWs w = bwd_carve(p.workspace, p.total_tokens, p.n_seqs, hq, hv, D, C);
+  Launcher L{stream};
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, stream, w, p.cu_seqlens, p.n_seqs, p.total_tokens, C,
+                     ncm);
+  L.check();
+  const T* q = static_cast<const T*>(p.q);
+  const T* k = static_cast<const T*>(p.k);
+  const T* v = static_cast<const T*>(p.v);
+  if (p.total_tokens > 0) {
+    hipLaunchKernelGGL(bwd_stage_qk_kernel<T>, dim3((unsigned)(ncm * hq)), dim3(256), 0, stream, w, q, k,
+                       p.q_stride, p.k_stride, hq, D, C, p.l2norm);
+    L.check();
+  }
+  const int64_t CC = (int64_t)C * C, CD = (int64_t)C * D, DD = (int64_t)D * D;
+  const int* nc = w.nc;
+  // Gram matrices per QK head: KK = Kn Kn^T, QK = Qn Kn^T
+  run_gemm(L, gemm(w.Kn, w.Kn, w.KK, C, C, D, D, D, C, 0, 1, hq * CD, CD, 1, hq * CD, CD, 1, hq * CC, CC, hq, 1.f, 0, nc), ncm);
+  run_gemm(L, gemm(w.Qn, w.Kn, w.QK, C, C, D, D, D, C, 0, 1, hq * CD, CD, 1, hq * CD, CD, 1, hq * CC, CC, hq, 1.f, 0, nc), ncm);
+  if (L.err != hipSuccess) return L.err;
+  if (p.total_tokens > 0) {
+    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3((unsigned)(ncm * hv)), dim3(256), 0, stream, w, p.g, p.beta, v,
+                       p.v_stride, static_cast<const T*>(p.d_o), hq, hv, D, C, p.scale, p.erase);
+    L.check();
+  }
+  // per V head (stride hv * size per chunk, size per head)
+  auto VH = [&](float* A, float* B, float* Cm, int M, int N, int K, int lda, int ldb, int ldc, int ta, int tb,
+                int64_t sa, int64_t sb, int64_t sc, float alpha, int accum, int b_hdiv = 1, int64_t b_chunk = -1) {
+    const int64_t bsc = b_chunk < 0 ? hv * sb : b_chunk;
+    run_gemm(L, gemm(A, B, Cm, M, N, K, lda, ldb, ldc, ta, tb, hv * sa, sa, 1, bsc, sb, b_hdiv, hv * sc, sc, hv,
+                     alpha, accum, nc),
+             ncm);
+  };
+  float** cc = w.cc;
+  float** cd = w.cd;
+  float** dd = w.dd;
+  // W = T BK, Ut = T BV
+  VH(cc[cT], cd[mBK], cd[mW], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
+  VH(cc[cT], cd[mBV], cd[mUt], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
+  if (L.err != hipSuccess) return L.err;
+  const size_t chain_lds = (2 * CD + (int64_t)D * kCW + (int64_t)C * kCW) * sizeof(float);
+  {
+    const void* ks[2] = {D == 64 ? reinterpret_cast<const void*>(bwd_chain_kernel<false, 64>)
+                                 : reinterpret_cast<const void*>(bwd_chain_kernel<false, 128>),
+                         D == 64 ? reinterpret_cast<const void*>(bwd_chain_kernel<true, 64>)
+                                 : reinterpret_cast<const void*>(bwd_chain_kernel<true, 128>)};
+    for (const void* f : ks) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chain_lds);
+      if (e != hipSuccess) return e;
+    }
+  }
+  const dim3 cgrid((unsigned)(p.n_seqs * hv), (unsigned)(D / kCW));
+  if (D == 64)
+    hipLaunchKernelGGL((bwd_chain_kernel<false, 64>), cgrid, dim3(256), chain_lds, stream, w, p.initial_state,
+                       (float*)nullptr, hv, C);
+  else
+    hipLaunchKernelGGL((bwd_chain_kernel<false, 128>), cgrid, dim3(256), chain_lds, stream, w, p.initial_state,
+                       (float*)nullptr, hv, C);
+  L.check();
+  // PdO = Pm^T dO, Z = GQ^T dO
+  VH(cc[cPm], cd[mDO], cd[mPdO], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);
+  VH(cd[mGQ], cd[mDO], dd[xZ], D, D, C, D, D, D, 1, 0, CD, CD, DD, 1.f, 0);
+  if (L.err != hipSuccess) return L.err;
+  if (D == 64)
+    hipLaunchKernelGGL((bwd_chain_kernel<true, 64>), cgrid, dim3(256), chain_lds, stream, w, p.d_final_state,
+                       p.d_initial_state, hv, C);
+  else
+    hipLaunchKernelGGL((bwd_chain_kernel<true, 128>), cgrid, dim3(256), chain_lds, stream, w, p.d_final_state,
+                       p.d_initial_state, hv, C);
+  L.check();
+  // chunk-local products
+  VH(cc[cT], cd[mDU], cd[mUt], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);      // TdU = T^T dU
+  VH(cd[mDU], dd[xXs], cd[mDW], C, D, D, D, D, D, 0, 1, CD, DD, CD, -1.f, 0);    // dW = -dU X^T
+  VH(cd[mDO], dd[xXs], cd[mDOX], C, D, D, D, D, D, 0, 1, CD, DD, CD, 1.f, 0);    // dOX = dO X^T
+  VH(cd[mU], dd[xDXs], cd[mUdX], C, D, D, D, D, D, 0, 1, CD, DD, CD, 1.f, 0);    // UdX = U dX'^T
+  VH(cd[mDO], cd[mU], cc[cDPm], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dPm = dO U^T
+  VH(cd[mDU], cd[mBV], cc[cDT], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dT = dU BV^T
+  VH(cd[mDW], cd[mBK], cc[cDT], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 1);     //    + dW BK^T
+  VH(cc[cDT], cc[cT], cc[cM1], C, C, C, C, C, C, 0, 1, CC, CC, CC, 1.f, 0);      // M1 = dT T^T
+  VH(cc[cT], cc[cM1], cc[cDT], C, C, C, C, C, C, 1, 0, CC, CC, CC, -1.f, 0);     // dA = -T^T M1
+  VH(cc[cT], cd[mDW], cd[mTdW], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);     // TdW = T^T dW
+  if (L.err != hipSuccess) return L.err;
+  if (p.total_tokens > 0) {
+    hipLaunchKernelGGL(bwd_cc_kernel, dim3((unsigned)(ncm * hv)), dim3(256), 0, stream, w, hq, hv, C, p.scale,
+                       p.erase);
+    L.check();
+  }
+  // dKn = dQK^T Qn + (dKK + dKK^T) Kn,  dQn = dQK Kn   (Kn, Qn per QK head)
+  VH(cc[cDPm], w.Qn, cd[mDKn], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0, grp, hq * CD);
+  VH(cc[cM1], w.Kn, cd[mDKn], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 1, grp, hq * CD);
+  VH(cc[cDPm], w.Kn, cd[mDQn], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0, grp, hq * CD);
+  if (L.err != hipSuccess) return L.err;
+  if (p.total_tokens > 0) {
+    hipLaunchKernelGGL(bwd_final_v_kernel<T>, dim3((unsigned)(ncm * hv)), dim3(256), 0, stream, w, v, p.v_stride,
+                       static_cast<T*>(p.dv), p.dv_stride, p.dg, p.dbeta, hq, hv, D, C, p.scale, p.erase);
+    L.check();
+    hipLaunchKernelGGL(bwd_final_qk_kernel<T>, dim3((unsigned)p.total_tokens, (unsigned)hq), dim3(64), 0, stream, w,
+                       p.cu_seqlens, p.n_seqs, q, k, p.q_stride, p.k_stride, static_cast<T*>(p.dq),
+                       static_cast<T*>(p.dk), p.dq_stride, p.dk_stride, hq, hv, D, C, p.l2norm);
+    L.check();
+  }
+  return L.err;
+}
+
+template <typename T>
+hipError_t conv_backward_impl(const ConvBwdParams& p, hipStream_t stream) {
+  const T* x = static_cast<const T*>(p.x);
+  const T* w = static_cast<const T*>(p.weight);
+  const T* b = static_cast<const T*>(p.bias);
+  const T* st = static_cast<const T*>(p.conv_state);
+  const T* dy = static_cast<const T*>(p.dy);
+  const int cg = (p.channels + 255) / 256;
+  const int ntiles = (int)((p.total_tokens + kConvTT - 1) / kConvTT);
+  float* part = static_cast<float*>(p.workspace);
+  if (ntiles > 0) {
+    hipLaunchKernelGGL(conv_bwd_dw_kernel<T>, dim3(ntiles, cg), dim3(256), 0, stream, x, w, b, st, dy, p.cu_seqlens,
+                       p.n_seqs, p.total_tokens, p.channels, p.width, p.act, part);
+    hipLaunchKernelGGL(conv_bwd_dx_kernel<T>, dim3(ntiles, cg), dim3(256), 0, stream, x, w, b, st, dy,
+                       p.d_new_state, p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.width, p.act,
+                       static_cast<T*>(p.dx));
+  }
+  hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3(cg), dim3(256), 0, stream, part, ntiles, p.channels, p.width,
+                     p.dweight, p.dbias);
+  if (p.d_conv_state)
+    hipLaunchKernelGGL(conv_bwd_state_kernel<T>, dim3(p.n_seqs, cg), dim3(256), 0, stream, x, w, b, st, dy,
+                       p.d_new_state, p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.width, p.act,
+                       p.d_conv_state);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_backward_workspace_bytes(int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d, int chunk) {
+  return bwd_sizes(total_tokens, n_seqs, h_qk, h_v, d, chunk).total;
+}
+
+hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int d, hipStream_t stream) {
+  return io_dtype == 1 ? prefill_backward_impl<__bf16>(p, d, stream) : prefill_backward_impl<float>(p, d, stream);
+}
+
+size_t conv1d_backward_workspace_bytes(int64_t total_tokens, int channels) {
+  const int64_t ntiles = (total_tokens + kConvTT - 1) / kConvTT;
+  return a256((size_t)(ntiles > 0 ? ntiles : 1) * channels * 5 * sizeof(float));
+}
+
+hipError_t launch_conv1d_backward(const ConvBwdParams& p, int dtype, hipStream_t stream) {
+  return dtype == 1 ? conv_backward_impl<__bf16>(p, stream) : conv_backward_impl<float>(p, stream);
+}
+
+}  // namespace gdn

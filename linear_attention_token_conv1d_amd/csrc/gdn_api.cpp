@@ -99,6 +99,113 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
   return GDN_OK;
 }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + nb && y < x + na;
+}
+
+gdn_status check_prefill_backward(const gdn_prefill_backward_args* a) {
+  const char* f = "gdn_prefill_backward";
+  if (!a) return fail(GDN_ERR_INVALID_ARG, "%s: args is NULL", f);
+  if (a->struct_size < sizeof(gdn_prefill_backward_args))
+    return fail(GDN_ERR_INVALID_ARG, "%s: struct_size %u < %zu", f, a->struct_size,
+                sizeof(gdn_prefill_backward_args));
+  if (!is_dtype(a->io_dtype)) return fail(GDN_ERR_INVALID_ARG, "%s: bad io_dtype %d", f, a->io_dtype);
+  if (a->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_NO_ERASE))
+    return fail(GDN_ERR_INVALID_ARG, "%s: unknown flags 0x%x", f, a->flags);
+  if (a->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "%s: n_seqs %d < 1", f, a->n_seqs);
+  if (a->total_tokens < 0 || a->total_tokens > INT32_MAX)
+    return fail(GDN_ERR_INVALID_ARG, "%s: total_tokens out of range", f);
+  if (a->h_qk < 1 || a->h_v < 1 || a->h_v % a->h_qk)
+    return fail(GDN_ERR_INVALID_ARG, "%s: h_v (%d) must be a positive multiple of h_qk (%d)", f, a->h_v, a->h_qk);
+  if (a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: d_k = d_v in {64, 128} required (got %d, %d)", f, a->d_k, a->d_v);
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: chunk %d not in {16, 32, 64}", f, a->chunk);
+  if (a->total_tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->d_o || !a->dq || !a->dk ||
+                              !a->dv || !a->dg || !a->dbeta))
+    return fail(GDN_ERR_INVALID_ARG, "%s: q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta are required", f);
+  if (a->n_seqs > 1 && !a->cu_seqlens)
+    return fail(GDN_ERR_INVALID_ARG, "%s: cu_seqlens is required when n_seqs > 1", f);
+  const int64_t hk = (int64_t)a->h_qk * a->d_k, hv = (int64_t)a->h_v * a->d_v;
+  if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hv || a->dq_stride < hk || a->dk_stride < hk ||
+      a->dv_stride < hv)
+    return fail(GDN_ERR_INVALID_ARG, "%s: token strides smaller than a token's heads", f);
+  const void* ptrs16[] = {a->q, a->k, a->v, a->d_o, a->dq, a->dk, a->dv, a->initial_state, a->d_final_state,
+                          a->d_initial_state};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return fail(GDN_ERR_ALIGNMENT, "%s: tensors must be 16-byte aligned", f);
+  if (!aligned(a->g, 4) || !aligned(a->beta, 4) || !aligned(a->cu_seqlens, 4) || !aligned(a->dg, 4) ||
+      !aligned(a->dbeta, 4))
+    return fail(GDN_ERR_ALIGNMENT, "%s: g, beta, dg, dbeta and cu_seqlens must be 4-byte aligned", f);
+  // outputs must not overlap inputs (extents from the first to the last element)
+  const size_t es = esize(a->io_dtype), T = (size_t)a->total_tokens;
+  const size_t nS = (size_t)a->n_seqs * a->h_v * a->d_v * a->d_k * 4;
+  auto span = [&](int64_t stride, int64_t width, size_t e) { return T ? ((T - 1) * stride + width) * e : 0; };
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{a->q, span(a->q_stride, hk, es)}, {a->k, span(a->k_stride, hk, es)},
+                   {a->v, span(a->v_stride, hv, es)}, {a->d_o, T * hv * es},
+                   {a->g, T * a->h_v * 4}, {a->beta, T * a->h_v * 4},
+                   {a->initial_state, a->initial_state ? nS : 0}, {a->d_final_state, a->d_final_state ? nS : 0}};
+  const R outs[] = {{a->dq, span(a->dq_stride, hk, es)}, {a->dk, span(a->dk_stride, hk, es)},
+                    {a->dv, span(a->dv_stride, hv, es)}, {a->dg, T * a->h_v * 4}, {a->dbeta, T * a->h_v * 4},
+                    {a->d_initial_state, a->d_initial_state ? nS : 0}};
+  for (const R& o : outs)
+    for (const R& i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return fail(GDN_ERR_INVALID_ARG, "%s: an output overlaps an input", f);
+  const size_t need = gdn::prefill_backward_workspace_bytes(a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->d_k,
+                                                            a->chunk);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes required", f, need);
+  if (!aligned(a->workspace, 256)) return fail(GDN_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", f);
+  return GDN_OK;
+}
+
+gdn_status check_conv1d_backward(const gdn_conv1d_backward_args* a) {
+  const char* f = "gdn_conv1d_backward";
+  if (!a) return fail(GDN_ERR_INVALID_ARG, "%s: args is NULL", f);
+  if (a->struct_size < sizeof(gdn_conv1d_backward_args))
+    return fail(GDN_ERR_INVALID_ARG, "%s: struct_size %u < %zu", f, a->struct_size,
+                sizeof(gdn_conv1d_backward_args));
+  if (!is_dtype(a->dtype)) return fail(GDN_ERR_INVALID_ARG, "%s: bad dtype %d", f, a->dtype);
+  if (a->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "%s: n_seqs %d < 1", f, a->n_seqs);
+  if (a->total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: total_tokens < 0", f);
+  if (a->channels < 1) return fail(GDN_ERR_INVALID_ARG, "%s: channels %d < 1", f, a->channels);
+  if (a->width < 2 || a->width > 4) return fail(GDN_ERR_UNSUPPORTED, "%s: width %d not in 2..4", f, a->width);
+  if (a->activation != GDN_ACT_NONE && a->activation != GDN_ACT_SILU)
+    return fail(GDN_ERR_INVALID_ARG, "%s: bad activation %d", f, a->activation);
+  if (!a->weight || !a->dweight || (a->total_tokens > 0 && (!a->x || !a->dy || !a->dx)))
+    return fail(GDN_ERR_INVALID_ARG, "%s: x, weight, dy, dx and dweight are required", f);
+  if (a->dbias && !a->bias) return fail(GDN_ERR_INVALID_ARG, "%s: dbias needs bias", f);
+  if (a->n_seqs > 1 && !a->cu_seqlens)
+    return fail(GDN_ERR_INVALID_ARG, "%s: cu_seqlens is required when n_seqs > 1", f);
+  const size_t es = esize(a->dtype);
+  const void* pe[] = {a->x, a->weight, a->bias, a->conv_state, a->dy, a->dx};
+  for (const void* p : pe)
+    if (!aligned(p, es)) return fail(GDN_ERR_ALIGNMENT, "%s: misaligned tensor", f);
+  const void* p4[] = {a->cu_seqlens, a->d_new_state, a->dweight, a->dbias, a->d_conv_state};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return fail(GDN_ERR_ALIGNMENT, "%s: misaligned fp32 or int32 tensor", f);
+  const size_t TC = (size_t)a->total_tokens * a->channels;
+  const size_t nS = (size_t)a->n_seqs * a->channels * (a->width - 1);
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{a->x, TC * es}, {a->dy, TC * es}, {a->weight, (size_t)a->channels * a->width * es},
+                   {a->bias, a->bias ? a->channels * es : 0}, {a->conv_state, a->conv_state ? nS * es : 0},
+                   {a->d_new_state, a->d_new_state ? nS * 4 : 0}};
+  const R outs[] = {{a->dx, TC * es}, {a->dweight, (size_t)a->channels * a->width * 4},
+                    {a->dbias, a->dbias ? a->channels * 4u : 0}, {a->d_conv_state, a->d_conv_state ? nS * 4 : 0}};
+  for (const R& o : outs)
+    for (const R& i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return fail(GDN_ERR_INVALID_ARG, "%s: an output overlaps an input", f);
+  const size_t need = gdn::conv1d_backward_workspace_bytes(a->total_tokens, a->channels);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes required", f, need);
+  if (!aligned(a->workspace, 256)) return fail(GDN_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", f);
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +332,50 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
     return finish(gdn::launch_decode(p, a->io_dtype, a->state_dtype, a->d_k, s), s, "gdn_decode_step");
   } catch (...) {
     return fail(GDN_ERR_HIP, "gdn_decode_step: internal error");
+  }
+}
+
+size_t gdn_prefill_backward_workspace_size(const gdn_prefill_backward_args* a) {
+  if (!a || a->struct_size < sizeof(gdn_prefill_backward_args) || a->n_seqs < 1 || a->total_tokens < 0 ||
+      a->h_qk < 1 || a->h_v < 1 || a->h_v % a->h_qk || a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128) ||
+      (a->chunk != 16 && a->chunk != 32 && a->chunk != 64))
+    return 0;
+  return gdn::prefill_backward_workspace_bytes(a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->d_k, a->chunk);
+}
+
+gdn_status gdn_prefill_backward(const gdn_prefill_backward_args* a, void* stream) {
+  try {
+    const gdn_status s = check_prefill_backward(a);
+    if (s != GDN_OK) return s;
+    gdn::PrefillBwdParams p{a->q, a->k, a->v, a->q_stride, a->k_stride, a->v_stride, a->g, a->beta,
+                            a->initial_state, a->cu_seqlens, a->d_o, a->d_final_state, a->dq, a->dk, a->dv,
+                            a->dq_stride, a->dk_stride, a->dv_stride, a->dg, a->dbeta, a->d_initial_state,
+                            a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
+                            (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1,
+                            a->scale, a->workspace};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_prefill_backward(p, a->io_dtype, a->d_k, st), st, "gdn_prefill_backward");
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "gdn_prefill_backward: internal error");
+  }
+}
+
+size_t gdn_conv1d_backward_workspace_size(const gdn_conv1d_backward_args* a) {
+  if (!a || a->struct_size < sizeof(gdn_conv1d_backward_args) || a->total_tokens < 0 || a->channels < 1) return 0;
+  return gdn::conv1d_backward_workspace_bytes(a->total_tokens, a->channels);
+}
+
+gdn_status gdn_conv1d_backward(const gdn_conv1d_backward_args* a, void* stream) {
+  try {
+    const gdn_status s = check_conv1d_backward(a);
+    if (s != GDN_OK) return s;
+    gdn::ConvBwdParams p{a->x, a->weight, a->bias, a->conv_state, a->cu_seqlens, a->dy, a->d_new_state, a->dx,
+                         a->dweight, a->dbias, a->d_conv_state, a->total_tokens, a->n_seqs, a->channels,
+                         a->width, a->activation, a->workspace};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_conv1d_backward(p, a->dtype, st), st, "gdn_conv1d_backward");
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "gdn_conv1d_backward: internal error");
   }
 }
 

@@ -79,4 +79,61 @@ size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, i
 bool prefill_supported(int io_dtype, int d, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream);
 
+struct PrefillBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_stride;
+  int64_t k_stride;
+  int64_t v_stride;
+  const float* g;
+  const float* beta;
+  const float* initial_state;
+  const int32_t* cu_seqlens;
+  const void* d_o;
+  const float* d_final_state;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t dq_stride;
+  int64_t dk_stride;
+  int64_t dv_stride;
+  float* dg;
+  float* dbeta;
+  float* d_initial_state;
+  int64_t total_tokens;
+  int32_t n_seqs;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t chunk;
+  int32_t l2norm;
+  int32_t erase;
+  float scale;
+  void* workspace;
+};
+size_t prefill_backward_workspace_bytes(int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d, int chunk);
+hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int d, hipStream_t stream);
+
+struct ConvBwdParams {
+  const void* x;
+  const void* weight;
+  const void* bias;
+  const void* conv_state;
+  const int32_t* cu_seqlens;
+  const void* dy;
+  const float* d_new_state;
+  void* dx;
+  float* dweight;
+  float* dbias;
+  float* d_conv_state;
+  int64_t total_tokens;
+  int32_t n_seqs;
+  int32_t channels;
+  int32_t width;
+  int32_t act;
+  void* workspace;
+};
+size_t conv1d_backward_workspace_bytes(int64_t total_tokens, int channels);
+hipError_t launch_conv1d_backward(const ConvBwdParams& p, int dtype, hipStream_t stream);
+
 }  // namespace gdn

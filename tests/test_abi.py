@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
     for n in names:
         assert re.search(rf"\bT {n}$", out, flags=re.M), n
-    assert L.gdn_abi_version() == gdn.ABI_VERSION == 2
+    assert L.gdn_abi_version() == gdn.ABI_VERSION == 3
 
 
 def test_struct_layout_matches_header():
@@ -128,3 +128,94 @@ def test_workspace_size_query():
     # offsets (256 B) + (1024/64 + 1) chunks x 48 heads x (Tb + P bf16 + 4 fp32 rows)
     assert n == 256 + 17 * 48 * (2 * 64 * 64 * 2 + 16 * 64)
     assert gdn.lib().gdn_status_string(5) == b"GDN_ERR_HIP"
+
+
+@pytest.mark.parametrize("cname,pyt", [("gdn_prefill_backward_args", "PrefillBwdArgs"),
+                                       ("gdn_conv1d_backward_args", "ConvBwdArgs"),
+                                       ("gdn_prefill_args", "PrefillArgs"), ("gdn_conv1d_args", "ConvArgs"),
+                                       ("gdn_decode_args", "DecodeArgs")])
+def test_every_field_offset_matches_header(cname, pyt):
+    """Every field of the binding's ctypes struct sits at the header's offset."""
+    st = getattr(gdn, pyt)
+    lines = [f'printf("size %zu\\n", sizeof({cname}));']
+    lines += [f'printf("{f} %zu\\n", offsetof({cname}, {f}));' for f, _ in st._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"gdn.h\"\nint main(void) {\n" + "\n".join(lines) + \
+        "\nreturn 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = dict(l.split(" ") for l in subprocess.run([exe], capture_output=True, text=True,
+                                                         check=True).stdout.split("\n") if l)
+    assert int(got["size"]) == ctypes.sizeof(st)
+    for f, _ in st._fields_:
+        assert int(got[f]) == getattr(st, f).offset, f
+
+
+def _bwd_args(**kw):
+    a = gdn.PrefillBwdArgs(struct_size=ctypes.sizeof(gdn.PrefillBwdArgs), flags=1, io_dtype=1, n_seqs=1,
+                           total_tokens=128, h_qk=2, h_v=4, d_k=64, d_v=64, chunk=64, scale=1.0)
+    base = 1 << 32
+    for i, f in enumerate(["q", "k", "v", "g", "beta", "d_o", "dq", "dk", "dv", "dg", "dbeta"]):
+        setattr(a, f, base + i * (1 << 24))
+    a.q_stride = a.k_stride = a.dq_stride = a.dk_stride = 128
+    a.v_stride = a.dv_stride = 256
+    a.workspace = 1 << 40
+    a.workspace_bytes = gdn.lib().gdn_prefill_backward_workspace_size(ctypes.byref(a))
+    for f, v in kw.items():
+        setattr(a, f, v)
+    return a
+
+
+def test_prefill_backward_validation():
+    """Host-side rejections of gdn_prefill_backward (no launch: the pointers are never touched)."""
+    L = gdn.lib()
+    call = lambda a: L.gdn_prefill_backward(ctypes.byref(a), None)
+    assert _bwd_args().workspace_bytes > 0
+    assert call(_bwd_args(d_k=96, d_v=96)) == 2
+    assert call(_bwd_args(chunk=48)) == 2
+    assert call(_bwd_args(h_v=3)) == 1
+    assert call(_bwd_args(flags=8)) == 1
+    assert call(_bwd_args(d_o=0)) == 1
+    assert call(_bwd_args(n_seqs=2)) == 1  # cu_seqlens missing
+    assert call(_bwd_args(dq_stride=64)) == 1
+    assert call(_bwd_args(dq=(1 << 32) + 8)) == 3
+    assert call(_bwd_args(dk=(1 << 32) + 16)) == 1  # dk overlaps q
+    a = _bwd_args()
+    a.workspace_bytes -= 1
+    assert call(a) == 4
+    assert call(_bwd_args(workspace=(1 << 40) + 16)) == 3
+    a = _bwd_args(struct_size=8)
+    assert call(a) == 1
+    # the workspace grows with the chunk count and the heads
+    s1 = L.gdn_prefill_backward_workspace_size(ctypes.byref(_bwd_args(total_tokens=1024)))
+    s2 = L.gdn_prefill_backward_workspace_size(ctypes.byref(_bwd_args(total_tokens=2048)))
+    assert s2 > s1 > 0
+    assert L.gdn_prefill_backward_workspace_size(ctypes.byref(_bwd_args(d_k=96, d_v=96))) == 0
+
+
+def test_conv1d_backward_validation():
+    L = gdn.lib()
+    def args(**kw):
+        a = gdn.ConvBwdArgs(struct_size=ctypes.sizeof(gdn.ConvBwdArgs), dtype=1, n_seqs=1, channels=64,
+                            total_tokens=100, width=4, activation=1)
+        base = 1 << 32
+        for i, f in enumerate(["x", "weight", "dy", "dx", "dweight"]):
+            setattr(a, f, base + i * (1 << 24))
+        a.workspace = 1 << 40
+        a.workspace_bytes = L.gdn_conv1d_backward_workspace_size(ctypes.byref(a))
+        for f, v in kw.items():
+            setattr(a, f, v)
+        return a
+    call = lambda a: L.gdn_conv1d_backward(ctypes.byref(a), None)
+    assert args().workspace_bytes >= 2 * 64 * 5 * 4
+    assert call(args(width=5)) == 2
+    assert call(args(activation=7)) == 1
+    assert call(args(dy=0)) == 1
+    assert call(args(dbias=(1 << 32) + (6 << 24))) == 1  # dbias without bias
+    assert call(args(dx=(1 << 32) + 64)) == 1  # dx overlaps x
+    assert call(args(n_seqs=3)) == 1
+    a = args()
+    a.workspace_bytes = 16
+    assert call(a) == 4
