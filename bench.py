@@ -7,6 +7,10 @@ delta rule), inputs already resident in HBM.  The default workload is the
 also carries the decode leg: gdn_decode_step on the 27B-shaped batch of 256
 sequences x 48 V heads with a bf16 state, 64 consecutive steps.
 
+The `backward` object times the training backward of the same layer:
+gdn_prefill_backward then gdn_conv1d_backward, with the forward's conv output
+and the output gradient resident.
+
 Prints ONE JSON line.  `value` is prefill tokens/s/layer (conv + prefill).
 `roofline` is for the dominant kernel (the prefill kernel): algorithmic
 FLOPs per launch / its average duration from HIP events on the stream it
@@ -37,6 +41,16 @@ def prefill_flops_per_token(cfg):
     Gram matrices once per QK head (4 C d_k)."""
     C, dk, dv = cfg["chunk"], cfg["d_k"], cfg["d_v"]
     return cfg["h_v"] * (2 * C * dk + 4 * C * dv + 6 * dk * dv) + cfg["h_qk"] * 4 * C * dk
+
+
+def backward_flops_per_token(cfg):
+    """Contraction FLOPs per token of the chunked backward as computed (fp32):
+    per V head and chunk, 22 C x C x d products (recomputed W and Ut, Pm^T dO,
+    T^T dU, dPm, dT (2), T^T dW, dK^ (2), dQ^ ...), 16 C x d x d products (the
+    two chains' 4, Z, dW, dO X^T, U dX'^T) and 4 C^3 (dT T^T, T^T M1), plus
+    the two Gram matrices per QK head; divided by the C tokens of a chunk."""
+    C, d = cfg["chunk"], cfg["d_k"]
+    return cfg["h_v"] * (22 * C * d + 16 * d * d + 4 * C * C) + cfg["h_qk"] * 4 * C * d
 
 
 def decode_bytes_per_step(cfg):
@@ -185,6 +199,81 @@ def run_prefill(name, steps, warmup, do_cpu, cpu_tokens):
     return res
 
 
+def run_backward(name, steps, warmup, do_cpu):
+    import torch
+    import gdn_inputs
+    import linear_attention_token_conv1d_amd as gdn
+
+    inp = gdn_inputs.prefill_inputs(name)
+    cfg = inp["cfg"]
+    dev = torch.device("cuda:0")
+    x = inp["x"].to(dev)
+    w = inp["conv_weight"].to(dev)
+    g = inp["g"].to(dev)
+    beta = inp["beta"].to(dev)
+    s0 = None if inp["initial_state"] is None else inp["initial_state"].to(dev)
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].to(dev)
+    T, hq, hv, d, N = inp["T"], cfg["h_qk"], cfg["h_v"], cfg["d_k"], inp["n_seqs"]
+    y = gdn.conv1d(x, w, None, None, cu, "silu")
+    q, k, v = gdn.split_qkv(y, hq, d, hv, d)
+    gen = torch.Generator().manual_seed(1)
+    do = torch.randn((T, hv, d), generator=gen).to(torch.bfloat16).to(dev)
+    dy = torch.zeros_like(y)
+    dq, dk, dv = gdn.split_qkv(dy, hq, d, hv, d)
+    dg = torch.empty((T, hv), dtype=torch.float32, device=dev)
+    db = torch.empty_like(dg)
+    ds0 = torch.empty((N, hv, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_backward_workspace_size(q, v, N, cfg["chunk"]), dtype=torch.uint8, device=dev)
+    cws = torch.empty(gdn.conv1d_backward_workspace_size(T, y.shape[1]), dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(x)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gdn.prefill_backward(q, k, v, g, beta, do, s0, None, cu, cfg["chunk"], 1.0, True, True, dq=dq, dk=dk,
+                             dv=dv, dg=dg, dbeta=db, d_initial_state=ds0, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        gdn.conv1d_backward(x, w, dy, None, None, cu, "silu", None, dx=dx, d_conv_state=False, workspace=cws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    k_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    flops = backward_flops_per_token(cfg) * T
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    res = {"tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "prefill_backward_ms": round(k_ms, 4),
+           "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / PEAK_F32_TFLOPS, 4), "traffic": None,
+                        "kernel": "gdn_prefill_backward (fp32 batched GEMMs, two chains, combine kernels)",
+                        "flops_per_launch": flops},
+           "config": {"workload": f"{name} backward: gdn_prefill_backward + gdn_conv1d_backward, B={N} T={T} "
+                                  f"h_qk={hq} h_v={hv} d={d} chunk={cfg['chunk']}, bf16 io, fp32 arithmetic"}}
+    if do_cpu:
+        from oracle import gdn_oracle as orc
+        tok = 1024
+        h = 0
+        qn, kn, vn = (t[:tok, h:h + 1].double().cpu().numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        orc.gated_delta_rule_backward(qn, kn, vn, g[:tok, h:h + 1].double().cpu().numpy(),
+                                      beta[:tok, h:h + 1].double().cpu().numpy(),
+                                      do[:tok, h:h + 1].double().cpu().numpy(), segment=64)
+        dt = (time.perf_counter() - t0) * (T / tok) * hv
+        res["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s/layer", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle backward of V head 0 over the first {tok} tokens, fp64 numpy, "
+                                         f"one process; time scaled by {T // tok} x {hv} heads"}
+    return res
+
+
 def run_decode(steps, warmup, do_cpu):
     import numpy as np
     import torch
@@ -250,6 +339,7 @@ def main():
                     choices=["qwen35_9b_prefill", "qwen35_27b_prefill", "qwen35_27b_varlen"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters)")
@@ -277,6 +367,8 @@ def main():
         line["cpu_baseline"] = pre["cpu_baseline"]
     if not args.no_decode:
         line["decode"] = run_decode(args.steps, args.warmup, not args.no_cpu_baseline)
+    if not args.no_backward:
+        line["backward"] = run_backward(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

@@ -336,15 +336,18 @@ gdn_status gdn_prefill_backward(const gdn_prefill_backward_args* args, void* str
  * Qwen3.5", section 5, and the conv state of "Mamba hybrid model selection",
  * per-request memory section).
  *
- *   dtype, n_seqs, total_tokens, channels, width, activation, x, weight,
- *   bias, cu_seqlens: as passed to the forward call.
+ *   dtype, n_seqs, total_tokens, channels (multiple of 8), width,
+ *   activation, x, weight, bias, cu_seqlens: as passed to the forward call
+ *   (x 16-byte aligned).
  *   conv_state   [n_seqs, C, W-1] in dtype: the state the forward call READ
  *                (the forward overwrites its buffer, so keep a copy), or NULL
  *                for zeros.
- *   dy           [T, C] in dtype: gradient of the loss with respect to y.
+ *   dy           [T, C] in dtype, 16-byte aligned: gradient of the loss with
+ *                respect to y.
  *   d_new_state  [n_seqs, C, W-1] fp32 gradient with respect to the state the
  *                forward call wrote, or NULL for zero.
- *   dx           [T, C] in dtype; must not overlap any input.
+ *   dx           [T, C] in dtype, 16-byte aligned; must not overlap any
+ *                input.
  *   dweight      [C, W] fp32;  dbias [C] fp32 or NULL (only with bias).
  *   d_conv_state [n_seqs, C, W-1] fp32, or NULL (not formed).
  *   workspace    at least gdn_conv1d_backward_workspace_size() bytes,

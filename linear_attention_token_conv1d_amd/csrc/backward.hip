@@ -250,15 +250,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
   __shared__ float sG[64], sGam[64], sE[64], sB[64];
   __shared__ float sA[64][65];
   __shared__ float sT[64][65];
-  if (tid == 0) {
-    float G = 0.f;
-    for (int r = 0; r < C; ++r) {
-      const bool in = r < cr.len;
-      G += in ? g[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
-      sG[r] = G;
-      sB[r] = in ? beta[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
-    }
+  for (int r = tid; r < C; r += blockDim.x) {
+    const bool in = r < cr.len;
+    sG[r] = in ? g[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+    sB[r] = in ? beta[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
   }
+  __syncthreads();
+  if (tid == 0)
+    for (int r = 1; r < C; ++r) sG[r] += sG[r - 1];
   __syncthreads();
   float* vec = w.vec + bv * kNVec * C;
   for (int r = tid; r < C; r += blockDim.x) {
@@ -310,21 +309,49 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
 }
 
 // ----------------------------------------------------------------- chain
-// One workgroup per (sequence, V head, 16 state columns).  Per chunk, with Y
-// the D x 16 state slice:
+// One workgroup per (sequence, V head, 16 state columns) and direction.  Per
+// chunk, with Y the D x 16 state slice:
 //   forward: store Y as X_c;   U  = Ut  - W Y;         Y = gam Y + EK^T U
 //   reverse: store Y as dX'_c; dU = PdO + EK Y;        Y = gam Y + Z - W^T dU
 // (chunks in reverse order).  Y starts from the initial state (forward) or
 // the final-state gradient (reverse); the reverse chain's last Y is the
-// initial-state gradient.
+// initial-state gradient.  The two directions need nothing from each other
+// (the reverse chain reads only the recomputed chunk quantities), so one
+// launch runs both.  The next chunk's two C x D operands are fetched into
+// registers while the current chunk computes.
 constexpr int kCW = 16;
-template <bool REV, int D>
-__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdWs w, const float* s_in, float* s_out, int h_v,
-                                                        int C) {
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that waits for this wave's LDS operations only (vector
+// memory loads and stores stay in flight: the compiler still waits for a
+// load before its value is used).  __syncthreads() would also drain every
+// outstanding global access, the next chunk's prefetch included.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+template <bool REV, int NPF>
+__device__ __forceinline__ void chain_fetch(const BwdWs& w, int gc, int h, int h_v, int cd, int tid,
+                                            v4f (&r1)[NPF], v4f (&r2)[NPF]) {
+  const int64_t b = (int64_t)gc * h_v + h;
+  const v4f* p1 = reinterpret_cast<const v4f*>(w.cd[REV ? mEK : mW] + b * cd);
+  const v4f* p2 = reinterpret_cast<const v4f*>(w.cd[REV ? mW : mEK] + b * cd);
+#pragma unroll
+  for (int u = 0; u < NPF; ++u) {
+    r1[u] = p1[tid + 256 * u];
+    r2[u] = p2[tid + 256 * u];
+  }
+}
+
+template <bool REV, int D, int C>
+__device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, float* s_out, int h_v) {
   const int n = blockIdx.x / h_v, h = blockIdx.x % h_v, col0 = blockIdx.y * kCW, tid = threadIdx.x;
   extern __shared__ float lds[];
-  float* P1 = lds;             // C x D
-  float* P2 = P1 + C * D;      // C x D
+  constexpr int LP = D + 4;    // P1 row pitch: the 16 rows a wave reads fall in distinct banks
+  float* P1 = lds;             // C x LP
+  float* P2 = P1 + C * LP;     // C x D
   float* Y = P2 + C * D;       // D x 16
   float* Uv = Y + D * kCW;     // C x 16
   for (int e = tid; e < D * kCW; e += 256) {
@@ -332,35 +359,48 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdWs w, const float* s_
     Y[e] = s_in ? s_in[(((int64_t)n * h_v + h) * D + col0 + c) * D + k] : 0.f;
   }
   const int c_lo = w.co[n], c_hi = w.co[n + 1];
+  constexpr int NPF = C * D / 1024;  // float4 per thread per operand
   constexpr int NPT = D / 16;             // state outputs per thread
   constexpr int TPR = kCW / NPT;          // threads per state row
   const int yk = tid / TPR, yc = (tid % TPR) * NPT;
-  for (int i = 0; i < c_hi - c_lo; ++i) {
+  v4f r1[NPF], r2[NPF];
+  const int nchunks = c_hi - c_lo;
+  if (nchunks > 0) chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, C * D, tid, r1, r2);
+  for (int i = 0; i < nchunks; ++i) {
     const int gc = REV ? c_hi - 1 - i : c_lo + i;
     const int64_t b = (int64_t)gc * h_v + h;
-    const float4* p1 = reinterpret_cast<const float4*>(w.cd[REV ? mEK : mW] + b * C * D);
-    const float4* p2 = reinterpret_cast<const float4*>(w.cd[REV ? mW : mEK] + b * C * D);
-    __syncthreads();  // the previous chunk is done with P1, P2, Uv and Y
-    for (int e = tid; e < C * D / 4; e += 256) {
-      reinterpret_cast<float4*>(P1)[e] = p1[e];
-      reinterpret_cast<float4*>(P2)[e] = p2[e];
+    lds_barrier();  // the previous chunk is done with P1, P2, Uv and Y
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int q = tid + 256 * u;
+      *reinterpret_cast<v4f*>(P1 + (q / (D / 4)) * LP + (q % (D / 4)) * 4) = r1[u];
+      reinterpret_cast<v4f*>(P2)[q] = r2[u];
     }
+    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, C * D, tid, r1, r2);
     float* ys = w.dd[REV ? xDXs : xXs] + b * D * D;
     for (int e = tid; e < D * kCW; e += 256) ys[(int64_t)(e / kCW) * D + col0 + e % kCW] = Y[e];
-    __syncthreads();
+    lds_barrier();
     // R1 = P1 Y, then U = Vb -/+ R1 (C x 16)
     const float* vb = w.cd[REV ? mPdO : mUt] + b * C * D;
     float* uo = w.cd[REV ? mDU : mU] + b * C * D;
     for (int e = tid; e < C * (kCW / 4); e += 256) {
       const int r = e / (kCW / 4), c4 = (e % (kCW / 4)) * 4;
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      for (int k = 0; k < D; ++k) {
-        const float pk = P1[r * D + k];
-        const float4 y = *reinterpret_cast<const float4*>(&Y[k * kCW + c4]);
-        a0 = fmaf(pk, y.x, a0);
-        a1 = fmaf(pk, y.y, a1);
-        a2 = fmaf(pk, y.z, a2);
-        a3 = fmaf(pk, y.w, a3);
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        float pk[8];
+        v4f y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          pk[u] = P1[r * LP + k0 + u];
+          y[u] = *reinterpret_cast<const v4f*>(&Y[(k0 + u) * kCW + c4]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a0 = fmaf(pk[u], y[u].x, a0);
+          a1 = fmaf(pk[u], y[u].y, a1);
+          a2 = fmaf(pk[u], y[u].z, a2);
+          a3 = fmaf(pk[u], y[u].w, a3);
+        }
       }
       const float4 v = *reinterpret_cast<const float4*>(vb + (int64_t)r * D + col0 + c4);
       const float4 u = REV ? make_float4(v.x + a0, v.y + a1, v.z + a2, v.w + a3)
@@ -368,16 +408,30 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdWs w, const float* s_
       *reinterpret_cast<float4*>(&Uv[r * kCW + c4]) = u;
       *reinterpret_cast<float4*>(uo + (int64_t)r * D + col0 + c4) = u;
     }
-    __syncthreads();
+    lds_barrier();
     // Y = gam Y +/- P2^T U (+ Z)
     const float gam = w.vec[b * kNVec * C + kVecGam * C + C - 1];
     float acc[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) acc[j] = 0.f;
-    for (int r = 0; r < C; ++r) {
-      const float pk = P2[r * D + yk];
+    for (int r0 = 0; r0 < C; r0 += 4) {
+      float pk[4];
+      v4f uv[4][NPT / 4];
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) acc[j] = fmaf(pk, Uv[r * kCW + yc + j], acc[j]);
+      for (int u = 0; u < 4; ++u) {
+        pk[u] = P2[(r0 + u) * D + yk];
+#pragma unroll
+        for (int q = 0; q < NPT / 4; ++q) uv[u][q] = *reinterpret_cast<const v4f*>(&Uv[(r0 + u) * kCW + yc + 4 * q]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < NPT / 4; ++q) {
+          acc[4 * q + 0] = fmaf(pk[u], uv[u][q].x, acc[4 * q + 0]);
+          acc[4 * q + 1] = fmaf(pk[u], uv[u][q].y, acc[4 * q + 1]);
+          acc[4 * q + 2] = fmaf(pk[u], uv[u][q].z, acc[4 * q + 2]);
+          acc[4 * q + 3] = fmaf(pk[u], uv[u][q].w, acc[4 * q + 3]);
+        }
     }
     if constexpr (REV) {
       const float* z = w.dd[xZ] + b * D * D + (int64_t)yk * D + col0 + yc;
@@ -389,12 +443,30 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdWs w, const float* s_
     }
   }
   if (REV && s_out) {
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < D * kCW; e += 256) {
       const int k = e / kCW, c = e % kCW;
       s_out[(((int64_t)n * h_v + h) * D + col0 + c) * D + k] = Y[e];
     }
   }
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void bwd_chains_kernel(BwdWs w, const float* s0, const float* dsf, float* ds0,
+                                                         int h_v) {
+  if (blockIdx.z == 0) chain_body<false, D, C>(w, s0, nullptr, h_v);
+  else chain_body<true, D, C>(w, dsf, ds0, h_v);
+}
+
+template <int D, int C>
+hipError_t launch_chains(const BwdWs& w, const PrefillBwdParams& p, hipStream_t stream) {
+  const size_t lds = (C * (D + 4) + C * D + D * kCW + C * kCW) * sizeof(float);
+  const void* f = reinterpret_cast<const void*>(bwd_chains_kernel<D, C>);
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chains_kernel<D, C>), dim3((unsigned)(p.n_seqs * p.h_v), D / kCW, 2), dim3(256), lds,
+                     stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v);
+  return hipGetLastError();
 }
 
 // ------------------------------------------- C x C gradient combination
@@ -565,9 +637,7 @@ __global__ __launch_bounds__(64) void bwd_final_qk_kernel(BwdWs w, const int32_t
 
 // ------------------------------------------------------------ conv backward
 // z = sum_j w_j xp[t + j] (+ b) over the padded history xp = (state ++ x) of
-// the token's sequence, y = act(z).  dz = dy act'(z); per token tile the
-// partial sums of dz xp[t + j] (weight) and dz (bias) go to the workspace.
-constexpr int kConvTT = 64;
+// the token's sequence, y = act(z), dz = dy act'(z).
 
 __device__ inline void seq_of(const int32_t* cu, int n_seqs, int64_t T, int64_t t, int& n, int64_t& s,
                               int64_t& e) {
@@ -595,47 +665,107 @@ __device__ inline float conv_dz(const T* x, const T* w, const T* bias, const T* 
   return d * sg * (1.0f + z * (1.0f - sg));
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* x, const T* w, const T* bias, const T* state,
-                                                          const T* dy, const int32_t* cu, int n_seqs, int64_t Tt,
-                                                          int C, int W, int act, float* part) {
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= C) return;
-  const int64_t t0 = (int64_t)blockIdx.x * kConvTT, t1 = min(t0 + kConvTT, Tt);
-  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  int n = 0;
-  int64_t s = 0, e = 0;
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t == t0 || t >= e) seq_of(cu, n_seqs, Tt, t, n, s, e);
-    const int64_t u = t - s;
-    const float dz = conv_dz(x, w, bias, state, dy, s, n, C, W, c, u, act);
-    for (int j = 0; j < W; ++j) acc[j] = fmaf(dz, conv_xp(x, state, s, n, C, W, c, u + j), acc[j]);
-    acc[4] += dz;
-  }
-  float* p = part + ((int64_t)blockIdx.x * C + c) * 5;
-  for (int j = 0; j < 5; ++j) p[j] = acc[j];
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const T* x, const T* w, const T* bias, const T* state,
-                                                          const T* dy, const float* dns, const int32_t* cu,
-                                                          int n_seqs, int64_t Tt, int C, int W, int act, T* dx) {
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= C) return;
-  const int64_t t0 = (int64_t)blockIdx.x * kConvTT, t1 = min(t0 + kConvTT, Tt);
-  int n = 0;
-  int64_t s = 0, e = 0;
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t == t0 || t >= e) seq_of(cu, n_seqs, Tt, t, n, s, e);
-    const int64_t L = e - s, i = t - s + (W - 1);  // padded index of this token
-    float acc = 0.f;
+// One pass per (token tile, 8 channels): each thread walks the tile plus the
+// W-1 tokens after it, computing every dz once.  dz_tau adds w_{W-1-k} dz_tau
+// to the pending dx of token tau - k (k < W, same sequence); a token's dx is
+// complete once tau has moved W-1 past it, or at its sequence's end, where
+// the gradient of the new conv state adds onto the last W-1 tokens.  The
+// weight and bias partial sums of the tile's own tokens go to the workspace.
+constexpr int kConvBT = 32;
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(const T* x, const T* w, const T* bias, const T* state,
+                                                       const T* dy, const float* dns, const int32_t* cu,
+                                                       int n_seqs, int64_t Tt, int C, int act, T* dx,
+                                                       float* part) {
+  const int c0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c0 >= C) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kConvBT, t1 = min(t0 + kConvBT, Tt), tend = min(t1 + W - 1, Tt);
+  float wt[W][8], bs[8], xw[W][8], pend[W][8], aw[W + 1][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
     for (int j = 0; j < W; ++j) {
-      const int64_t u = i - j;
-      if (u >= 0 && u < L) acc = fmaf(to_f32(w[c * W + j]), conv_dz(x, w, bias, state, dy, s, n, C, W, c, u, act), acc);
+      wt[j][i] = to_f32(w[(c0 + i) * W + j]);
+      aw[j][i] = 0.f;
     }
-    if (dns && i >= L) acc += dns[((int64_t)n * C + c) * (W - 1) + (i - L)];
-    dx[t * C + c] = from_f32<T>(acc);
+    aw[W][i] = 0.f;
+    bs[i] = bias ? to_f32(bias[c0 + i]) : 0.f;
   }
+  int n = 0;
+  int64_t s = 0, e = 0;
+  for (int64_t tau = t0; tau < tend; ++tau) {
+    if (tau == t0 || tau >= e) {
+      seq_of(cu, n_seqs, Tt, tau, n, s, e);
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xw[j][i] = conv_xp(x, state, s, n, C, W, c0 + i, tau - s + j);
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pend[k][i] = 0.f;
+    }
+    float d8[8];
+    load8(x + tau * C + c0, xw[W - 1]);
+    load8(dy + tau * C + c0, d8);
+    float dz[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float z = bs[i];
+#pragma unroll
+      for (int j = 0; j < W; ++j) z = fmaf(wt[j][i], xw[j][i], z);
+      if (act) {
+        const float sg = 1.0f / (1.0f + expf(-z));
+        dz[i] = d8[i] * sg * (1.0f + z * (1.0f - sg));
+      } else {
+        dz[i] = d8[i];
+      }
+    }
+    if (tau < t1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < W; ++j) aw[j][i] = fmaf(dz[i], xw[j][i], aw[j][i]);
+        aw[W][i] += dz[i];
+      }
+    }
+#pragma unroll
+    for (int k = W - 1; k > 0; --k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pend[k][i] = pend[k - 1][i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pend[0][i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      if (tau - k >= s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pend[k][i] = fmaf(wt[W - 1 - k][i], dz[i], pend[k][i]);
+    const int64_t td = tau - (W - 1);
+    if (td >= s && td >= t0 && td < t1) store8(dx + td * C + c0, pend[W - 1]);
+    if (tau == e - 1) {
+      const int64_t L = e - s;
+#pragma unroll
+      for (int k = 0; k < W - 1; ++k) {
+        const int64_t t = tau - k;
+        if (t >= s && t >= t0 && t < t1) {
+          const int64_t ip = t - s + W - 1;
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            v[i] = pend[k][i] + ((dns && ip >= L) ? dns[((int64_t)n * C + c0 + i) * (W - 1) + (ip - L)] : 0.f);
+          store8(dx + t * C + c0, v);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xw[j][i] = xw[j + 1][i];
+  }
+  float* pp = part + (int64_t)blockIdx.x * 5 * C + c0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) store8(pp + (int64_t)j * C, aw[j]);
+  store8(pp + (int64_t)4 * C, aw[W]);
 }
 
 template <typename T>
@@ -663,7 +793,7 @@ __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* part,
   if (c >= C) return;
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < ntiles; ++t)
-    for (int j = 0; j < 5; ++j) acc[j] += part[((int64_t)t * C + c) * 5 + j];
+    for (int j = 0; j < 5; ++j) acc[j] += part[((int64_t)t * 5 + j) * C + c];
   for (int j = 0; j < W; ++j) dweight[c * W + j] = acc[j];
   if (dbias) dbias[c] = acc[4];
 }
@@ -735,36 +865,20 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
   VH(cc[cT], cd[mBK], cd[mW], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
   VH(cc[cT], cd[mBV], cd[mUt], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
   if (L.err != hipSuccess) return L.err;
-  const size_t chain_lds = (2 * CD + (int64_t)D * kCW + (int64_t)C * kCW) * sizeof(float);
-  {
-    const void* ks[2] = {D == 64 ? reinterpret_cast<const void*>(bwd_chain_kernel<false, 64>)
-                                 : reinterpret_cast<const void*>(bwd_chain_kernel<false, 128>),
-                         D == 64 ? reinterpret_cast<const void*>(bwd_chain_kernel<true, 64>)
-                                 : reinterpret_cast<const void*>(bwd_chain_kernel<true, 128>)};
-    for (const void* f : ks) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chain_lds);
-      if (e != hipSuccess) return e;
-    }
-  }
-  const dim3 cgrid((unsigned)(p.n_seqs * hv), (unsigned)(D / kCW));
-  if (D == 64)
-    hipLaunchKernelGGL((bwd_chain_kernel<false, 64>), cgrid, dim3(256), chain_lds, stream, w, p.initial_state,
-                       (float*)nullptr, hv, C);
-  else
-    hipLaunchKernelGGL((bwd_chain_kernel<false, 128>), cgrid, dim3(256), chain_lds, stream, w, p.initial_state,
-                       (float*)nullptr, hv, C);
-  L.check();
-  // PdO = Pm^T dO, Z = GQ^T dO
+  // PdO = Pm^T dO, Z = GQ^T dO (the reverse chain's inputs)
   VH(cc[cPm], cd[mDO], cd[mPdO], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);
   VH(cd[mGQ], cd[mDO], dd[xZ], D, D, C, D, D, D, 1, 0, CD, CD, DD, 1.f, 0);
   if (L.err != hipSuccess) return L.err;
-  if (D == 64)
-    hipLaunchKernelGGL((bwd_chain_kernel<true, 64>), cgrid, dim3(256), chain_lds, stream, w, p.d_final_state,
-                       p.d_initial_state, hv, C);
-  else
-    hipLaunchKernelGGL((bwd_chain_kernel<true, 128>), cgrid, dim3(256), chain_lds, stream, w, p.d_final_state,
-                       p.d_initial_state, hv, C);
-  L.check();
+  {
+    hipError_t e;
+    if (D == 64)
+      e = C == 16 ? launch_chains<64, 16>(w, p, stream) : C == 32 ? launch_chains<64, 32>(w, p, stream)
+                                                          : launch_chains<64, 64>(w, p, stream);
+    else
+      e = C == 16 ? launch_chains<128, 16>(w, p, stream) : C == 32 ? launch_chains<128, 32>(w, p, stream)
+                                                           : launch_chains<128, 64>(w, p, stream);
+    if (e != hipSuccess) return e;
+  }
   // chunk-local products
   VH(cc[cT], cd[mDU], cd[mUt], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);      // TdU = T^T dU
   VH(cd[mDU], dd[xXs], cd[mDW], C, D, D, D, D, D, 0, 1, CD, DD, CD, -1.f, 0);    // dW = -dU X^T
@@ -807,14 +921,21 @@ hipError_t conv_backward_impl(const ConvBwdParams& p, hipStream_t stream) {
   const T* st = static_cast<const T*>(p.conv_state);
   const T* dy = static_cast<const T*>(p.dy);
   const int cg = (p.channels + 255) / 256;
-  const int ntiles = (int)((p.total_tokens + kConvTT - 1) / kConvTT);
+  const int cg8 = (p.channels / 8 + 255) / 256;
+  const int ntiles = (int)((p.total_tokens + kConvBT - 1) / kConvBT);
   float* part = static_cast<float*>(p.workspace);
   if (ntiles > 0) {
-    hipLaunchKernelGGL(conv_bwd_dw_kernel<T>, dim3(ntiles, cg), dim3(256), 0, stream, x, w, b, st, dy, p.cu_seqlens,
-                       p.n_seqs, p.total_tokens, p.channels, p.width, p.act, part);
-    hipLaunchKernelGGL(conv_bwd_dx_kernel<T>, dim3(ntiles, cg), dim3(256), 0, stream, x, w, b, st, dy,
-                       p.d_new_state, p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.width, p.act,
-                       static_cast<T*>(p.dx));
+    const dim3 grid(ntiles, cg8);
+    T* dx = static_cast<T*>(p.dx);
+    if (p.width == 4)
+      hipLaunchKernelGGL((conv_bwd_kernel<T, 4>), grid, dim3(256), 0, stream, x, w, b, st, dy, p.d_new_state,
+                         p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.act, dx, part);
+    else if (p.width == 3)
+      hipLaunchKernelGGL((conv_bwd_kernel<T, 3>), grid, dim3(256), 0, stream, x, w, b, st, dy, p.d_new_state,
+                         p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.act, dx, part);
+    else
+      hipLaunchKernelGGL((conv_bwd_kernel<T, 2>), grid, dim3(256), 0, stream, x, w, b, st, dy, p.d_new_state,
+                         p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.act, dx, part);
   }
   hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3(cg), dim3(256), 0, stream, part, ntiles, p.channels, p.width,
                      p.dweight, p.dbias);
@@ -836,7 +957,7 @@ hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int 
 }
 
 size_t conv1d_backward_workspace_bytes(int64_t total_tokens, int channels) {
-  const int64_t ntiles = (total_tokens + kConvTT - 1) / kConvTT;
+  const int64_t ntiles = (total_tokens + kConvBT - 1) / kConvBT;
   return a256((size_t)(ntiles > 0 ? ntiles : 1) * channels * 5 * sizeof(float));
 }
 

@@ -172,7 +172,8 @@ gdn_status check_conv1d_backward(const gdn_conv1d_backward_args* a) {
   if (!is_dtype(a->dtype)) return fail(GDN_ERR_INVALID_ARG, "%s: bad dtype %d", f, a->dtype);
   if (a->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "%s: n_seqs %d < 1", f, a->n_seqs);
   if (a->total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "%s: total_tokens < 0", f);
-  if (a->channels < 1) return fail(GDN_ERR_INVALID_ARG, "%s: channels %d < 1", f, a->channels);
+  if (a->channels < 8 || a->channels % 8)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: channels (%d) must be a positive multiple of 8", f, a->channels);
   if (a->width < 2 || a->width > 4) return fail(GDN_ERR_UNSUPPORTED, "%s: width %d not in 2..4", f, a->width);
   if (a->activation != GDN_ACT_NONE && a->activation != GDN_ACT_SILU)
     return fail(GDN_ERR_INVALID_ARG, "%s: bad activation %d", f, a->activation);
@@ -182,7 +183,9 @@ gdn_status check_conv1d_backward(const gdn_conv1d_backward_args* a) {
   if (a->n_seqs > 1 && !a->cu_seqlens)
     return fail(GDN_ERR_INVALID_ARG, "%s: cu_seqlens is required when n_seqs > 1", f);
   const size_t es = esize(a->dtype);
-  const void* pe[] = {a->x, a->weight, a->bias, a->conv_state, a->dy, a->dx};
+  if (!aligned(a->x, 16) || !aligned(a->dy, 16) || !aligned(a->dx, 16))
+    return fail(GDN_ERR_ALIGNMENT, "%s: x, dy and dx must be 16-byte aligned", f);
+  const void* pe[] = {a->weight, a->bias, a->conv_state};
   for (const void* p : pe)
     if (!aligned(p, es)) return fail(GDN_ERR_ALIGNMENT, "%s: misaligned tensor", f);
   const void* p4[] = {a->cu_seqlens, a->d_new_state, a->dweight, a->dbias, a->d_conv_state};
@@ -361,7 +364,9 @@ gdn_status gdn_prefill_backward(const gdn_prefill_backward_args* a, void* stream
 }
 
 size_t gdn_conv1d_backward_workspace_size(const gdn_conv1d_backward_args* a) {
-  if (!a || a->struct_size < sizeof(gdn_conv1d_backward_args) || a->total_tokens < 0 || a->channels < 1) return 0;
+  if (!a || a->struct_size < sizeof(gdn_conv1d_backward_args) || a->total_tokens < 0 || a->channels < 8 ||
+      a->channels % 8)
+    return 0;
   return gdn::conv1d_backward_workspace_bytes(a->total_tokens, a->channels);
 }
 

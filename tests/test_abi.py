@@ -216,6 +216,8 @@ def test_conv1d_backward_validation():
     assert call(args(dbias=(1 << 32) + (6 << 24))) == 1  # dbias without bias
     assert call(args(dx=(1 << 32) + 64)) == 1  # dx overlaps x
     assert call(args(n_seqs=3)) == 1
+    assert call(args(channels=60)) == 2
+    assert call(args(dy=(1 << 32) + (2 << 24) + 8)) == 3
     a = args()
     a.workspace_bytes = 16
     assert call(a) == 4
