@@ -155,6 +155,41 @@ struct BG {
   const int* nc;
 };
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that waits for this wave's LDS operations only (vector
+// memory loads and stores stay in flight: the compiler still waits for a
+// load before its value is used).  __syncthreads() would also drain every
+// outstanding global access, a prefetch of the next stage included.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A 64 x 64 output tile per workgroup on fp32 MFMA (16x16x4): wave w owns the
+// 32 x 32 quadrant (w / 2, w % 2) as four 16 x 16 accumulators.  K is staged
+// 32 at a time through LDS (k-major, so both operands are read with
+// consecutive lanes on consecutive rows / columns); the next stage's global
+// loads are issued before the current stage's MFMAs.  In a 16x16x4 MFMA lane
+// l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of its 16 x 4 and
+// 4 x 16 slices, and holds C rows 4 (l / 16) .. +3 of column l % 16.
+constexpr int kGK = 32;
+__device__ __forceinline__ void bg_fetch(const BG& p, const float* A, const float* B, int m0, int n0, int k0,
+                                         int tid, float (&ra)[8], float (&rb)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + 256 * u;
+    const int mm = p.ta ? (e & 63) : (e >> 5), ka = p.ta ? (e >> 6) : (e & 31);
+    const int m = m0 + mm, k = k0 + ka;
+    ra[u] = (m < p.M && k < p.K) ? (p.ta ? A[(int64_t)k * p.lda + m] : A[(int64_t)m * p.lda + k]) : 0.f;
+    const int nn = p.tb ? (e >> 5) : (e & 63), kb = p.tb ? (e & 31) : (e >> 6);
+    const int n = n0 + nn, kk = k0 + kb;
+    rb[u] = (n < p.N && kk < p.K) ? (p.tb ? B[(int64_t)n * p.ldb + kk] : B[(int64_t)kk * p.ldb + n]) : 0.f;
+  }
+}
+
 __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
   const int z = blockIdx.x, gc = z / p.H, h = z % p.H;
   if (gc >= *p.nc) return;
@@ -163,48 +198,51 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
   const float* A = p.A + gc * p.a_sc + (int64_t)(h / p.a_hdiv) * p.a_sh;
   const float* B = p.B + gc * p.b_sc + (int64_t)(h / p.b_hdiv) * p.b_sh;
   float* Cm = p.Cm + gc * p.c_sc + (int64_t)h * p.c_sh;
-  __shared__ float As[16][68], Bs[16][68];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < p.K; k0 += 16) {
-    for (int e = tid; e < 1024; e += 256) {
-      const int mm = p.ta ? (e & 63) : (e >> 4), kk = p.ta ? (e >> 6) : (e & 15);
-      const int m = m0 + mm, k = k0 + kk;
-      float v = 0.f;
-      if (m < p.M && k < p.K) v = p.ta ? A[(int64_t)k * p.lda + m] : A[(int64_t)m * p.lda + k];
-      As[kk][mm] = v;
-    }
-    for (int e = tid; e < 1024; e += 256) {
-      const int nn = p.tb ? (e >> 4) : (e & 63), kk = p.tb ? (e & 15) : (e >> 6);
-      const int n = n0 + nn, k = k0 + kk;
-      float v = 0.f;
-      if (n < p.N && k < p.K) v = p.tb ? B[(int64_t)n * p.ldb + k] : B[(int64_t)k * p.ldb + n];
-      Bs[kk][nn] = v;
-    }
-    __syncthreads();
+  __shared__ float As[kGK][68], Bs[kGK][68];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mw = (wave >> 1) * 32, nw = (wave & 1) * 32, l16 = lane & 15, g4 = lane >> 4;
+  v4f acc[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  float ra[8], rb[8];
+  bg_fetch(p, A, B, m0, n0, 0, tid, ra, rb);
+  for (int k0 = 0; k0 < p.K; k0 += kGK) {
+    lds_barrier();  // the previous stage's MFMAs are done reading As, Bs
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u;
+      if (p.ta) As[e >> 6][e & 63] = ra[u];
+      else As[e & 31][e >> 5] = ra[u];
+      if (p.tb) Bs[e & 31][e >> 5] = rb[u];
+      else Bs[e >> 6][e & 63] = rb[u];
     }
-    __syncthreads();
+    if (k0 + kGK < p.K) bg_fetch(p, A, B, m0, n0, k0 + kGK, tid, ra, rb);
+    lds_barrier();
+#pragma unroll
+    for (int ks = 0; ks < kGK; ks += 4) {
+      const float a0 = As[ks + g4][mw + l16], a1 = As[ks + g4][mw + 16 + l16];
+      const float b0 = Bs[ks + g4][nw + l16], b1 = Bs[ks + g4][nw + 16 + l16];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
-      if (m < p.M && n < p.N) {
-        float* c = Cm + (int64_t)m * p.ldc + n;
-        const float v = p.alpha * acc[i][j];
-        *c = p.accum ? *c + v : v;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + mw + 16 * i + 4 * g4 + r, n = n0 + nw + 16 * j + l16;
+        if (m < p.M && n < p.N) {
+          float* c = Cm + (int64_t)m * p.ldc + n;
+          const float v = p.alpha * acc[i][j][r];
+          *c = p.accum ? *c + v : v;
+        }
       }
-    }
 }
 
 // ------------------------------------------------------- stage: Kn, Qn
@@ -320,18 +358,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
 // launch runs both.  The next chunk's two C x D operands are fetched into
 // registers while the current chunk computes.
 constexpr int kCW = 16;
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-// Workgroup barrier that waits for this wave's LDS operations only (vector
-// memory loads and stores stay in flight: the compiler still waits for a
-// load before its value is used).  __syncthreads() would also drain every
-// outstanding global access, the next chunk's prefetch included.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 template <bool REV, int NPF>
 __device__ __forceinline__ void chain_fetch(const BwdWs& w, int gc, int h, int h_v, int cd, int tid,
                                             v4f (&r1)[NPF], v4f (&r2)[NPF]) {
