@@ -253,7 +253,8 @@ def run_backward(name, steps, warmup, do_cpu):
     res = {"tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "prefill_backward_ms": round(k_ms, 4),
            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tflops / PEAK_F32_TFLOPS, 4), "traffic": None,
+                        "frac": round(tflops / PEAK_F32_TFLOPS, 4),
+                        "traffic": measured_traffic(f"backward_{name}_traffic.md", "backward.hip"),
                         "kernel": "gdn_prefill_backward (fp32 batched GEMMs, two chains, combine kernels)",
                         "flops_per_launch": flops},
            "config": {"workload": f"{name} backward: gdn_prefill_backward + gdn_conv1d_backward, B={N} T={T} "
