@@ -24,6 +24,8 @@
 // Every product runs in fp32.  The design favours simple, independently
 // checkable stages: a batched fp32 GEMM with LDS tiles, two chain launches,
 // and elementwise kernels that combine the pieces.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -495,6 +497,169 @@ hipError_t launch_chains(const BwdWs& w, const PrefillBwdParams& p, hipStream_t 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------- chain, bf16 operands
+// The same two chains for bf16 inputs, on bf16 MFMA (16x16x32): the chunk
+// operands and the state slice are rounded to bf16 as MFMA operands (as the
+// forward scan does with its state), while the state itself, U and every
+// stored result stay fp32.  One wave per 16 state columns; the four waves of
+// a workgroup share one bf16 LDS copy of the chunk's two C x D operands, both
+// row-major.  A 32-deep k-step takes k = 4g + j (j < 4), then 16 + 4g + j - 4
+// (g = lane / 16): the accumulator tiles 2s and 2s + 1 of Y (or of U) are the
+// B operand as they stand, R = P1 Y reads rows of P1, and the update reads
+// P1-shaped tiles of P2 transposed (ds_read_b64_tr_b16).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+__device__ __forceinline__ bf16x8_t frag_rows(const __bf16* row, int g, bool half) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * g);
+  const uint2 hi = half ? make_uint2(0u, 0u) : *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// m = column c0 + l16 of a row-major tile, k = rows r0 + 4g + {0..3} (+16)
+__device__ __forceinline__ bf16x8_t frag_cols(const __bf16* P, int ld, int r0, int c0, int l16, int g, bool half) {
+  const __bf16* p = P + (r0 + 4 * g + (l16 >> 2)) * ld + c0 + 4 * (l16 & 3);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(__attribute__((address_space(3))) __bf16*)(p));
+  short4v hi = {0, 0, 0, 0};
+  if (!half)
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4v*)(__attribute__((address_space(3))) __bf16*)(p + 16 * ld));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ bf16x8_t frag_acc(const v4f& a, const v4f& b) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])));
+}
+
+constexpr int kBCols = 64;  // state columns per workgroup (16 per wave)
+
+template <bool REV, int D, int C>
+__device__ __forceinline__ void chain_rows16(const BwdWs& w, int gc, int h, int h_v, int col, int g4,
+                                             float (&vb)[C / 16][4], float (&zz)[D / 16][4]) {
+  const int64_t b = (int64_t)gc * h_v + h;
+  const float* v = w.cd[REV ? mPdO : mUt] + b * C * D + col;
+#pragma unroll
+  for (int rb = 0; rb < C / 16; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vb[rb][i] = v[(int64_t)(16 * rb + 4 * g4 + i) * D];
+  if constexpr (REV) {
+    const float* z = w.dd[xZ] + b * D * D + col;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[kb][i] = z[(int64_t)(16 * kb + 4 * g4 + i) * D];
+  }
+}
+
+template <bool REV, int D, int C>
+__device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_in, float* s_out, int h_v) {
+  constexpr int NR = C / 16, NK = D / 16, NPF = C * D / 1024, LD = D + 8;
+  constexpr int NRS = (C + 31) / 32;   // 32-deep k-steps over the chunk rows
+  constexpr bool HALF = C == 16;
+  const int n = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int col = blockIdx.y * kBCols + 16 * wave + l16;
+  extern __shared__ float lds[];
+  __bf16* P1 = reinterpret_cast<__bf16*>(lds);  // C x LD
+  __bf16* P2 = P1 + C * LD;                      // C x LD
+  const int64_t srow = (((int64_t)n * h_v + h) * D + col) * D;
+  v4f Y[NK];
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Y[kb][i] = s_in ? s_in[srow + 16 * kb + 4 * g4 + i] : 0.f;
+  const int c_lo = w.co[n], c_hi = w.co[n + 1], nchunks = c_hi - c_lo;
+  v4f r1[NPF], r2[NPF];
+  float vb[NR][4], zz[NK][4];
+  if (nchunks > 0) {
+    chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, C * D, tid, r1, r2);
+    chain_rows16<REV, D, C>(w, REV ? c_hi - 1 : c_lo, h, h_v, col, g4, vb, zz);
+  }
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < nchunks; ++i) {
+    const int gc = REV ? c_hi - 1 - i : c_lo + i;
+    const int64_t b = (int64_t)gc * h_v + h;
+    lds_barrier();  // every wave is done with the previous chunk's P1, P2
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int q = tid + 256 * u, r = q / (D / 4), k4 = (q % (D / 4)) * 4;
+      *reinterpret_cast<uint2*>(P1 + r * LD + k4) =
+          make_uint2(pack_bf16x2(r1[u][0], r1[u][1]), pack_bf16x2(r1[u][2], r1[u][3]));
+      *reinterpret_cast<uint2*>(P2 + r * LD + k4) =
+          make_uint2(pack_bf16x2(r2[u][0], r2[u][1]), pack_bf16x2(r2[u][2], r2[u][3]));
+    }
+    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, C * D, tid, r1, r2);
+    float* ys = w.dd[REV ? xDXs : xXs] + b * D * D + col;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ys[(int64_t)(16 * kb + 4 * g4 + j) * D] = Y[kb][j];
+    lds_barrier();
+    // R = P1 Y (C x 16), then U = Vb -/+ R
+    v4f R[NR];
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb) R[rb] = zero4;
+#pragma unroll
+    for (int kp = 0; kp < NK / 2; ++kp) {
+      const bf16x8_t bop = frag_acc(Y[2 * kp], Y[2 * kp + 1]);
+#pragma unroll
+      for (int rb = 0; rb < NR; ++rb)
+        R[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_rows(P1 + (16 * rb + l16) * LD + 32 * kp, g4, false),
+                                                        bop, R[rb], 0, 0, 0);
+    }
+    float* uo = w.cd[REV ? mDU : mU] + b * C * D + col;
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        R[rb][j] = REV ? vb[rb][j] + R[rb][j] : vb[rb][j] - R[rb][j];
+        uo[(int64_t)(16 * rb + 4 * g4 + j) * D] = R[rb][j];
+      }
+    // Y = gam Y (+ Z) +/- P2^T U
+    const float gam = w.vec[b * kNVec * C + kVecGam * C + C - 1];
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Y[kb][j] = gam * Y[kb][j] + (REV ? zz[kb][j] : 0.f);
+#pragma unroll
+    for (int rp = 0; rp < NRS; ++rp) {
+      v4f ua = R[2 * rp], ub = HALF ? zero4 : R[(2 * rp + 1) < NR ? 2 * rp + 1 : 0];
+      if (REV) {
+        ua = -ua;
+        ub = -ub;
+      }
+      const bf16x8_t bop = frag_acc(ua, ub);
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb)
+        Y[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_cols(P2, LD, 32 * rp, 16 * kb, l16, g4, HALF), bop,
+                                                        Y[kb], 0, 0, 0);
+    }
+    if (i + 1 < nchunks) chain_rows16<REV, D, C>(w, REV ? gc - 1 : gc + 1, h, h_v, col, g4, vb, zz);
+  }
+  if (REV && s_out) {
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_out[srow + 16 * kb + 4 * g4 + i] = Y[kb][i];
+  }
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void bwd_chains_bf16_kernel(BwdWs w, const float* s0, const float* dsf,
+                                                              float* ds0, int h_v) {
+  if (blockIdx.z == 0) chain_body_bf16<false, D, C>(w, s0, nullptr, h_v);
+  else chain_body_bf16<true, D, C>(w, dsf, ds0, h_v);
+}
+
+template <int D, int C>
+hipError_t launch_chains_bf16(const BwdWs& w, const PrefillBwdParams& p, hipStream_t stream) {
+  const size_t lds = (size_t)2 * C * (D + 8) * sizeof(__bf16);
+  hipLaunchKernelGGL((bwd_chains_bf16_kernel<D, C>), dim3((unsigned)(p.n_seqs * p.h_v), D / kBCols, 2), dim3(256),
+                     lds, stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v);
+  return hipGetLastError();
+}
+
 // ------------------------------------------- C x C gradient combination
 // Per (chunk, V head), from dPm and dA = -T^T dT T^T:
 //   dQK  = scale Gam o dPm (lower incl.)            -> written over dPm
@@ -897,12 +1062,21 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
   if (L.err != hipSuccess) return L.err;
   {
     hipError_t e;
-    if (D == 64)
-      e = C == 16 ? launch_chains<64, 16>(w, p, stream) : C == 32 ? launch_chains<64, 32>(w, p, stream)
-                                                          : launch_chains<64, 64>(w, p, stream);
-    else
-      e = C == 16 ? launch_chains<128, 16>(w, p, stream) : C == 32 ? launch_chains<128, 32>(w, p, stream)
-                                                           : launch_chains<128, 64>(w, p, stream);
+    if constexpr (std::is_same<T, __bf16>::value) {
+      if (D == 64)
+        e = C == 16 ? launch_chains_bf16<64, 16>(w, p, stream) : C == 32 ? launch_chains_bf16<64, 32>(w, p, stream)
+                                                               : launch_chains_bf16<64, 64>(w, p, stream);
+      else
+        e = C == 16 ? launch_chains_bf16<128, 16>(w, p, stream)
+                    : C == 32 ? launch_chains_bf16<128, 32>(w, p, stream) : launch_chains_bf16<128, 64>(w, p, stream);
+    } else {
+      if (D == 64)
+        e = C == 16 ? launch_chains<64, 16>(w, p, stream) : C == 32 ? launch_chains<64, 32>(w, p, stream)
+                                                            : launch_chains<64, 64>(w, p, stream);
+      else
+        e = C == 16 ? launch_chains<128, 16>(w, p, stream) : C == 32 ? launch_chains<128, 32>(w, p, stream)
+                                                             : launch_chains<128, 64>(w, p, stream);
+    }
     if (e != hipSuccess) return e;
   }
   // chunk-local products
