@@ -279,7 +279,8 @@ gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
  *   d_o          [T, h_v, d_v] in io_dtype, contiguous.
  *   d_final_state [n_seqs, h_v, d_v, d_k] fp32, or NULL for zero.
  *   dq, dk       [T, h_qk, d_k] in io_dtype with token strides dq_stride and
- *                dk_stride; dv [T, h_v, d_v] with dv_stride.  They may be
+ *                dk_stride; dv [T, h_v, d_v] with dv_stride (every token
+ *                stride, inputs' included, a multiple of 8 elements).  They may be
  *                column slices of one [T, C] buffer (the conv output's
  *                gradient) and must not overlap any input.
  *   dg, dbeta    [T, h_v] fp32.

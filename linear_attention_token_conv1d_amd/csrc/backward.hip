@@ -335,16 +335,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
   float* GQ = w.cd[mGQ] + bv * C * D;
   float* BV = w.cd[mBV] + bv * C * D;
   float* DO = w.cd[mDO] + bv * C * D;
-  for (int e = tid; e < C * D; e += blockDim.x) {
+  for (int e = 4 * tid; e < C * D; e += 4 * blockDim.x) {
     const int r = e / D, c = e % D;
     const bool in = r < cr.len;
-    const float kn = Kn[e];
-    BK[e] = erase ? sB[r] * sGam[r] * kn : 0.f;
-    EK[e] = sE[r] * kn;
-    GQ[e] = scale * sGam[r] * Qn[e];
+    const v4f kn = *reinterpret_cast<const v4f*>(Kn + e), qn = *reinterpret_cast<const v4f*>(Qn + e);
+    const float bg = erase ? sB[r] * sGam[r] : 0.f;
+    *reinterpret_cast<v4f*>(BK + e) = bg * kn;
+    *reinterpret_cast<v4f*>(EK + e) = sE[r] * kn;
+    *reinterpret_cast<v4f*>(GQ + e) = (scale * sGam[r]) * qn;
     const int64_t tok = (int64_t)(cr.t0 + r);
-    BV[e] = in ? sB[r] * to_f32(v[tok * vs + (int64_t)h * D + c]) : 0.f;
-    DO[e] = in ? to_f32(d_o[(tok * h_v + h) * D + c]) : 0.f;
+    float vv[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
+    if (in) {
+      load4(v + tok * vs + (int64_t)h * D + c, vv);
+      load4(d_o + (tok * h_v + h) * D + c, dd);
+    }
+    *reinterpret_cast<v4f*>(BV + e) = v4f{sB[r] * vv[0], sB[r] * vv[1], sB[r] * vv[2], sB[r] * vv[3]};
+    *reinterpret_cast<v4f*>(DO + e) = v4f{dd[0], dd[1], dd[2], dd[3]};
   }
 }
 
@@ -779,12 +785,20 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
   float* dKn = w.cd[mDKn] + bv * C * D;
   float* dQn = w.cd[mDQn] + bv * C * D;
   const float* UdX = w.cd[mUdX] + bv * C * D;
-  for (int e = tid; e < C * D; e += 256) {
+  for (int e = 4 * tid; e < C * D; e += 4 * 256) {
     const int r = e / D, c = e % D;
-    const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r];
-    dKn[e] += (erase ? be * gm * TdW[e] : 0.f) + vec[kVecE * C + r] * UdX[e];
-    dQn[e] += scale * gm * DOX[e];
-    if (r < cr.len) dv[(int64_t)(cr.t0 + r) * dvs + (int64_t)h * D + c] = from_f32<T>(be * TdU[e]);
+    const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r], ee = vec[kVecE * C + r];
+    const float bg = erase ? be * gm : 0.f;
+    v4f dk = *reinterpret_cast<const v4f*>(dKn + e), dq = *reinterpret_cast<const v4f*>(dQn + e);
+    dk += bg * *reinterpret_cast<const v4f*>(TdW + e) + ee * *reinterpret_cast<const v4f*>(UdX + e);
+    dq += (scale * gm) * *reinterpret_cast<const v4f*>(DOX + e);
+    *reinterpret_cast<v4f*>(dKn + e) = dk;
+    *reinterpret_cast<v4f*>(dQn + e) = dq;
+    if (r < cr.len) {
+      const v4f t = be * *reinterpret_cast<const v4f*>(TdU + e);
+      float o[4] = {t[0], t[1], t[2], t[3]};
+      store4(dv + (int64_t)(cr.t0 + r) * dvs + (int64_t)h * D + c, o);
+    }
   }
 }
 

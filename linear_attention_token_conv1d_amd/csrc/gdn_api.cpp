@@ -133,6 +133,8 @@ gdn_status check_prefill_backward(const gdn_prefill_backward_args* a) {
   if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hv || a->dq_stride < hk || a->dk_stride < hk ||
       a->dv_stride < hv)
     return fail(GDN_ERR_INVALID_ARG, "%s: token strides smaller than a token's heads", f);
+  if ((a->q_stride | a->k_stride | a->v_stride | a->dq_stride | a->dk_stride | a->dv_stride) % 8)
+    return fail(GDN_ERR_ALIGNMENT, "%s: token strides must be multiples of 8 elements", f);
   const void* ptrs16[] = {a->q, a->k, a->v, a->d_o, a->dq, a->dk, a->dv, a->initial_state, a->d_final_state,
                           a->d_initial_state};
   for (const void* p : ptrs16)

@@ -181,6 +181,7 @@ def test_prefill_backward_validation():
     assert call(_bwd_args(n_seqs=2)) == 1  # cu_seqlens missing
     assert call(_bwd_args(dq_stride=64)) == 1
     assert call(_bwd_args(dq=(1 << 32) + 8)) == 3
+    assert call(_bwd_args(dv_stride=260)) == 3
     assert call(_bwd_args(dk=(1 << 32) + 16)) == 1  # dk overlaps q
     a = _bwd_args()
     a.workspace_bytes -= 1
