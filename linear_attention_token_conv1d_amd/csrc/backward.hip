@@ -677,7 +677,7 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(BwdWs w, int h_qk, int h_v,
   if (gc >= *w.nc) return;
   const int hq = h / (h_v / h_qk);
   const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
-  __shared__ float sGG[64][65], sDK[64][65], sG[64], sB[64];
+  __shared__ float sGG[64][65], sDK[64][65], sDB[64][65], sG[64], sB[64];
   float* vec = w.vec + bv * kNVec * C;
   for (int r = tid; r < C; r += 256) {
     sG[r] = vec[kVecG * C + r];
@@ -692,14 +692,16 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(BwdWs w, int h_qk, int h_v,
     const int r = e / C, j = e % C;
     const float gm = j <= r ? expf(sG[r] - sG[j]) : 0.f;
     const float dp = dPm[e];
-    float gg = scale * gm * QK[e] * dp, dk = 0.f;
+    float gg = scale * gm * QK[e] * dp, dk = 0.f, db = 0.f;
     if (erase && j < r) {
-      const float da = dA[e];
-      dk = sB[r] * gm * da;
-      gg += dk * KK[e];
+      const float gka = gm * KK[e] * dA[e];
+      dk = sB[r] * gm * dA[e];
+      gg += sB[r] * gka;
+      db = gka;
     }
     sGG[r][j] = gg;
     sDK[r][j] = dk;
+    sDB[r][j] = db;
     dPm[e] = scale * gm * dp;
   }
   __syncthreads();
@@ -710,7 +712,7 @@ __global__ __launch_bounds__(256) void bwd_cc_kernel(BwdWs w, int h_qk, int h_v,
     for (int j = 0; j < C; ++j) {
       row += sGG[r][j];
       col += sGG[j][r];
-      if (erase && j < r) db += expf(sG[r] - sG[j]) * KK[(int64_t)r * C + j] * dA[(int64_t)r * C + j];
+      db += sDB[r][j];
     }
     vec[kVecDGx * C + r] = row - col;
     vec[kVecDBx * C + r] = db;
@@ -992,15 +994,25 @@ __global__ __launch_bounds__(256) void conv_bwd_state_kernel(const T* x, const T
   }
 }
 
+// Per 64 channels: four thread groups each sum every fourth tile, then the
+// four partial sums are added in a fixed order (deterministic results).
 __global__ __launch_bounds__(256) void conv_bwd_reduce_kernel(const float* part, int ntiles, int C, int W,
                                                               float* dweight, float* dbias) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
+  __shared__ float red[4][5][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6, c = blockIdx.x * 64 + cl;
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < ntiles; ++t)
-    for (int j = 0; j < 5; ++j) acc[j] += part[((int64_t)t * 5 + j) * C + c];
-  for (int j = 0; j < W; ++j) dweight[c * W + j] = acc[j];
-  if (dbias) dbias[c] = acc[4];
+  if (c < C)
+    for (int t = grp; t < ntiles; t += 4)
+#pragma unroll
+      for (int j = 0; j < 5; ++j) acc[j] += part[((int64_t)t * 5 + j) * C + c];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) red[grp][j][cl] = acc[j];
+  __syncthreads();
+  if (grp == 0 && c < C) {
+    for (int j = 0; j < 5; ++j) acc[j] = ((red[0][j][cl] + red[1][j][cl]) + red[2][j][cl]) + red[3][j][cl];
+    for (int j = 0; j < W; ++j) dweight[c * W + j] = acc[j];
+    if (dbias) dbias[c] = acc[4];
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -1151,8 +1163,8 @@ hipError_t conv_backward_impl(const ConvBwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((conv_bwd_kernel<T, 2>), grid, dim3(256), 0, stream, x, w, b, st, dy, p.d_new_state,
                          p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.act, dx, part);
   }
-  hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3(cg), dim3(256), 0, stream, part, ntiles, p.channels, p.width,
-                     p.dweight, p.dbias);
+  hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((p.channels + 63) / 64), dim3(256), 0, stream, part, ntiles,
+                     p.channels, p.width, p.dweight, p.dbias);
   if (p.d_conv_state)
     hipLaunchKernelGGL(conv_bwd_state_kernel<T>, dim3(p.n_seqs, cg), dim3(256), 0, stream, x, w, b, st, dy,
                        p.d_new_state, p.cu_seqlens, p.n_seqs, p.total_tokens, p.channels, p.width, p.act,
