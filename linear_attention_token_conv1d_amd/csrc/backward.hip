@@ -178,17 +178,29 @@ __device__ __forceinline__ void lds_barrier() {
 // l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of its 16 x 4 and
 // 4 x 16 slices, and holds C rows 4 (l / 16) .. +3 of column l % 16.
 constexpr int kGK = 32;
+// Global -> registers for one 32-deep stage: two 16-byte loads per operand
+// per thread (M, N and K are multiples of 16, so a 4-element group is
+// either wholly inside or wholly outside the matrix).
 __device__ __forceinline__ void bg_fetch(const BG& p, const float* A, const float* B, int m0, int n0, int k0,
-                                         int tid, float (&ra)[8], float (&rb)[8]) {
+                                         int tid, v4f (&ra)[2], v4f (&rb)[2]) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + 256 * u;
-    const int mm = p.ta ? (e & 63) : (e >> 5), ka = p.ta ? (e >> 6) : (e & 31);
-    const int m = m0 + mm, k = k0 + ka;
-    ra[u] = (m < p.M && k < p.K) ? (p.ta ? A[(int64_t)k * p.lda + m] : A[(int64_t)m * p.lda + k]) : 0.f;
-    const int nn = p.tb ? (e >> 5) : (e & 63), kb = p.tb ? (e & 31) : (e >> 6);
-    const int n = n0 + nn, kk = k0 + kb;
-    rb[u] = (n < p.N && kk < p.K) ? (p.tb ? B[(int64_t)n * p.ldb + kk] : B[(int64_t)kk * p.ldb + n]) : 0.f;
+  for (int u = 0; u < 2; ++u) {
+    const int f = tid + 256 * u;
+    if (p.ta) {  // A stored [k][m]: 4 consecutive m
+      const int k = k0 + (f >> 4), m = m0 + (f & 15) * 4;
+      ra[u] = (k < p.K && m < p.M) ? *reinterpret_cast<const v4f*>(A + (int64_t)k * p.lda + m) : z;
+    } else {     // A stored [m][k]: 4 consecutive k
+      const int m = m0 + (f >> 3), k = k0 + (f & 7) * 4;
+      ra[u] = (m < p.M && k < p.K) ? *reinterpret_cast<const v4f*>(A + (int64_t)m * p.lda + k) : z;
+    }
+    if (p.tb) {  // B stored [n][k]: 4 consecutive k
+      const int n = n0 + (f >> 3), k = k0 + (f & 7) * 4;
+      rb[u] = (n < p.N && k < p.K) ? *reinterpret_cast<const v4f*>(B + (int64_t)n * p.ldb + k) : z;
+    } else {     // B stored [k][n]: 4 consecutive n
+      const int k = k0 + (f >> 4), n = n0 + (f & 15) * 4;
+      rb[u] = (k < p.K && n < p.N) ? *reinterpret_cast<const v4f*>(B + (int64_t)k * p.ldb + n) : z;
+    }
   }
 }
 
@@ -208,17 +220,25 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  float ra[8], rb[8];
+  v4f ra[2], rb[2];
   bg_fetch(p, A, B, m0, n0, 0, tid, ra, rb);
   for (int k0 = 0; k0 < p.K; k0 += kGK) {
     lds_barrier();  // the previous stage's MFMAs are done reading As, Bs
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u;
-      if (p.ta) As[e >> 6][e & 63] = ra[u];
-      else As[e & 31][e >> 5] = ra[u];
-      if (p.tb) Bs[e & 31][e >> 5] = rb[u];
-      else Bs[e >> 6][e & 63] = rb[u];
+    for (int u = 0; u < 2; ++u) {
+      const int f = tid + 256 * u;
+      if (p.ta) {
+        *reinterpret_cast<v4f*>(&As[f >> 4][(f & 15) * 4]) = ra[u];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) As[(f & 7) * 4 + j][f >> 3] = ra[u][j];
+      }
+      if (p.tb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Bs[(f & 7) * 4 + j][f >> 3] = rb[u][j];
+      } else {
+        *reinterpret_cast<v4f*>(&Bs[f >> 4][(f & 15) * 4]) = rb[u];
+      }
     }
     if (k0 + kGK < p.K) bg_fetch(p, A, B, m0, n0, k0 + kGK, tid, ra, rb);
     lds_barrier();
