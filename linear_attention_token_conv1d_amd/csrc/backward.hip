@@ -212,7 +212,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
   const float* A = p.A + gc * p.a_sc + (int64_t)(h / p.a_hdiv) * p.a_sh;
   const float* B = p.B + gc * p.b_sc + (int64_t)(h / p.b_hdiv) * p.b_sh;
   float* Cm = p.Cm + gc * p.c_sc + (int64_t)h * p.c_sh;
-  __shared__ float As[kGK][68], Bs[kGK][68];
+  __shared__ float smem[2 * kGK * 68];  // A and B stages; the output tile at the end
+  float(*As)[68] = reinterpret_cast<float(*)[68]>(smem);
+  float(*Bs)[68] = reinterpret_cast<float(*)[68]>(smem + kGK * 68);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mw = (wave >> 1) * 32, nw = (wave & 1) * 32, l16 = lane & 15, g4 = lane >> 4;
   v4f acc[2][2];
@@ -252,19 +254,27 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
       acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
   }
+  // the 64 x 64 tile through LDS, then whole 16-byte rows to memory
+  float(*Cs)[68] = reinterpret_cast<float(*)[68]>(smem);
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + mw + 16 * i + 4 * g4 + r, n = n0 + nw + 16 * j + l16;
-        if (m < p.M && n < p.N) {
-          float* c = Cm + (int64_t)m * p.ldc + n;
-          const float v = p.alpha * acc[i][j][r];
-          *c = p.accum ? *c + v : v;
-        }
-      }
+      for (int r = 0; r < 4; ++r) Cs[mw + 16 * i + 4 * g4 + r][nw + 16 * j + l16] = p.alpha * acc[i][j][r];
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int f = tid + 256 * u, mm = f >> 4, n4 = (f & 15) * 4;
+    const int m = m0 + mm, n = n0 + n4;
+    if (m < p.M && n < p.N) {
+      v4f* c = reinterpret_cast<v4f*>(Cm + (int64_t)m * p.ldc + n);
+      v4f v = *reinterpret_cast<const v4f*>(&Cs[mm][n4]);
+      if (p.accum) v += *c;
+      *c = v;
+    }
+  }
 }
 
 // ------------------------------------------------------- stage: Kn, Qn
