@@ -771,14 +771,29 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
   const float* DU = w.cd[mDU] + bv * C * D;
   const float* PdO = w.cd[mPdO] + bv * C * D;
   const float* TdU = w.cd[mUt] + bv * C * D;  // T^T dU was written over Ut
+  // row dots: lane covers D / 64 consecutive columns of row r (one wave per row)
+  const int per = D / 64;  // 1 or 2
   for (int r = wave; r < C; r += 4) {
     float a = 0.f, s = 0.f, u = 0.f, b1 = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      const int64_t e = (int64_t)r * D + c;
-      a += GQ[e] * DOX[e];
-      s += TdW[e] * Kn[e];
-      u += U[e] * (DU[e] - PdO[e]);
-      if (r < cr.len) b1 += to_f32(v[(int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c]) * TdU[e];
+    const int c0 = per * lane;
+    const int64_t e = (int64_t)r * D + c0;
+    if (per == 2) {
+      const float2 gq = *reinterpret_cast<const float2*>(GQ + e), dx = *reinterpret_cast<const float2*>(DOX + e);
+      const float2 tw = *reinterpret_cast<const float2*>(TdW + e), kn = *reinterpret_cast<const float2*>(Kn + e);
+      const float2 uu = *reinterpret_cast<const float2*>(U + e), du = *reinterpret_cast<const float2*>(DU + e);
+      const float2 pd = *reinterpret_cast<const float2*>(PdO + e), tu = *reinterpret_cast<const float2*>(TdU + e);
+      a = gq.x * dx.x + gq.y * dx.y;
+      s = tw.x * kn.x + tw.y * kn.y;
+      u = uu.x * (du.x - pd.x) + uu.y * (du.y - pd.y);
+      if (r < cr.len) {
+        const T* vr = v + (int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c0;
+        b1 = to_f32(vr[0]) * tu.x + to_f32(vr[1]) * tu.y;
+      }
+    } else {
+      a = GQ[e] * DOX[e];
+      s = TdW[e] * Kn[e];
+      u = U[e] * (DU[e] - PdO[e]);
+      if (r < cr.len) b1 = to_f32(v[(int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c0]) * TdU[e];
     }
     a = wave_sum(a);
     s = wave_sum(s);
@@ -795,7 +810,10 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
   const float* Xs = w.dd[xXs] + bv * D * D;
   const float* dXs = w.dd[xDXs] + bv * D * D;
   float xd = 0.f;
-  for (int e = tid; e < D * D; e += 256) xd += Xs[e] * dXs[e];
+  for (int e = 4 * tid; e < D * D; e += 4 * 256) {
+    const v4f x4 = *reinterpret_cast<const v4f*>(Xs + e), d4 = *reinterpret_cast<const v4f*>(dXs + e);
+    xd += x4[0] * d4[0] + x4[1] * d4[1] + x4[2] * d4[2] + x4[3] * d4[3];
+  }
   xd = wave_sum(xd);
   if (lane == 0) sRed[wave] = xd;
   __syncthreads();
