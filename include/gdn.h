@@ -259,7 +259,9 @@ gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
 /* ------------------------------------------------------------------------
  * gdn_prefill_backward -- gradients of gdn_prefill, for training through the
  * chunked form ("Inside Qwen3.5", section 5: the gated delta rule layer is
- * trained at scale; "DeltaNet explained", the chunkwise training form).
+ * trained at scale; "Hybrid Mamba-Transformer MoE", the training
+ * infrastructure section: the linear-recurrence layers need training paths
+ * of their own).
  *
  * Given the forward call's inputs and the gradients of a loss with respect to
  * its outputs (d_o, d_final_state), writes the gradients with respect to q,
@@ -268,8 +270,9 @@ gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
  * recurrence: per chunk the state-independent quantities are recomputed, the
  * chunk-start states are rebuilt by a forward chain over the chunks, the
  * state gradients run back over the chunks, and each chunk's own gradients
- * follow from both.  Arithmetic is fp32 throughout (fp32 inputs are used as
- * given, bf16 inputs are widened exactly).
+ * follow from both.  Arithmetic is fp32 (bf16 inputs are widened exactly),
+ * except that with bf16 inputs the two serial chains take bf16 MFMA
+ * operands, as the forward scan does; their accumulators stay fp32.
  *
  *   flags, io_dtype, n_seqs, total_tokens, h_qk, h_v, d_k, d_v, chunk,
  *   scale, q, k, v (with their strides), g, beta, initial_state, cu_seqlens:

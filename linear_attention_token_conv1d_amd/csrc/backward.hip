@@ -3,8 +3,8 @@
 //
 // Per chunk of one sequence and one V head (K^, Q^ the normalised keys and
 // queries, rows past the chunk's end padded with zeros and beta = g = 0, so
-// every chunk is a full C rows), the forward is ("Inside Qwen3.5", sections
-// 4-5; "DeltaNet explained", the chunkwise WY form):
+// every chunk is a full C rows), the forward is the recurrence of "Inside
+// Qwen3.5", sections 4-5, unrolled over one chunk (an exact rearrangement):
 //   G = cumsum(g), gam = e^G, e_j = e^{G_{C-1} - G_j}, Gam_rj = e^{G_r - G_j}
 //   A = strict_lower(beta_r Gam_rj K^_r.K^_j),  T = (I + A)^-1
 //   W = T diag(beta gam) K^,  Ut = T diag(beta) V,  U = Ut - W X
@@ -21,9 +21,11 @@
 //      dK^, dQ^, dV, dbeta and dG (then dg is the reverse cumulative sum of dG);
 //   5. dK^ and dQ^ of a QK head add up over the V heads that read it and
 //      pass back through the L2 norm.
-// Every product runs in fp32.  The design favours simple, independently
-// checkable stages: a batched fp32 GEMM with LDS tiles, two chain launches,
-// and elementwise kernels that combine the pieces.
+// The stages stay simple and separately checkable: a batched fp32-MFMA GEMM
+// over (chunk, head) for the state-independent and chunk-local products, one
+// launch that runs both serial chains (bf16 MFMA operands for bf16 inputs,
+// fp32 VALU for fp32 inputs, fp32 state either way), and elementwise kernels
+// that combine the pieces.  Every intermediate is an fp32 workspace array.
 #include <type_traits>
 
 #include "gdn_device.h"
