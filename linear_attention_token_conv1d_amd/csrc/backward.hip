@@ -39,10 +39,12 @@ namespace {
 // (n_seqs + 1), then one (sequence, first token, rows) record per chunk.
 // Then fp32 arrays, each [max_chunks][heads][rows][cols]:
 //   per QK head: Kn, Qn (C x D), KK, QK (C x C)
-//   per V head:  vec (8 x C), five C x C, sixteen C x D and three D x D
-enum { kVecG = 0, kVecGam, kVecE, kVecBeta, kVecDGx, kVecDBx, kNVec = 8 };
+//   per V head:  vec (8 x C), five C x C, thirteen C x D and three D x D
+// vec rows: G, gam, e, beta, two gradient partials, beta gam (0 without the
+// erase term) and scale gam; the last two scale K^ and Q^ rows on the fly
+enum { kVecG = 0, kVecGam, kVecE, kVecBeta, kVecDGx, kVecDBx, kVecBG, kVecSG, kNVec };
 enum { cT = 0, cPm, cDPm, cDT, cM1, kNCC };
-enum { mBK = 0, mEK, mGQ, mBV, mDO, mW, mUt, mU, mDU, mPdO, mDW, mDOX, mUdX, mTdW, mDKn, mDQn, kNCD };
+enum { mBV = 0, mDO, mW, mUt, mU, mDU, mPdO, mDW, mDOX, mUdX, mTdW, mDKn, mDQn, kNCD };
 enum { xXs = 0, xDXs, xZ, kNDD };
 
 struct ChunkRec {
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(BwdWs w, const int32_t* c
 
 // ---------------------------------------------------------- batched GEMM
 // C[b] = alpha op(A[b]) op(B[b]) (+ C[b] when accum), fp32, for every chunk
-// b = (chunk, head) in use.  op(A) is M x K (A row-major M x K, or K x M when
+// b = (chunk, head) in use; an operand may have each stored row scaled first.  op(A) is M x K (A row-major M x K, or K x M when
 // ta), op(B) is K x N (B row-major K x N, or N x K when tb).  A QK-head
 // operand is shared by the V heads of its group (head index / hdiv).
 struct BG {
@@ -157,6 +159,11 @@ struct BG {
   int a_hdiv, b_hdiv, H, ta, tb, accum;
   float alpha;
   const int* nc;
+  // optional per-row scales of the stored operand rows (a row of the per
+  // (chunk, V head) vec block, e.g. beta gam for the rows of K^), or null
+  const float* as;
+  const float* bs;
+  int vstr;  // floats per (chunk, head) vec block
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -183,26 +190,34 @@ constexpr int kGK = 32;
 // Global -> registers for one 32-deep stage: two 16-byte loads per operand
 // per thread (M, N and K are multiples of 16, so a 4-element group is
 // either wholly inside or wholly outside the matrix).
-__device__ __forceinline__ void bg_fetch(const BG& p, const float* A, const float* B, int m0, int n0, int k0,
-                                         int tid, v4f (&ra)[2], v4f (&rb)[2]) {
+__device__ __forceinline__ void bg_fetch(const BG& p, const float* A, const float* B, const float* as,
+                                         const float* bs, int m0, int n0, int k0, int tid, v4f (&ra)[2],
+                                         v4f (&rb)[2]) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int f = tid + 256 * u;
+    int ar, br;  // stored rows of the two groups
     if (p.ta) {  // A stored [k][m]: 4 consecutive m
       const int k = k0 + (f >> 4), m = m0 + (f & 15) * 4;
+      ar = k;
       ra[u] = (k < p.K && m < p.M) ? *reinterpret_cast<const v4f*>(A + (int64_t)k * p.lda + m) : z;
     } else {     // A stored [m][k]: 4 consecutive k
       const int m = m0 + (f >> 3), k = k0 + (f & 7) * 4;
+      ar = m;
       ra[u] = (m < p.M && k < p.K) ? *reinterpret_cast<const v4f*>(A + (int64_t)m * p.lda + k) : z;
     }
     if (p.tb) {  // B stored [n][k]: 4 consecutive k
       const int n = n0 + (f >> 3), k = k0 + (f & 7) * 4;
+      br = n;
       rb[u] = (n < p.N && k < p.K) ? *reinterpret_cast<const v4f*>(B + (int64_t)n * p.ldb + k) : z;
     } else {     // B stored [k][n]: 4 consecutive n
       const int k = k0 + (f >> 4), n = n0 + (f & 15) * 4;
+      br = k;
       rb[u] = (k < p.K && n < p.N) ? *reinterpret_cast<const v4f*>(B + (int64_t)k * p.ldb + n) : z;
     }
+    if (as && ar < (p.ta ? p.K : p.M)) ra[u] *= as[ar];
+    if (bs && br < (p.tb ? p.N : p.K)) rb[u] *= bs[br];
   }
 }
 
@@ -214,6 +229,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
   const float* A = p.A + gc * p.a_sc + (int64_t)(h / p.a_hdiv) * p.a_sh;
   const float* B = p.B + gc * p.b_sc + (int64_t)(h / p.b_hdiv) * p.b_sh;
   float* Cm = p.Cm + gc * p.c_sc + (int64_t)h * p.c_sh;
+  const int64_t vb = ((int64_t)gc * p.H + h) * p.vstr;  // vec block of this (chunk, head)
+  const float* as = p.as ? p.as + vb : nullptr;
+  const float* bs = p.bs ? p.bs + vb : nullptr;
   __shared__ float smem[2 * kGK * 68];  // A and B stages; the output tile at the end
   float(*As)[68] = reinterpret_cast<float(*)[68]>(smem);
   float(*Bs)[68] = reinterpret_cast<float(*)[68]>(smem + kGK * 68);
@@ -225,7 +243,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v4f ra[2], rb[2];
-  bg_fetch(p, A, B, m0, n0, 0, tid, ra, rb);
+  bg_fetch(p, A, B, as, bs, m0, n0, 0, tid, ra, rb);
   for (int k0 = 0; k0 < p.K; k0 += kGK) {
     lds_barrier();  // the previous stage's MFMAs are done reading As, Bs
 #pragma unroll
@@ -244,7 +262,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
         *reinterpret_cast<v4f*>(&Bs[f >> 4][(f & 15) * 4]) = rb[u];
       }
     }
-    if (k0 + kGK < p.K) bg_fetch(p, A, B, m0, n0, k0 + kGK, tid, ra, rb);
+    if (k0 + kGK < p.K) bg_fetch(p, A, B, as, bs, m0, n0, k0 + kGK, tid, ra, rb);
     lds_barrier();
 #pragma unroll
     for (int ks = 0; ks < kGK; ks += 4) {
@@ -309,7 +327,7 @@ __global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, 
 
 // ----------------------------------------- prep: gates, T, Pm, scaled rows
 // Per (chunk, V head): G, gam, e, beta; T = (I + A)^-1 by forward
-// substitution; Pm; and the row-scaled operands BK, EK, GQ, BV and dO.
+// substitution; Pm; the row scalings of K^ and Q^ (vec rows); beta V and dO.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, const float* beta, const T* v,
                                                        int64_t vs, const T* d_o, int h_qk, int h_v, int D,
@@ -339,6 +357,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
     vec[kVecGam * C + r] = sGam[r];
     vec[kVecE * C + r] = sE[r];
     vec[kVecBeta * C + r] = sB[r];
+    vec[kVecBG * C + r] = erase ? sB[r] * sGam[r] : 0.f;
+    vec[kVecSG * C + r] = scale * sGam[r];
   }
   const float* KK = w.KK + bq * C * C;
   const float* QK = w.QK + bq * C * C;
@@ -360,21 +380,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
   }
   float* Tm = w.cc[cT] + bv * C * C;
   for (int e = tid; e < C * C; e += blockDim.x) Tm[e] = sT[e / C][e % C];
-  const float* Kn = w.Kn + bq * C * D;
-  const float* Qn = w.Qn + bq * C * D;
-  float* BK = w.cd[mBK] + bv * C * D;
-  float* EK = w.cd[mEK] + bv * C * D;
-  float* GQ = w.cd[mGQ] + bv * C * D;
+  // beta V and dO in the chunk layout (the row scalings of K^ and Q^ are
+  // applied where they are read)
   float* BV = w.cd[mBV] + bv * C * D;
   float* DO = w.cd[mDO] + bv * C * D;
   for (int e = 4 * tid; e < C * D; e += 4 * blockDim.x) {
     const int r = e / D, c = e % D;
     const bool in = r < cr.len;
-    const v4f kn = *reinterpret_cast<const v4f*>(Kn + e), qn = *reinterpret_cast<const v4f*>(Qn + e);
-    const float bg = erase ? sB[r] * sGam[r] : 0.f;
-    *reinterpret_cast<v4f*>(BK + e) = bg * kn;
-    *reinterpret_cast<v4f*>(EK + e) = sE[r] * kn;
-    *reinterpret_cast<v4f*>(GQ + e) = (scale * sGam[r]) * qn;
     const int64_t tok = (int64_t)(cr.t0 + r);
     float vv[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
     if (in) {
@@ -398,21 +410,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
 // launch runs both.  The next chunk's two C x D operands are fetched into
 // registers while the current chunk computes.
 constexpr int kCW = 16;
+// W and diag(e) K^ of one chunk (e K^ formed from the QK head's rows of K^)
 template <bool REV, int NPF>
-__device__ __forceinline__ void chain_fetch(const BwdWs& w, int gc, int h, int h_v, int cd, int tid,
-                                            v4f (&r1)[NPF], v4f (&r2)[NPF]) {
-  const int64_t b = (int64_t)gc * h_v + h;
-  const v4f* p1 = reinterpret_cast<const v4f*>(w.cd[REV ? mEK : mW] + b * cd);
-  const v4f* p2 = reinterpret_cast<const v4f*>(w.cd[REV ? mW : mEK] + b * cd);
+__device__ __forceinline__ void chain_fetch(const BwdWs& w, int gc, int h, int h_v, int h_qk, int D, int C,
+                                            int tid, v4f (&r1)[NPF], v4f (&r2)[NPF]) {
+  const int64_t b = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + h / (h_v / h_qk);
+  const v4f* pw = reinterpret_cast<const v4f*>(w.cd[mW] + b * C * D);
+  const v4f* pk = reinterpret_cast<const v4f*>(w.Kn + bq * C * D);
+  const float* e = w.vec + b * kNVec * C + kVecE * C;
 #pragma unroll
   for (int u = 0; u < NPF; ++u) {
-    r1[u] = p1[tid + 256 * u];
-    r2[u] = p2[tid + 256 * u];
+    const int q = tid + 256 * u;
+    const v4f wv = pw[q], ek = e[q / (D / 4)] * pk[q];
+    r1[u] = REV ? ek : wv;
+    r2[u] = REV ? wv : ek;
   }
 }
 
 template <bool REV, int D, int C>
-__device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, float* s_out, int h_v) {
+__device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, float* s_out, int h_v, int h_qk) {
   const int n = blockIdx.x / h_v, h = blockIdx.x % h_v, col0 = blockIdx.y * kCW, tid = threadIdx.x;
   extern __shared__ float lds[];
   constexpr int LP = D + 4;    // P1 row pitch: the 16 rows a wave reads fall in distinct banks
@@ -431,7 +447,7 @@ __device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, fl
   const int yk = tid / TPR, yc = (tid % TPR) * NPT;
   v4f r1[NPF], r2[NPF];
   const int nchunks = c_hi - c_lo;
-  if (nchunks > 0) chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, C * D, tid, r1, r2);
+  if (nchunks > 0) chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, h_qk, D, C, tid, r1, r2);
   for (int i = 0; i < nchunks; ++i) {
     const int gc = REV ? c_hi - 1 - i : c_lo + i;
     const int64_t b = (int64_t)gc * h_v + h;
@@ -442,7 +458,7 @@ __device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, fl
       *reinterpret_cast<v4f*>(P1 + (q / (D / 4)) * LP + (q % (D / 4)) * 4) = r1[u];
       reinterpret_cast<v4f*>(P2)[q] = r2[u];
     }
-    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, C * D, tid, r1, r2);
+    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, h_qk, D, C, tid, r1, r2);
     float* ys = w.dd[REV ? xDXs : xXs] + b * D * D;
     for (int e = tid; e < D * kCW; e += 256) ys[(int64_t)(e / kCW) * D + col0 + e % kCW] = Y[e];
     lds_barrier();
@@ -519,9 +535,9 @@ __device__ __forceinline__ void chain_body(const BwdWs& w, const float* s_in, fl
 
 template <int D, int C>
 __global__ __launch_bounds__(256) void bwd_chains_kernel(BwdWs w, const float* s0, const float* dsf, float* ds0,
-                                                         int h_v) {
-  if (blockIdx.z == 0) chain_body<false, D, C>(w, s0, nullptr, h_v);
-  else chain_body<true, D, C>(w, dsf, ds0, h_v);
+                                                         int h_v, int h_qk) {
+  if (blockIdx.z == 0) chain_body<false, D, C>(w, s0, nullptr, h_v, h_qk);
+  else chain_body<true, D, C>(w, dsf, ds0, h_v, h_qk);
 }
 
 template <int D, int C>
@@ -531,7 +547,7 @@ hipError_t launch_chains(const BwdWs& w, const PrefillBwdParams& p, hipStream_t 
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_chains_kernel<D, C>), dim3((unsigned)(p.n_seqs * p.h_v), D / kCW, 2), dim3(256), lds,
-                     stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v);
+                     stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v, p.h_qk);
   return hipGetLastError();
 }
 
@@ -591,7 +607,8 @@ __device__ __forceinline__ void chain_rows16(const BwdWs& w, int gc, int h, int 
 }
 
 template <bool REV, int D, int C>
-__device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_in, float* s_out, int h_v) {
+__device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_in, float* s_out, int h_v,
+                                                int h_qk) {
   constexpr int NR = C / 16, NK = D / 16, NPF = C * D / 1024, LD = D + 8;
   constexpr int NRS = (C + 31) / 32;   // 32-deep k-steps over the chunk rows
   constexpr bool HALF = C == 16;
@@ -611,7 +628,7 @@ __device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_i
   v4f r1[NPF], r2[NPF];
   float vb[NR][4], zz[NK][4];
   if (nchunks > 0) {
-    chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, C * D, tid, r1, r2);
+    chain_fetch<REV, NPF>(w, REV ? c_hi - 1 : c_lo, h, h_v, h_qk, D, C, tid, r1, r2);
     chain_rows16<REV, D, C>(w, REV ? c_hi - 1 : c_lo, h, h_v, col, g4, vb, zz);
   }
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -627,7 +644,7 @@ __device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_i
       *reinterpret_cast<uint2*>(P2 + r * LD + k4) =
           make_uint2(pack_bf16x2(r2[u][0], r2[u][1]), pack_bf16x2(r2[u][2], r2[u][3]));
     }
-    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, C * D, tid, r1, r2);
+    if (i + 1 < nchunks) chain_fetch<REV, NPF>(w, REV ? gc - 1 : gc + 1, h, h_v, h_qk, D, C, tid, r1, r2);
     float* ys = w.dd[REV ? xDXs : xXs] + b * D * D + col;
 #pragma unroll
     for (int kb = 0; kb < NK; ++kb)
@@ -685,16 +702,16 @@ __device__ __forceinline__ void chain_body_bf16(const BwdWs& w, const float* s_i
 
 template <int D, int C>
 __global__ __launch_bounds__(256) void bwd_chains_bf16_kernel(BwdWs w, const float* s0, const float* dsf,
-                                                              float* ds0, int h_v) {
-  if (blockIdx.z == 0) chain_body_bf16<false, D, C>(w, s0, nullptr, h_v);
-  else chain_body_bf16<true, D, C>(w, dsf, ds0, h_v);
+                                                              float* ds0, int h_v, int h_qk) {
+  if (blockIdx.z == 0) chain_body_bf16<false, D, C>(w, s0, nullptr, h_v, h_qk);
+  else chain_body_bf16<true, D, C>(w, dsf, ds0, h_v, h_qk);
 }
 
 template <int D, int C>
 hipError_t launch_chains_bf16(const BwdWs& w, const PrefillBwdParams& p, hipStream_t stream) {
   const size_t lds = (size_t)2 * C * (D + 8) * sizeof(__bf16);
   hipLaunchKernelGGL((bwd_chains_bf16_kernel<D, C>), dim3((unsigned)(p.n_seqs * p.h_v), D / kBCols, 2), dim3(256),
-                     lds, stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v);
+                     lds, stream, w, p.initial_state, p.d_final_state, p.d_initial_state, p.h_v, p.h_qk);
   return hipGetLastError();
 }
 
@@ -765,7 +782,7 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
   const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
   const float* vec = w.vec + bv * kNVec * C;
   __shared__ float sDG[64], sDB[64], sU[64], sRed[4];
-  const float* GQ = w.cd[mGQ] + bv * C * D;
+  const float* Qn = w.Qn + bq * C * D;
   const float* DOX = w.cd[mDOX] + bv * C * D;
   const float* TdW = w.cd[mTdW] + bv * C * D;
   const float* Kn = w.Kn + bq * C * D;
@@ -780,7 +797,7 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
     const int c0 = per * lane;
     const int64_t e = (int64_t)r * D + c0;
     if (per == 2) {
-      const float2 gq = *reinterpret_cast<const float2*>(GQ + e), dx = *reinterpret_cast<const float2*>(DOX + e);
+      const float2 gq = *reinterpret_cast<const float2*>(Qn + e), dx = *reinterpret_cast<const float2*>(DOX + e);
       const float2 tw = *reinterpret_cast<const float2*>(TdW + e), kn = *reinterpret_cast<const float2*>(Kn + e);
       const float2 uu = *reinterpret_cast<const float2*>(U + e), du = *reinterpret_cast<const float2*>(DU + e);
       const float2 pd = *reinterpret_cast<const float2*>(PdO + e), tu = *reinterpret_cast<const float2*>(TdU + e);
@@ -792,7 +809,7 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
         b1 = to_f32(vr[0]) * tu.x + to_f32(vr[1]) * tu.y;
       }
     } else {
-      a = GQ[e] * DOX[e];
+      a = Qn[e] * DOX[e];
       s = TdW[e] * Kn[e];
       u = U[e] * (DU[e] - PdO[e]);
       if (r < cr.len) b1 = to_f32(v[(int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c0]) * TdU[e];
@@ -803,7 +820,7 @@ __global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, i
     b1 = wave_sum(b1);
     if (lane == 0) {
       const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r];
-      sDG[r] = a + (erase ? be * gm * s : 0.f) + vec[kVecDGx * C + r] - u;
+      sDG[r] = vec[kVecSG * C + r] * a + (erase ? be * gm * s : 0.f) + vec[kVecDGx * C + r] - u;
       sDB[r] = b1 + vec[kVecDBx * C + r] + (erase ? gm * s : 0.f);
       sU[r] = u;
     }
@@ -1078,7 +1095,7 @@ BG gemm(const float* A, const float* B, float* Cm, int M, int N, int K, int lda,
         int64_t a_sc, int64_t a_sh, int a_hdiv, int64_t b_sc, int64_t b_sh, int b_hdiv, int64_t c_sc, int64_t c_sh,
         int H, float alpha, int accum, const int* nc) {
   return BG{A, B, Cm, M, N, K, lda, ldb, ldc, a_sc, a_sh, b_sc, b_sh, c_sc, c_sh, a_hdiv, b_hdiv, H, ta, tb,
-            accum, alpha, nc};
+            accum, alpha, nc, nullptr, nullptr, 0};
 }
 
 void run_gemm(Launcher& L, const BG& p, int64_t ncm) {
@@ -1128,13 +1145,25 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
   float** cc = w.cc;
   float** cd = w.cd;
   float** dd = w.dd;
-  // W = T BK, Ut = T BV
-  VH(cc[cT], cd[mBK], cd[mW], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
+  // W = T diag(beta gam) K^ (rows of K^ scaled as they are read), Ut = T BV
+  {
+    BG g = gemm(cc[cT], w.Kn, cd[mW], C, D, C, C, D, D, 0, 0, hv * CC, CC, 1, hq * CD, CD, grp, hv * CD, CD, hv,
+                1.f, 0, nc);
+    g.bs = w.vec + kVecBG * C;
+    g.vstr = kNVec * C;
+    run_gemm(L, g, ncm);
+  }
   VH(cc[cT], cd[mBV], cd[mUt], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0);
   if (L.err != hipSuccess) return L.err;
-  // PdO = Pm^T dO, Z = GQ^T dO (the reverse chain's inputs)
+  // PdO = Pm^T dO and Z (the reverse chain's inputs)
   VH(cc[cPm], cd[mDO], cd[mPdO], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);
-  VH(cd[mGQ], cd[mDO], dd[xZ], D, D, C, D, D, D, 1, 0, CD, CD, DD, 1.f, 0);
+  {  // Z = (scale diag(gam) Q^)^T dO
+    BG g = gemm(w.Qn, cd[mDO], dd[xZ], D, D, C, D, D, D, 1, 0, hq * CD, CD, grp, hv * CD, CD, 1, hv * DD, DD, hv,
+                1.f, 0, nc);
+    g.as = w.vec + kVecSG * C;
+    g.vstr = kNVec * C;
+    run_gemm(L, g, ncm);
+  }
   if (L.err != hipSuccess) return L.err;
   {
     hipError_t e;
@@ -1162,7 +1191,13 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
   VH(cd[mU], dd[xDXs], cd[mUdX], C, D, D, D, D, D, 0, 1, CD, DD, CD, 1.f, 0);    // UdX = U dX'^T
   VH(cd[mDO], cd[mU], cc[cDPm], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dPm = dO U^T
   VH(cd[mDU], cd[mBV], cc[cDT], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dT = dU BV^T
-  VH(cd[mDW], cd[mBK], cc[cDT], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 1);     //    + dW BK^T
+  {  //    + dW (diag(beta gam) K^)^T
+    BG g = gemm(cd[mDW], w.Kn, cc[cDT], C, C, D, D, D, C, 0, 1, hv * CD, CD, 1, hq * CD, CD, grp, hv * CC, CC, hv,
+                1.f, 1, nc);
+    g.bs = w.vec + kVecBG * C;
+    g.vstr = kNVec * C;
+    run_gemm(L, g, ncm);
+  }
   VH(cc[cDT], cc[cT], cc[cM1], C, C, C, C, C, C, 0, 1, CC, CC, CC, 1.f, 0);      // M1 = dT T^T
   VH(cc[cT], cc[cM1], cc[cDT], C, C, C, C, C, C, 1, 0, CC, CC, CC, -1.f, 0);     // dA = -T^T M1
   VH(cc[cT], cd[mDW], cd[mTdW], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);     // TdW = T^T dW
