@@ -308,20 +308,31 @@ __global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* Kn = w.Kn + ((int64_t)gc * h_qk + hq) * C * D;
   float* Qn = w.Qn + ((int64_t)gc * h_qk + hq) * C * D;
-  for (int r = wave; r < C; r += 4) {
-    for (int which = 0; which < 2; ++which) {
-      const T* src = which ? q : k;
-      float* dst = which ? Qn : Kn;
-      float v[2] = {0.f, 0.f};
-      if (r < cr.len)
-        for (int i = 0; i < D / 64; ++i)
-          v[i] = to_f32(src[(int64_t)(cr.t0 + r) * (which ? qs : ks) + (int64_t)hq * D + lane + 64 * i]);
-      float ss = 0.f;
-      for (int i = 0; i < D / 64; ++i) ss += v[i] * v[i];
-      ss = wave_sum(ss);
-      const float rn = (l2norm && r < cr.len) ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
-      for (int i = 0; i < D / 64; ++i) dst[(int64_t)r * D + lane + 64 * i] = v[i] * rn;
-    }
+  // a wave takes 4 rows at a time, all their loads issued before the sums
+  for (int r0 = 4 * wave; r0 < C; r0 += 16) {
+    float v[4][2][2];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = r0 + rr;
+          v[rr][which][i] = (r < cr.len && i < D / 64)
+                                ? to_f32((which ? q : k)[(int64_t)(cr.t0 + r) * (which ? qs : ks) + (int64_t)hq * D +
+                                                         lane + 64 * i])
+                                : 0.f;
+        }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const int r = r0 + rr;
+        const float ss = wave_sum(v[rr][which][0] * v[rr][which][0] + v[rr][which][1] * v[rr][which][1]);
+        const float rn = (l2norm && r < cr.len) ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
+        float* dst = which ? Qn : Kn;
+        for (int i = 0; i < D / 64; ++i) dst[(int64_t)r * D + lane + 64 * i] = v[rr][which][i] * rn;
+      }
   }
 }
 
