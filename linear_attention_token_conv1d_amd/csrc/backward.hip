@@ -957,6 +957,29 @@ __device__ inline float conv_dz(const T* x, const T* w, const T* bias, const T* 
 // the gradient of the new conv state adds onto the last W-1 tokens.  The
 // weight and bias partial sums of the tile's own tokens go to the workspace.
 constexpr int kConvBT = 32;
+
+// 8 consecutive elements as raw bits (16 B of bf16, 32 B of fp32), so that
+// loads can run ahead of the arithmetic that widens them
+template <typename T> struct Row8;
+template <> struct Row8<__bf16> {
+  uint4 a;
+  __device__ __forceinline__ void load(const __bf16* p) { a = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  }
+};
+template <> struct Row8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 template <typename T, int W>
 __global__ __launch_bounds__(256) void conv_bwd_kernel(const T* x, const T* w, const T* bias, const T* state,
                                                        const T* dy, const float* dns, const int32_t* cu,
@@ -978,7 +1001,24 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const T* x, const T* w, c
   }
   int n = 0;
   int64_t s = 0, e = 0;
+  // x and dy rows two tokens ahead
+  Row8<T> px[2], pd[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (t0 + u < tend) {
+      px[u].load(x + (t0 + u) * C + c0);
+      pd[u].load(dy + (t0 + u) * C + c0);
+    }
   for (int64_t tau = t0; tau < tend; ++tau) {
+    float d8[8];
+    px[0].get(xw[W - 1]);
+    pd[0].get(d8);
+    px[0] = px[1];
+    pd[0] = pd[1];
+    if (tau + 2 < tend) {
+      px[1].load(x + (tau + 2) * C + c0);
+      pd[1].load(dy + (tau + 2) * C + c0);
+    }
     if (tau == t0 || tau >= e) {
       seq_of(cu, n_seqs, Tt, tau, n, s, e);
 #pragma unroll
@@ -990,9 +1030,6 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const T* x, const T* w, c
 #pragma unroll
         for (int i = 0; i < 8; ++i) pend[k][i] = 0.f;
     }
-    float d8[8];
-    load8(x + tau * C + c0, xw[W - 1]);
-    load8(dy + tau * C + c0, d8);
     float dz[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
