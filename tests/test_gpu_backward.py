@@ -260,3 +260,33 @@ def test_prefill_backward_27b_size_sampled_group():
     report("prefill_backward[27B, group 0]", **errs)
     for n, e in errs.items():
         assert e < TOL_BF16, (n, e)
+
+
+@pytest.mark.parametrize("lens", [[0], [0, 0, 0]])
+def test_backward_empty_inputs(lens):
+    """No tokens at all: the state gradient passes straight through (or is
+    zero without a final-state gradient), the conv weight gradient is zero and
+    the conv-state gradient is the new-state gradient."""
+    h_qk, h_v, d = 1, 2, 64
+    N = len(lens)
+    cu = gdn_inputs.cu_from_lengths(lens) if N > 1 else None
+    q = torch.zeros((0, h_qk, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    v = torch.zeros((0, h_v, d), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((0, h_v), dtype=torch.float32, device="cuda")
+    beta = torch.zeros_like(g)
+    do = torch.zeros((0, h_v, d), dtype=torch.bfloat16, device="cuda")
+    dsf = _rand((N, h_v, d, d), torch.float32, 0.3, seed=100).cuda()
+    got = gdn.prefill_backward(q, k, v, g, beta, do, None, dsf, dev(cu))
+    got0 = gdn.prefill_backward(q, k, v, g, beta, do, None, None, dev(cu))
+    torch.cuda.synchronize()
+    assert torch.equal(got[5], dsf)
+    assert torch.count_nonzero(got0[5]).item() == 0
+    C = 2 * h_qk * d + h_v * d
+    x = torch.zeros((0, C), dtype=torch.bfloat16, device="cuda")
+    w = _rand((C, 4), torch.bfloat16, 0.5, seed=101).cuda()
+    dns = _rand((N, C, 3), torch.float32, seed=102).cuda()
+    dx, dw, _, dst = gdn.conv1d_backward(x, w, torch.zeros_like(x), None, None, dev(cu), "silu", dns)
+    torch.cuda.synchronize()
+    assert dx.numel() == 0 and torch.count_nonzero(dw).item() == 0
+    assert torch.equal(dst, dns)
