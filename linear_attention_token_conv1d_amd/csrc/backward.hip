@@ -21,11 +21,12 @@
 //      dK^, dQ^, dV, dbeta and dG (then dg is the reverse cumulative sum of dG);
 //   5. dK^ and dQ^ of a QK head add up over the V heads that read it and
 //      pass back through the L2 norm.
-// The stages stay simple and separately checkable: a batched fp32-MFMA GEMM
-// over (chunk, head) for the state-independent and chunk-local products, one
-// launch that runs both serial chains (bf16 MFMA operands for bf16 inputs,
-// fp32 VALU for fp32 inputs, fp32 state either way), and elementwise kernels
-// that combine the pieces.  Every intermediate is an fp32 workspace array.
+// The stages: a batched fp32-MFMA GEMM over (chunk, head) for the
+// state-independent products, one launch that runs both serial chains (bf16
+// MFMA operands for bf16 inputs, fp32 VALU for fp32 inputs, fp32 state either
+// way), one fused kernel per (chunk, V head) for every chunk-local gradient,
+// and a per-token kernel for the QK-head sums and the L2-norm backward.
+// Every array passed between stages is an fp32 workspace array.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -39,12 +40,12 @@ namespace {
 // (n_seqs + 1), then one (sequence, first token, rows) record per chunk.
 // Then fp32 arrays, each [max_chunks][heads][rows][cols]:
 //   per QK head: Kn, Qn (C x D), KK, QK (C x C)
-//   per V head:  vec (8 x C), five C x C, thirteen C x D and three D x D
-// vec rows: G, gam, e, beta, two gradient partials, beta gam (0 without the
-// erase term) and scale gam; the last two scale K^ and Q^ rows on the fly
-enum { kVecG = 0, kVecGam, kVecE, kVecBeta, kVecDGx, kVecDBx, kVecBG, kVecSG, kNVec };
-enum { cT = 0, cPm, cDPm, cDT, cM1, kNCC };
-enum { mBV = 0, mDO, mW, mUt, mU, mDU, mPdO, mDW, mDOX, mUdX, mTdW, mDKn, mDQn, kNCD };
+//   per V head:  vec (6 x C), two C x C, nine C x D and three D x D
+// vec rows: G, gam, e, beta, beta gam (0 without the erase term) and scale
+// gam; the last two scale K^ and Q^ rows on the fly
+enum { kVecG = 0, kVecGam, kVecE, kVecBeta, kVecBG, kVecSG, kNVec };
+enum { cT = 0, cPm, kNCC };
+enum { mBV = 0, mDO, mW, mUt, mU, mDU, mPdO, mDKn, mDQn, kNCD };
 enum { xXs = 0, xDXs, xZ, kNDD };
 
 struct ChunkRec {
@@ -726,160 +727,445 @@ hipError_t launch_chains_bf16(const BwdWs& w, const PrefillBwdParams& p, hipStre
   return hipGetLastError();
 }
 
-// ------------------------------------------- C x C gradient combination
-// Per (chunk, V head), from dPm and dA = -T^T dT T^T:
-//   dQK  = scale Gam o dPm (lower incl.)            -> written over dPm
-//   dKK  = beta_r Gam o dA (strict lower), stored as dKK + dKK^T -> over M1
-//   Gam_rj dGam_rj (from Pm and A) summed into dG: + over rows, - over columns
-//   dbeta_r from A: sum_j Gam_rj KK_rj dA_rj
-__global__ __launch_bounds__(256) void bwd_cc_kernel(BwdWs w, int h_qk, int h_v, int C, float scale, int erase) {
-  const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
-  if (gc >= *w.nc) return;
-  const int hq = h / (h_v / h_qk);
-  const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
-  __shared__ float sGG[64][65], sDK[64][65], sDB[64][65], sG[64], sB[64];
-  float* vec = w.vec + bv * kNVec * C;
-  for (int r = tid; r < C; r += 256) {
-    sG[r] = vec[kVecG * C + r];
-    sB[r] = vec[kVecBeta * C + r];
-  }
-  __syncthreads();
-  const float* KK = w.KK + bq * C * C;
-  const float* QK = w.QK + bq * C * C;
-  float* dPm = w.cc[cDPm] + bv * C * C;
-  const float* dA = w.cc[cDT] + bv * C * C;
-  for (int e = tid; e < C * C; e += 256) {
-    const int r = e / C, j = e % C;
-    const float gm = j <= r ? expf(sG[r] - sG[j]) : 0.f;
-    const float dp = dPm[e];
-    float gg = scale * gm * QK[e] * dp, dk = 0.f, db = 0.f;
-    if (erase && j < r) {
-      const float gka = gm * KK[e] * dA[e];
-      dk = sB[r] * gm * dA[e];
-      gg += sB[r] * gka;
-      db = gka;
+// ------------------------------------------------ chunk-local, one kernel
+// Per (chunk, V head), once the chains have stored X_c, dX'_c, U and dU:
+// every chunk-local gradient in one workgroup on fp32 MFMA (16x16x4), so the
+// C x d and C x C intermediates never leave the CU.  Eight waves: wave w
+// owns rows 16 (w % 4) .. +15 of every C-row result and one half of its
+// columns (w / 4), so a tile row sum is two half-row partials and the dK^
+// and dQ^ tiles accumulate in registers across the products.  dU, U, dO and
+// T sit in LDS (U's and dO's space is reused for dW and dT T^T once they are
+// done); X and dX' are read as MFMA operands straight from memory.
+//   dPm = dO U^T -> dQK = scale Gam o dPm (lower incl.)
+//   T^T dU -> dv = diag(beta) T^T dU, and dbeta's V term
+//   dT = dU (diag(beta) V)^T + dW (diag(beta gam) K^)^T,  dW = -dU X^T
+//   dO X^T -> dQ^ += scale diag(gam) dO X^T, and dG's gam term
+//   U dX'^T -> dK^ += diag(e) U dX'^T
+//   dA = -T^T dT T^T -> dKK = beta Gam o dA (strict lower)
+//   T^T dW -> dK^ += diag(beta gam) T^T dW, and the beta gam terms
+//   dK^ += dQK^T Q^ + (dKK + dKK^T) K^,  dQ^ += dQK K^
+// then dG (with the Gam row and column sums), its reverse cumulative sum dg,
+// and dbeta.  MFMA lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+// of a 16 x 4 / 4 x 16 slice and holds C rows 4 (l / 16) .. +3 of column
+// l % 16; row16_sum adds a tile row over its 16 columns.
+// Per-row scalars: G, gam, e, beta, beta gam, scale gam, u, then two
+// half-row partials each of Q^ . dO X^T, K^ . T^T dW, V . T^T dU, the dbeta
+// part of dA and the Gam terms' row sums.
+enum { lG = 0, lGam, lE, lBeta, lBG, lSG, lU, lA0, lA1, lS0, lS1, lB0, lB1, lDB0, lDB1, lR0, lR1, kLRows };
+
+template <int D, int C>
+struct LocalLayout {
+  static constexpr int P1 = D + 4, P2 = C + 4;
+  static constexpr int oDU = 0, oU = oDU + C * P1, oDO = oU + C * P1, oT = oDO + C * P1, oX = oT + C * P2,
+                       oY = oX + C * P2, oV = oY + C * P2, oCol = oV + kLRows * C, oRed = oCol + 4 * C,
+                       floats = oRed + 8;
+};
+
+__device__ __forceinline__ v4f mma4(float a, float b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc[nt] += sum_k A[r][k] B[16 nt + n][k] for this lane's tile row r, with
+// both operands stored k-contiguous (a: this lane's row of A; b: the first
+// B row of the tiles).  Lane (l16, g4) takes k = k0 + 4 g4 + j into MFMA j,
+// the same permutation of k for both operands, so each operand arrives in
+// one 16-byte load.
+template <int NT>
+__device__ __forceinline__ void mm_kk(v4f (&acc)[NT], const float* a, const float* b, int ldb, int K, int l16,
+                                      int g4) {
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const v4f av = *reinterpret_cast<const v4f*>(a + k0 + 4 * g4);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const v4f bv = *reinterpret_cast<const v4f*>(b + (int64_t)(16 * nt + l16) * ldb + k0 + 4 * g4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[nt] = mma4(av[j], bv[j], acc[nt]);
     }
-    sGG[r][j] = gg;
-    sDK[r][j] = dk;
-    sDB[r][j] = db;
-    dPm[e] = scale * gm * dp;
-  }
-  __syncthreads();
-  float* sym = w.cc[cM1] + bv * C * C;
-  for (int e = tid; e < C * C; e += 256) sym[e] = sDK[e / C][e % C] + sDK[e % C][e / C];
-  for (int r = tid; r < C; r += 256) {
-    float row = 0.f, col = 0.f, db = 0.f;
-    for (int j = 0; j < C; ++j) {
-      row += sGG[r][j];
-      col += sGG[j][r];
-      db += sDB[r][j];
-    }
-    vec[kVecDGx * C + r] = row - col;
-    vec[kVecDBx * C + r] = db;
   }
 }
 
-// --------------------------------------------------------- final, V head
-// Per (chunk, V head): dG, its reverse cumulative sum dg, dbeta, dv, and
-// the per-V-head parts of dK^ and dQ^ completed in place.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_final_v_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
-                                                          float* dg, float* dbeta, int h_qk, int h_v, int D, int C,
-                                                          float scale, int erase) {
+// acc[nt] += sum_k At[k][r] B[k][16 nt + n] (A stored transposed: at points
+// at column r of At; B stored k-major from its first tile column).
+template <int NT>
+__device__ __forceinline__ void mm_tn(v4f (&acc)[NT], const float* at, int lda, const float* b, int ldb, int K,
+                                      int l16, int g4) {
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    const float av = at[(k0 + g4) * lda];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = mma4(av, b[(k0 + g4) * ldb + 16 * nt + l16], acc[nt]);
+  }
+}
+
+// Sum over the 4 lane groups of a wave (the 16 rows of a tile column held in
+// lanes l16, l16 + 16, l16 + 32, l16 + 48).
+__device__ __forceinline__ float col4_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
+                                                        float* dg, float* dbeta, int h_qk, int h_v, float scale,
+                                                        int erase) {
+  using L = LocalLayout<D, C>;
+  // NH tiles of d columns and NCH tiles of C columns per wave; with C = 16
+  // the C x C products are one tile, taken by the first half alone
+  constexpr int P1 = L::P1, P2 = L::P2, NN = D / 16, NC = C / 16, NH = NN / 2, NCH = NC >= 2 ? NC / 2 : 1;
+  constexpr int NT = 512;
   const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
   if (gc >= *w.nc) return;
   const ChunkRec cr = w.ct[gc];
-  const int hq = h / (h_v / h_qk), lane = tid & 63, wave = tid >> 6;
+  const int hq = h / (h_v / h_qk), lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int mt = wave & 3, ch = wave >> 2, r0 = 16 * mt, cb = ch * (D / 2), jb = NC >= 2 ? ch * (C / 2) : 0;
+  const bool rows = mt < NC, ccw = rows && (NC >= 2 || ch == 0);
   const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
+  extern __shared__ float lds[];
+  float* sDU = lds + L::oDU;
+  float* sU = lds + L::oU;    // U, then dW
+  float* sDO = lds + L::oDO;  // dO, then dT T^T
+  float* sT = lds + L::oT;
+  float* sX = lds + L::oX;    // dQK
+  float* sY = lds + L::oY;    // dT, then dKK
+  float* sV = lds + L::oV;    // per-row scalars, kLRows x C
+  float* sCol = lds + L::oCol;  // column sums of the Gam terms per row tile, 4 x C
+  float* sRed = lds + L::oRed;
+  const float* gDU = w.cd[mDU] + bv * C * D;
+  const float* gU = w.cd[mU] + bv * C * D;
+  const float* gDO = w.cd[mDO] + bv * C * D;
+  const float* gBV = w.cd[mBV] + bv * C * D;
+  const float* gPdO = w.cd[mPdO] + bv * C * D;
+  const float* gT = w.cc[cT] + bv * C * C;
+  const float* gKK = w.KK + bq * C * C;
+  const float* gQK = w.QK + bq * C * C;
+  const float* gKn = w.Kn + bq * C * D;
+  const float* gQn = w.Qn + bq * C * D;
+  const float* gXs = w.dd[xXs] + bv * D * D;
+  const float* gdXs = w.dd[xDXs] + bv * D * D;
   const float* vec = w.vec + bv * kNVec * C;
-  __shared__ float sDG[64], sDB[64], sU[64], sRed[4];
-  const float* Qn = w.Qn + bq * C * D;
-  const float* DOX = w.cd[mDOX] + bv * C * D;
-  const float* TdW = w.cd[mTdW] + bv * C * D;
-  const float* Kn = w.Kn + bq * C * D;
-  const float* U = w.cd[mU] + bv * C * D;
-  const float* DU = w.cd[mDU] + bv * C * D;
-  const float* PdO = w.cd[mPdO] + bv * C * D;
-  const float* TdU = w.cd[mUt] + bv * C * D;  // T^T dU was written over Ut
-  // row dots: lane covers D / 64 consecutive columns of row r (one wave per row)
-  const int per = D / 64;  // 1 or 2
-  for (int r = wave; r < C; r += 4) {
-    float a = 0.f, s = 0.f, u = 0.f, b1 = 0.f;
-    const int c0 = per * lane;
-    const int64_t e = (int64_t)r * D + c0;
-    if (per == 2) {
-      const float2 gq = *reinterpret_cast<const float2*>(Qn + e), dx = *reinterpret_cast<const float2*>(DOX + e);
-      const float2 tw = *reinterpret_cast<const float2*>(TdW + e), kn = *reinterpret_cast<const float2*>(Kn + e);
-      const float2 uu = *reinterpret_cast<const float2*>(U + e), du = *reinterpret_cast<const float2*>(DU + e);
-      const float2 pd = *reinterpret_cast<const float2*>(PdO + e), tu = *reinterpret_cast<const float2*>(TdU + e);
-      a = gq.x * dx.x + gq.y * dx.y;
-      s = tw.x * kn.x + tw.y * kn.y;
-      u = uu.x * (du.x - pd.x) + uu.y * (du.y - pd.y);
-      if (r < cr.len) {
-        const T* vr = v + (int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c0;
-        b1 = to_f32(vr[0]) * tu.x + to_f32(vr[1]) * tu.y;
-      }
-    } else {
-      a = Qn[e] * DOX[e];
-      s = TdW[e] * Kn[e];
-      u = U[e] * (DU[e] - PdO[e]);
-      if (r < cr.len) b1 = to_f32(v[(int64_t)(cr.t0 + r) * vs + (int64_t)h * D + c0]) * TdU[e];
-    }
-    a = wave_sum(a);
-    s = wave_sum(s);
-    u = wave_sum(u);
-    b1 = wave_sum(b1);
-    if (lane == 0) {
-      const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r];
-      sDG[r] = vec[kVecSG * C + r] * a + (erase ? be * gm * s : 0.f) + vec[kVecDGx * C + r] - u;
-      sDB[r] = b1 + vec[kVecDBx * C + r] + (erase ? gm * s : 0.f);
-      sU[r] = u;
-    }
-  }
-  // <X, dX'> for the decay of the whole chunk
-  const float* Xs = w.dd[xXs] + bv * D * D;
-  const float* dXs = w.dd[xDXs] + bv * D * D;
-  float xd = 0.f;
-  for (int e = 4 * tid; e < D * D; e += 4 * 256) {
-    const v4f x4 = *reinterpret_cast<const v4f*>(Xs + e), d4 = *reinterpret_cast<const v4f*>(dXs + e);
-    xd += x4[0] * d4[0] + x4[1] * d4[1] + x4[2] * d4[2] + x4[3] * d4[3];
-  }
-  xd = wave_sum(xd);
-  if (lane == 0) sRed[wave] = xd;
-  __syncthreads();
-  if (tid == 0) {
-    float us = 0.f;
-    for (int r = 0; r < C; ++r) us += sU[r];
-    sDG[C - 1] += us + vec[kVecGam * C + C - 1] * (sRed[0] + sRed[1] + sRed[2] + sRed[3]);
-    float run = 0.f;
-    for (int r = C - 1; r >= 0; --r) {
-      run += sDG[r];
-      sDG[r] = run;
-    }
-  }
-  __syncthreads();
-  for (int r = tid; r < cr.len; r += 256) {
-    dg[(int64_t)(cr.t0 + r) * h_v + h] = sDG[r];
-    dbeta[(int64_t)(cr.t0 + r) * h_v + h] = sDB[r];
-  }
-  float* dKn = w.cd[mDKn] + bv * C * D;
-  float* dQn = w.cd[mDQn] + bv * C * D;
-  const float* UdX = w.cd[mUdX] + bv * C * D;
-  for (int e = 4 * tid; e < C * D; e += 4 * 256) {
+  // ---- stage dU, U, dO, T and the per-row scalars
+  for (int e = 4 * tid; e < C * D; e += 4 * NT) {
     const int r = e / D, c = e % D;
-    const float be = vec[kVecBeta * C + r], gm = vec[kVecGam * C + r], ee = vec[kVecE * C + r];
-    const float bg = erase ? be * gm : 0.f;
-    v4f dk = *reinterpret_cast<const v4f*>(dKn + e), dq = *reinterpret_cast<const v4f*>(dQn + e);
-    dk += bg * *reinterpret_cast<const v4f*>(TdW + e) + ee * *reinterpret_cast<const v4f*>(UdX + e);
-    dq += (scale * gm) * *reinterpret_cast<const v4f*>(DOX + e);
-    *reinterpret_cast<v4f*>(dKn + e) = dk;
-    *reinterpret_cast<v4f*>(dQn + e) = dq;
-    if (r < cr.len) {
-      const v4f t = be * *reinterpret_cast<const v4f*>(TdU + e);
-      float o[4] = {t[0], t[1], t[2], t[3]};
-      store4(dv + (int64_t)(cr.t0 + r) * dvs + (int64_t)h * D + c, o);
+    *reinterpret_cast<v4f*>(sDU + r * P1 + c) = *reinterpret_cast<const v4f*>(gDU + e);
+    *reinterpret_cast<v4f*>(sU + r * P1 + c) = *reinterpret_cast<const v4f*>(gU + e);
+    *reinterpret_cast<v4f*>(sDO + r * P1 + c) = *reinterpret_cast<const v4f*>(gDO + e);
+  }
+  for (int e = 4 * tid; e < C * C; e += 4 * NT)
+    *reinterpret_cast<v4f*>(sT + (e / C) * P2 + e % C) = *reinterpret_cast<const v4f*>(gT + e);
+  for (int e = tid; e < C; e += NT) {
+    sV[lG * C + e] = vec[kVecG * C + e];
+    sV[lGam * C + e] = vec[kVecGam * C + e];
+    sV[lE * C + e] = vec[kVecE * C + e];
+    sV[lBeta * C + e] = vec[kVecBeta * C + e];
+    sV[lBG * C + e] = vec[kVecBG * C + e];
+    sV[lSG * C + e] = vec[kVecSG * C + e];
+#pragma unroll
+    for (int q = lU; q < kLRows; ++q) sV[q * C + e] = 0.f;
+  }
+  lds_barrier();
+  const v4f z4 = {0.f, 0.f, 0.f, 0.f};
+  v4f accK[NH], accQ[NH], accW[NH];
+  if (ccw) {
+    // ---- dPm = dO U^T -> dQK = scale Gam o dPm (lower incl.); Gam terms of dG
+    v4f acc[NCH];
+#pragma unroll
+    for (int nt = 0; nt < NCH; ++nt) acc[nt] = z4;
+    mm_kk<NCH>(acc, sDO + (r0 + l16) * P1, sU + jb * P1, P1, D, l16, g4);
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NCH; ++nt) {
+      const int j = jb + 16 * nt + l16;
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        const float dq = j <= r ? scale * expf(sV[lG * C + r] - sV[lG * C + j]) * acc[nt][i] : 0.f;
+        sX[r * P2 + j] = dq;
+        const float gg = gQK[r * C + j] * dq;
+        rs[i] += gg;
+        cs += gg;
+      }
+      cs = col4_sum(cs);
+      if (g4 == 0) sCol[mt * C + j] = cs;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = row16_sum(rs[i]);
+      if (l16 == 0) sV[(lR0 + ch) * C + r0 + 4 * g4 + i] = x;
     }
   }
+  if (rows) {
+    // ---- T^T dU -> dv = diag(beta) T^T dU, and dbeta's V term
+    {
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) accW[nt] = z4;
+      mm_tn<NH>(accW, sT + r0 + l16, P2, sDU + cb, P1, C, l16, g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        const bool in = r < cr.len;
+        const float be = sV[lBeta * C + r];
+        const int64_t tok = (int64_t)(cr.t0 + r);
+        float b1 = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          const int c = cb + 16 * nt + l16;
+          if (in) {
+            b1 += to_f32(v[tok * vs + (int64_t)h * D + c]) * accW[nt][i];
+            dv[tok * dvs + (int64_t)h * D + c] = from_f32<T>(be * accW[nt][i]);
+          }
+        }
+        b1 = row16_sum(b1);
+        if (l16 == 0) sV[(lB0 + ch) * C + r] = b1;
+      }
+    }
+    // ---- dT = dU (diag(beta) V)^T; the dW term is added below
+    if (ccw) {
+      v4f acc[NCH];
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt) acc[nt] = z4;
+      mm_kk<NCH>(acc, sDU + (r0 + l16) * P1, gBV + (int64_t)jb * D, D, D, l16, g4);
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(r0 + 4 * g4 + i) * P2 + jb + 16 * nt + l16] = acc[nt][i];
+    }
+    // ---- dO X^T and dW = -dU X^T (X stored [d_k][d_v], so B[n][k] = X[n][k] is k-contiguous)
+    {
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) {
+        accQ[nt] = z4;
+        accW[nt] = z4;
+      }
+      const float* ao = sDO + (r0 + l16) * P1;
+      const float* aw = sDU + (r0 + l16) * P1;
+      const float* bx = gXs + (int64_t)(cb + l16) * D;
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        const v4f a1 = *reinterpret_cast<const v4f*>(ao + k0 + 4 * g4);
+        const v4f a2 = *reinterpret_cast<const v4f*>(aw + k0 + 4 * g4);
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          const v4f b = *reinterpret_cast<const v4f*>(bx + (int64_t)16 * nt * D + k0 + 4 * g4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            accQ[nt] = mma4(a1[j], b[j], accQ[nt]);
+            accW[nt] = mma4(a2[j], b[j], accW[nt]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        const float sg = sV[lSG * C + r];
+        float a = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          a += gQn[r * D + cb + 16 * nt + l16] * accQ[nt][i];
+          accQ[nt][i] *= sg;  // dQ^ starts as scale gam dO X^T
+          accW[nt][i] = -accW[nt][i];
+        }
+        a = row16_sum(a);
+        if (l16 == 0) sV[(lA0 + ch) * C + r] = a;
+      }
+    }
+    // ---- dK^ starts as diag(e) U dX'^T; u_r = U_r . (dU_r - (Pm^T dO)_r)
+    {
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) accK[nt] = z4;
+      mm_kk<NH>(accK, sU + (r0 + l16) * P1, gdXs + (int64_t)cb * D, D, D, l16, g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ee = sV[lE * C + r0 + 4 * g4 + i];
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) accK[nt][i] *= ee;
+      }
+      for (int rr = 0; rr < 8; ++rr) {
+        const int r = r0 + 8 * ch + rr;
+        float u = 0.f;
+        for (int c = lane; c < D; c += 64) u += sU[r * P1 + c] * (sDU[r * P1 + c] - gPdO[r * D + c]);
+        u = wave_sum(u);
+        if (lane == 0) sV[lU * C + r] = u;
+      }
+    }
+  }
+  // <X, dX'> over the whole d_k x d_v block (every wave)
+  {
+    float xd = 0.f;
+    for (int e = 4 * tid; e < D * D; e += 4 * NT) {
+      const v4f x4 = *reinterpret_cast<const v4f*>(gXs + e), d4 = *reinterpret_cast<const v4f*>(gdXs + e);
+      xd += x4[0] * d4[0] + x4[1] * d4[1] + x4[2] * d4[2] + x4[3] * d4[3];
+    }
+    xd = wave_sum(xd);
+    if (lane == 0) sRed[wave] = xd;
+  }
+  lds_barrier();  // every wave is done with U and dO
+  float* sW = sU;
+  if (rows) {
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sW[(r0 + 4 * g4 + i) * P1 + cb + 16 * nt + l16] = accW[nt][i];
+  }
+  lds_barrier();
+  float* sM = sDO;
+  if (erase) {
+    // ---- dT += dW (diag(beta gam) K^)^T, then M = dT T^T
+    if (ccw) {
+      v4f acc[NCH];
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt) acc[nt] = z4;
+      mm_kk<NCH>(acc, sW + (r0 + l16) * P1, gKn + (int64_t)jb * D, D, D, l16, g4);
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt) {
+        const int j = jb + 16 * nt + l16;
+        const float bg = sV[lBG * C + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(r0 + 4 * g4 + i) * P2 + j] += bg * acc[nt][i];
+      }
+    }
+    lds_barrier();  // both halves of each dT row are complete
+    if (ccw) {
+      v4f acc[NCH];
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt) acc[nt] = z4;
+      mm_kk<NCH>(acc, sY + (r0 + l16) * P2, sT + jb * P2, P2, C, l16, g4);
+#pragma unroll
+      for (int nt = 0; nt < NCH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sM[(r0 + 4 * g4 + i) * P2 + jb + 16 * nt + l16] = acc[nt][i];
+    }
+    lds_barrier();
+  }
+  // ---- dA = -T^T M -> dKK = beta Gam o dA (strict lower) over dT; dbeta's A
+  // term; the dKK Gam terms of dG
+  if (ccw) {
+    v4f acc[NCH];
+#pragma unroll
+    for (int nt = 0; nt < NCH; ++nt) acc[nt] = z4;
+    if (erase) mm_tn<NCH>(acc, sT + r0 + l16, P2, sM + jb, P2, C, l16, g4);
+    float rs[4] = {0.f, 0.f, 0.f, 0.f}, db[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NCH; ++nt) {
+      const int j = jb + 16 * nt + l16;
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        float dkk = 0.f;
+        if (erase && j < r) {
+          const float gda = -expf(sV[lG * C + r] - sV[lG * C + j]) * acc[nt][i];  // Gam o dA
+          dkk = sV[lBeta * C + r] * gda;
+          db[i] += gKK[r * C + j] * gda;
+        }
+        sY[r * P2 + j] = dkk;
+        const float gg = gKK[r * C + j] * dkk;
+        rs[i] += gg;
+        cs += gg;
+      }
+      cs = col4_sum(cs);
+      if (g4 == 0) sCol[mt * C + j] += cs;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = row16_sum(rs[i]), y = row16_sum(db[i]);
+      if (l16 == 0) {
+        sV[(lR0 + ch) * C + r0 + 4 * g4 + i] += x;
+        sV[(lDB0 + ch) * C + r0 + 4 * g4 + i] = y;
+      }
+    }
+  }
+  lds_barrier();
+  if (rows) {
+    // ---- T^T dW -> dK^ += diag(beta gam) T^T dW, and s_r = K^_r . (T^T dW)_r
+    if (erase) {
+      v4f acc[NH];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) acc[nt] = z4;
+      mm_tn<NH>(acc, sT + r0 + l16, P2, sW + cb, P1, C, l16, g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        const float bg = sV[lBG * C + r];
+        float sd = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          sd += gKn[r * D + cb + 16 * nt + l16] * acc[nt][i];
+          accK[nt][i] += bg * acc[nt][i];
+        }
+        sd = row16_sum(sd);
+        if (l16 == 0) sV[(lS0 + ch) * C + r] = sd;
+      }
+    }
+    // ---- dK^ += dQK^T Q^ + (dKK + dKK^T) K^,  dQ^ += dQK K^
+    const int r = r0 + l16;
+#pragma unroll 2
+    for (int k0 = 0; k0 < C; k0 += 4) {
+      const int j = k0 + g4;
+      const float a1 = sX[j * P2 + r];
+      const float a2 = sY[r * P2 + j] + sY[j * P2 + r];
+      const float a3 = sX[r * P2 + j];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) {
+        const float qn = gQn[j * D + cb + 16 * nt + l16], kn = gKn[j * D + cb + 16 * nt + l16];
+        accK[nt] = mma4(a1, qn, accK[nt]);
+        accK[nt] = mma4(a2, kn, accK[nt]);
+        accQ[nt] = mma4(a3, kn, accQ[nt]);
+      }
+    }
+    float* gdKn = w.cd[mDKn] + bv * C * D;
+    float* gdQn = w.cd[mDQn] + bv * C * D;
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t e = (int64_t)(r0 + 4 * g4 + i) * D + cb + 16 * nt + l16;
+        gdKn[e] = accK[nt][i];
+        gdQn[e] = accQ[nt][i];
+      }
+  }
+  lds_barrier();
+  // ---- dG per row, its reverse cumulative sum dg (a suffix scan over the
+  // lanes of wave 0, lane r holding row r), and dbeta
+  if (wave == 0) {
+    const int r = lane;
+    const bool on = r < C;
+    float col = 0.f, d = 0.f, u = 0.f;
+    if (on) {
+      for (int q = 0; q < NC; ++q) col += sCol[q * C + r];
+      u = sV[lU * C + r];
+      d = sV[lSG * C + r] * (sV[lA0 * C + r] + sV[lA1 * C + r]) +
+          sV[lBG * C + r] * (sV[lS0 * C + r] + sV[lS1 * C + r]) + sV[lR0 * C + r] + sV[lR1 * C + r] - col - u;
+    }
+    const float us = wave_sum(u);
+    float xd = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xd += sRed[q];
+    if (r == C - 1) d += us + sV[lGam * C + r] * xd;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) {
+      const float t = __shfl_down(d, off, 64);
+      if (r + off < 64) d += t;
+    }
+    if (r < cr.len) {
+      const int64_t t = (int64_t)(cr.t0 + r);
+      dg[t * h_v + h] = d;
+      dbeta[t * h_v + h] = sV[lB0 * C + r] + sV[lB1 * C + r] + sV[lDB0 * C + r] + sV[lDB1 * C + r] +
+                           (erase ? sV[lGam * C + r] * (sV[lS0 * C + r] + sV[lS1 * C + r]) : 0.f);
+    }
+  }
+}
+
+template <typename T, int D, int C>
+hipError_t launch_local(const BwdWs& w, const PrefillBwdParams& p, int64_t ncm, hipStream_t stream) {
+  const size_t lds = (size_t)LocalLayout<D, C>::floats * sizeof(float);
+  const void* f = reinterpret_cast<const void*>(bwd_local_kernel<T, D, C>);
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_local_kernel<T, D, C>), dim3((unsigned)(ncm * p.h_v)), dim3(512), lds, stream, w,
+                     static_cast<const T*>(p.v), p.v_stride, static_cast<T*>(p.dv), p.dv_stride, p.dg, p.dbeta,
+                     p.h_qk, p.h_v, p.scale, p.erase);
+  return hipGetLastError();
 }
 
 // -------------------------------------------------------- final, QK head
@@ -1232,38 +1518,16 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
     }
     if (e != hipSuccess) return e;
   }
-  // chunk-local products
-  VH(cc[cT], cd[mDU], cd[mUt], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);      // TdU = T^T dU
-  VH(cd[mDU], dd[xXs], cd[mDW], C, D, D, D, D, D, 0, 1, CD, DD, CD, -1.f, 0);    // dW = -dU X^T
-  VH(cd[mDO], dd[xXs], cd[mDOX], C, D, D, D, D, D, 0, 1, CD, DD, CD, 1.f, 0);    // dOX = dO X^T
-  VH(cd[mU], dd[xDXs], cd[mUdX], C, D, D, D, D, D, 0, 1, CD, DD, CD, 1.f, 0);    // UdX = U dX'^T
-  VH(cd[mDO], cd[mU], cc[cDPm], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dPm = dO U^T
-  VH(cd[mDU], cd[mBV], cc[cDT], C, C, D, D, D, C, 0, 1, CD, CD, CC, 1.f, 0);     // dT = dU BV^T
-  {  //    + dW (diag(beta gam) K^)^T
-    BG g = gemm(cd[mDW], w.Kn, cc[cDT], C, C, D, D, D, C, 0, 1, hv * CD, CD, 1, hq * CD, CD, grp, hv * CC, CC, hv,
-                1.f, 1, nc);
-    g.bs = w.vec + kVecBG * C;
-    g.vstr = kNVec * C;
-    run_gemm(L, g, ncm);
-  }
-  VH(cc[cDT], cc[cT], cc[cM1], C, C, C, C, C, C, 0, 1, CC, CC, CC, 1.f, 0);      // M1 = dT T^T
-  VH(cc[cT], cc[cM1], cc[cDT], C, C, C, C, C, C, 1, 0, CC, CC, CC, -1.f, 0);     // dA = -T^T M1
-  VH(cc[cT], cd[mDW], cd[mTdW], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0);     // TdW = T^T dW
-  if (L.err != hipSuccess) return L.err;
+  // every chunk-local gradient, one workgroup per (chunk, V head)
   if (p.total_tokens > 0) {
-    hipLaunchKernelGGL(bwd_cc_kernel, dim3((unsigned)(ncm * hv)), dim3(256), 0, stream, w, hq, hv, C, p.scale,
-                       p.erase);
-    L.check();
-  }
-  // dKn = dQK^T Qn + (dKK + dKK^T) Kn,  dQn = dQK Kn   (Kn, Qn per QK head)
-  VH(cc[cDPm], w.Qn, cd[mDKn], C, D, C, C, D, D, 1, 0, CC, CD, CD, 1.f, 0, grp, hq * CD);
-  VH(cc[cM1], w.Kn, cd[mDKn], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 1, grp, hq * CD);
-  VH(cc[cDPm], w.Kn, cd[mDQn], C, D, C, C, D, D, 0, 0, CC, CD, CD, 1.f, 0, grp, hq * CD);
-  if (L.err != hipSuccess) return L.err;
-  if (p.total_tokens > 0) {
-    hipLaunchKernelGGL(bwd_final_v_kernel<T>, dim3((unsigned)(ncm * hv)), dim3(256), 0, stream, w, v, p.v_stride,
-                       static_cast<T*>(p.dv), p.dv_stride, p.dg, p.dbeta, hq, hv, D, C, p.scale, p.erase);
-    L.check();
+    hipError_t e;
+    if (D == 64)
+      e = C == 16 ? launch_local<T, 64, 16>(w, p, ncm, stream)
+                  : C == 32 ? launch_local<T, 64, 32>(w, p, ncm, stream) : launch_local<T, 64, 64>(w, p, ncm, stream);
+    else
+      e = C == 16 ? launch_local<T, 128, 16>(w, p, ncm, stream)
+                  : C == 32 ? launch_local<T, 128, 32>(w, p, ncm, stream) : launch_local<T, 128, 64>(w, p, ncm, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_final_qk_kernel<T>, dim3((unsigned)p.total_tokens, (unsigned)hq), dim3(64), 0, stream, w,
                        p.cu_seqlens, p.n_seqs, q, k, p.q_stride, p.k_stride, static_cast<T*>(p.dq),
                        static_cast<T*>(p.dk), p.dq_stride, p.dk_stride, hq, hv, D, C, p.l2norm);
