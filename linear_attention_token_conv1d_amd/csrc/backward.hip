@@ -730,9 +730,9 @@ hipError_t launch_chains_bf16(const BwdWs& w, const PrefillBwdParams& p, hipStre
 // ------------------------------------------------ chunk-local, one kernel
 // Per (chunk, V head), once the chains have stored X_c, dX'_c, U and dU:
 // every chunk-local gradient in one workgroup on fp32 MFMA (16x16x4), so the
-// C x d and C x C intermediates never leave the CU.  Eight waves: wave w
-// owns rows 16 (w % 4) .. +15 of every C-row result and one half of its
-// columns (w / 4), so a tile row sum is two half-row partials and the dK^
+// C x d and C x C intermediates never leave the CU.  4 NP waves: wave w
+// owns rows 16 (w % 4) .. +15 of every C-row result and one of NP column
+// parts (w / 4), so a tile row sum is NP partials and the dK^
 // and dQ^ tiles accumulate in registers across the products.  dU, U, dO and
 // T sit in LDS (U's and dO's space is reused for dW and dT T^T once they are
 // done); X and dX' are read as MFMA operands straight from memory.
@@ -748,17 +748,18 @@ hipError_t launch_chains_bf16(const BwdWs& w, const PrefillBwdParams& p, hipStre
 // and dbeta.  MFMA lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
 // of a 16 x 4 / 4 x 16 slice and holds C rows 4 (l / 16) .. +3 of column
 // l % 16; row16_sum adds a tile row over its 16 columns.
-// Per-row scalars: G, gam, e, beta, beta gam, scale gam, u, then two
-// half-row partials each of Q^ . dO X^T, K^ . T^T dW, V . T^T dU, the dbeta
-// part of dA and the Gam terms' row sums.
-enum { lG = 0, lGam, lE, lBeta, lBG, lSG, lU, lA0, lA1, lS0, lS1, lB0, lB1, lDB0, lDB1, lR0, lR1, kLRows };
+// Per-row scalars: G, gam, e, beta, beta gam, scale gam, u, then one partial
+// per column part (NP of them) each of Q^ . dO X^T, K^ . T^T dW, V . T^T dU,
+// the dbeta part of dA and the Gam terms' row sums.
+enum { lG = 0, lGam, lE, lBeta, lBG, lSG, lU };
 
-template <int D, int C>
+template <int D, int C, int NP>
 struct LocalLayout {
+  static constexpr int lA = lU + 1, lS = lA + NP, lB = lS + NP, lDB = lB + NP, lR = lDB + NP, nRows = lR + NP;
   static constexpr int P1 = D + 4, P2 = C + 4;
   static constexpr int oDU = 0, oU = oDU + C * P1, oDO = oU + C * P1, oT = oDO + C * P1, oX = oT + C * P2,
-                       oY = oX + C * P2, oV = oY + C * P2, oCol = oV + kLRows * C, oRed = oCol + 4 * C,
-                       floats = oRed + 8;
+                       oY = oX + C * P2, oV = oY + C * P2, oCol = oV + nRows * C, oRed = oCol + 4 * C,
+                       floats = oRed + 4 * NP;
 };
 
 __device__ __forceinline__ v4f mma4(float a, float b, const v4f& c) {
@@ -805,21 +806,21 @@ __device__ __forceinline__ float col4_sum(float x) {
   return x;
 }
 
-template <typename T, int D, int C>
-__global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
+template <typename T, int D, int C, int NP>
+__global__ __launch_bounds__(256 * NP) void bwd_local_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
                                                         float* dg, float* dbeta, int h_qk, int h_v, float scale,
                                                         int erase) {
-  using L = LocalLayout<D, C>;
-  // NH tiles of d columns and NCH tiles of C columns per wave; with C = 16
-  // the C x C products are one tile, taken by the first half alone
-  constexpr int P1 = L::P1, P2 = L::P2, NN = D / 16, NC = C / 16, NH = NN / 2, NCH = NC >= 2 ? NC / 2 : 1;
-  constexpr int NT = 512;
+  using L = LocalLayout<D, C, NP>;
+  // NH tiles of d columns per wave; the C x C products split into NCP parts
+  // of NCH tiles (NCP < NP when C has fewer tiles than there are parts)
+  constexpr int P1 = L::P1, P2 = L::P2, NN = D / 16, NC = C / 16, NH = NN / NP;
+  constexpr int NCP = NC < NP ? NC : NP, NCH = NC / NCP, NT = 256 * NP, RPW = 16 / NP;
   const int gc = blockIdx.x / h_v, h = blockIdx.x % h_v, tid = threadIdx.x;
   if (gc >= *w.nc) return;
   const ChunkRec cr = w.ct[gc];
   const int hq = h / (h_v / h_qk), lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
-  const int mt = wave & 3, ch = wave >> 2, r0 = 16 * mt, cb = ch * (D / 2), jb = NC >= 2 ? ch * (C / 2) : 0;
-  const bool rows = mt < NC, ccw = rows && (NC >= 2 || ch == 0);
+  const int mt = wave & 3, ch = wave >> 2, r0 = 16 * mt, cb = ch * (D / NP), jb = 16 * NCH * ch;
+  const bool rows = mt < NC, ccw = rows && ch < NCP;
   const int64_t bv = (int64_t)gc * h_v + h, bq = (int64_t)gc * h_qk + hq;
   extern __shared__ float lds[];
   float* sDU = lds + L::oDU;
@@ -828,7 +829,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
   float* sT = lds + L::oT;
   float* sX = lds + L::oX;    // dQK
   float* sY = lds + L::oY;    // dT, then dKK
-  float* sV = lds + L::oV;    // per-row scalars, kLRows x C
+  float* sV = lds + L::oV;    // per-row scalars, nRows x C
   float* sCol = lds + L::oCol;  // column sums of the Gam terms per row tile, 4 x C
   float* sRed = lds + L::oRed;
   const float* gDU = w.cd[mDU] + bv * C * D;
@@ -861,7 +862,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
     sV[lBG * C + e] = vec[kVecBG * C + e];
     sV[lSG * C + e] = vec[kVecSG * C + e];
 #pragma unroll
-    for (int q = lU; q < kLRows; ++q) sV[q * C + e] = 0.f;
+    for (int q = lU; q < L::nRows; ++q) sV[q * C + e] = 0.f;
   }
   lds_barrier();
   const v4f z4 = {0.f, 0.f, 0.f, 0.f};
@@ -892,7 +893,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = row16_sum(rs[i]);
-      if (l16 == 0) sV[(lR0 + ch) * C + r0 + 4 * g4 + i] = x;
+      if (l16 == 0) sV[(L::lR + ch) * C + r0 + 4 * g4 + i] = x;
     }
   }
   if (rows) {
@@ -917,7 +918,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
           }
         }
         b1 = row16_sum(b1);
-        if (l16 == 0) sV[(lB0 + ch) * C + r] = b1;
+        if (l16 == 0) sV[(L::lB + ch) * C + r] = b1;
       }
     }
     // ---- dT = dU (diag(beta) V)^T; the dW term is added below
@@ -966,7 +967,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
           accW[nt][i] = -accW[nt][i];
         }
         a = row16_sum(a);
-        if (l16 == 0) sV[(lA0 + ch) * C + r] = a;
+        if (l16 == 0) sV[(L::lA + ch) * C + r] = a;
       }
     }
     // ---- dK^ starts as diag(e) U dX'^T; u_r = U_r . (dU_r - (Pm^T dO)_r)
@@ -980,8 +981,8 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt) accK[nt][i] *= ee;
       }
-      for (int rr = 0; rr < 8; ++rr) {
-        const int r = r0 + 8 * ch + rr;
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int r = r0 + RPW * ch + rr;
         float u = 0.f;
         for (int c = lane; c < D; c += 64) u += sU[r * P1 + c] * (sDU[r * P1 + c] - gPdO[r * D + c]);
         u = wave_sum(u);
@@ -1070,8 +1071,8 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
     for (int i = 0; i < 4; ++i) {
       const float x = row16_sum(rs[i]), y = row16_sum(db[i]);
       if (l16 == 0) {
-        sV[(lR0 + ch) * C + r0 + 4 * g4 + i] += x;
-        sV[(lDB0 + ch) * C + r0 + 4 * g4 + i] = y;
+        sV[(L::lR + ch) * C + r0 + 4 * g4 + i] += x;
+        sV[(L::lDB + ch) * C + r0 + 4 * g4 + i] = y;
       }
     }
   }
@@ -1094,7 +1095,7 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
           accK[nt][i] += bg * acc[nt][i];
         }
         sd = row16_sum(sd);
-        if (l16 == 0) sV[(lS0 + ch) * C + r] = sd;
+        if (l16 == 0) sV[(L::lS + ch) * C + r] = sd;
       }
     }
     // ---- dK^ += dQK^T Q^ + (dKK + dKK^T) K^,  dQ^ += dQK K^
@@ -1130,17 +1131,25 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
   if (wave == 0) {
     const int r = lane;
     const bool on = r < C;
-    float col = 0.f, d = 0.f, u = 0.f;
+    float col = 0.f, d = 0.f, u = 0.f, db = 0.f;
     if (on) {
       for (int q = 0; q < NC; ++q) col += sCol[q * C + r];
+      float a = 0.f, sd = 0.f, rw = 0.f;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        a += sV[(L::lA + q) * C + r];
+        sd += sV[(L::lS + q) * C + r];
+        rw += sV[(L::lR + q) * C + r];
+        db += sV[(L::lB + q) * C + r] + sV[(L::lDB + q) * C + r];
+      }
       u = sV[lU * C + r];
-      d = sV[lSG * C + r] * (sV[lA0 * C + r] + sV[lA1 * C + r]) +
-          sV[lBG * C + r] * (sV[lS0 * C + r] + sV[lS1 * C + r]) + sV[lR0 * C + r] + sV[lR1 * C + r] - col - u;
+      d = sV[lSG * C + r] * a + sV[lBG * C + r] * sd + rw - col - u;
+      if (erase) db += sV[lGam * C + r] * sd;
     }
     const float us = wave_sum(u);
     float xd = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xd += sRed[q];
+    for (int q = 0; q < 4 * NP; ++q) xd += sRed[q];
     if (r == C - 1) d += us + sV[lGam * C + r] * xd;
 #pragma unroll
     for (int off = 1; off < 64; off *= 2) {
@@ -1150,19 +1159,22 @@ __global__ __launch_bounds__(512) void bwd_local_kernel(BwdWs w, const T* v, int
     if (r < cr.len) {
       const int64_t t = (int64_t)(cr.t0 + r);
       dg[t * h_v + h] = d;
-      dbeta[t * h_v + h] = sV[lB0 * C + r] + sV[lB1 * C + r] + sV[lDB0 * C + r] + sV[lDB1 * C + r] +
-                           (erase ? sV[lGam * C + r] * (sV[lS0 * C + r] + sV[lS1 * C + r]) : 0.f);
+      dbeta[t * h_v + h] = db;
     }
   }
 }
 
+// Column parts per row tile: 4 (16 waves, 4 per SIMD at one workgroup per CU)
+constexpr int kLocalParts = 4;
+
 template <typename T, int D, int C>
 hipError_t launch_local(const BwdWs& w, const PrefillBwdParams& p, int64_t ncm, hipStream_t stream) {
-  const size_t lds = (size_t)LocalLayout<D, C>::floats * sizeof(float);
-  const void* f = reinterpret_cast<const void*>(bwd_local_kernel<T, D, C>);
+  constexpr int NP = kLocalParts;
+  const size_t lds = (size_t)LocalLayout<D, C, NP>::floats * sizeof(float);
+  const void* f = reinterpret_cast<const void*>(bwd_local_kernel<T, D, C, NP>);
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_local_kernel<T, D, C>), dim3((unsigned)(ncm * p.h_v)), dim3(512), lds, stream, w,
+  hipLaunchKernelGGL((bwd_local_kernel<T, D, C, NP>), dim3((unsigned)(ncm * p.h_v)), dim3(256 * NP), lds, stream, w,
                      static_cast<const T*>(p.v), p.v_stride, static_cast<T*>(p.dv), p.dv_stride, p.dg, p.dbeta,
                      p.h_qk, p.h_v, p.scale, p.erase);
   return hipGetLastError();
