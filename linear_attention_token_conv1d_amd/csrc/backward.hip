@@ -809,7 +809,9 @@ __device__ __forceinline__ float col4_sum(float x) {
 template <typename T, int D, int C, int NP>
 __global__ __launch_bounds__(256 * NP) void bwd_local_kernel(BwdWs w, const T* v, int64_t vs, T* dv, int64_t dvs,
                                                         float* dg, float* dbeta, int h_qk, int h_v, float scale,
-                                                        int erase) {
+                                                        int erase, const T* qx, const T* kx, int64_t qs, int64_t ks,
+                                                        T* dq, T* dk, int64_t dqs, int64_t dks, int l2norm,
+                                                        int direct) {
   using L = LocalLayout<D, C, NP>;
   // NH tiles of d columns per wave; the C x C products split into NCP parts
   // of NCH tiles (NCP < NP when C has fewer tiles than there are parts)
@@ -867,6 +869,7 @@ __global__ __launch_bounds__(256 * NP) void bwd_local_kernel(BwdWs w, const T* v
   lds_barrier();
   const v4f z4 = {0.f, 0.f, 0.f, 0.f};
   v4f accK[NH], accQ[NH], accW[NH];
+  float xk[NH][4], xq[NH][4];
   if (ccw) {
     // ---- dPm = dO U^T -> dQK = scale Gam o dPm (lower incl.); Gam terms of dG
     v4f acc[NCH];
@@ -1098,6 +1101,22 @@ __global__ __launch_bounds__(256 * NP) void bwd_local_kernel(BwdWs w, const T* v
         if (l16 == 0) sV[(L::lS + ch) * C + r] = sd;
       }
     }
+    // raw q, k rows for the L2-norm backward below, fetched ahead of the
+    // last products
+    if (direct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = r0 + 4 * g4 + i;
+        const bool in = rr < cr.len;
+        const int64_t t = (int64_t)(cr.t0 + rr);
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          const int c = cb + 16 * nt + l16;
+          xk[nt][i] = in ? to_f32(kx[t * ks + (int64_t)hq * D + c]) : 0.f;
+          xq[nt][i] = in ? to_f32(qx[t * qs + (int64_t)hq * D + c]) : 0.f;
+        }
+      }
+    }
     // ---- dK^ += dQK^T Q^ + (dKK + dKK^T) K^,  dQ^ += dQK K^
     const int r = r0 + l16;
 #pragma unroll 2
@@ -1114,16 +1133,74 @@ __global__ __launch_bounds__(256 * NP) void bwd_local_kernel(BwdWs w, const T* v
         accQ[nt] = mma4(a3, kn, accQ[nt]);
       }
     }
-    float* gdKn = w.cd[mDKn] + bv * C * D;
-    float* gdQn = w.cd[mDQn] + bv * C * D;
+    if (!direct) {  // summed over the group's V heads by the QK-head kernel
+      float* gdKn = w.cd[mDKn] + bv * C * D;
+      float* gdQn = w.cd[mDQn] + bv * C * D;
 #pragma unroll
-    for (int nt = 0; nt < NH; ++nt)
+      for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t e = (int64_t)(r0 + 4 * g4 + i) * D + cb + 16 * nt + l16;
+          gdKn[e] = accK[nt][i];
+          gdQn[e] = accQ[nt][i];
+        }
+    }
+  }
+  if (direct) {
+    // One V head reads this QK head, so dK^ and dQ^ are complete: back through
+    // x^ = x / sqrt(|x|^2 + eps) here, dx = r (dx^ - x^ (x^ . dx^)) with
+    // r = 1 / sqrt(|x|^2 + eps), the row sums over the NP column parts
+    // exchanged through dU's space (dead since the dW store)
+    float* sP = sDU;  // [4][NP][C]: |k|^2, k . dK^, |q|^2, q . dQ^
+    if (rows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t e = (int64_t)(r0 + 4 * g4 + i) * D + cb + 16 * nt + l16;
-        gdKn[e] = accK[nt][i];
-        gdQn[e] = accQ[nt][i];
+        const int r = r0 + 4 * g4 + i;
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          p0 += xk[nt][i] * xk[nt][i];
+          p1 += xk[nt][i] * accK[nt][i];
+          p2 += xq[nt][i] * xq[nt][i];
+          p3 += xq[nt][i] * accQ[nt][i];
+        }
+        p0 = row16_sum(p0);
+        p1 = row16_sum(p1);
+        p2 = row16_sum(p2);
+        p3 = row16_sum(p3);
+        if (l16 == 0) {
+          sP[(0 * NP + ch) * C + r] = p0;
+          sP[(1 * NP + ch) * C + r] = p1;
+          sP[(2 * NP + ch) * C + r] = p2;
+          sP[(3 * NP + ch) * C + r] = p3;
+        }
       }
+    }
+    lds_barrier();
+    if (rows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * g4 + i;
+        if (r >= cr.len) continue;
+        const int64_t t = (int64_t)(cr.t0 + r);
+        float sk = 0.f, dkx = 0.f, sq = 0.f, dqx = 0.f;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          sk += sP[(0 * NP + q) * C + r];
+          dkx += sP[(1 * NP + q) * C + r];
+          sq += sP[(2 * NP + q) * C + r];
+          dqx += sP[(3 * NP + q) * C + r];
+        }
+        const float rk = l2norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.f, rq = l2norm ? 1.0f / sqrtf(sq + 1e-6f) : 1.f;
+        const float ck = l2norm ? dkx * rk * rk * rk : 0.f, cq = l2norm ? dqx * rq * rq * rq : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) {
+          const int c = cb + 16 * nt + l16;
+          dk[t * dks + (int64_t)hq * D + c] = from_f32<T>(accK[nt][i] * rk - xk[nt][i] * ck);
+          dq[t * dqs + (int64_t)hq * D + c] = from_f32<T>(accQ[nt][i] * rq - xq[nt][i] * cq);
+        }
+      }
+    }
   }
   lds_barrier();
   // ---- dG per row, its reverse cumulative sum dg (a suffix scan over the
@@ -1176,7 +1253,9 @@ hipError_t launch_local(const BwdWs& w, const PrefillBwdParams& p, int64_t ncm, 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_local_kernel<T, D, C, NP>), dim3((unsigned)(ncm * p.h_v)), dim3(256 * NP), lds, stream, w,
                      static_cast<const T*>(p.v), p.v_stride, static_cast<T*>(p.dv), p.dv_stride, p.dg, p.dbeta,
-                     p.h_qk, p.h_v, p.scale, p.erase);
+                     p.h_qk, p.h_v, p.scale, p.erase, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+                     p.q_stride, p.k_stride, static_cast<T*>(p.dq), static_cast<T*>(p.dk), p.dq_stride, p.dk_stride,
+                     p.l2norm, p.h_v == p.h_qk);
   return hipGetLastError();
 }
 
@@ -1540,10 +1619,13 @@ hipError_t prefill_backward_impl(const PrefillBwdParams& p, int D, hipStream_t s
       e = C == 16 ? launch_local<T, 128, 16>(w, p, ncm, stream)
                   : C == 32 ? launch_local<T, 128, 32>(w, p, ncm, stream) : launch_local<T, 128, 64>(w, p, ncm, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_final_qk_kernel<T>, dim3((unsigned)p.total_tokens, (unsigned)hq), dim3(64), 0, stream, w,
-                       p.cu_seqlens, p.n_seqs, q, k, p.q_stride, p.k_stride, static_cast<T*>(p.dq),
-                       static_cast<T*>(p.dk), p.dq_stride, p.dk_stride, hq, hv, D, C, p.l2norm);
-    L.check();
+    // with one V head per QK head the fused kernel has written dq and dk
+    if (hv != hq) {
+      hipLaunchKernelGGL(bwd_final_qk_kernel<T>, dim3((unsigned)p.total_tokens, (unsigned)hq), dim3(64), 0, stream, w,
+                         p.cu_seqlens, p.n_seqs, q, k, p.q_stride, p.k_stride, static_cast<T*>(p.dq),
+                         static_cast<T*>(p.dk), p.dq_stride, p.dk_stride, hq, hv, D, C, p.l2norm);
+      L.check();
+    }
   }
   return L.err;
 }

@@ -67,13 +67,17 @@ def _run_and_compare(lens, h_qk, h_v, d, io, chunk, erase=True, l2=True, s0=True
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("d,chunk", [(64, 16), (64, 64), (128, 32), (128, 64)])
-def test_prefill_backward_varlen_grouped(io, d, chunk):
-    _run_and_compare([70, 1, 0, 130, 33], 2, 4, d, io, chunk, seed=10)
+@pytest.mark.parametrize("h_qk,h_v", [(2, 4), (3, 3)])
+def test_prefill_backward_varlen_grouped(io, d, chunk, h_qk, h_v):
+    """Two V heads per QK head (dq, dk summed over the group by the QK-head
+    kernel) and one (the chunk-local kernel goes back through the L2 norm)."""
+    _run_and_compare([70, 1, 0, 130, 33], h_qk, h_v, d, io, chunk, seed=10)
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_prefill_backward_erase_off(io):
-    _run_and_compare([150, 7], 1, 3, 64, io, 64, erase=False, seed=20)
+@pytest.mark.parametrize("h_qk,h_v", [(1, 3), (2, 2)])
+def test_prefill_backward_erase_off(io, h_qk, h_v):
+    _run_and_compare([150, 7], h_qk, h_v, 64, io, 64, erase=False, seed=20)
 
 
 def test_prefill_backward_without_l2_norm_and_scale():
