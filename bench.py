@@ -255,7 +255,7 @@ def run_backward(name, steps, warmup, do_cpu):
            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / PEAK_F32_TFLOPS, 4),
                         "traffic": measured_traffic(f"backward_{name}_traffic.md", "backward.hip"),
-                        "kernel": "gdn_prefill_backward (fp32 batched GEMMs, two chains, fused chunk-local kernel, QK-head kernel)",
+                        "kernel": "gdn_prefill_backward (fp32 batched GEMMs, two chains, fused chunk-local kernel; a QK-head kernel when a QK head has several V heads)",
                         "flops_per_launch": flops},
            "config": {"workload": f"{name} backward: gdn_prefill_backward + gdn_conv1d_backward, B={N} T={T} "
                                   f"h_qk={hq} h_v={hv} d={d} chunk={cfg['chunk']}, bf16 io, fp32 arithmetic"}}
