@@ -381,33 +381,37 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
     Pm[e] = j <= r ? scale * expf(sG[r] - sG[j]) * QK[e] : 0.f;
   }
   __syncthreads();
-  // (I + A) T = I, A strictly lower: row i of T is e_i - sum_{j<i} A_ij T_j
-  for (int i = 0; i < C; ++i) {
-    if (tid < C) {
-      float s = i == tid ? 1.f : 0.f;
-      for (int j = 0; j < i; ++j) s -= sA[i][j] * sT[j][tid];
-      sT[i][tid] = s;
+  // (I + A) T = I, A strictly lower: row i of T is e_i - sum_{j<i} A_ij T_j.
+  // Lane c of wave 0 solves column c alone (it reads back only its own
+  // writes, and A is read-only here), so the rows need no barrier; the other
+  // waves meanwhile write beta V and dO in the chunk layout (the row scalings
+  // of K^ and Q^ are applied where they are read).
+  if (tid < 64) {
+    if (tid < C)
+      for (int i = 0; i < C; ++i) {
+        float s = i == tid ? 1.f : 0.f;
+        for (int j = 0; j < i; ++j) s -= sA[i][j] * sT[j][tid];
+        sT[i][tid] = s;
+      }
+  } else {
+    float* BV = w.cd[mBV] + bv * C * D;
+    float* DO = w.cd[mDO] + bv * C * D;
+    for (int e = 4 * (tid - 64); e < C * D; e += 4 * (blockDim.x - 64)) {
+      const int r = e / D, c = e % D;
+      const bool in = r < cr.len;
+      const int64_t tok = (int64_t)(cr.t0 + r);
+      float vv[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
+      if (in) {
+        load4(v + tok * vs + (int64_t)h * D + c, vv);
+        load4(d_o + (tok * h_v + h) * D + c, dd);
+      }
+      *reinterpret_cast<v4f*>(BV + e) = v4f{sB[r] * vv[0], sB[r] * vv[1], sB[r] * vv[2], sB[r] * vv[3]};
+      *reinterpret_cast<v4f*>(DO + e) = v4f{dd[0], dd[1], dd[2], dd[3]};
     }
-    __syncthreads();
   }
+  __syncthreads();
   float* Tm = w.cc[cT] + bv * C * C;
   for (int e = tid; e < C * C; e += blockDim.x) Tm[e] = sT[e / C][e % C];
-  // beta V and dO in the chunk layout (the row scalings of K^ and Q^ are
-  // applied where they are read)
-  float* BV = w.cd[mBV] + bv * C * D;
-  float* DO = w.cd[mDO] + bv * C * D;
-  for (int e = 4 * tid; e < C * D; e += 4 * blockDim.x) {
-    const int r = e / D, c = e % D;
-    const bool in = r < cr.len;
-    const int64_t tok = (int64_t)(cr.t0 + r);
-    float vv[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in) {
-      load4(v + tok * vs + (int64_t)h * D + c, vv);
-      load4(d_o + (tok * h_v + h) * D + c, dd);
-    }
-    *reinterpret_cast<v4f*>(BV + e) = v4f{sB[r] * vv[0], sB[r] * vv[1], sB[r] * vv[2], sB[r] * vv[3]};
-    *reinterpret_cast<v4f*>(DO + e) = v4f{dd[0], dd[1], dd[2], dd[3]};
-  }
 }
 
 // ----------------------------------------------------------------- chain
