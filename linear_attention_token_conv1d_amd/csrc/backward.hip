@@ -352,14 +352,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdWs w, const float* g, 
   __shared__ float sG[64], sGam[64], sE[64], sB[64];
   __shared__ float sA[64][65];
   __shared__ float sT[64][65];
-  for (int r = tid; r < C; r += blockDim.x) {
+  if (tid < 64) {  // G = cumsum(g): an inclusive scan over the lanes of wave 0
+    const int r = tid;
     const bool in = r < cr.len;
-    sG[r] = in ? g[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
-    sB[r] = in ? beta[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+    float x = in ? g[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) {
+      const float t = __shfl_up(x, off, 64);
+      if (r >= off) x += t;
+    }
+    if (r < C) {
+      sG[r] = x;
+      sB[r] = in ? beta[(int64_t)(cr.t0 + r) * h_v + h] : 0.f;
+    }
   }
-  __syncthreads();
-  if (tid == 0)
-    for (int r = 1; r < C; ++r) sG[r] += sG[r - 1];
   __syncthreads();
   float* vec = w.vec + bv * kNVec * C;
   for (int r = tid; r < C; r += blockDim.x) {
