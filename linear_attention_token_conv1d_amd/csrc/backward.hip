@@ -299,14 +299,27 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BG p) {
 }
 
 // ------------------------------------------------------- stage: Kn, Qn
+// Two consecutive elements (4-byte aligned for bf16, 8-byte for fp32).
+__device__ __forceinline__ void load2(const __bf16* p, float& a, float& b) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  a = __uint_as_float(u << 16);
+  b = __uint_as_float(u & 0xffff0000u);
+}
+__device__ __forceinline__ void load2(const float* p, float& a, float& b) {
+  const float2 f = *reinterpret_cast<const float2*>(p);
+  a = f.x;
+  b = f.y;
+}
+
 // Per (chunk, QK head): the normalised key and query rows, zero past the end.
+// Lane l holds elements D/64 l .. of a row (one 4- or 8-byte access each way).
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, const T* k, int64_t qs,
                                                            int64_t ks, int h_qk, int D, int C, int l2norm) {
   const int gc = blockIdx.x / h_qk, hq = blockIdx.x % h_qk;
   if (gc >= *w.nc) return;
   const ChunkRec cr = w.ct[gc];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, per = D / 64, c0 = per * lane;
   float* Kn = w.Kn + ((int64_t)gc * h_qk + hq) * C * D;
   float* Qn = w.Qn + ((int64_t)gc * h_qk + hq) * C * D;
   // a wave takes 4 rows at a time, all their loads issued before the sums
@@ -315,15 +328,15 @@ __global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, 
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int which = 0; which < 2; ++which)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = r0 + rr;
-          v[rr][which][i] = (r < cr.len && i < D / 64)
-                                ? to_f32((which ? q : k)[(int64_t)(cr.t0 + r) * (which ? qs : ks) + (int64_t)hq * D +
-                                                         lane + 64 * i])
-                                : 0.f;
+      for (int which = 0; which < 2; ++which) {
+        const int r = r0 + rr;
+        v[rr][which][0] = v[rr][which][1] = 0.f;
+        if (r < cr.len) {
+          const T* src = (which ? q : k) + (int64_t)(cr.t0 + r) * (which ? qs : ks) + (int64_t)hq * D + c0;
+          if (per == 2) load2(src, v[rr][which][0], v[rr][which][1]);
+          else v[rr][which][0] = to_f32(src[0]);
         }
+      }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -331,8 +344,9 @@ __global__ __launch_bounds__(256) void bwd_stage_qk_kernel(BwdWs w, const T* q, 
         const int r = r0 + rr;
         const float ss = wave_sum(v[rr][which][0] * v[rr][which][0] + v[rr][which][1] * v[rr][which][1]);
         const float rn = (l2norm && r < cr.len) ? 1.0f / sqrtf(ss + 1e-6f) : 1.0f;
-        float* dst = which ? Qn : Kn;
-        for (int i = 0; i < D / 64; ++i) dst[(int64_t)r * D + lane + 64 * i] = v[rr][which][i] * rn;
+        float* dst = (which ? Qn : Kn) + (int64_t)r * D + c0;
+        if (per == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[rr][which][0] * rn, v[rr][which][1] * rn);
+        else dst[0] = v[rr][which][0] * rn;
       }
   }
 }
