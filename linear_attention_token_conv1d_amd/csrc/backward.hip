@@ -1296,28 +1296,36 @@ __global__ __launch_bounds__(64) void bwd_final_qk_kernel(BwdWs w, const int32_t
   const int n = cu ? seq_index(cu, n_seqs, t) : 0;
   const int64_t s = cu ? cu[n] : 0;
   const int gc = w.co[n] + (int)((t - s) / C), r = (int)((t - s) % C);
+  // lane l holds elements D/64 l .. of the row (one 4- or 8-byte access each)
+  const int per = D / 64, c0 = per * lane;
   for (int which = 0; which < 2; ++which) {
     const float* src = which ? w.cd[mDQn] : w.cd[mDKn];
+    const T* xs = (which ? q : k) + t * (which ? qs : ks) + (int64_t)hq * D + c0;
     float d[2] = {0.f, 0.f}, x[2] = {0.f, 0.f};
-    for (int i = 0; i < D / 64; ++i) {
-      for (int j = 0; j < grp; ++j)
-        d[i] += src[(((int64_t)gc * h_v + hq * grp + j) * C + r) * D + lane + 64 * i];
-      x[i] = to_f32((which ? q : k)[t * (which ? qs : ks) + (int64_t)hq * D + lane + 64 * i]);
-    }
-    if (l2norm) {
-      float ss = 0.f, xd = 0.f;
-      for (int i = 0; i < D / 64; ++i) {
-        ss += x[i] * x[i];
-        xd += x[i] * d[i];
+    for (int j = 0; j < grp; ++j) {
+      const float* sr = src + (((int64_t)gc * h_v + hq * grp + j) * C + r) * D + c0;
+      if (per == 2) {
+        const float2 f = *reinterpret_cast<const float2*>(sr);
+        d[0] += f.x;
+        d[1] += f.y;
+      } else {
+        d[0] += sr[0];
       }
-      ss = wave_sum(ss);
-      xd = wave_sum(xd);
-      const float rn = 1.0f / sqrtf(ss + 1e-6f);
-      for (int i = 0; i < D / 64; ++i) d[i] = d[i] * rn - x[i] * xd * rn * rn * rn;
     }
-    T* dst = which ? dq : dk;
-    const int64_t st = which ? dqs : dks;
-    for (int i = 0; i < D / 64; ++i) dst[t * st + (int64_t)hq * D + lane + 64 * i] = from_f32<T>(d[i]);
+    if (per == 2) load2(xs, x[0], x[1]);
+    else x[0] = to_f32(xs[0]);
+    if (l2norm) {
+      const float ss = wave_sum(x[0] * x[0] + x[1] * x[1]), xd = wave_sum(x[0] * d[0] + x[1] * d[1]);
+      const float rn = 1.0f / sqrtf(ss + 1e-6f);
+      for (int i = 0; i < 2; ++i) d[i] = d[i] * rn - x[i] * xd * rn * rn * rn;
+    }
+    T* dst = (which ? dq : dk) + t * (which ? dqs : dks) + (int64_t)hq * D + c0;
+    if (per == 2) {
+      const T o[2] = {from_f32<T>(d[0]), from_f32<T>(d[1])};
+      __builtin_memcpy(dst, o, sizeof(o));
+    } else {
+      dst[0] = from_f32<T>(d[0]);
+    }
   }
 }
 
