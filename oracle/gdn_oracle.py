@@ -57,6 +57,7 @@ __all__ = [
     "chunked_gated_delta_rule",
     "unrolled_product_form",
     "round_to_bf16",
+    "ring_to_chronological",
     "l2_normalize_backward",
     "gated_delta_rule_backward",
     "causal_conv1d_backward",
@@ -123,6 +124,27 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activa
     else:
         assert activation in (None, "none")
     return y, new_state
+
+
+def ring_to_chronological(conv_state, conv_head):
+    """The conv state of each sequence in chronological order (oldest first).
+
+    conv_state [N, C, M] holds the last M = W-1 inputs of every channel in a
+    ring of M slots; conv_head [N] is the slot of the oldest one, so the j-th
+    oldest input sits in slot (head + j) mod M.  A ring is a storage layout of
+    the same (channels, width - 1) conv buffer the per-request memory section
+    of "Mamba hybrid model selection" describes: a decode step can overwrite
+    the oldest slot and advance the head instead of moving every slot.
+    """
+    cs = _f64(conv_state)
+    heads = np.asarray(conv_head).reshape(-1)
+    N, _, M = cs.shape
+    out = np.empty_like(cs)
+    for n in range(N):
+        h = int(heads[n]) % M
+        for j in range(M):
+            out[n, :, j] = cs[n, :, (h + j) % M]
+    return out
 
 
 def split_qkv(y, h_qk, d_k, h_v, d_v):

@@ -432,3 +432,39 @@ def test_varlen_lengths_recipe():
     rng = np.random.default_rng(0)
     L = gdn_inputs.varlen_lengths(8, 262144, 4096, 65536, rng)
     assert L.sum() == 262144 and L.min() >= 4096 and L.max() <= 65536 and len(L) == 8
+
+
+def test_ring_to_chronological_by_hand():
+    """Hand-worked ring of three slots holding inputs a, b, c of one channel:
+    with head 1 the oldest input is slot 1, so the order is (b, c, a); with
+    head 2 it is (c, a, b); head 0 is the chronological layout itself."""
+    a, b, c = 1.0, 2.0, 3.0
+    ring = np.array([[[a, b, c]]] * 3)  # three sequences, one channel, slots 0..2
+    got = orc.ring_to_chronological(ring, np.array([0, 1, 2]))
+    assert got[0, 0].tolist() == [a, b, c]
+    assert got[1, 0].tolist() == [b, c, a]
+    assert got[2, 0].tolist() == [c, a, b]
+
+
+def test_ring_step_equals_shift():
+    """Writing the new input over the oldest slot and advancing the head holds
+    the same chronological conv state as shifting the slots, step after step,
+    for every starting head; the decode oracle consumes that state."""
+    rng = np.random.default_rng(5)
+    N, C, M = 3, 4, 3
+    ring = rng.standard_normal((N, C, M))
+    head = np.array([0, 1, 2])
+    chrono = orc.ring_to_chronological(ring, head)
+    for _ in range(7):
+        x = rng.standard_normal((N, C))
+        for n in range(N):                       # ring step: one slot, head + 1
+            ring[n, :, head[n]] = x[n]
+        head = (head + 1) % M
+        chrono = np.concatenate([chrono[:, :, 1:], x[:, :, None]], axis=2)  # shift step
+        assert np.array_equal(orc.ring_to_chronological(ring, head), chrono)
+    # and the conv over one more token reads the same history either way
+    w = rng.standard_normal((C, M + 1))
+    xt = rng.standard_normal((1, C))
+    y_ring, _ = orc.causal_conv1d(xt, w, conv_state=orc.ring_to_chronological(ring, head)[:1], activation=None)
+    expect = sum(w[:, j] * chrono[0, :, j] for j in range(M)) + w[:, M] * xt[0]
+    assert np.allclose(y_ring[0], expect, rtol=0, atol=1e-12)
