@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -84,11 +84,26 @@ typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activatio
  *   bias         [C] or NULL.
  *   y            [T, C] output; must not overlap x.
  *   conv_state   [n_seqs, C, W-1] in/out, or NULL.  On return it holds the
- *                last W-1 inputs of (old state ++ sequence), oldest first; a
- *                zero-length sequence keeps its state.
+ *                last W-1 inputs of (old state ++ sequence), oldest first
+ *                (chronological: slot 0 the oldest); a zero-length sequence
+ *                keeps its inputs.
  *   cu_seqlens   [n_seqs + 1] int32 device array of sequence offsets
  *                (0 = cu[0] <= cu[1] <= ... = T), or NULL for one sequence.
  *                Values are trusted (not validated on the host).
+ *   conv_head    [n_seqs] int32 ring heads of conv_state, or NULL.  With a
+ *                head h, the state's W-1 slots form a ring: the j-th oldest
+ *                input sits in slot (h + j) mod (W-1), so that a decode step
+ *                can replace one slot instead of shifting all of them (the
+ *                conv state is a fixed (channels, width - 1) buffer per
+ *                request, "Mamba hybrid model selection", per-request memory
+ *                section).  On entry 0 <= h < W-1 (taken mod W-1); on return
+ *                the state is chronological and every head is 0.  NULL means
+ *                chronological on entry.  Ignored without conv_state.  The
+ *                library uses the bits above the lowest 8 of each head as a
+ *                reader count during the call: nothing else may access
+ *                conv_head until the call has finished on the stream.
+ * Structs from callers built against ABI 3 (struct_size without conv_head)
+ * are accepted and read as conv_head = NULL.
  * ---------------------------------------------------------------------- */
 typedef struct gdn_conv1d_args {
   uint32_t struct_size;
@@ -104,6 +119,7 @@ typedef struct gdn_conv1d_args {
   void* y;
   void* conv_state;
   const int32_t* cu_seqlens;
+  int32_t* conv_head;
 } gdn_conv1d_args;
 
 gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
@@ -117,9 +133,9 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  * sequence start; the last chunk may be partial).
  *
  *   io_dtype     GDN_BF16 or GDN_F32: dtype of q, k, v and o.  The state is
- *                always fp32; accumulation is fp32.  With GDN_BF16 the dense
- *                chunk contractions run on bf16 MFMA; with GDN_F32 on fp32
- *                MFMA.
+ *                carried in fp32 inside the call; accumulation is fp32.  With
+ *                GDN_BF16 the dense chunk contractions run on bf16 MFMA; with
+ *                GDN_F32 on fp32 MFMA.
  *   flags        GDN_FLAG_L2NORM_QK to normalise q and k inside the call;
  *                GDN_FLAG_NO_ERASE for the erase-off variant (same chunked
  *                machinery with A = 0, i.e. T = I, and U = diag(beta) V).
@@ -134,8 +150,8 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  *   v            [T, h_v, d_v] with token stride v_stride.
  *   g, beta      [T, h_v] fp32: log-decay (alpha = exp(g) in (0, 1]) and
  *                write strength.
- *   initial_state [n_seqs, h_v, d_v, d_k] fp32, or NULL for zeros.
- *   final_state  [n_seqs, h_v, d_v, d_k] fp32, or NULL; may alias
+ *   initial_state [n_seqs, h_v, d_v, d_k] in state_dtype, or NULL for zeros.
+ *   final_state  [n_seqs, h_v, d_v, d_k] in state_dtype, or NULL; may alias
  *                initial_state.
  *   o            [T, h_v, d_v] in io_dtype.
  *   cu_seqlens   as in gdn_conv1d.
@@ -148,7 +164,7 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  *                boundary states already exist on chip, and a recurrent cache
  *                can be reused only from states stored at block boundaries
  *                ("Mamba hybrid model selection", adoption checklist).
- *   chunk_states [R, h_v, d_v, d_k] fp32, R = sum_n E_n with
+ *   chunk_states [R, h_v, d_v, d_k] in state_dtype, R = sum_n E_n with
  *                E_n = floor(max(len_n - 1, 0) / (K chunk)); sequence n's
  *                states are rows sum_{m<n} E_m + j - 1.  NULL when K = 0.
  *   state_idx    [n_seqs] int32 or NULL: sequence n reads initial_state and
@@ -157,6 +173,15 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* args, void* stream);
  *                slots across requests ("Mamba hybrid model selection",
  *                concurrent-requests section).  Slots must be distinct and
  *                inside both pools; they are not read on the host.
+ *   state_dtype  GDN_F32 or GDN_BF16: dtype of initial_state, final_state
+ *                and chunk_states in memory.  The model keeps its recurrent
+ *                state in fp32 ("Inside Qwen3.5", config note); a bf16 pool
+ *                halves the bytes a decode step moves ("Mamba hybrid model
+ *                selection", adoption checklist: the state's precision is a
+ *                choice).  bf16 states are read exactly and written with
+ *                round-to-nearest-even; inside the call the state is fp32.
+ * Structs from callers built against ABI 3 (struct_size without state_dtype)
+ * are accepted and read as state_dtype = GDN_F32.
  * ---------------------------------------------------------------------- */
 typedef struct gdn_prefill_args {
   uint32_t struct_size;
@@ -178,15 +203,16 @@ typedef struct gdn_prefill_args {
   int64_t v_stride;
   const float* g;
   const float* beta;
-  const float* initial_state;
-  float* final_state;
+  const void* initial_state;
+  void* final_state;
   void* o;
   const int32_t* cu_seqlens;
   void* workspace;
   size_t workspace_bytes;
   int32_t emit_every;
-  float* chunk_states;
+  void* chunk_states;
   const int32_t* state_idx;
+  int32_t state_dtype;
 } gdn_prefill_args;
 
 /* Bytes of workspace gdn_prefill needs for these arguments (pointers are not
@@ -199,7 +225,7 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  * gdn_decode_step -- one new token for each of n_seqs independent sequences.
  *
  * Fuses, per sequence: the conv step over the new token (reading the W-1
- * stored inputs, then shifting the new input into the conv state), SiLU, the
+ * stored inputs, then storing the new input in the conv state), SiLU, the
  * split into [q | k | v], the optional L2 norm, and one step of the gated
  * delta rule on that sequence's state, which is read once and written once
  * ("Inside Qwen3.5", section 8: decode is a read-modify-write of the
@@ -221,7 +247,19 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  *   conv_weight  [C, W], or NULL: then x already holds q|k|v (no conv, no
  *                activation, conv_state unused).
  *   conv_bias    [C] or NULL.
- *   conv_state   [n_seqs, C, W-1] in/out (oldest first); required with a conv.
+ *   conv_state   [n_seqs, C, W-1] in/out; required with a conv.  Without a
+ *                ring head it is chronological (slot 0 the oldest) and the
+ *                step shifts the new input in; with one, see conv_head.
+ *   conv_head    [n_seqs] int32 ring heads, or NULL (chronological).  The
+ *                j-th oldest input sits in slot (h + j) mod (W-1); the step
+ *                reads the W-1 slots in that order, overwrites only slot h
+ *                (the oldest) with the new input and sets the head to
+ *                (h + 1) mod (W-1): one slot written per step instead of W-1
+ *                ("Mamba hybrid model selection", per-request memory
+ *                section: a fixed (channels, width - 1) conv buffer per
+ *                request).  Indexed like conv_state (by state_idx when given).
+ *                On entry 0 <= h < W-1 (taken mod W-1).  As in gdn_conv1d,
+ *                the bits above the lowest 8 count readers during the call.
  *   g, beta      [n_seqs, h_v] fp32.
  *   state        [n_seqs, h_v, d_v, d_k] in/out, in state_dtype.
  *   o            [n_seqs, h_v, d_v] in io_dtype.
@@ -229,6 +267,8 @@ gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
  *                are slot state_idx[n] of [slots, ...] pools (NULL: slot n);
  *                x, g, beta and o stay indexed by n.  Slots must be distinct
  *                and inside both pools; they are not read on the host.
+ * Structs from callers built against ABI 3 (struct_size without conv_head)
+ * are accepted and read as conv_head = NULL.
  * ---------------------------------------------------------------------- */
 typedef struct gdn_decode_args {
   uint32_t struct_size;
@@ -252,6 +292,7 @@ typedef struct gdn_decode_args {
   void* state;
   void* o;
   const int32_t* state_idx;
+  int32_t* conv_head;
 } gdn_decode_args;
 
 gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
@@ -389,6 +430,22 @@ gdn_status gdn_conv1d_backward(const gdn_conv1d_backward_args* args, void* strea
 const char* gdn_status_string(gdn_status status);
 const char* gdn_last_error(void); /* thread-local detail of the last failure */
 int gdn_abi_version(void);
+
+/* Measurement aids: ceilings measured on the machine at hand, against which
+ * a kernel's roofline fraction is also quoted.
+ *   gdn_probe_mfma   launches `blocks` workgroups of four waves, each wave
+ *                    issuing iters x 8 independent bf16 MFMAs (16x16x32);
+ *                    writes one value per thread to out [blocks * 256] fp32
+ *                    (device).  gdn_probe_mfma_flops gives the FLOPs of one
+ *                    launch.
+ *   gdn_probe_copy   copies `bytes` (a multiple of 16; 16-byte aligned,
+ *                    non-overlapping device buffers) with streaming 16-byte
+ *                    loads and stores.
+ * Both return GDN_ERR_INVALID_ARG on bad arguments, GDN_ERR_HIP when the
+ * launch fails. */
+int64_t gdn_probe_mfma_flops(int32_t iters, int32_t blocks);
+gdn_status gdn_probe_mfma(int32_t iters, int32_t blocks, float* out, void* stream);
+gdn_status gdn_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

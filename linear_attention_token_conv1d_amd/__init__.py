@@ -22,7 +22,8 @@ import os
 import torch
 
 __all__ = ["conv1d", "prefill", "decode_step", "gdn_layer", "prefill_workspace_size", "lib",
-           "prefill_backward", "conv1d_backward", "gdn_layer_backward", "GdnError", "LIB_PATH"]
+           "prefill_backward", "conv1d_backward", "gdn_layer_backward", "GdnError", "LIB_PATH",
+           "probe_mfma", "probe_copy"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
@@ -30,7 +31,7 @@ F32, BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 FLAG_L2NORM_QK = 1
 FLAG_NO_ERASE = 2
-ABI_VERSION = 3  # the gdn.h this binding matches
+ABI_VERSION = 4  # the gdn.h this binding matches
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _c_void_p = ctypes.c_void_p
 
@@ -45,7 +46,7 @@ class ConvArgs(ctypes.Structure):
                 ("total_tokens", ctypes.c_int64), ("width", ctypes.c_int32),
                 ("activation", ctypes.c_int32), ("x", _c_void_p), ("weight", _c_void_p),
                 ("bias", _c_void_p), ("y", _c_void_p), ("conv_state", _c_void_p),
-                ("cu_seqlens", _c_void_p)]
+                ("cu_seqlens", _c_void_p), ("conv_head", _c_void_p)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -59,7 +60,7 @@ class PrefillArgs(ctypes.Structure):
                 ("beta", _c_void_p), ("initial_state", _c_void_p), ("final_state", _c_void_p),
                 ("o", _c_void_p), ("cu_seqlens", _c_void_p), ("workspace", _c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("emit_every", ctypes.c_int32),
-                ("chunk_states", _c_void_p), ("state_idx", _c_void_p)]
+                ("chunk_states", _c_void_p), ("state_idx", _c_void_p), ("state_dtype", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -70,7 +71,7 @@ class DecodeArgs(ctypes.Structure):
                 ("activation", ctypes.c_int32), ("scale", ctypes.c_float), ("x", _c_void_p),
                 ("conv_weight", _c_void_p), ("conv_bias", _c_void_p), ("conv_state", _c_void_p),
                 ("g", _c_void_p), ("beta", _c_void_p), ("state", _c_void_p), ("o", _c_void_p),
-                ("state_idx", _c_void_p)]
+                ("state_idx", _c_void_p), ("conv_head", _c_void_p)]
 
 
 _lib = None
@@ -126,6 +127,12 @@ def lib():
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.gdn_probe_mfma_flops.restype = ctypes.c_int64
+        L.gdn_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, _c_void_p, _c_void_p]
+        L.gdn_probe_mfma.restype = ctypes.c_int
+        L.gdn_probe_copy.argtypes = [_c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+        L.gdn_probe_copy.restype = ctypes.c_int
         if L.gdn_abi_version() != ABI_VERSION:
             raise GdnError("libgdn.so ABI version mismatch")
         _lib = L
@@ -168,11 +175,14 @@ def _cu(cu_seqlens, n_tokens):
     return cu_seqlens, cu_seqlens.numel() - 1
 
 
-def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="silu", out=None):
+def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="silu", out=None,
+           conv_head=None):
     """Causal depthwise conv over packed sequences: x [T, C] -> y [T, C].
 
     weight [C, W]; conv_state [N, C, W-1] is read and then updated in place
-    (None: zero history, nothing written)."""
+    (None: zero history, nothing written).  conv_head [N] int32: the state's
+    ring heads (slot of the oldest input); on return the state is
+    chronological and the heads are 0."""
     _contig(x, "x")
     T, C = x.shape
     _contig(weight, "weight", x.dtype)
@@ -180,17 +190,20 @@ def conv1d(x, weight, bias=None, conv_state=None, cu_seqlens=None, activation="s
         _contig(bias, "bias", x.dtype)
     if conv_state is not None:
         _contig(conv_state, "conv_state", x.dtype)
+    if conv_head is not None:
+        _contig(conv_head, "conv_head", torch.int32)
     cu, N = _cu(cu_seqlens, T)
     y = torch.empty_like(x) if out is None else _contig(out, "out", x.dtype)
     a = ConvArgs(ctypes.sizeof(ConvArgs), _DT[x.dtype], N, C, T, weight.shape[1],
                  ACT_SILU if activation == "silu" else ACT_NONE, _ptr(x), _ptr(weight), _ptr(bias),
-                 _ptr(y), _ptr(conv_state), _ptr(cu))
+                 _ptr(y), _ptr(conv_state), _ptr(cu), _ptr(conv_head))
     _check(lib().gdn_conv1d(ctypes.byref(a), _stream(x.device)), "gdn_conv1d")
     return y
 
 
 def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
-                  workspace=None, erase=True, emit_every=0, chunk_states=None, state_idx=None):
+                  workspace=None, erase=True, emit_every=0, chunk_states=None, state_idx=None,
+                  state_dtype=torch.float32):
     T, h_qk, d_k = q.shape
     h_v, d_v = v.shape[1], v.shape[2]
     flags = (FLAG_L2NORM_QK if l2norm else 0) | (0 if erase else FLAG_NO_ERASE)
@@ -199,7 +212,7 @@ def _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk,
                     k.stride(0), v.stride(0), _ptr(g), _ptr(beta), _ptr(initial_state),
                     _ptr(final_state), _ptr(o), _ptr(cu), _ptr(workspace),
                     0 if workspace is None else workspace.numel(), emit_every, _ptr(chunk_states),
-                    _ptr(state_idx))
+                    _ptr(state_idx), _DT[state_dtype])
     return a
 
 
@@ -229,16 +242,18 @@ def _head_view(t, name, heads_dim_ok=True):
 
 def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, scale=1.0,
             l2norm=True, output_final_state=True, o=None, final_state=None, workspace=None,
-            erase=True, emit_every=0, chunk_states=None, state_idx=None):
+            erase=True, emit_every=0, chunk_states=None, state_idx=None, state_dtype=None):
     """Chunked gated delta rule.  q, k [T, H_qk, d], v [T, H_v, d] (bf16 or fp32,
-    token stride free), g, beta [T, H_v] fp32, initial_state [N, H_v, d, d] fp32.
+    token stride free), g, beta [T, H_v] fp32, initial_state [N, H_v, d, d].
     erase=False runs the erase-off variant S_t = a_t S_{t-1} + b_t v_t k_t^T.
     emit_every=K > 0 also returns the chunk-boundary states [rows, H_v, d, d]
     (see chunk_state_rows) as a third result.  state_idx [N] int32 maps each
     sequence to a slot of the initial_state / final_state pools (both then
-    given by the caller).
+    given by the caller).  state_dtype (torch.float32 or torch.bfloat16; by
+    default that of the state tensors passed, else fp32) is the dtype of the
+    initial, final and chunk-boundary states in memory.
 
-    Returns (o [T, H_v, d], final_state [N, H_v, d, d] fp32 or None)."""
+    Returns (o [T, H_v, d], final_state [N, H_v, d, d] or None)."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _head_view(t, nm)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -248,8 +263,14 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, sca
     _contig(beta, "beta", torch.float32)
     cu, N = _cu(cu_seqlens, T)
     h_v, d_v = v.shape[1], v.shape[2]
-    if initial_state is not None:
-        _contig(initial_state, "initial_state", torch.float32)
+    if state_dtype is None:
+        given = [t for t in (initial_state, final_state, chunk_states) if t is not None]
+        state_dtype = given[0].dtype if given else torch.float32
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise GdnError("state_dtype must be torch.float32 or torch.bfloat16")
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state"), (chunk_states, "chunk_states")):
+        if t is not None:
+            _contig(t, nm, state_dtype)
     if o is None:
         o = torch.empty((T, h_v, d_v), dtype=q.dtype, device=q.device)
     if state_idx is not None:
@@ -257,17 +278,17 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, sca
         if output_final_state and final_state is None:
             raise GdnError("with state_idx, pass the final_state pool")
     if output_final_state and final_state is None:
-        final_state = torch.empty((N, h_v, d_v, q.shape[2]), dtype=torch.float32, device=q.device)
+        final_state = torch.empty((N, h_v, d_v, q.shape[2]), dtype=state_dtype, device=q.device)
     if emit_every > 0 and chunk_states is None:
         lengths = [T] if cu is None else (cu[1:] - cu[:-1]).tolist()
         rows = chunk_state_rows(lengths, chunk, emit_every)
-        chunk_states = torch.empty((max(rows, 1), h_v, d_v, q.shape[2]), dtype=torch.float32, device=q.device)
+        chunk_states = torch.empty((max(rows, 1), h_v, d_v, q.shape[2]), dtype=state_dtype, device=q.device)
     need = prefill_workspace_size(q, v, N, chunk, emit_every)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a = _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm,
                       workspace if need else None, erase, emit_every, chunk_states if emit_every > 0 else None,
-                      state_idx)
+                      state_idx, state_dtype)
     _check(lib().gdn_prefill(ctypes.byref(a), _stream(q.device)), "gdn_prefill")
     if emit_every > 0:
         return o, final_state, chunk_states
@@ -296,12 +317,14 @@ def gdn_layer(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, conv_bias=None, conv
 
 
 def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=None, conv_bias=None,
-                activation="silu", l2norm=True, scale=1.0, o=None, erase=True, state_idx=None):
+                activation="silu", l2norm=True, scale=1.0, o=None, erase=True, state_idx=None,
+                conv_head=None):
     """One token for each of N sequences.  x [N, C] (pre-conv, or q|k|v when
     conv_weight is None); state [N, H_v, d, d] (bf16 or fp32) and conv_state
     [N, C, W-1] are updated in place.  Returns o [N, H_v, d].  erase=False runs
     the erase-off variant; state_idx [N] int32 picks each sequence's slot of
-    the state and conv_state pools."""
+    the state and conv_state pools; conv_head (int32, one per conv-state slot)
+    makes the conv state a ring: one slot is written and the head advances."""
     _contig(x, "x")
     N = x.shape[0]
     _contig(g, "g", torch.float32)
@@ -314,6 +337,8 @@ def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=No
         _contig(conv_bias, "conv_bias", x.dtype)
     if state_idx is not None:
         _contig(state_idx, "state_idx", torch.int32)
+    if conv_head is not None:
+        _contig(conv_head, "conv_head", torch.int32)
     if o is None:
         o = torch.empty((N, h_v, d), dtype=x.dtype, device=x.device)
     W = conv_weight.shape[1] if conv_weight is not None else 4
@@ -322,7 +347,7 @@ def decode_step(x, g, beta, state, h_qk, h_v, d, conv_weight=None, conv_state=No
                    _DT[state.dtype], N, h_qk, h_v, d, d, W,
                    ACT_SILU if activation == "silu" else ACT_NONE, scale, _ptr(x), _ptr(conv_weight),
                    _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
-                   _ptr(state_idx))
+                   _ptr(state_idx), _ptr(conv_head))
     _check(lib().gdn_decode_step(ctypes.byref(a), _stream(x.device)), "gdn_decode_step")
     return o
 
@@ -440,3 +465,40 @@ def gdn_layer_backward(x, conv_weight, g, beta, h_qk, d_k, h_v, d_v, d_o, conv_b
     dx, dw, db, dcs = conv1d_backward(x, conv_weight, dy, conv_bias, conv_state, cu_seqlens, "silu",
                                       d_new_conv_state)
     return dx, dw, db, dg, dbeta, ds0, dcs
+
+
+def probe_mfma(iters=2048, blocks=2048, device=None):
+    """Measured dense bf16 MFMA rate: one launch of the library's MFMA probe
+    (blocks x 4 waves, each iters x 8 independent 16x16x32 MFMAs), timed with
+    HIP events on the current stream.  Returns TFLOP/s."""
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    L = lib()
+    st = _stream(dev)
+    _check(L.gdn_probe_mfma(iters, blocks, _ptr(out), st), "gdn_probe_mfma")  # warm-up
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    _check(L.gdn_probe_mfma(iters, blocks, _ptr(out), st), "gdn_probe_mfma")
+    b.record()
+    torch.cuda.synchronize(dev)
+    return L.gdn_probe_mfma_flops(iters, blocks) / (a.elapsed_time(b) * 1e-3) / 1e12
+
+
+def probe_copy(nbytes=1 << 30, reps=5, device=None):
+    """Measured streaming copy rate (read + write bytes / s) of a device copy
+    of nbytes through the library's copy probe, best of reps.  Returns GB/s."""
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    L = lib()
+    st = _stream(dev)
+    best = 0.0
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        _check(L.gdn_probe_copy(_ptr(src), _ptr(dst), nbytes, st), "gdn_probe_copy")
+        b.record()
+        torch.cuda.synchronize(dev)
+        best = max(best, 2 * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best

@@ -12,6 +12,14 @@
 // State kernel (launched after, on the same stream, so the main kernel has
 // read every old state first): for each sequence, the new conv state is the
 // last W-1 inputs of (old state ++ sequence), oldest first.
+//
+// Ring heads: with conv_head, input j (oldest first) of a stored state sits
+// in slot (head + j) mod (W-1).  Both kernels read in that order; the state
+// kernel writes chronologically and sets the head to 0.  Every state-kernel
+// workgroup of a sequence reads its head, so the reset must wait until all
+// of them have: each adds 1 << 8 to the head word when it reads it (the low
+// 8 bits, the head, are unchanged), and the workgroup that finds the count
+// of the others already there is the last reader and stores 0.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -49,16 +57,26 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int n_seqs, int64_t t
   return lo;
 }
 
+// ring head of sequence s (0 without heads), reduced to a slot index
+template <int W>
+__device__ __forceinline__ int ring_head(const ConvParams& p, int s) {
+  return p.conv_head ? (int)((uint32_t)(p.conv_head[s] & 0xff) % (W - 1)) : 0;
+}
+
 template <typename T, int W>
 __device__ __forceinline__ void load_history(const ConvParams& p, int s, int64_t c0,
                                              float (&win)[W - 1][8]) {
   // positions before a sequence start: the conv state, oldest first, or zeros
   if (p.conv_state) {
     const T* st = reinterpret_cast<const T*>(p.conv_state) + ((int64_t)s * p.channels + c0) * (W - 1);
+    const int h = ring_head<W>(p, s);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int j = 0; j < W - 1; ++j) win[j][e] = to_f32(st[e * (W - 1) + j]);
+      for (int j = 0; j < W - 1; ++j) {
+        const int slot = j + h < W - 1 ? j + h : j + h - (W - 1);
+        win[j][e] = to_f32(st[e * (W - 1) + slot]);
+      }
   } else {
 #pragma unroll
     for (int j = 0; j < W - 1; ++j)
@@ -192,43 +210,63 @@ __global__ __launch_bounds__(kThreads) void conv1d_kernel(ConvParams p) {
   }
 }
 
+// Ring heads of a chronological rewrite: every workgroup of sequence s reads
+// its head once; after all of its threads have, thread 0 counts the
+// workgroup in, and the last of the sequence's workgroups stores head 0.
+__device__ __forceinline__ void release_head(const ConvParams& p, int s) {
+  if (!p.conv_head) return;
+  __syncthreads();  // every thread of this workgroup has used the head
+  if (threadIdx.x == 0) {
+    const int readers = (int)gridDim.x;
+    const int32_t before = atomicAdd(p.conv_head + s, 1 << 8);
+    if ((before >> 8) == readers - 1) atomicExch(p.conv_head + s, 0);
+  }
+}
+
 template <typename T, int W>
 __global__ __launch_bounds__(kThreads) void conv_state_kernel(ConvParams p) {
   const int64_t c0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
-  if (c0 >= p.channels) return;
   const int s = blockIdx.y;
-  const int64_t C = p.channels;
-  const int64_t start = p.cu_seqlens ? p.cu_seqlens[s] : 0;
-  const int64_t end = p.cu_seqlens ? p.cu_seqlens[s + 1] : p.total_tokens;
-  const T* x = reinterpret_cast<const T*>(p.x);
-  T* st = reinterpret_cast<T*>(p.conv_state) + ((int64_t)s * C + c0) * (W - 1);
-  float old[W - 1][8];
+  if (c0 < p.channels) {
+    const int64_t C = p.channels;
+    const int64_t start = p.cu_seqlens ? p.cu_seqlens[s] : 0;
+    const int64_t end = p.cu_seqlens ? p.cu_seqlens[s + 1] : p.total_tokens;
+    const T* x = reinterpret_cast<const T*>(p.x);
+    T* st = reinterpret_cast<T*>(p.conv_state) + ((int64_t)s * C + c0) * (W - 1);
+    // old state, oldest first (ring order with a head)
+    const int h = ring_head<W>(p, s);
+    float old[W - 1][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) old[j][e] = to_f32(st[e * (W - 1) + j]);
-  float nw[W - 1][8];
+      for (int j = 0; j < W - 1; ++j) {
+        const int slot = j + h < W - 1 ? j + h : j + h - (W - 1);
+        old[j][e] = to_f32(st[e * (W - 1) + slot]);
+      }
+    float nw[W - 1][8];
 #pragma unroll
-  for (int j = 0; j < W - 1; ++j) {
-    const int64_t pos = end - (W - 1) + j;  // position of new slot j
-    if (pos >= start) {
-      float v[8];
-      unpack8(ld8raw(x + pos * C + c0), v);
+    for (int j = 0; j < W - 1; ++j) {
+      const int64_t pos = end - (W - 1) + j;  // position of new slot j
+      if (pos >= start) {
+        float v[8];
+        unpack8(ld8raw(x + pos * C + c0), v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) nw[j][e] = v[e];
-    } else {
-      const int64_t slot = (W - 1) - (start - pos);  // still inside the old state
+        for (int e = 0; e < 8; ++e) nw[j][e] = v[e];
+      } else {
+        const int64_t back = (W - 1) - (start - pos);  // still inside the old state
 #pragma unroll
-      for (int i = 0; i < W - 1; ++i)
-        if (i == slot)
+        for (int i = 0; i < W - 1; ++i)
+          if (i == back)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) nw[j][e] = old[i][e];
+            for (int e = 0; e < 8; ++e) nw[j][e] = old[i][e];
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) st[e * (W - 1) + j] = from_f32<T>(nw[j][e]);
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int j = 0; j < W - 1; ++j) st[e * (W - 1) + j] = from_f32<T>(nw[j][e]);
+  release_head(p, s);
 }
 
 template <typename T, int W>

@@ -2,9 +2,14 @@
 //
 // One workgroup owns (sequence n, QK head hq) and therefore the grp = h_v/h_qk
 // V heads that read that QK head.  It
-//   1. runs the conv step (+ SiLU) for its q, k and v channels, shifting the
-//      new input into the conv state (each channel is read and written by the
-//      thread that owns it, so the in-place update is race-free);
+//   1. runs the conv step (+ SiLU) for its q, k and v channels, storing the
+//      new input in the conv state (each channel is read and written by the
+//      thread that owns it, so the in-place update is race-free): without
+//      ring heads the W-1 slots shift; with them only slot `head` (the
+//      oldest input) is overwritten, and the last of the sequence's h_qk
+//      workgroups to read the head advances it (each adds 1 << 8 to the head
+//      word after reading it, keeping the low 8 bits, so the one that finds
+//      the other h_qk - 1 counts there knows every reader is done);
 //   2. L2-normalises q and k (one wave, fp32);
 //   3. streams the grp*d_v state rows once: each row S_i (d_k values) is
 //      loaded by 16 lanes, reduced against k and q with DPP row sums, then
@@ -90,6 +95,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const IoT* wt = reinterpret_cast<const IoT*>(p.conv_weight);
   const IoT* bias = reinterpret_cast<const IoT*>(p.conv_bias);
   IoT* cst = reinterpret_cast<IoT*>(p.conv_state);
+  // ring head of this sequence's conv state (0 and a shift without heads)
+  const bool ring = p.conv_head != nullptr;
+  const int head = ring ? (int)((uint32_t)(p.conv_head[slot] & 0xff) % (uint32_t)(W - 1)) : 0;
   auto conv_batch = [&](int base) {
     int64_t cc[kConvBatch];
     IoT xr[kConvBatch], wv[kConvBatch][4], hv[kConvBatch][3], bv[kConvBatch];
@@ -109,8 +117,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const int wm = wt ? W - 1 : 0, hm = wt ? W - 2 : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[j][i] = wp[min(i, wm)];
+      // history i (oldest first) sits in slot (head + i) mod (W - 1)
 #pragma unroll
-      for (int i = 0; i < 3; ++i) hv[j][i] = st[min(i, hm)];
+      for (int i = 0; i < 3; ++i) {
+        const int hi = min(i, hm) + head;
+        hv[j][i] = st[hi < W - 1 ? hi : hi - (W - 1)];
+      }
       bv[j] = bias ? bias[c] : x[c];
     }
 #pragma unroll
@@ -126,11 +138,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           const float xi = i < W - 1 ? to_f32(hv[j][min(i, 2)]) : (i == W - 1 ? y : 0.f);
           acc += to_f32(wv[j][i]) * xi;
         }
-        // shift the new input in: the history keeps the last W-1 inputs
+        // the history keeps the last W-1 inputs: the new one replaces the
+        // oldest (ring), or everything shifts by one slot
         IoT* st = cst + (slot * C + cc[j]) * (W - 1);
+        if (ring) {
+          st[head] = xr[j];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-          if (i < W - 1) st[i] = i + 1 < W - 1 ? hv[j][min(i + 1, 2)] : xr[j];
+          for (int i = 0; i < 3; ++i)
+            if (i < W - 1) st[i] = i + 1 < W - 1 ? hv[j][min(i + 1, 2)] : xr[j];
+        }
         y = p.act ? silu(acc) : acc;
       }
       s_q[cl] = y;
@@ -146,6 +163,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     s_be[tid] = b_in;
   }
   __syncthreads();
+  // every thread of this workgroup has read the ring head: count the
+  // workgroup in; the sequence's last reader advances the head
+  if (ring && tid == 0) {
+    const int32_t before = atomicAdd(p.conv_head + slot, 1 << 8);
+    if ((before >> 8) == p.h_qk - 1) atomicExch(p.conv_head + slot, (int32_t)((head + 1) % (W - 1)));
+  }
 
   // ---- 2. L2 norms of q and k, and k.q after normalisation
   if (wave == 0) {

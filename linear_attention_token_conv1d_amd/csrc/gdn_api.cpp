@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -50,11 +51,31 @@ gdn_status finish(hipError_t e, hipStream_t stream, const char* what) {
 bool is_dtype(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
 size_t esize(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Fields added after ABI 3 read as their defaults from a shorter struct.
+int32_t prefill_state_dtype(const gdn_prefill_args* a) {
+  return a->struct_size >= sizeof(gdn_prefill_args) ? a->state_dtype : (int32_t)GDN_F32;
+}
+int32_t* conv_head_of(const gdn_conv1d_args* a) {
+  return a->struct_size >= sizeof(gdn_conv1d_args) ? a->conv_head : nullptr;
+}
+int32_t* conv_head_of(const gdn_decode_args* a) {
+  return a->struct_size >= sizeof(gdn_decode_args) ? a->conv_head : nullptr;
+}
+
 gdn_status check_prefill(const gdn_prefill_args* a) {
   if (!a) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: args is NULL");
-  if (a->struct_size < sizeof(gdn_prefill_args))
+  if (a->struct_size < offsetof(gdn_prefill_args, state_dtype))
     return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: struct_size %u < %zu", a->struct_size,
-                sizeof(gdn_prefill_args));
+                offsetof(gdn_prefill_args, state_dtype));
+  if (!is_dtype(prefill_state_dtype(a)))
+    return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: bad state_dtype %d", prefill_state_dtype(a));
   if (!is_dtype(a->io_dtype)) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: bad io_dtype %d", a->io_dtype);
   if (a->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_NO_ERASE))
     return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: unknown flags 0x%x", a->flags);
@@ -83,6 +104,12 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
   const void* ptrs16[] = {a->q, a->k, a->v, a->o, a->initial_state, a->final_state};
   for (const void* p : ptrs16)
     if (!aligned(p, 16)) return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: tensors must be 16-byte aligned");
+  if (a->initial_state && a->final_state && a->initial_state != a->final_state) {
+    // the two pools may be the same buffer, but must not partly overlap
+    const size_t ns = (size_t)a->n_seqs * a->h_v * a->d_v * a->d_k * esize(prefill_state_dtype(a));
+    if (!a->state_idx && overlaps(a->initial_state, ns, a->final_state, ns))
+      return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: final_state partly overlaps initial_state");
+  }
   if (!aligned(a->g, 4) || !aligned(a->beta, 4) || !aligned(a->cu_seqlens, 4))
     return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: g, beta, cu_seqlens must be 4-byte aligned");
   if (a->emit_every < 0) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: emit_every %d < 0", a->emit_every);
@@ -97,13 +124,6 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
   if (need && !aligned(a->workspace, 256))
     return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: workspace must be 256-byte aligned");
   return GDN_OK;
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const char* x = static_cast<const char*>(a);
-  const char* y = static_cast<const char*>(b);
-  return x < y + nb && y < x + na;
 }
 
 gdn_status check_prefill_backward(const gdn_prefill_backward_args* a) {
@@ -234,9 +254,9 @@ int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 gdn_status gdn_conv1d(const gdn_conv1d_args* a, void* stream) {
   try {
     if (!a) return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: args is NULL");
-    if (a->struct_size < sizeof(gdn_conv1d_args))
+    if (a->struct_size < offsetof(gdn_conv1d_args, conv_head))
       return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: struct_size %u < %zu", a->struct_size,
-                  sizeof(gdn_conv1d_args));
+                  offsetof(gdn_conv1d_args, conv_head));
     if (!is_dtype(a->dtype)) return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: bad dtype %d", a->dtype);
     if (a->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: n_seqs %d < 1", a->n_seqs);
     if (a->total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: total_tokens < 0");
@@ -254,15 +274,17 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* a, void* stream) {
     if (!aligned(a->x, 16) || !aligned(a->y, 16))
       return fail(GDN_ERR_ALIGNMENT, "gdn_conv1d: x and y must be 16-byte aligned");
     if (!aligned(a->weight, esize(a->dtype)) || !aligned(a->bias, esize(a->dtype)) ||
-        !aligned(a->conv_state, esize(a->dtype)) || !aligned(a->cu_seqlens, 4))
-      return fail(GDN_ERR_ALIGNMENT, "gdn_conv1d: misaligned weight, bias, conv_state or cu_seqlens");
+        !aligned(a->conv_state, esize(a->dtype)) || !aligned(a->cu_seqlens, 4) ||
+        !aligned(conv_head_of(a), 4))
+      return fail(GDN_ERR_ALIGNMENT, "gdn_conv1d: misaligned weight, bias, conv_state, cu_seqlens or conv_head");
     const size_t bytes = (size_t)a->total_tokens * a->channels * esize(a->dtype);
     const char* xb = static_cast<const char*>(a->x);
     const char* yb = static_cast<const char*>(a->y);
     if (bytes && xb < yb + bytes && yb < xb + bytes)
       return fail(GDN_ERR_INVALID_ARG, "gdn_conv1d: y must not overlap x");
     gdn::ConvParams p{a->x, a->weight, a->bias, a->y, a->conv_state, a->cu_seqlens,
-                      a->total_tokens, a->n_seqs, a->channels, a->width, a->activation};
+                      a->total_tokens, a->n_seqs, a->channels, a->width, a->activation,
+                      a->conv_state ? conv_head_of(a) : nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_conv1d(p, a->dtype, s), s, "gdn_conv1d");
   } catch (...) {
@@ -271,7 +293,7 @@ gdn_status gdn_conv1d(const gdn_conv1d_args* a, void* stream) {
 }
 
 size_t gdn_prefill_workspace_size(const gdn_prefill_args* a) {
-  if (!a || a->struct_size < sizeof(gdn_prefill_args)) return 0;
+  if (!a || a->struct_size < offsetof(gdn_prefill_args, state_dtype)) return 0;
   return gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v, a->d_k, a->chunk,
                                       a->emit_every > 0 ? a->emit_every : 0);
 }
@@ -285,7 +307,7 @@ gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
                          a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
                          (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale, a->workspace,
                          a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->emit_every,
-                         a->chunk_states, a->state_idx};
+                         a->chunk_states, a->state_idx, prefill_state_dtype(a) == GDN_BF16 ? 1 : 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_prefill(p, a->io_dtype, a->d_k, s), s, "gdn_prefill");
   } catch (...) {
@@ -296,9 +318,9 @@ gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
 gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
   try {
     if (!a) return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: args is NULL");
-    if (a->struct_size < sizeof(gdn_decode_args))
+    if (a->struct_size < offsetof(gdn_decode_args, conv_head))
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: struct_size %u < %zu", a->struct_size,
-                  sizeof(gdn_decode_args));
+                  offsetof(gdn_decode_args, conv_head));
     if (!is_dtype(a->io_dtype) || !is_dtype(a->state_dtype))
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: bad io_dtype/state_dtype");
     if (a->flags & ~(GDN_FLAG_L2NORM_QK | GDN_FLAG_NO_ERASE))
@@ -321,8 +343,8 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
       return fail(GDN_ERR_INVALID_ARG, "gdn_decode_step: conv_state is required with a conv");
     if (!aligned(a->state, 16))
       return fail(GDN_ERR_ALIGNMENT, "gdn_decode_step: state must be 16-byte aligned");
-    if (!aligned(a->state_idx, 4))
-      return fail(GDN_ERR_ALIGNMENT, "gdn_decode_step: state_idx must be 4-byte aligned");
+    if (!aligned(a->state_idx, 4) || !aligned(conv_head_of(a), 4))
+      return fail(GDN_ERR_ALIGNMENT, "gdn_decode_step: state_idx and conv_head must be 4-byte aligned");
     const size_t es = esize(a->io_dtype);
     if (!aligned(a->x, es) || !aligned(a->o, es) || !aligned(a->conv_weight, es) ||
         !aligned(a->conv_bias, es) || !aligned(a->conv_state, es) || !aligned(a->g, 4) ||
@@ -332,7 +354,8 @@ gdn_status gdn_decode_step(const gdn_decode_args* a, void* stream) {
     gdn::DecodeParams p{a->x, a->conv_weight, a->conv_bias, a->conv_state, a->g, a->beta,
                         a->state, a->o, a->n_seqs, a->h_qk, a->h_v, a->conv_weight ? a->width : 4,
                         a->activation, (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale,
-                        (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->state_idx};
+                        (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->state_idx,
+                        a->conv_weight ? conv_head_of(a) : nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(gdn::launch_decode(p, a->io_dtype, a->state_dtype, a->d_k, s), s, "gdn_decode_step");
   } catch (...) {

@@ -20,6 +20,7 @@ struct ConvParams {
   int32_t channels;
   int32_t width;
   int32_t act;
+  int32_t* conv_head;  // [n_seqs] ring heads of conv_state, or null (chronological)
 };
 hipError_t launch_conv1d(const ConvParams& p, int dtype, hipStream_t stream);
 
@@ -41,6 +42,7 @@ struct DecodeParams {
   float scale;
   int32_t erase;  // 0: erase-off variant, S_t = a_t S_{t-1} + b_t v_t k_t^T
   const int32_t* state_idx;  // [n_seqs] state and conv-state slots, or null (slot n)
+  int32_t* conv_head;        // ring heads of the conv-state pool, or null (chronological)
 };
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, int state_dtype, int d,
                          hipStream_t stream);
@@ -54,8 +56,8 @@ struct PrefillParams {
   int64_t v_stride;
   const float* g;
   const float* beta;
-  const float* initial_state;
-  float* final_state;
+  const void* initial_state;  // fp32 or bf16 (state_bf16)
+  void* final_state;
   void* o;
   const int32_t* cu_seqlens;
   int64_t total_tokens;
@@ -69,8 +71,9 @@ struct PrefillParams {
   size_t workspace_bytes;
   int32_t erase;  // 0: erase-off variant (A = 0, U = diag(beta) V)
   int32_t emit_every;        // > 0: the state after every emit_every-th whole chunk
-  float* chunk_states;       // [rows, h_v, d_v, d_k] (rows from the plan)
+  void* chunk_states;        // [rows, h_v, d_v, d_k] (rows from the plan)
   const int32_t* state_idx;  // [n_seqs] state slots, or null (slot n)
+  int32_t state_bf16;        // initial/final/chunk states stored as bf16 (else fp32)
 };
 // Workspace of gdn_prefill: chunk offsets plus, per (chunk, V head), the
 // chunk operands Tb, P and four per-token scalar rows.

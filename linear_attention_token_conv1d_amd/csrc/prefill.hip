@@ -39,6 +39,7 @@
 //  join  only after a split scan of one long sequence (see split_plan):
 //        adds S_m w_t to the second segment's outputs and forms the final
 //        state.
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -152,6 +153,24 @@ template <> struct Raw8<float> {
 };
 
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
+
+// Four consecutive elements of a caller's state tensor (fp32, or bf16 when
+// the call stores its states as bf16), at element offset i (a multiple of 4).
+__device__ __forceinline__ f32x4 load_state4(const void* base, size_t i, bool bf16) {
+  if (bf16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const __bf16*>(base) + i);
+    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  }
+  const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
+  return f32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void store_state4(void* base, size_t i, const f32x4& v, bool bf16) {
+  if (bf16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(base) + i) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i) = make_float4(v[0], v[1], v[2], v[3]);
+}
 
 // Accumulator tile 2s+1 of a chunk, or zeros when the chunk has an odd
 // number of 16-token tiles (the second half of the last k-step is empty).
@@ -954,10 +973,13 @@ struct ScanLayout {
   static constexpr int PADO = 16 / E;
   static constexpr int LDO = cols + PADO;  // O staging rows [token][cols]
   static constexpr int obuf = C * LDO * E;
-  // O leaves through the staging tiles when they fit in LDS (every bf16
-  // shape); otherwise (large fp32 tiles) each lane stores its elements.
-  static constexpr bool stage_o = 2 * buf + 2 * obuf <= 160 * 1024;
-  static constexpr int bytes = 2 * buf + (stage_o ? 2 * obuf : 0);
+  // Two chunk buffers (the next chunk lands while this one is computed) when
+  // they fit in LDS; otherwise (fp32 at chunk 64) one, loaded between chunks.
+  static constexpr int nbuf = 2 * buf <= 160 * 1024 ? 2 : 1;
+  // O leaves through the staging tiles when they fit in LDS as well;
+  // otherwise each lane stores its elements.
+  static constexpr bool stage_o = nbuf * buf + 2 * obuf <= 160 * 1024;
+  static constexpr int bytes = nbuf * buf + (stage_o ? 2 * obuf : 0);
   static constexpr int NOV = (C * cols / 8 + threads - 1) / threads;  // O vectors per thread
 };
 
@@ -972,9 +994,11 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
   // compiler can then see that the next chunk's direct-to-LDS loads never
   // touch what the current chunk reads, and inserts no wait for them.
   __shared__ __align__(16) unsigned char sb0[L::buf];
-  __shared__ __align__(16) unsigned char sb1[L::buf];
+  __shared__ __align__(16) unsigned char sb1[L::nbuf == 2 ? L::buf : 16];
   __shared__ __align__(16) unsigned char so0[L::stage_o ? L::obuf : 16];
   __shared__ __align__(16) unsigned char so1[L::stage_o ? L::obuf : 16];
+  // with one chunk buffer, every chunk is computed from sb0
+  unsigned char* const sbn = L::nbuf == 2 ? sb1 : sb0;
 
   const PlanView pv = plan_view(p, ws, C);
   const ScanSlot slot = scan_slot(p, pv, NB);
@@ -1039,11 +1063,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       st[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (p.initial_state) {
-        const float4 v4 = *reinterpret_cast<const float4*>(p.initial_state + sbase + (size_t)lcol(ct) * D +
-                                                           pidx<DT>(dt, 4 * g4));
-        st[ct][dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
-      }
+      if (p.initial_state)
+        st[ct][dt] = load_state4(p.initial_state, sbase + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4), p.state_bf16);
     }
 
   // one chunk: store the previous chunk's O, start the next chunk's loads
@@ -1060,7 +1081,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
     if constexpr (L::stage_o) {
       if (c > 0) store_o(oprev, t0 - C, C);
     }
-    if (c + 1 < nch) issue(c + 1, nxt);
+    if (L::nbuf == 2 && c + 1 < nch) issue(c + 1, nxt);
     constexpr int KS = (NT + 1) / 2;  // k-steps over the chunk's tokens
     constexpr bool HALF = NT == 1;    // a 16-token chunk: half-empty k-step
 
@@ -1190,23 +1211,26 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
     }
     // the state after every emit_every-th whole chunk inside the sequence
     if (p.emit_every > 0 && (c + 1) % p.emit_every == 0 && t0 + C < seq_end) {
-      float* dst = p.chunk_states + ((size_t)(erow + (c + 1) / p.emit_every - 1) * p.h_v + h) * D * D +
-                   (size_t)(blk * L::cols) * D;
+      const size_t dst = ((size_t)(erow + (c + 1) / p.emit_every - 1) * p.h_v + h) * D * D +
+                         (size_t)(blk * L::cols) * D;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(dst + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4)) =
-              make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
+          store_state4(p.chunk_states, dst + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4), st[ct][dt], p.state_bf16);
     }
     __syncthreads();  // waits for the next chunk's loads; frees `cur`
+    if (L::nbuf == 1 && c + 1 < nch) {
+      issue(c + 1, nxt);  // nxt == cur: every read of this chunk is done
+      __syncthreads();
+    }
   };
 
   if (nch > 0) issue(0, sb0);
   __syncthreads();  // waits for the loads of chunk 0
   for (int c = 0; c < nch; c += 2) {
-    step(c, sb0, sb1, so0, so1);
-    if (c + 1 < nch) step(c + 1, sb1, sb0, so1, so0);
+    step(c, sb0, sbn, so0, so1);
+    if (c + 1 < nch) step(c + 1, sbn, sb0, so1, so0);
   }
   if (L::stage_o && nch > 0) {
     const int64_t tl = seq_start + (int64_t)(nch - 1) * C;
@@ -1218,8 +1242,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(PrefillParams p, const un
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(p.final_state + sbase + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4)) =
-            make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
+        store_state4(p.final_state, sbase + (size_t)lcol(ct) * D + pidx<DT>(dt, 4 * g4), st[ct][dt], p.state_bf16);
   }
 }
 
@@ -1481,16 +1504,13 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
     const int erow = p.emit_every > 0 ? plan.erow(n) : 0;
     // initial state: the caller's (or zero) for a whole sequence or a first
     // segment, zero for a second segment, the identity for the transition
-    const float* s_init = role == 0 ? p.initial_state : nullptr;
+    const void* s_init = role == 0 ? p.initial_state : nullptr;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         st[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (s_init) {
-          const float4 v4 = *reinterpret_cast<const float4*>(s_init + srow(ct) + pidx<DT>(dt, 4 * g4));
-          st[ct][dt] = f32x4{v4.x, v4.y, v4.z, v4.w};
-        }
+        if (s_init) st[ct][dt] = load_state4(s_init, srow(ct) + pidx<DT>(dt, 4 * g4), p.state_bf16);
         if (role == 2) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -1630,13 +1650,12 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
       // the state after every emit_every-th whole chunk inside the sequence
       // (a split scan never emits: its second segment does not hold S)
       if (p.emit_every > 0 && (cbeg + c + 1) % p.emit_every == 0 && chunk_t0(c) + C < seq_end) {
-        float* dst = p.chunk_states + (size_t)(erow + (cbeg + c + 1) / p.emit_every - 1) * p.h_v * D * D;
+        const size_t dst = (size_t)(erow + (cbeg + c + 1) / p.emit_every - 1) * p.h_v * D * D;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<float4*>(dst + wrow(ct) + pidx<DT>(dt, 4 * g4)) =
-                make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
+            store_state4(p.chunk_states, dst + wrow(ct) + pidx<DT>(dt, 4 * g4), st[ct][dt], p.state_bf16);
       }
       publish_state();
       __syncthreads();  // B2: next chunk loaded, new state published
@@ -1651,17 +1670,18 @@ __global__ __launch_bounds__(64 * (NWR * (1 + OS) + NM)) void scan2_kernel(Prefi
     }
     // final state: the caller's, or the split's S_m (always: the join needs
     // it), S0 and Phi (only when the caller wants a final state)
-    float* s_fin = !sp.on ? p.final_state
-                 : role == 0 ? sp.s_mid
-                 : !p.final_state ? nullptr
-                 : role == 1 ? sp.s_zero : sp.phi;
+    // (the split's states are internal fp32; the caller's in its state dtype)
+    void* s_fin = !sp.on ? p.final_state
+                : role == 0 ? (void*)sp.s_mid
+                : !p.final_state ? nullptr
+                : role == 1 ? (void*)sp.s_zero : (void*)sp.phi;
+    const bool fin_bf16 = !sp.on && p.state_bf16;
     if (s_fin) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(s_fin + (sp.on ? wrow(ct) : srow(ct)) + pidx<DT>(dt, 4 * g4)) =
-              make_float4(st[ct][dt][0], st[ct][dt][1], st[ct][dt][2], st[ct][dt][3]);
+          store_state4(s_fin, (sp.on ? wrow(ct) : srow(ct)) + pidx<DT>(dt, 4 * g4), st[ct][dt], fin_bf16);
     }
     if (sp.on && role == 0) {  // S_m once more, as the join's bf16 operand
 #pragma unroll
@@ -1864,8 +1884,11 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) acc = mfma_tn(y[kb], w[kb], acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p.final_state[fs + (size_t)(16 * jb + 4 * g4 + i) * D + 16 * nb + l16] = acc[i];
+      for (int i = 0; i < 4; ++i) {
+        const size_t e = fs + (size_t)(16 * jb + 4 * g4 + i) * D + 16 * nb + l16;
+        if (p.state_bf16) reinterpret_cast<__bf16*>(p.final_state)[e] = (__bf16)acc[i];
+        else reinterpret_cast<float*>(p.final_state)[e] = acc[i];
+      }
     }
     return;
   }
@@ -1943,6 +1966,879 @@ __global__ __launch_bounds__(256) void join_kernel(PrefillParams p, ScanSplit sp
   }
 }
 
+// ------------------------------------------------------------- fused scan
+// bf16 at chunk 32 or 64: one launch runs the whole chunked recurrence with
+// each chunk's preparation folded in, so the call reads q, k, v, g and beta
+// once and writes o and the states, and nothing in between leaves the CU.
+// One workgroup per (sequence, V head, block of 16 NC CT d_v columns).  Per
+// chunk c there are two barriers, B1 and B2; between them:
+//   phase 1  chain waves (NC, 16 CT columns each): X1 = K S^T, R, U = Tb R;
+//              U is published (bf16); S^T <- gamma_last S^T + K^T diag(e rk)
+//              U in registers;
+//            output waves (NC, 16 CT columns each): Y = Q S^T (raw q rows)
+//              with the squared row
+//              norms of q from the same fragments, then the diagonal 16x16
+//              tiles of chunk c+1's Q K^T with their decay masks (into P);
+//            prep wave 0: the diagonal tiles of chunk c+1's K K^T, the row
+//              norms of k from their diagonals, and the inverses of the
+//              diagonal blocks of I + A by forward substitution in registers
+//              (one lane per column, the other columns' entries broadcast
+//              across the lanes of a row);
+//            prep waves 1-3: the tiles of chunk c+1's K K^T and Q K^T below
+//              the diagonal blocks with their decay masks only (one mask
+//              serves both): the row and column scalings come later;
+//   phase 2  chain: the new S published;
+//            output: O = scale rq (gamma Y + P diag(rk) U), stored;
+//            prep waves: the blocks of T = (I + A)^-1 below the diagonal
+//              blocks, split by column block (bf16 MFMA products, A's
+//              scalings applied as its blocks are converted), written as
+//              Tb = T diag(beta); the chunk's row scalars; then chunk c+2's
+//              raw rows, loaded to registers during the previous chunk, into
+//              the raw buffer chunk c has freed, with beta and the
+//              cumulative log-decay; then chunk c+3's loads.
+// With the norms folded in as row and column scalings, a partial chunk needs
+// no zeroing: rows past its end repeat its last row, and beta = g = 0 there
+// makes their rows of A, Tb and U zero.  The blocks of Tb and P above the
+// diagonal blocks stay zero and are cleared once.
+// Two raw buffers (K, Q, the block's V columns, per-token scalars) and two
+// prep buffers (Tb, P, per-token scalars) alternate by chunk parity; the
+// chunk loop is unrolled by two so that every LDS address is static.  A raw
+// buffer is free after B1 of the chunk that used it: the chain holds its K^T
+// fragments in registers by then and the outputs read Q in phase 1 only.
+// A wave64 VALU instruction costs four cycles and an LDS round trip far
+// more under load, so per-lane LDS offsets are computed once, outside the
+// loop, and the preparation keeps its serial steps (the substitution, the
+// prefix sum of g) in registers with cross-lane moves.
+
+// a's upper 32 lanes and b's lower 32 lanes trade places
+__device__ __forceinline__ void swap_hi32(float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t x = s[0];
+  const uint32_t y = s[1];
+  a = __uint_as_float(x);
+  b = __uint_as_float(y);
+}
+// a's odd rows of 16 lanes and b's even rows trade places
+__device__ __forceinline__ void swap_odd16(float& a, float& b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t x = s[0];
+  const uint32_t y = s[1];
+  a = __uint_as_float(x);
+  b = __uint_as_float(y);
+}
+// inclusive prefix sum over the 64 lanes: shifts within rows of 16, then
+// the totals of the rows below
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));  // row_shr:1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));  // row_shr:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));  // row_shr:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));  // row_shr:8
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  return x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+// Forward substitution for one column of the inverse of a unit lower
+// triangular 16x16 block: lane j of a row of 16 holds column j of the
+// negated strict lower part in nn; on return t (e_k on entry, k the lane's
+// column) is column k of the inverse.  Step j adds column j times t[j] to
+// the entries below j, column j reaching every lane of the row through a
+// row broadcast (DPP row_newbcast:j) folded into the multiply-add.  Each
+// step is one asm block opened by two wait states, which a VALU write of a
+// register before a DPP read of it requires.
+__device__ __forceinline__ void subst16(float (&t)[16], const float (&nn)[16]) {
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %15, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %16, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %17, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %18, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %19, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %20, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %21, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %22, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %23, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %24, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %10, %25, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %11, %26, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %12, %27, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %13, %28, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %14, %29, %30 row_newbcast:0 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[1]), "v"(nn[2]), "v"(nn[3]), "v"(nn[4]), "v"(nn[5]), "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[0]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %14, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %15, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %16, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %17, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %18, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %19, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %20, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %21, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %22, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %23, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %10, %24, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %11, %25, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %12, %26, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %13, %27, %28 row_newbcast:1 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[2]), "v"(nn[3]), "v"(nn[4]), "v"(nn[5]), "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[1]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %13, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %14, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %15, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %16, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %17, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %18, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %19, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %20, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %21, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %22, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %10, %23, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %11, %24, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %12, %25, %26 row_newbcast:2 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[3]), "v"(nn[4]), "v"(nn[5]), "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[2]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %12, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %13, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %14, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %15, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %16, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %17, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %18, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %19, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %20, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %21, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %10, %22, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %11, %23, %24 row_newbcast:3 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[4]), "v"(nn[5]), "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[3]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %11, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %12, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %13, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %14, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %15, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %16, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %17, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %18, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %19, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %20, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %10, %21, %22 row_newbcast:4 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[5]), "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[5]), "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[4]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %10, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %11, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %12, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %13, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %14, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %15, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %16, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %17, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %18, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %9, %19, %20 row_newbcast:5 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[6]), "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[6]), "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[5]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %9, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %10, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %11, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %12, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %13, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %14, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %15, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %16, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %8, %17, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[7]), "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[6]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %8, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %9, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %10, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %11, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %12, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %13, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %14, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %7, %15, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[8]), "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[7]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %7, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %8, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %9, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %10, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %11, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %12, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %6, %13, %14 row_newbcast:8 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[9]), "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[8]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %6, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %7, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %8, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %9, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %10, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %5, %11, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[10]), "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[9]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %5, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %6, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %7, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %8, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %4, %9, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[11]), "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[10]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %4, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %5, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %6, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %3, %7, %8 row_newbcast:11 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[12]), "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[11]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %3, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %4, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %2, %5, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[13]), "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[13]), "v"(nn[14]), "v"(nn[15]), "v"(t[12]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %2, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\tv_fmac_f32_dpp %1, %3, %4 row_newbcast:13 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[14]), "+v"(t[15])
+               : "v"(nn[14]), "v"(nn[15]), "v"(t[13]));
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:14 row_mask:0xf bank_mask:0xf"
+               : "+v"(t[15])
+               : "v"(nn[15]), "v"(t[14]));
+}
+
+template <int D, int C, int NC, int CT>
+struct FusedLayout {
+  static constexpr int NT = C / 16, DT = D / 16;
+  static constexpr int cols = 16 * NC * CT;
+  static constexpr int RBK = D * 2, RBC = C * 2, RBV = cols * 2, RBS = D * 2, RBU = C * 2;
+  using SK = Swz<RBK>;
+  using SC = Swz<RBC>;
+  using SV = SwzT<RBV, RowV<NT, RBV / 16>>;
+  using SS = SwzT<RBS, RowSeq<RBS>>;
+  using SU = SwzT<RBU, RowSeq<RBU>>;
+  // raw buffer: K, Q rows [C][D] (swizzled), V [C][cols], then per-token
+  // fp32 rows: beta, G log2(e) (cumulative log-decay in base 2), rk
+  static constexpr int rK = 0, rQ = C * RBK, rV = 2 * C * RBK, rSc = rV + C * RBV;
+  static constexpr int raw = rSc + 12 * C;
+  // prep buffer: Tb, P~ [C][C] (swizzled), then per-token fp32 rows:
+  // gamma rk (0 without the erase), gamma, e rk, gamma_last, rk
+  static constexpr int NVEC = 5;
+  static constexpr int pTb = 0, pP = C * RBC, pVec = 2 * C * RBC;
+  static constexpr int prep = pVec + 4 * NVEC * C;
+  static constexpr int LDF = C + 4;  // fp32 A / T rows
+  static constexpr int bytes = 2 * raw + 2 * prep + C * LDF * 4 + cols * RBS + cols * RBU;
+  static constexpr int threads = 64 * (2 * NC + 4);
+  static_assert(NT == 2 || NT == 4, "chunks of 32 or 64 tokens");
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Off-diagonal tile pairs (row block mt > column block tj) of prep wave pw
+// (1..3), chosen so that a wave's pairs share operand tiles
+struct TilePair { int mt, tj; };
+template <int NT>
+constexpr int pairs_of(int pw) { return NT == 2 ? (pw == 1 ? 1 : 0) : 2; }
+template <int NT>
+constexpr TilePair pair_at(int pw, int i) {
+  return NT == 2 ? TilePair{1, 0}
+       : pw == 1 ? (i == 0 ? TilePair{1, 0} : TilePair{2, 0})
+       : pw == 2 ? (i == 0 ? TilePair{3, 0} : TilePair{3, 1})
+                 : (i == 0 ? TilePair{2, 1} : TilePair{3, 2});
+}
+template <int D, int C, int NC, int CT>
+__global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams p, const unsigned char* ws) {
+  using L = FusedLayout<D, C, NC, CT>;
+  using T = __bf16;
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  using SK = typename L::SK;
+  using SC = typename L::SC;
+  using SV = typename L::SV;
+  using SS = typename L::SS;
+  using SU = typename L::SU;
+  constexpr int NT = L::NT, DT = L::DT, DKS = D / 32, KS = NT / 2, LDF = L::LDF;
+  constexpr int NB = D / L::cols;
+  __shared__ __align__(16) unsigned char raw0[L::raw];
+  __shared__ __align__(16) unsigned char raw1[L::raw];
+  __shared__ __align__(16) unsigned char prp0[L::prep];
+  __shared__ __align__(16) unsigned char prp1[L::prep];
+  __shared__ __align__(16) float sA[C * LDF];
+  __shared__ __align__(16) unsigned char sS[L::cols * L::RBS];
+  __shared__ __align__(16) unsigned char sU[L::cols * L::RBU];
+
+  const PlanView plan = plan_view(p, ws, C);
+  const ScanSlot slot = scan_slot(p, plan, NB);
+  if (!slot.valid) return;
+  const int blk = slot.blk, h = slot.h, n = slot.n;
+  const int hq = h / (p.h_v / p.h_qk);
+  // the wave index is uniform across a wave: keep it (and every role and job
+  // parameter derived from it) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int64_t seq_start = p.cu_seqlens ? as_const(p.cu_seqlens)[n] : 0;
+  const int64_t seq_end = p.cu_seqlens ? as_const(p.cu_seqlens)[n + 1] : p.total_tokens;
+  const int nch = plan.off(n + 1) - plan.off(n);
+  auto chunk_t0 = [&](int c) __attribute__((always_inline)) { return seq_start + (int64_t)c * C; };
+  auto chunk_len = [&](int c) __attribute__((always_inline)) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
+  auto fence = [&]() __attribute__((always_inline)) {  // this wave's LDS writes are done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vm_lgkm0<63>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // roles: waves w and w + 4 share a SIMD.  Chain waves come first (one per
+  // SIMD), then the output waves, then the four prep waves, numbered so
+  // that prep wave 0 (the diagonal solve) sits beside an output wave rather
+  // than a chain wave when the layout allows it.
+  const bool chain = wave < NC;
+  const bool outw = wave >= NC && wave < 2 * NC;
+  const bool prepw = wave >= 2 * NC;
+  const int pi = prepw ? (wave - 2 * NC + (NC == 2 ? 2 : 0)) & 3 : -1;
+  const int lt = prepw ? pi * 64 + lane : 0;  // loader thread 0..255
+
+  // fragment reads of the K, Q tiles (token rows 16 t + l16, d_k 32 s + 8 g
+  // .. + 7): byte offsets inside a tile, computed once
+  uint32_t fo[NT][DKS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int s = 0; s < DKS; ++s) fo[t][s] = (uint32_t)SK::off(t * 16 + l16, (32 * s + 8 * g4) * 2);
+  auto kfrag = [&](const unsigned char* tile, int t, int s) __attribute__((always_inline)) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(tile + fo[t][s]));
+  };
+
+  // ---------------------------------------------------------- decay masks
+  // Gram tiles are formed transposed: tile (mt, tj) holds rows j = 16 tj +
+  // 4g + i, column r = 16 mt + l16 of K K^T (or K Q^T), so that a lane holds
+  // row r, columns j0 .. j0 + 3 of A (or P).  With raw rows k, q:
+  //   A_rj = beta_r rk_r e^{G_r - G_j} rk_j (k_r . k_j)         (j <  r)
+  //   P_rj = scale rq_r e^{G_r - G_j} rk_j (q_r . k_j)          (j <= r)
+  // The masks write only e^{G_r - G_j} times the raw product (A~, P~); the
+  // scalars hold G log2(e), so e^{G_r - G_j} = 2^{G2_r - G2_j} <= 1.
+  auto gram = [&](const unsigned char* A_t, const unsigned char* B_t, int mt, int tj) __attribute__((always_inline)) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DKS; ++s) M::mma(acc, kfrag(A_t, tj, s), kfrag(B_t, mt, s), false);
+    return acc;
+  };
+  // decay of a lane's four entries (0 where the mask removes them: j > r,
+  // or j >= r when strict)
+  auto decay = [&](const float* sc, int mt, int tj, bool strict, float (&w)[4]) __attribute__((always_inline)) {
+    const int r = mt * 16 + l16, j0 = tj * 16 + 4 * g4;
+    const float Gr = sc[C + r];
+    const float4 Gj = *reinterpret_cast<const float4*>(sc + C + j0);
+    const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = __builtin_amdgcn_exp2f(Gr - gj[i]);
+      w[i] = mt > tj ? x : (strict ? (j0 + i < r ? x : 0.f) : (j0 + i <= r ? x : 0.f));
+    }
+  };
+  auto put_p = [&](unsigned char* P_s, int mt, int tj, const float (&w)[4], const f32x4& qk) __attribute__((always_inline)) {
+    const int r = mt * 16 + l16, j0 = tj * 16 + 4 * g4;
+    *reinterpret_cast<uint2*>(P_s + SC::off(r, j0 * 2)) =
+        make_uint2(pack_bf16x2(w[0] * qk[0], w[1] * qk[1]), pack_bf16x2(w[2] * qk[2], w[3] * qk[3]));
+  };
+
+  // ------------------------------------------------- raw rows (prep waves)
+  constexpr int NLD = 256;
+  constexpr int RT = D / 8;                      // 16-byte pieces per K / Q row
+  constexpr int NKP = (C * RT + NLD - 1) / NLD;  // K (and Q) pieces per loader thread
+  constexpr int VT = L::cols / 8;                // pieces per row of this block's V
+  constexpr int NVP = (C * VT + NLD - 1) / NLD;
+  gdn_u4 kr[NKP], qr[NKP], vr[NVP];  // native vectors: kept in registers
+  float gr = 0.f, br = 0.f;
+  // per piece: global offsets inside a full chunk (bytes from the chunk's
+  // first row) and LDS offsets in the tile, computed once
+  uint32_t kgo[NKP], qgo[NKP], kso[NKP], vgo[NVP], vso[NVP];
+#pragma unroll
+  for (int i = 0; i < NKP; ++i) {
+    const int e = min(lt + NLD * i, C * RT - 1);
+    const int r = e / RT, c0 = (e % RT) * 8;
+    kgo[i] = (uint32_t)(r * p.k_stride + c0) * 2u;
+    qgo[i] = (uint32_t)(r * p.q_stride + c0) * 2u;
+    kso[i] = (uint32_t)SK::off(r, c0 * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < NVP; ++i) {
+    const int e = min(lt + NLD * i, C * VT - 1);
+    const int r = e / VT, c0 = (e % VT) * 8;
+    vgo[i] = (uint32_t)(r * p.v_stride + c0) * 2u;
+    vso[i] = (uint32_t)SV::off(r, c0 * 2);
+  }
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + (int64_t)hq * D);
+  const unsigned char* qg = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + (int64_t)hq * D);
+  const unsigned char* vg =
+      reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + (int64_t)h * D + blk * L::cols);
+  // chunk c's rows into registers; in a partial chunk, rows past its end
+  // re-read its last row
+  auto load_raw = [&](int c) __attribute__((always_inline)) {
+    const int64_t t0 = chunk_t0(c);
+    const int Lc = chunk_len(c);
+    const unsigned char* kc = kg + t0 * p.k_stride * 2;
+    const unsigned char* qc = qg + t0 * p.q_stride * 2;
+    const unsigned char* vc = vg + t0 * p.v_stride * 2;
+    if (Lc == C) {
+#pragma unroll
+      for (int i = 0; i < NKP; ++i) {
+        kr[i] = *reinterpret_cast<const gdn_u4*>(kc + kgo[i]);
+        qr[i] = *reinterpret_cast<const gdn_u4*>(qc + qgo[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NVP; ++i) vr[i] = *reinterpret_cast<const gdn_u4*>(vc + vgo[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NKP; ++i) {
+        const int e = min(lt + NLD * i, C * RT - 1);
+        const int64_t r = min(e / RT, Lc - 1);
+        const int c0 = (e % RT) * 8;
+        kr[i] = *reinterpret_cast<const gdn_u4*>(kc + (r * p.k_stride + c0) * 2);
+        qr[i] = *reinterpret_cast<const gdn_u4*>(qc + (r * p.q_stride + c0) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < NVP; ++i) {
+        const int e = min(lt + NLD * i, C * VT - 1);
+        const int64_t r = min(e / VT, Lc - 1);
+        vr[i] = *reinterpret_cast<const gdn_u4*>(vc + (r * p.v_stride + (e % VT) * 8) * 2);
+      }
+    }
+    if (pi == 1) {
+      const int64_t r = t0 + min(lane, Lc - 1);
+      gr = p.g[r * p.h_v + h];
+      br = p.beta[r * p.h_v + h];
+    }
+  };
+  // the registers of chunk c into raw buffer b, with beta and G log2(e) (G
+  // the cumulative sum of g; beta = g = 0 past the chunk's end).  Prep wave 1
+  // holds g and beta.
+  auto store_raw = [&](int c, unsigned char* b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NKP; ++i) {
+      if (NLD * (i + 1) <= C * RT || lt + NLD * i < C * RT) {
+        *reinterpret_cast<gdn_u4*>(b + L::rK + kso[i]) = kr[i];
+        *reinterpret_cast<gdn_u4*>(b + L::rQ + kso[i]) = qr[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NVP; ++i)
+      if (NLD * (i + 1) <= C * VT || lt + NLD * i < C * VT) *reinterpret_cast<gdn_u4*>(b + L::rV + vso[i]) = vr[i];
+    if (pi == 1) {
+      const int Lc = chunk_len(c);
+      const float G = wave_prefix_sum(lane < Lc ? gr : 0.f);
+      float* sc = reinterpret_cast<float*>(b + L::rSc);
+      if (lane < C) {
+        sc[lane] = lane < Lc ? br : 0.f;
+        sc[C + lane] = G * kLog2e;
+      }
+    }
+  };
+  // the blocks of Tb and P~ above the diagonal blocks: zero for good
+  auto zero_upper = [&](unsigned char* pb) __attribute__((always_inline)) {
+    constexpr int NUP = NT * (NT - 1) / 2 * 32;  // 16-byte pieces of one matrix
+    for (int e = lt; e < 2 * NUP; e += NLD) {
+      const int m = e / NUP;
+      int k = (e % NUP) / 32, mt = 0;
+      while (k >= NT - 1 - mt) { k -= NT - 1 - mt; ++mt; }
+      const int tj = mt + 1 + k, rr = (e % 32) / 2, hf = e % 2;
+      *reinterpret_cast<uint4*>(pb + (m ? L::pP : L::pTb) + SC::off(mt * 16 + rr, (tj * 16 + 8 * hf) * 2)) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  // ------------------------------------------------ preparation, phase 1
+  // prep wave 0: the NT diagonal tiles of K K^T.  A diagonal tile is
+  // symmetric, so lane (g, c) holds rows 4g + i of column c; its diagonal
+  // gives the row norms (lane (g, c) holds k_r . k_r, r = 16 t + c, when
+  // g = c / 4, in element c % 4).  Permlane swaps (a 4x4 transpose of lane
+  // row and tile) then hand lane (b, c) all of column c of tile b, from
+  // which it forms column c of the block's -A and solves for column c of
+  // (I + A_bb)^-1, written to sA (fp32, for the blocks below) and as Tb.
+  auto diag_solve = [&](unsigned char* b, unsigned char* pb) __attribute__((always_inline)) {
+    const unsigned char* K_s = b + L::rK;
+    float* sc = reinterpret_cast<float*>(b + L::rSc);
+    f32x4 col[4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) col[t] = gram(K_s, K_s, t, t);
+#pragma unroll
+    for (int t = NT; t < 4; ++t) col[t] = col[t - NT];  // two blocks: lane rows 2, 3 repeat blocks 0, 1
+    {
+      const int i = l16 & 3;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float x = i == 0 ? col[t][0] : i == 1 ? col[t][1] : i == 2 ? col[t][2] : col[t][3];
+        if (g4 == (l16 >> 2)) sc[2 * C + t * 16 + l16] = p.l2norm ? rsqrtf(x + 1e-6f) : 1.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a0 = col[0][i], a1 = col[1][i], a2 = col[2][i], a3 = col[3][i];
+      swap_hi32(a0, a2);
+      swap_hi32(a1, a3);
+      swap_odd16(a0, a1);
+      swap_odd16(a2, a3);
+      col[0][i] = a0; col[1][i] = a1; col[2][i] = a2; col[3][i] = a3;
+    }
+    // col[q][e] = k_{16 cb + 4q + e} . k_{16 cb + k}: column k of block cb
+    fence();  // the norms are written
+    const int bb = g4, k = l16, cb = bb & (NT - 1);
+    const int j = 16 * cb + k;
+    const float rkj = sc[2 * C + j], G2j = sc[C + j], bj = sc[j];
+    float nn[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 be = *reinterpret_cast<const float4*>(sc + 16 * cb + 4 * q);
+      const float4 gg = *reinterpret_cast<const float4*>(sc + C + 16 * cb + 4 * q);
+      const float4 rr = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * cb + 4 * q);
+      const float bq[4] = {be.x, be.y, be.z, be.w}, gq[4] = {gg.x, gg.y, gg.z, gg.w}, rq[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q + e;  // row 16 cb + i; e^{G_i - G_j} <= 1 where kept (i > k)
+        const float a = bq[e] * rq[e] * rkj * __builtin_amdgcn_exp2f(gq[e] - G2j) * col[q][e];
+        nn[i] = (p.erase && i > k) ? -a : 0.f;
+      }
+    }
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = i == k ? 1.f : 0.f;
+    subst16(t, nn);
+    if (bb < NT) {
+      float* out = sA + 16 * bb * LDF + j;
+      unsigned char* tb = pb + L::pTb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        out[i * LDF] = t[i];
+        *reinterpret_cast<__bf16*>(tb + SC::off(16 * bb + i, j * 2)) = (__bf16)(t[i] * bj);
+      }
+    }
+  };
+  // prep waves 1-3: their tiles below the diagonal blocks, K K^T and Q K^T
+  // at the same (mt, tj) sharing one decay
+  auto pairs = [&](const unsigned char* b, unsigned char* pb, auto pw) __attribute__((always_inline)) {
+    constexpr int PW = decltype(pw)::value;
+    const unsigned char* K_s = b + L::rK;
+    const unsigned char* Q_s = b + L::rQ;
+    const float* sc = reinterpret_cast<const float*>(b + L::rSc);
+    unsigned char* P_s = pb + L::pP;
+#pragma unroll
+    for (int o = 0; o < pairs_of<NT>(PW); ++o) {
+      const TilePair tp = pair_at<NT>(PW, o);
+      const int mt = tp.mt, tj = tp.tj;
+      const f32x4 kk = gram(K_s, K_s, mt, tj);
+      const f32x4 qk = gram(K_s, Q_s, mt, tj);
+      float w[4];
+      decay(sc, mt, tj, true, w);
+      const int r = mt * 16 + l16, j0 = tj * 16 + 4 * g4;
+      *reinterpret_cast<float4*>(sA + r * LDF + j0) = make_float4(w[0] * kk[0], w[1] * kk[1], w[2] * kk[2], w[3] * kk[3]);
+      put_p(P_s, mt, tj, w, qk);
+    }
+  };
+  auto prep_phase1 = [&](unsigned char* b, unsigned char* pb) __attribute__((always_inline)) {
+    if (pi == 0) diag_solve(b, pb);
+    else if (pi == 1) pairs(b, pb, std::integral_constant<int, 1>{});
+    else if (pi == 2) pairs(b, pb, std::integral_constant<int, 2>{});
+    else pairs(b, pb, std::integral_constant<int, 3>{});
+  };
+  // output waves: the diagonal tiles of Q K^T (tiles ow, ow + NC, ...)
+  auto prep1_pdiag = [&](const unsigned char* b, unsigned char* pb, int ow) __attribute__((always_inline)) {
+    const unsigned char* K_s = b + L::rK;
+    const unsigned char* Q_s = b + L::rQ;
+    const float* sc = reinterpret_cast<const float*>(b + L::rSc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t % NC != ow) continue;
+      const f32x4 qk = gram(K_s, Q_s, t, t);
+      float w[4];
+      decay(sc, t, t, false, w);
+      put_p(pb + L::pP, t, t, w, qk);
+    }
+  };
+
+  // ------------------------------------------------ preparation, phase 2
+  // The blocks of T below the diagonal blocks follow from (I + A) T = I:
+  //   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,
+  //   X_ij = A_i0 T_0j + A_i1 T_1j,
+  //   T_2j = -T_22 X_2j,  T_3j = -T_33 (X_3j + A_32 T_2j)      (j = 0, 1)
+  // on bf16 MFMA (16x16x32, k over two 16-blocks; a block above the
+  // diagonal enters as zero; A's blocks take their row scaling beta_r rk_r
+  // and column scaling rk_j as they are converted), each written as a block
+  // of Tb = T diag(beta).  Prep wave 1 forms T_32 (T_10 when there are two
+  // blocks), wave 2 column block 0 (T_10, T_20, T_30), wave 3 column block 1
+  // (T_21, T_31), wave 0 the row scalars.
+  auto prep_phase2 = [&](const unsigned char* b, unsigned char* pb) __attribute__((always_inline)) {
+    const float* sc = reinterpret_cast<const float*>(b + L::rSc);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto colb = [&](int bi, int bj) __attribute__((always_inline)) {  // accumulator layout: rows 4g + i, column c
+      const float* a = sA + (16 * bi + 4 * g4) * LDF + 16 * bj + l16;
+      return f32x4{a[0], a[LDF], a[2 * LDF], a[3 * LDF]};
+    };
+    // A fragment, rows 16 bi + l16 over blocks bj0 | bj1 (bj1 < 0: zeros),
+    // of T (scaled = false) or of A (from A~, scaled)
+    auto rowf = [&](int bi, int bj0, int bj1, bool scaled) __attribute__((always_inline)) {
+      const int r = 16 * bi + l16;
+      const float* a = sA + r * LDF + 4 * g4;
+      float4 x = *reinterpret_cast<const float4*>(a + 16 * bj0);
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bj1 >= 0) y = *reinterpret_cast<const float4*>(a + 16 * bj1);
+      if (scaled) {
+        const float fa = p.erase ? sc[r] * sc[2 * C + r] : 0.f;
+        const float4 k0 = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * bj0 + 4 * g4);
+        x = make_float4(fa * k0.x * x.x, fa * k0.y * x.y, fa * k0.z * x.z, fa * k0.w * x.w);
+        if (bj1 >= 0) {
+          const float4 k1 = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * bj1 + 4 * g4);
+          y = make_float4(fa * k1.x * y.x, fa * k1.y * y.y, fa * k1.z * y.z, fa * k1.w * y.w);
+        }
+      }
+      return __builtin_bit_cast(frag, make_uint4(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w),
+                                                 pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)));
+    };
+    // block (bi, bj) of Tb from T in accumulator layout
+    auto put_tb = [&](int bi, int bj, const f32x4& t) __attribute__((always_inline)) {
+      unsigned char* tb = pb + L::pTb;
+      const float bc = sc[16 * bj + l16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<__bf16*>(tb + SC::off(16 * bi + 4 * g4 + i, (16 * bj + l16) * 2)) = (__bf16)(t[i] * bc);
+    };
+    // T_{2b+1, 2b}
+    auto level1 = [&](int bb) __attribute__((always_inline)) {
+      f32x4 x = zero, l = zero;
+      M::mma(x, rowf(2 * bb + 1, 2 * bb, -1, true), M::acc(colb(2 * bb, 2 * bb), zero), false);
+      M::mma(l, rowf(2 * bb + 1, 2 * bb + 1, -1, false), M::acc(x, zero), false);
+      return -l;
+    };
+    // T_2j, T_3j from X_2j, X_3j
+    auto lower_pair = [&](int jb, f32x4 x2, f32x4 x3) __attribute__((always_inline)) {
+      f32x4 t2 = zero, t3 = zero;
+      M::mma(t2, rowf(2, 2, -1, false), M::acc(x2, zero), false);
+      t2 = -t2;
+      put_tb(2, jb, t2);
+      M::mma(x3, rowf(3, 2, -1, true), M::acc(t2, zero), false);
+      M::mma(t3, rowf(3, 3, -1, false), M::acc(x3, zero), false);
+      put_tb(3, jb, -t3);
+    };
+    if constexpr (NT == 2) {
+      if (pi == 1) put_tb(1, 0, level1(0));
+    } else {
+      if (pi == 1) {
+        put_tb(3, 2, level1(1));
+      } else if (pi == 2) {
+        const f32x4 t10 = level1(0);
+        put_tb(1, 0, t10);
+        const frag bt = M::acc(colb(0, 0), t10);
+        f32x4 x2 = zero, x3 = zero;
+        M::mma(x2, rowf(2, 0, 1, true), bt, false);
+        M::mma(x3, rowf(3, 0, 1, true), bt, false);
+        lower_pair(0, x2, x3);
+      } else if (pi == 3) {
+        const frag bt = M::acc(colb(1, 1), zero);
+        f32x4 x2 = zero, x3 = zero;
+        M::mma(x2, rowf(2, 1, -1, true), bt, false);
+        M::mma(x3, rowf(3, 1, -1, true), bt, false);
+        lower_pair(1, x2, x3);
+      }
+    }
+    // row scalars: gamma rk (0 without the erase: R = V), gamma, e rk,
+    // gamma_last (G of padding rows equals the last row's), rk
+    if (pi == 0 && lane < C) {
+      float* vec = reinterpret_cast<float*>(pb + L::pVec);
+      const float G = sc[C + lane], Gl = sc[2 * C - 1], eg = __builtin_amdgcn_exp2f(G), rk = sc[2 * C + lane];
+      vec[lane] = p.erase ? eg * rk : 0.f;
+      vec[C + lane] = eg;
+      vec[2 * C + lane] = __builtin_amdgcn_exp2f(Gl - G) * rk;
+      vec[3 * C + lane] = __builtin_amdgcn_exp2f(Gl);
+      vec[4 * C + lane] = rk;
+    }
+  };
+
+  // ------------------------------------------------------------ prologue
+  if (nch > 0) {
+    if (prepw) {
+      zero_upper(prp0);
+      zero_upper(prp1);
+      load_raw(0);
+      store_raw(0, raw0);
+      if (nch > 1) load_raw(1);
+    }
+    barrier_vm<63>();  // raw chunk 0 visible
+    if (prepw) prep_phase1(raw0, prp0);
+    if (outw) prep1_pdiag(raw0, prp0, wave - NC);
+    barrier_vm<63>();  // chunk 0's T_bb, A~ and norms complete
+    if (prepw) {
+      prep_phase2(raw0, prp0);
+      if (nch > 1) {
+        store_raw(1, raw1);
+        if (nch > 2) load_raw(2);
+      }
+    }
+  }
+  if (chain) {
+    // ---------------------------------------------------------- chain waves
+    // S^T (d_k x this wave's 16 CT columns) in CT x DT accumulator tiles;
+    // row 4g+i of tile dt is d_k index pidx<DT>(dt, 4g+i)
+    auto colof = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * wave + ct) + l16; };
+    f32x4 st[CT][DT];
+    const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
+    auto srow = [&](int ct) __attribute__((always_inline)) {
+      return (((size_t)sslot * p.h_v + h) * D + (size_t)(blk * L::cols + colof(ct))) * D;
+    };
+    auto wrow = [&](int ct) __attribute__((always_inline)) {
+      return ((size_t)h * D + (size_t)(blk * L::cols + colof(ct))) * D;
+    };
+    const int erow = p.emit_every > 0 ? plan.erow(n) : 0;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        st[ct][dt] = p.initial_state ? load_state4(p.initial_state, srow(ct) + pidx<DT>(dt, 4 * g4), p.state_bf16)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    auto publish_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int u = 0; u < DT / 2; ++u)
+          *reinterpret_cast<frag*>(sS + SS::off(colof(ct), (32 * u + 8 * g4) * 2)) = M::acc(st[ct][2 * u], st[ct][2 * u + 1]);
+    };
+    publish_state();
+    barrier_vm<63>();  // the initial state and chunk 0's preparation are visible
+    auto step = [&](int c, const unsigned char* rb, const unsigned char* pb) __attribute__((always_inline)) {
+      const unsigned char* K_t = rb + L::rK;
+      const unsigned char* V_t = rb + L::rV;
+      const unsigned char* Tb_t = pb + L::pTb;
+      const float* vec = reinterpret_cast<const float*>(pb + L::pVec);
+      // V[token pidx(mt, 4g) + e][column] by one transposing read per tile
+      uint2 vw[CT][NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          const int r0 = pidx<NT>(mt, 4 * g4);
+          vw[ct][mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(
+              __attribute__((address_space(3))) unsigned char*)(V_t + SV::off(r0 + (l16 >> 2),
+                                                                              (16 * (CT * wave + ct) + 4 * (l16 & 3)) * 2))));
+        }
+      frag at[KS][NT];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) at[s][mt] = frag_row_s<T, SC>(Tb_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+      // X1 = K S^T
+      f32x4 x1[CT][NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) x1[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DKS; ++s) {
+        frag ak[NT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) ak[mt] = frag_row_s<T, SK>(K_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const frag bs = M::acc(st[ct][2 * s], st[ct][2 * s + 1]);
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) M::mma(x1[ct][mt], ak[mt], bs, false);
+        }
+      }
+      // R = V - diag(gamma rk) X1
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const float4 vq = *reinterpret_cast<const float4*>(vec + pidx<NT>(mt, 4 * g4));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          x1[ct][mt][0] = bf16_lo(vw[ct][mt].x) - vq.x * x1[ct][mt][0];
+          x1[ct][mt][1] = bf16_hi(vw[ct][mt].x) - vq.y * x1[ct][mt][1];
+          x1[ct][mt][2] = bf16_lo(vw[ct][mt].y) - vq.z * x1[ct][mt][2];
+          x1[ct][mt][3] = bf16_hi(vw[ct][mt].y) - vq.w * x1[ct][mt][3];
+        }
+      }
+      // U = Tb R
+      f32x4 u[CT][NT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) u[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const frag bs = M::acc(x1[ct][2 * s], x1[ct][2 * s + 1]);
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) M::mma(u[ct][mt], at[s][mt], bs, false);
+        }
+      // publish U as bf16 rows [column][token]
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          *reinterpret_cast<frag*>(sU + SU::off(colof(ct), (32 * s + 8 * g4) * 2)) = M::acc(u[ct][2 * s], u[ct][2 * s + 1]);
+      // U' = diag(e rk) U
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const float4 vq = *reinterpret_cast<const float4*>(vec + 2 * C + pidx<NT>(mt, 4 * g4));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          u[ct][mt][0] *= vq.x; u[ct][mt][1] *= vq.y; u[ct][mt][2] *= vq.z; u[ct][mt][3] *= vq.w;
+        }
+      }
+      // S^T <- gamma_last S^T + K^T U', before B1 (the raw buffer is refilled
+      // after it); the new state is published after B1, once the output
+      // waves are done with the old one
+      const float gl = vec[3 * C];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st[ct][dt] *= gl;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        frag bs[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bs[ct] = M::acc(u[ct][2 * s], u[ct][2 * s + 1]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const frag kt = frag_kt<T, L::RBK, DT>(K_t, dt, 32 * s + 8 * g4, l16, false);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], kt, bs[ct], false);
+        }
+      }
+      barrier_vm<63>();  // B1
+      // the state after every emit_every-th whole chunk inside the sequence
+      if (p.emit_every > 0 && (c + 1) % p.emit_every == 0 && chunk_t0(c) + C < seq_end) {
+        const size_t dst = (size_t)(erow + (c + 1) / p.emit_every - 1) * p.h_v * D * D;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            store_state4(p.chunk_states, dst + wrow(ct) + pidx<DT>(dt, 4 * g4), st[ct][dt], p.state_bf16);
+      }
+      publish_state();
+      barrier_vm<63>();  // B2
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, raw0, prp0);
+      if (c + 1 < nch) step(c + 1, raw1, prp1);
+    }
+    if (p.final_state) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          store_state4(p.final_state, srow(ct) + pidx<DT>(dt, 4 * g4), st[ct][dt], p.state_bf16);
+    }
+  } else if (outw) {
+    // --------------------------------------------------------- output waves
+    const int ow = wave - NC;
+    const int64_t o_stride = (int64_t)p.h_v * D;
+    T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D + blk * L::cols + 4 * g4;
+    auto colr = [&](int ct) __attribute__((always_inline)) { return 16 * (CT * ow + ct) + l16; };
+    barrier_vm<63>();  // the initial state and chunk 0's preparation are visible
+    // rb, pb: chunk c; rn, pn: chunk c+1 (its diagonal Q K^T tiles)
+    auto step = [&](int c, const unsigned char* rb, const unsigned char* pb, const unsigned char* rn,
+                    unsigned char* pn) __attribute__((always_inline)) {
+      const unsigned char* Q_t = rb + L::rQ;
+      const unsigned char* P_t = pb + L::pP;
+      const float* vec = reinterpret_cast<const float*>(pb + L::pVec);
+      // O^T tile (ct, nt): rows 4g + i = columns 16 (CT ow + ct) + 4g + i,
+      // column l16 = token pidx(nt, l16).  First Y^T = S Q^T (raw q), scaled
+      // by gamma; the lane's part of |q|^2 comes from the same fragments
+      f32x4 o[CT][NT];
+      float qq[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        qq[nt] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o[ct][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s = 0; s < DKS; ++s) {
+        frag as[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) as[ct] = frag_row_s<T, SS>(sS, colr(ct), 32 * s + 8 * g4, false);
+        frag bq[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bq[nt] = frag_row_s<T, SK>(Q_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], as[ct], bq[nt], false);
+          const uint4 w = __builtin_bit_cast(uint4, bq[nt]);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            qq[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ww[j]), __builtin_bit_cast(bf16x2, ww[j]), qq[nt], false);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float gm = vec[C + pidx<NT>(nt, l16)];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= gm;
+        // sum over the four lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+        float a = qq[nt], b = qq[nt];
+        swap_hi32(a, b);
+        a += b;
+        b = a;
+        swap_odd16(a, b);
+        qq[nt] = a + b;
+      }
+      if (c + 1 < nch) prep1_pdiag(rn, pn, ow);
+      barrier_vm<63>();  // B1: U is published
+      // O^T += (U diag(rk))^T P~^T
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const float4 r0 = *reinterpret_cast<const float4*>(vec + 4 * C + 32 * s + 8 * g4);
+        const float4 r1 = *reinterpret_cast<const float4*>(vec + 4 * C + 32 * s + 8 * g4 + 4);
+        frag au[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const uint4 uw = __builtin_bit_cast(uint4, frag_row_s<T, SU>(sU, colr(ct), 32 * s + 8 * g4, false));
+          au[ct] = __builtin_bit_cast(frag, make_uint4(
+              pack_bf16x2(bf16_lo(uw.x) * r0.x, bf16_hi(uw.x) * r0.y), pack_bf16x2(bf16_lo(uw.y) * r0.z, bf16_hi(uw.y) * r0.w),
+              pack_bf16x2(bf16_lo(uw.z) * r1.x, bf16_hi(uw.z) * r1.y), pack_bf16x2(bf16_lo(uw.w) * r1.z, bf16_hi(uw.w) * r1.w)));
+        }
+        frag bp[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], au[ct], bp[nt], false);
+      }
+      const int Lc = chunk_len(c);
+      T* oc = og + chunk_t0(c) * o_stride;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = pidx<NT>(nt, l16);
+        const float f = p.scale * (p.l2norm ? rsqrtf(qq[nt] + 1e-6f) : 1.0f);
+        if (tok < Lc) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<uint2*>(oc + (int64_t)tok * o_stride + 16 * (CT * ow + ct)) =
+                make_uint2(pack_bf16x2(f * o[ct][nt][0], f * o[ct][nt][1]), pack_bf16x2(f * o[ct][nt][2], f * o[ct][nt][3]));
+        }
+      }
+      barrier_vm<63>();  // B2
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, raw0, prp0, raw1, prp1);
+      if (c + 1 < nch) step(c + 1, raw1, prp1, raw0, prp0);
+    }
+  } else {
+    // ---------------------------------------------------------- prep waves
+    barrier_vm<63>();  // the initial state and chunk 0's preparation are visible
+    // rb: chunk c (free after B1), then chunk c+2; rn, pn: chunk c+1
+    auto step = [&](int c, unsigned char* rb, unsigned char* rn, unsigned char* pn) __attribute__((always_inline)) {
+      if (c + 1 < nch) prep_phase1(rn, pn);
+      barrier_vm<63>();  // B1
+      if (c + 1 < nch) prep_phase2(rn, pn);
+      if (c + 2 < nch) {
+        store_raw(c + 2, rb);
+        if (c + 3 < nch) load_raw(c + 3);
+      }
+      barrier_vm<63>();  // B2: loads of the chunk after next stay in flight
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, raw0, raw1, prp1);
+      if (c + 1 < nch) step(c + 1, raw1, raw0, prp0);
+    }
+  }
+}
+
+#define GDN_FUSED(D, C) \
+  template __global__ void fused_kernel<D, C, 1, 1>(PrefillParams, const unsigned char*); \
+  template __global__ void fused_kernel<D, C, 2, 1>(PrefillParams, const unsigned char*); \
+  template __global__ void fused_kernel<D, C, 2, 2>(PrefillParams, const unsigned char*);
+GDN_FUSED(64, 32) GDN_FUSED(64, 64) GDN_FUSED(128, 32) GDN_FUSED(128, 64)
+#undef GDN_FUSED
+
 // ------------------------------------------------------------------ host
 constexpr int kLdsMax = 160 * 1024;
 // scan workgroup shape: kScanWaves waves, each owning kScanTiles 16-column
@@ -1984,8 +2880,67 @@ hipError_t launch_prep(const PrefillParams& p, unsigned char* ws, int64_t mc, hi
   }
 }
 
+// bf16 at chunk 32 and 64 runs the fused kernel (plan_kernel first with
+// cu_seqlens); its workspace is the plan's arrays only
+template <typename T, int C>
+constexpr bool fused_path() { return sizeof(T) == 2 && C >= 32; }
+// The fused kernel runs when its widest workgroups (64 columns) fill the
+// chip by themselves: many (sequence, V head) pairs, where it does the least
+// work per chunk.  With fewer, the serial chains of a few long sequences set
+// the time, and the separate preparation and scan launches are faster.
+// GDN_PREFILL_FUSED=1 or 0 forces the choice (tuning and comparison); the
+// workspace query follows it.
+inline bool use_fused(int io_dtype, int chunk, int n_seqs, int h_v, int d) {
+  const char* e = std::getenv("GDN_PREFILL_FUSED");  // read per call: tests switch it in-process
+  const int forced = e && e[0] ? (e[0] == '0' ? 0 : 1) : -1;
+  if (io_dtype != 1 || chunk < 32) return false;
+  if (forced >= 0) return forced == 1;
+  return (int64_t)n_seqs * h_v * (d / 64) >= kScanCUs;
+}
+
+// Columns per fused workgroup (16, 32 or 64): the narrowest block that
+// still puts every workgroup on the chip at once (the serial chains then run
+// side by side), else the widest (the least preparation repeated per column
+// block).  GDN_FUSED_COLS forces a width (tuning).
+inline int fused_cols(const PrefillParams& p, int d) {
+  const char* e = std::getenv("GDN_FUSED_COLS");
+  const int forced = e ? std::atoi(e) : 0;
+  if ((forced == 16 || forced == 32 || forced == 64) && forced <= d) return forced;
+  const int64_t units = (int64_t)p.n_seqs * p.h_v;
+  if (units * (d / 16) <= kScanCUs) return 16;
+  if (units * (d / 32) <= kScanCUs) return 32;
+  return 64;
+}
+
+template <int D, int C, int NC, int CT>
+hipError_t launch_fused_cfg(const PrefillParams& p, const unsigned char* ws, hipStream_t stream) {
+  using FL = FusedLayout<D, C, NC, CT>;
+  const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / FL::cols);
+  hipLaunchKernelGGL((fused_kernel<D, C, NC, CT>), dim3(grid), dim3(FL::threads), 0, stream, p, ws);
+  return hipGetLastError();
+}
+
+template <int D, int C>
+hipError_t launch_fused(const PrefillParams& p, hipStream_t stream) {
+  unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+  if (p.cu_seqlens) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.n_seqs, p.total_tokens, C,
+                       p.emit_every, reinterpret_cast<int32_t*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (fused_cols(p, D)) {
+    case 16: return launch_fused_cfg<D, C, 1, 1>(p, ws, stream);
+    case 32: return launch_fused_cfg<D, C, 2, 1>(p, ws, stream);
+    default: return launch_fused_cfg<D, C, 2, 2>(p, ws, stream);
+  }
+}
+
 template <typename T, int D, int C>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+  if constexpr (fused_path<T, C>()) {
+    if (use_fused(1, C, p.n_seqs, p.h_v, D)) return launch_fused<D, C>(p, stream);
+  }
   if constexpr (!fits<T, D, C>()) {
     return hipErrorInvalidConfiguration;  // rejected by prefill_supported() first
   } else {
@@ -2073,6 +3028,7 @@ size_t rec_c(int chunk) {
 size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk,
                                int emit_every) {
   if (n_seqs < 1 || total_tokens < 0 || h_v < 1 || (chunk != 16 && chunk != 32 && chunk != 64)) return 0;
+  if (use_fused(io_dtype, chunk, n_seqs, h_v, d)) return off_bytes(n_seqs);  // the fused kernel: the plan only
   const size_t rec = io_dtype == 1 ? rec_c<__bf16>(chunk) : rec_c<float>(chunk);
   const size_t recs_end = off_bytes(n_seqs) + (size_t)max_chunks(total_tokens, n_seqs, chunk) * h_v * rec;
   return split_plan(io_dtype, total_tokens, n_seqs, h_v, d, chunk, emit_every, recs_end).bytes;

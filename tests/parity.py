@@ -22,6 +22,21 @@ def rel_err(gpu, ref):
     return float(np.abs(g - r).max() / denom)
 
 
+def rel_err_per(gpu, ref, axis):
+    """The largest norm-wise error over the slices along `axis` (each V head,
+    or each sequence): max over i of max|gpu_i - ref_i| / max|ref_i|.  A
+    slice of small magnitude cannot hide behind the tensor-wide maximum."""
+    g = gpu.detach().double().cpu().numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    g, r = np.moveaxis(g, axis, 0), np.moveaxis(r, axis, 0)
+    worst = 0.0
+    for gi, ri in zip(g, r):
+        denom = np.abs(ri).max()
+        worst = max(worst, float(np.abs(gi - ri).max() / denom) if denom > 0 else float(np.abs(gi).max()))
+    return worst
+
+
 def np64(t):
     return None if t is None else t.double().cpu().numpy()
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
     for n in names:
         assert re.search(rf"\bT {n}$", out, flags=re.M), n
-    assert L.gdn_abi_version() == gdn.ABI_VERSION == 3
+    assert L.gdn_abi_version() == gdn.ABI_VERSION == 4
 
 
 def test_struct_layout_matches_header():
@@ -82,9 +82,15 @@ def _prefill(**kw):
     (dict(q=0), 1), (dict(n_seqs=0), 1), (dict(n_seqs=2), 1), (dict(io_dtype=7), 1),
     (dict(q_stride=100), 1), (dict(q_stride=260), 3), (dict(q=0x1001), 3), (dict(flags=8), 1),
     (dict(struct_size=8), 1), (dict(total_tokens=-1), 1),
-    (dict(io_dtype=0, d_k=128, d_v=128, chunk=64), 2),
+    # fp32 at chunk 64 is supported for both head widths: only the workspace is missing
+    (dict(io_dtype=0, d_k=128, d_v=128, chunk=64), 4), (dict(io_dtype=0, d_k=64, d_v=64, chunk=64), 4),
     (dict(emit_every=-1), 1), (dict(emit_every=2), 1), (dict(emit_every=2, chunk_states=0x7008), 3),
-    (dict(state_idx=0x7002), 3),
+    (dict(state_idx=0x7002), 3), (dict(state_dtype=7), 1),
+    # a struct of the previous ABI (no state_dtype) is read as fp32 states
+    (dict(struct_size=gdn.PrefillArgs.state_dtype.offset), 4),
+    (dict(struct_size=gdn.PrefillArgs.state_dtype.offset - 8), 1),
+    # final_state may alias initial_state exactly, not partly
+    (dict(initial_state=0x100000, final_state=0x100010), 1),
 ])
 def test_prefill_validation(kw, code):
     st, msg = _prefill(**kw)
@@ -111,6 +117,16 @@ def test_conv_and_decode_validation():
     assert L.gdn_decode_step(ctypes.byref(d), None) == 2  # more than 16 V heads per QK head
     d.h_qk, d.h_v, d.state = 2, 6, 0x5008
     assert L.gdn_decode_step(ctypes.byref(d), None) == 3
+    d.state, d.conv_head = 0x5000, 0x7002
+    assert L.gdn_decode_step(ctypes.byref(d), None) == 3  # misaligned ring heads
+    a.conv_head = 0x7002
+    assert L.gdn_conv1d(ctypes.byref(a), None) == 3
+    # structs of the previous ABI (no conv_head) are accepted; shorter ones are not
+    a.conv_head, a.y = 0, 0x3000
+    a.struct_size = gdn.ConvArgs.conv_head.offset - 8
+    assert L.gdn_conv1d(ctypes.byref(a), None) == 1
+    d.struct_size = gdn.DecodeArgs.conv_head.offset - 8
+    assert L.gdn_decode_step(ctypes.byref(d), None) == 1
 
 
 def test_prefill_requires_workspace():
@@ -125,8 +141,16 @@ def test_workspace_size_query():
                         h_v=48, d_k=128, d_v=128, chunk=64)
     a.io_dtype = 1
     n = gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a))
-    # offsets (256 B) + (1024/64 + 1) chunks x 48 heads x (Tb + P bf16 + 4 fp32 rows)
+    # one sequence of 48 heads runs the separate preparation and scan: offsets
+    # + (1024/64 + 1) chunks x 48 heads x (Tb + P in the io dtype + 4 fp32 rows)
     assert n == 256 + 17 * 48 * (2 * 64 * 64 * 2 + 16 * 64)
+    # 100 sequences run the fused kernel: only the plan's arrays (chunk
+    # offsets, scan order, emitted-state rows), padded to 256 bytes
+    a.n_seqs = 100
+    assert gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a)) == (100 * 3 + 2) * 4 // 256 * 256 + 256
+    a.n_seqs, a.io_dtype = 1, 0
+    n = gdn.lib().gdn_prefill_workspace_size(ctypes.byref(a))
+    assert n == 256 + 17 * 48 * (2 * 64 * 64 * 4 + 16 * 64)
     assert gdn.lib().gdn_status_string(5) == b"GDN_ERR_HIP"
 
 

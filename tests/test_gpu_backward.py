@@ -243,7 +243,9 @@ def test_prefill_backward_27b_size_sampled_group():
     """The 27B-shaped layer at full length (T = 65,536, 16 QK / 48 V heads,
     1,024 chunks in one chain, a non-zero initial state) through conv + split,
     then prefill_backward with a final-state gradient; the oracle checks QK
-    head group 0 (V heads 0-2), whose gradients depend on no other head."""
+    head groups 0 and 15 (V heads 0-2 and 45-47: the first and the last group,
+    which the workgroup placement puts on different XCDs), whose gradients
+    depend on no other head."""
     inp = gdn_inputs.prefill_inputs("qwen35_27b_prefill", seed=0)
     cfg = inp["cfg"]
     h_qk, h_v, d = cfg["h_qk"], cfg["h_v"], cfg["d_k"]
@@ -255,15 +257,16 @@ def test_prefill_backward_27b_size_sampled_group():
     g, beta, s0 = dev(inp["g"]), dev(inp["beta"]), dev(inp["initial_state"])
     got = gdn.prefill_backward(q, k, v, g, beta, dev(do), s0, dev(dsf))
     torch.cuda.synchronize()
-    hs = slice(0, grp)
-    ref = orc.gated_delta_rule_backward(np64(q[:, 0:1]), np64(k[:, 0:1]), np64(v[:, hs]), np64(g[:, hs]),
-                                        np64(beta[:, hs]), np64(do[:, hs]), np64(s0[:, hs]), np64(dsf[:, hs]),
-                                        segment=64)
-    mine = [got[0][:, 0:1], got[1][:, 0:1], got[2][:, hs], got[3][:, hs], got[4][:, hs], got[5][:, hs]]
-    errs = {n: rel_err(a, b) for n, a, b in zip(NAMES, mine, ref)}
-    report("prefill_backward[27B, group 0]", **errs)
-    for n, e in errs.items():
-        assert e < TOL_BF16, (n, e)
+    for qg in (0, h_qk - 1):
+        hs, qs = slice(qg * grp, (qg + 1) * grp), slice(qg, qg + 1)
+        ref = orc.gated_delta_rule_backward(np64(q[:, qs]), np64(k[:, qs]), np64(v[:, hs]), np64(g[:, hs]),
+                                            np64(beta[:, hs]), np64(do[:, hs]), np64(s0[:, hs]),
+                                            np64(dsf[:, hs]), segment=64)
+        mine = [got[0][:, qs], got[1][:, qs], got[2][:, hs], got[3][:, hs], got[4][:, hs], got[5][:, hs]]
+        errs = {n: rel_err(a, b) for n, a, b in zip(NAMES, mine, ref)}
+        report(f"prefill_backward[27B, group {qg}]", **errs)
+        for n, e in errs.items():
+            assert e < TOL_BF16, (qg, n, e)
 
 
 @pytest.mark.parametrize("lens", [[0], [0, 0, 0]])

@@ -13,7 +13,7 @@ import torch
 import gdn_inputs
 import linear_attention_token_conv1d_amd as gdn
 from oracle import gdn_oracle as orc
-from parity import TOL_BF16, TOL_F32, dev, np64, rel_err, report
+from parity import TOL_BF16, TOL_F32, dev, np64, rel_err, rel_err_per, report
 
 pytestmark = pytest.mark.gpu
 
@@ -43,24 +43,37 @@ def _run_layer(name, heads, **kw):
                                 cu_seqlens=None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy(),
                                 v_heads=heads, x_is_selected=True)
     print(f"[{name}] oracle {time.time() - t0:.1f}s", flush=True)
-    e = dict(o=rel_err(o_s, ro), state=rel_err(S_s, rS), conv_state=rel_err(cs_s, rcs))
+    e = dict(o=rel_err(o_s, ro), state=rel_err(S_s, rS), conv_state=rel_err(cs_s, rcs),
+             o_per_head=rel_err_per(o_s, ro, 1), state_per_head=rel_err_per(S_s, rS, 1))
+    if inp["cu_seqlens"] is not None:  # each sequence on its own
+        cu = inp["cu_seqlens"].numpy()
+        e["o_per_seq"] = max(rel_err(o_s[cu[n]:cu[n + 1]], ro[cu[n]:cu[n + 1]])
+                             for n in range(N) if cu[n + 1] > cu[n])
+        e["state_per_seq"] = rel_err_per(S_s, rS, 0)
     report(f"[{name}] heads {heads}", **e)
     return e
 
 
+def _ok(e):
+    return all(v < TOL_BF16 for k, v in e.items() if k != "conv_state") and e["conv_state"] == 0.0
+
+
 def test_qwen35_9b_layer_prefill():
     e = _run_layer("qwen35_9b_prefill", [0, 13, 31])
-    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+    assert _ok(e)
 
 
 def test_qwen35_27b_grouped_prefill():
-    e = _run_layer("qwen35_27b_prefill", [0, 1, 2, 46])
-    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+    # the first QK group whole, and heads of the last group (placement deals
+    # QK groups round-robin over the XCDs)
+    e = _run_layer("qwen35_27b_prefill", [0, 1, 2, 46, 47])
+    assert _ok(e)
 
 
 def test_qwen35_27b_varlen_prefill():
-    e = _run_layer("qwen35_27b_varlen", [7])
-    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+    # V heads of the first, middle and last QK groups, over all 8 sequences
+    e = _run_layer("qwen35_27b_varlen", [0, 7, 24, 47])
+    assert _ok(e)
 
 
 def test_qwen35_27b_batched_decode_64_steps():
@@ -70,11 +83,15 @@ def test_qwen35_27b_batched_decode_64_steps():
     S, cs = dev(inp["state"]), dev(inp["conv_state"])
     w = dev(inp["conv_weight"])
     xs, gs, bs = dev(inp["x"]), dev(inp["g"]), dev(inp["beta"])
+    # the conv state as a ring (head 0 at the start), as bench.py runs it
+    hd = torch.zeros(N, dtype=torch.int32, device="cuda")
     outs = []
     for i in range(cfg["steps"]):
-        outs.append(gdn.decode_step(xs[i], gs[i], bs[i], S, hq, hv, d, conv_weight=w, conv_state=cs))
+        outs.append(gdn.decode_step(xs[i], gs[i], bs[i], S, hq, hv, d, conv_weight=w, conv_state=cs,
+                                    conv_head=hd))
     torch.cuda.synchronize()
-    seqs = [0, 77, 255]
+    assert bool((hd == cfg["steps"] % (cfg["width"] - 1)).all())
+    seqs = [0, 1, 37, 77, 128, 200, 254, 255]  # spread over the batch, the last included
     o_gpu = torch.stack(outs)[:, seqs].cpu()
     rS, rcs = np64(inp["state"][seqs]), np64(inp["conv_state"][seqs])
     dS = rS.copy()
@@ -87,11 +104,13 @@ def test_qwen35_27b_batched_decode_64_steps():
         od_i, dS, dcs = orc.decode_step(xi, wn, gi, bi, dS, dcs, hq, d, hv, d, round_state_bf16=True)
         ro.append(o_i)
         do.append(od_i)
+    cs_chrono = orc.ring_to_chronological(np64(cs[seqs]), hd[seqs].cpu().numpy())
     e = dict(o=rel_err(o_gpu, np.stack(ro)), state=rel_err(S[seqs].cpu(), rS),
-             conv_state=rel_err(cs[seqs].cpu(), rcs))
+             conv_state=rel_err(cs_chrono, rcs), o_per_seq=rel_err_per(o_gpu, np.stack(ro), 1),
+             state_per_seq=rel_err_per(S[seqs].cpu(), rS, 0))
     diag = dict(o_vs_bf16_oracle=rel_err(o_gpu, np.stack(do)), state_vs_bf16_oracle=rel_err(S[seqs].cpu(), dS))
     report(f"[qwen35_27b_decode] seqs {seqs}", **e, **diag)
-    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+    assert _ok(e)
 
 
 def test_tiny_fp32_layer_every_head():

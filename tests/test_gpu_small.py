@@ -157,13 +157,15 @@ def test_prefill_ragged(io, d, chunk):
     (2048, 8, 40, 128, 64, True, True),  # 64-column split
 ])
 def test_prefill_one_long_sequence_split(T, hq, hv, d, chunk, s0, fin):
-    """One sequence of 32+ chunks whose heads leave most CUs idle: the scan runs
-    the two halves side by side (the second from a zero state and as its own
-    transition) and joins them.  Outputs and final state must match the
-    token-by-token oracle as on the one-pass path."""
+    """One sequence of 32+ chunks whose heads leave most CUs idle.  At chunk
+    16 the scan runs the two halves side by side (the second from a zero
+    state and as its own transition) and joins them; at chunks 32 and 64 the
+    fused kernel runs one chain per column block over every chunk.  Outputs
+    and final state must match the token-by-token oracle either way."""
     q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, "bf16", 90, s0=s0)
-    # the split is in use: its workspace holds the extra states and outputs
-    assert gdn.prefill_workspace_size(dev(q), dev(v), 1, chunk) > gdn.prefill_workspace_size(dev(q), dev(v), 2, chunk)
+    if chunk == 16:
+        # the split is in use: its workspace holds the extra states and outputs
+        assert gdn.prefill_workspace_size(dev(q), dev(v), 1, chunk) > gdn.prefill_workspace_size(dev(q), dev(v), 2, chunk)
     o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0) if s0 else None, chunk=chunk,
                        output_final_state=fin)
     ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0) if s0 else None)
@@ -384,3 +386,20 @@ def test_layer_conv_then_prefill():
     e = dict(o=rel_err(o, ro), state=rel_err(S, rS), conv_state=rel_err(cs_d, rcs))
     report("layer[bf16]", **e)
     assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16 and e["conv_state"] == 0.0
+
+
+@pytest.mark.parametrize("d,chunk", [(128, 64), (128, 32), (64, 64)])
+def test_prefill_many_heads_wider_blocks(d, chunk):
+    """Enough (sequence, V head) units that the fused kernel takes 32-column
+    workgroups instead of 16-column ones: 9 sequences (an empty one, one
+    token, exact and ragged chunks) x 8 V heads over 2 QK heads."""
+    lens = [130, 0, 1, 64, 200, 65, 33, 127, 96]
+    hq, hv = 2, 8
+    T = sum(lens)
+    q, k, v, g, b, S0 = _prefill_case(T, hq, hv, d, "bf16", 140, lens)
+    cu = gdn_inputs.cu_from_lengths(lens)
+    o, S = gdn.prefill(dev(q), dev(k), dev(v), dev(g), dev(b), dev(S0), cu_seqlens=dev(cu), chunk=chunk)
+    ro, rS = orc.gated_delta_rule(np64(q), np64(k), np64(v), np64(g), np64(b), np64(S0), cu_seqlens=cu.numpy())
+    e = dict(o=rel_err(o, ro), state=rel_err(S, rS))
+    report(f"prefill_many_heads[d={d},C={chunk}]", **e)
+    assert e["o"] < TOL_BF16 and e["state"] < TOL_BF16
