@@ -221,6 +221,19 @@ size_t gdn_prefill_workspace_size(const gdn_prefill_args* args);
 
 gdn_status gdn_prefill(const gdn_prefill_args* args, void* stream);
 
+/* gdn_prefill_noalloc -- gdn_prefill that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory (code under
+ * stream capture, serving loops and harnesses that forbid allocation).
+ * Same arguments and results as gdn_prefill, restricted to io_dtype GDN_BF16
+ * at chunk 32 or 64 (the fused kernel; else GDN_ERR_UNSUPPORTED) and n_seqs
+ * <= GDN_NOALLOC_MAX_SEQS (else GDN_ERR_INVALID_ARG); workspace and
+ * workspace_bytes are ignored.  The per-call plan (chunk offsets, scan order,
+ * emitted-state rows) lives in a static device array of about 96 KiB, one per
+ * GPU, held until the process ends and shared by every call on that GPU:
+ * calls that overlap on one GPU (concurrent streams or threads) race. */
+#define GDN_NOALLOC_MAX_SEQS 8192
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args* args, void* stream);
+
 /* ------------------------------------------------------------------------
  * gdn_decode_step -- one new token for each of n_seqs independent sequences.
  *

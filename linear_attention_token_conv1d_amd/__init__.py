@@ -23,7 +23,7 @@ import torch
 
 __all__ = ["conv1d", "prefill", "decode_step", "gdn_layer", "prefill_workspace_size", "lib",
            "prefill_backward", "conv1d_backward", "gdn_layer_backward", "GdnError", "LIB_PATH",
-           "probe_mfma", "probe_copy"]
+           "probe_mfma", "probe_copy", "prefill_noalloc", "NOALLOC_MAX_SEQS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
@@ -110,7 +110,7 @@ def lib():
             raise GdnError(f"{LIB_PATH} is not built; run python -m linear_attention_token_conv1d_amd._build")
         L = ctypes.CDLL(LIB_PATH)
         for name, argt in (("gdn_conv1d", ConvArgs), ("gdn_prefill", PrefillArgs),
-                           ("gdn_decode_step", DecodeArgs), ("gdn_prefill_backward", PrefillBwdArgs),
+                           ("gdn_prefill_noalloc", PrefillArgs), ("gdn_decode_step", DecodeArgs), ("gdn_prefill_backward", PrefillBwdArgs),
                            ("gdn_conv1d_backward", ConvBwdArgs)):
             f = getattr(L, name)
             f.argtypes = [ctypes.POINTER(argt), _c_void_p]
@@ -292,6 +292,29 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk=64, sca
     _check(lib().gdn_prefill(ctypes.byref(a), _stream(q.device)), "gdn_prefill")
     if emit_every > 0:
         return o, final_state, chunk_states
+    return o, final_state
+
+
+NOALLOC_MAX_SEQS = 8192
+
+
+def prefill_noalloc(q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, chunk=64, scale=1.0,
+                    l2norm=True, erase=True, emit_every=0, chunk_states=None, state_idx=None):
+    """gdn_prefill_noalloc: prefill into caller-given outputs (o, final_state
+    or None, chunk_states when emit_every > 0) with no workspace and no
+    allocation inside the call; bf16 io at chunk 32 or 64, at most
+    NOALLOC_MAX_SEQS sequences.  The plan lives in a static per-GPU array:
+    calls that overlap on one GPU race."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _head_view(t, nm)
+    _contig(g, "g", torch.float32)
+    _contig(beta, "beta", torch.float32)
+    cu, N = _cu(cu_seqlens, q.shape[0])
+    given = [t for t in (initial_state, final_state, chunk_states) if t is not None]
+    state_dtype = given[0].dtype if given else torch.float32
+    a = _prefill_args(q, k, v, g, beta, initial_state, final_state, o, cu, N, chunk, scale, l2norm, None, erase,
+                      emit_every, chunk_states, state_idx, state_dtype)
+    _check(lib().gdn_prefill_noalloc(ctypes.byref(a), _stream(q.device)), "gdn_prefill_noalloc")
     return o, final_state
 
 

@@ -69,7 +69,7 @@ int32_t* conv_head_of(const gdn_decode_args* a) {
   return a->struct_size >= sizeof(gdn_decode_args) ? a->conv_head : nullptr;
 }
 
-gdn_status check_prefill(const gdn_prefill_args* a) {
+gdn_status check_prefill(const gdn_prefill_args* a, bool workspace = true) {
   if (!a) return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: args is NULL");
   if (a->struct_size < offsetof(gdn_prefill_args, state_dtype))
     return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: struct_size %u < %zu", a->struct_size,
@@ -117,6 +117,7 @@ gdn_status check_prefill(const gdn_prefill_args* a) {
     return fail(GDN_ERR_INVALID_ARG, "gdn_prefill: chunk_states is required when emit_every > 0");
   if (!aligned(a->chunk_states, 16) || !aligned(a->state_idx, 4))
     return fail(GDN_ERR_ALIGNMENT, "gdn_prefill: chunk_states must be 16-byte, state_idx 4-byte aligned");
+  if (!workspace) return GDN_OK;
   const size_t need = gdn::prefill_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_v,
                                                    a->d_k, a->chunk, a->emit_every);
   if (need && (!a->workspace || a->workspace_bytes < need))
@@ -298,18 +299,42 @@ size_t gdn_prefill_workspace_size(const gdn_prefill_args* a) {
                                       a->emit_every > 0 ? a->emit_every : 0);
 }
 
+static_assert(GDN_NOALLOC_MAX_SEQS == gdn::kNoAllocMaxSeqs, "static plan size");
+
+namespace {
+gdn::PrefillParams prefill_params(const gdn_prefill_args* a) {
+  return gdn::PrefillParams{a->q, a->k, a->v, a->q_stride, a->k_stride, a->v_stride,
+                            a->g, a->beta, a->initial_state, a->final_state, a->o, a->cu_seqlens,
+                            a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
+                            (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale, a->workspace,
+                            a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->emit_every,
+                            a->chunk_states, a->state_idx, prefill_state_dtype(a) == GDN_BF16 ? 1 : 0};
+}
+}  // namespace
+
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args* a, void* stream) {
+  try {
+    gdn_status st = check_prefill(a, false);
+    if (st != GDN_OK) return st;
+    if (a->io_dtype != GDN_BF16 || (a->chunk != 32 && a->chunk != 64))
+      return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_noalloc: bf16 io at chunk 32 or 64 required (got io_dtype %d, "
+                  "chunk %d)", a->io_dtype, a->chunk);
+    if (a->n_seqs > GDN_NOALLOC_MAX_SEQS)
+      return fail(GDN_ERR_INVALID_ARG, "gdn_prefill_noalloc: n_seqs %d exceeds the static plan's %d sequences",
+                  a->n_seqs, GDN_NOALLOC_MAX_SEQS);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_prefill_noalloc(prefill_params(a), a->d_k, s), s, "gdn_prefill_noalloc");
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "gdn_prefill_noalloc: internal error");
+  }
+}
+
 gdn_status gdn_prefill(const gdn_prefill_args* a, void* stream) {
   try {
     gdn_status st = check_prefill(a);
     if (st != GDN_OK) return st;
-    gdn::PrefillParams p{a->q, a->k, a->v, a->q_stride, a->k_stride, a->v_stride,
-                         a->g, a->beta, a->initial_state, a->final_state, a->o, a->cu_seqlens,
-                         a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->chunk,
-                         (a->flags & GDN_FLAG_L2NORM_QK) ? 1 : 0, a->scale, a->workspace,
-                         a->workspace_bytes, (a->flags & GDN_FLAG_NO_ERASE) ? 0 : 1, a->emit_every,
-                         a->chunk_states, a->state_idx, prefill_state_dtype(a) == GDN_BF16 ? 1 : 0};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return finish(gdn::launch_prefill(p, a->io_dtype, a->d_k, s), s, "gdn_prefill");
+    return finish(gdn::launch_prefill(prefill_params(a), a->io_dtype, a->d_k, s), s, "gdn_prefill");
   } catch (...) {
     return fail(GDN_ERR_HIP, "gdn_prefill: internal error");
   }

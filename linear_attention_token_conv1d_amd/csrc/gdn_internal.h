@@ -81,6 +81,10 @@ size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, i
                                int emit_every);
 bool prefill_supported(int io_dtype, int d, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream);
+// bf16 io at chunk 32 or 64 with n_seqs <= kNoAllocMaxSeqs: the fused kernel
+// with its plan arrays in a static per-device array (p.workspace ignored)
+constexpr int kNoAllocMaxSeqs = 8192;
+hipError_t launch_prefill_noalloc(const PrefillParams& p, int d, hipStream_t stream);
 
 struct PrefillBwdParams {
   const void* q;

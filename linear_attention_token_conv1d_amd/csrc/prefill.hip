@@ -40,6 +40,7 @@
 //        adds S_m w_t to the second segment's outputs and forms the final
 //        state.
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -202,7 +203,7 @@ struct Rec {
 
 // [chunk offsets: n_seqs+1 int32 | scan order: n_seqs int32 | rows of the
 //  emitted chunk-boundary states: n_seqs+1 int32], padded to 256 B
-__host__ __device__ inline size_t off_bytes(int n_seqs) { return (((size_t)n_seqs * 3 + 2) * 4 + 255) / 256 * 256; }
+__host__ __device__ constexpr size_t off_bytes(int n_seqs) { return (((size_t)n_seqs * 3 + 2) * 4 + 255) / 256 * 256; }
 
 __host__ __device__ inline int64_t max_chunks(int64_t T, int n_seqs, int C) { return T / C + n_seqs; }
 
@@ -3023,6 +3024,37 @@ size_t rec_c(int chunk) {
   return chunk == 16 ? Rec<T, 16>::bytes : chunk == 32 ? Rec<T, 32>::bytes : Rec<T, 64>::bytes;
 }
 
+// ------------------------------------------------- calls without allocation
+// The plan arrays of the fused kernel in a file-scope device array instead of
+// a caller's workspace, for gdn_prefill_noalloc.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code the array's
+// name is a host-side stand-in, not a device address: its address on each
+// device comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address reaches kernels.  Every call on a
+// GPU shares its copy, so calls that overlap on one GPU race; the plan
+// kernel writes every entry a call reads, so nothing needs clearing.
+static __device__ __align__(256) unsigned char scratch[off_bytes(kNoAllocMaxSeqs)];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_v, int d, int chunk,
@@ -3042,6 +3074,17 @@ bool prefill_supported(int io_dtype, int d, int chunk) {
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int d, hipStream_t stream) {
   if (io_dtype == 1) return d == 128 ? launch_c<__bf16, 128>(p, stream) : launch_c<__bf16, 64>(p, stream);
   return d == 128 ? launch_c<float, 128>(p, stream) : launch_c<float, 64>(p, stream);
+}
+
+hipError_t launch_prefill_noalloc(const PrefillParams& p0, int d, hipStream_t stream) {
+  PrefillParams p = p0;
+  void* ptr = nullptr;
+  const hipError_t e = scratch_address(&ptr);
+  if (e != hipSuccess) return e;
+  p.workspace = ptr;
+  p.workspace_bytes = sizeof(scratch);
+  if (d == 128) return p.chunk == 32 ? launch_fused<128, 32>(p, stream) : launch_fused<128, 64>(p, stream);
+  return p.chunk == 32 ? launch_fused<64, 32>(p, stream) : launch_fused<64, 64>(p, stream);
 }
 
 }  // namespace gdn

@@ -129,6 +129,27 @@ def test_conv_and_decode_validation():
     assert L.gdn_decode_step(ctypes.byref(d), None) == 1
 
 
+def test_prefill_noalloc_validation():
+    """gdn_prefill_noalloc checks its arguments like gdn_prefill (without the
+    workspace) and rejects what the fused kernel and its static plan cannot
+    take, before touching a GPU."""
+    L = gdn.lib()
+
+    def call(**kw):
+        base = dict(struct_size=ctypes.sizeof(gdn.PrefillArgs), io_dtype=1, n_seqs=1, total_tokens=64,
+                    h_qk=2, h_v=6, d_k=128, d_v=128, chunk=64, scale=1.0, q=0x1000, k=0x2000, v=0x3000,
+                    q_stride=256, k_stride=256, v_stride=768, g=0x4000, beta=0x5000, o=0x6000)
+        base.update(kw)
+        a = gdn.PrefillArgs(**base)
+        return L.gdn_prefill_noalloc(ctypes.byref(a), None), L.gdn_last_error().decode()
+
+    assert call(io_dtype=0)[0] == 2 and "bf16" in call(io_dtype=0)[1]
+    assert call(chunk=16)[0] == 2
+    st, msg = call(n_seqs=gdn.NOALLOC_MAX_SEQS + 1, cu_seqlens=0x8000)
+    assert st == 1 and "static plan" in msg
+    assert call(h_v=5)[0] == 1 and call(q=0x1001)[0] == 3 and call(emit_every=2)[0] == 1
+
+
 def test_prefill_requires_workspace():
     st, msg = _prefill()
     assert st == 4 and "workspace" in msg
