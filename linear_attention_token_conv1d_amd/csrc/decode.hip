@@ -35,14 +35,41 @@ constexpr int kConvBatch = 4;  // conv channels per thread whose loads issue tog
 template <int D>
 constexpr int kUnroll = GDN_DECODE_UNROLL * 16 <= D ? GDN_DECODE_UNROLL : D / 16;
 
-// State rows are read and written once per step: streaming accesses.
-template <int EPL, typename T>
-__device__ __forceinline__ void load_row(const T* p, float (&v)[EPL]) {
-  if constexpr (EPL == 8) load8_stream(p, v); else load4_stream(p, v);
+// State rows are read and written once per step: streaming accesses.  A
+// row is PE-element pieces (16 bytes, or the lane's whole share when that is
+// less), and the 16 lanes of a row take consecutive pieces: lane sub holds
+// pieces j * 16 + sub (j < EPL / PE), so every load and store instruction
+// covers one contiguous span.  Element e of the lane is d_k index
+// elem_d(sub, e).
+template <typename T, int EPL>
+constexpr int kPE = 16 / (int)sizeof(T) < EPL ? 16 / (int)sizeof(T) : EPL;
+template <typename T, int EPL>
+__device__ __forceinline__ int elem_d(int sub, int e) {
+  constexpr int PE = kPE<T, EPL>;
+  return ((e / PE) * 16 + sub) * PE + e % PE;
 }
 template <int EPL, typename T>
-__device__ __forceinline__ void store_row(T* p, const float (&v)[EPL]) {
-  if constexpr (EPL == 8) store8_stream(p, v); else store4_stream(p, v);
+__device__ __forceinline__ void load_row(const T* row, int sub, float (&v)[EPL]) {
+  constexpr int PE = kPE<T, EPL>;
+  static_assert(PE == 8 || PE == 4, "8- or 4-element pieces");
+#pragma unroll
+  for (int j = 0; j < EPL / PE; ++j) {
+    float w[PE];
+    if constexpr (PE == 8) load8_stream(row + (j * 16 + sub) * PE, w); else load4_stream(row + (j * 16 + sub) * PE, w);
+#pragma unroll
+    for (int i = 0; i < PE; ++i) v[j * PE + i] = w[i];
+  }
+}
+template <int EPL, typename T>
+__device__ __forceinline__ void store_row(T* row, int sub, const float (&v)[EPL]) {
+  constexpr int PE = kPE<T, EPL>;
+#pragma unroll
+  for (int j = 0; j < EPL / PE; ++j) {
+    float w[PE];
+#pragma unroll
+    for (int i = 0; i < PE; ++i) w[i] = v[j * PE + i];
+    if constexpr (PE == 8) store8_stream(row + (j * 16 + sub) * PE, w); else store4_stream(row + (j * 16 + sub) * PE, w);
+  }
 }
 
 template <typename IoT, typename StT, int D>
@@ -76,11 +103,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int sub = lane & 15;
   // state and conv-state slot of sequence n
   const int64_t slot = p.state_idx ? as_const(p.state_idx)[n] : n;
-  StT* S = reinterpret_cast<StT*>(p.state) + (slot * p.h_v + (int64_t)hq * grp) * D * D + sub * EPL;
+  StT* S = reinterpret_cast<StT*>(p.state) + (slot * p.h_v + (int64_t)hq * grp) * D * D;
   int rb = wave * 4 + (lane >> 4);
   float sv[U][EPL];
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * u) * D, sv[u]);
+  for (int u = 0; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * u) * D, sub, sv[u]);
 
   // ---- 1. conv step + activation over this workgroup's channels.  A thread
   // handles up to kConvBatch channels at a time and issues every load of the
@@ -191,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   float kf[EPL], qf[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    kf[e] = s_k[sub * EPL + e] * rk;
-    qf[e] = s_q[sub * EPL + e] * rq;
+    kf[e] = s_k[elem_d<StT, EPL>(sub, e)] * rk;
+    qf[e] = s_q[elem_d<StT, EPL>(sub, e)] * rq;
   }
   auto row_step = [&](int u) {
     const int r = rb + 16 * u;
@@ -207,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     float nv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) nv[e] = al * sv[u][e] + dl * kf[e];
-    store_row<EPL>(S + (int64_t)r * D, nv);
+    store_row<EPL>(S + (int64_t)r * D, sub, nv);
     if (sub == 0) s_o[r] = p.scale * (al * b + dl * kq);
   };
   // The row groups of a pass are processed in two halves; once a half is
@@ -224,11 +251,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       break;
     }
 #pragma unroll
-    for (int u = 0; u < H; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sv[u]);
+    for (int u = 0; u < H; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sub, sv[u]);
 #pragma unroll
     for (int u = H; u < U; ++u) row_step(u);
 #pragma unroll
-    for (int u = H; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sv[u]);
+    for (int u = H; u < U; ++u) load_row<EPL>(S + (int64_t)(rb + 16 * U + 16 * u) * D, sub, sv[u]);
     rb += 16 * U;
   }
   __syncthreads();

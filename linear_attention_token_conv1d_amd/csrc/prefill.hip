@@ -2489,42 +2489,61 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<__bf16*>(tb + SC::off(16 * bi + 4 * g4 + i, (16 * bj + l16) * 2)) = (__bf16)(t[i] * bc);
     };
-    // T_{2b+1, 2b}
-    auto level1 = [&](int bb) __attribute__((always_inline)) {
+    // Every operand is read before the first product (one LDS round trip);
+    // the blocks are written after the last.
+    // T_{i+1, i} = -T_{i+1, i+1} A_{i+1, i} T_ii
+    auto level1 = [&](const frag& a, const f32x4& tii, const frag& tnext) __attribute__((always_inline)) {
       f32x4 x = zero, l = zero;
-      M::mma(x, rowf(2 * bb + 1, 2 * bb, -1, true), M::acc(colb(2 * bb, 2 * bb), zero), false);
-      M::mma(l, rowf(2 * bb + 1, 2 * bb + 1, -1, false), M::acc(x, zero), false);
+      M::mma(x, a, M::acc(tii, zero), false);
+      M::mma(l, tnext, M::acc(x, zero), false);
       return -l;
     };
-    // T_2j, T_3j from X_2j, X_3j
-    auto lower_pair = [&](int jb, f32x4 x2, f32x4 x3) __attribute__((always_inline)) {
-      f32x4 t2 = zero, t3 = zero;
-      M::mma(t2, rowf(2, 2, -1, false), M::acc(x2, zero), false);
+    // T_2j = -T_22 X_2j,  T_3j = -T_33 (X_3j + A_32 T_2j)
+    auto lower_pair = [&](const frag& t22, const frag& a32, const frag& t33, const f32x4& x2, f32x4 x3,
+                          f32x4& t2, f32x4& t3) __attribute__((always_inline)) {
+      t2 = zero;
+      t3 = zero;
+      M::mma(t2, t22, M::acc(x2, zero), false);
       t2 = -t2;
-      put_tb(2, jb, t2);
-      M::mma(x3, rowf(3, 2, -1, true), M::acc(t2, zero), false);
-      M::mma(t3, rowf(3, 3, -1, false), M::acc(x3, zero), false);
-      put_tb(3, jb, -t3);
+      M::mma(x3, a32, M::acc(t2, zero), false);
+      M::mma(t3, t33, M::acc(x3, zero), false);
+      t3 = -t3;
     };
     if constexpr (NT == 2) {
-      if (pi == 1) put_tb(1, 0, level1(0));
+      if (pi == 1) {
+        const frag a10 = rowf(1, 0, -1, true), t11 = rowf(1, 1, -1, false);
+        const f32x4 t00 = colb(0, 0);
+        put_tb(1, 0, level1(a10, t00, t11));
+      }
     } else {
       if (pi == 1) {
-        put_tb(3, 2, level1(1));
+        const frag a32 = rowf(3, 2, -1, true), t33 = rowf(3, 3, -1, false);
+        const f32x4 t22 = colb(2, 2);
+        put_tb(3, 2, level1(a32, t22, t33));
       } else if (pi == 2) {
-        const f32x4 t10 = level1(0);
+        const frag a10 = rowf(1, 0, -1, true), t11 = rowf(1, 1, -1, false);
+        const frag a2 = rowf(2, 0, 1, true), a3 = rowf(3, 0, 1, true);
+        const frag t22 = rowf(2, 2, -1, false), a32 = rowf(3, 2, -1, true), t33 = rowf(3, 3, -1, false);
+        const f32x4 t00 = colb(0, 0);
+        const f32x4 t10 = level1(a10, t00, t11);
+        const frag bt = M::acc(t00, t10);
+        f32x4 x2 = zero, x3 = zero, t2, t3;
+        M::mma(x2, a2, bt, false);
+        M::mma(x3, a3, bt, false);
+        lower_pair(t22, a32, t33, x2, x3, t2, t3);
         put_tb(1, 0, t10);
-        const frag bt = M::acc(colb(0, 0), t10);
-        f32x4 x2 = zero, x3 = zero;
-        M::mma(x2, rowf(2, 0, 1, true), bt, false);
-        M::mma(x3, rowf(3, 0, 1, true), bt, false);
-        lower_pair(0, x2, x3);
+        put_tb(2, 0, t2);
+        put_tb(3, 0, t3);
       } else if (pi == 3) {
+        const frag a2 = rowf(2, 1, -1, true), a3 = rowf(3, 1, -1, true);
+        const frag t22 = rowf(2, 2, -1, false), a32 = rowf(3, 2, -1, true), t33 = rowf(3, 3, -1, false);
         const frag bt = M::acc(colb(1, 1), zero);
-        f32x4 x2 = zero, x3 = zero;
-        M::mma(x2, rowf(2, 1, -1, true), bt, false);
-        M::mma(x3, rowf(3, 1, -1, true), bt, false);
-        lower_pair(1, x2, x3);
+        f32x4 x2 = zero, x3 = zero, t2, t3;
+        M::mma(x2, a2, bt, false);
+        M::mma(x3, a3, bt, false);
+        lower_pair(t22, a32, t33, x2, x3, t2, t3);
+        put_tb(2, 1, t2);
+        put_tb(3, 1, t3);
       }
     }
     // row scalars: gamma rk (0 without the erase: R = V), gamma, e rk,

@@ -4,9 +4,10 @@
 //  mfma_probe_kernel  back-to-back independent bf16 MFMAs (16x16x32, eight
 //                     accumulators per wave, eight waves per SIMD): the
 //                     dense bf16 matrix rate the chip sustains.
-//  copy_probe_kernel  a streaming device copy, 16 bytes per lane with
-//                     non-temporal loads and stores: the HBM rate a plain
-//                     read-once / write-once stream sustains.
+//  copy_probe_kernel  a streaming device copy, 16 bytes per lane and step
+//                     with non-temporal loads and stores, the whole copy in
+//                     flight at once: the HBM rate a plain read-once /
+//                     write-once stream sustains.
 #include "../../include/gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -41,21 +42,19 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) 
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// One 16-byte piece per lane and step, 8 steps per lane, all loads issued
+// before the first store; a grid of n16 / 2048 workgroups puts the whole copy
+// in flight at once (no grid-stride loop whose iterations wait on each other).
+constexpr int kCopyPieces = 8;
 __global__ __launch_bounds__(256) void copy_probe_kernel(const gdn_u4* src, gdn_u4* dst, size_t n16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four independent 16-byte loads in flight per lane
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const gdn_u4 v0 = __builtin_nontemporal_load(src + i);
-    const gdn_u4 v1 = __builtin_nontemporal_load(src + i + stride);
-    const gdn_u4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const gdn_u4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    __builtin_nontemporal_store(v0, dst + i);
-    __builtin_nontemporal_store(v1, dst + i + stride);
-    __builtin_nontemporal_store(v2, dst + i + 2 * stride);
-    __builtin_nontemporal_store(v3, dst + i + 3 * stride);
-  }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const size_t base = (size_t)blockIdx.x * 256 * kCopyPieces + threadIdx.x;
+  gdn_u4 v[kCopyPieces];
+#pragma unroll
+  for (int j = 0; j < kCopyPieces; ++j)
+    if (base + (size_t)j * 256 < n16) v[j] = __builtin_nontemporal_load(src + base + (size_t)j * 256);
+#pragma unroll
+  for (int j = 0; j < kCopyPieces; ++j)
+    if (base + (size_t)j * 256 < n16) __builtin_nontemporal_store(v[j], dst + base + (size_t)j * 256);
 }
 
 }  // namespace
@@ -81,8 +80,11 @@ gdn_status gdn_probe_copy(const void* src, void* dst, size_t bytes, void* stream
   char* d = static_cast<char*>(dst);
   if (s < d + bytes && d < s + bytes) return GDN_ERR_INVALID_ARG;
   if (bytes == 0) return GDN_OK;
-  hipLaunchKernelGGL(gdn::copy_probe_kernel, dim3(2048), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const gdn::gdn_u4*>(src), static_cast<gdn::gdn_u4*>(dst), bytes / 16);
+  const size_t n16 = bytes / 16, per = (size_t)256 * gdn::kCopyPieces;
+  const size_t grid = (n16 + per - 1) / per;
+  if (grid > 0x7fffffff) return GDN_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(gdn::copy_probe_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const gdn::gdn_u4*>(src), static_cast<gdn::gdn_u4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
