@@ -27,6 +27,8 @@
 // way), one fused kernel per (chunk, V head) for every chunk-local gradient,
 // and a per-token kernel for the QK-head sums and the L2-norm backward.
 // Every array passed between stages is an fp32 workspace array.
+#include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -1695,13 +1697,120 @@ hipError_t conv_backward_impl(const ConvBwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- windows
+// The workspace above holds every chunk of the call (2.6 GB for the 9B
+// layer, 27 GB for the 27B one).  For one sequence whose workspace would pass
+// kBwdBudget the call runs in windows of wt tokens (a multiple of the chunk):
+//   1. a forward pass over the windows in order (gdn_prefill's own kernels,
+//      o into scratch) leaves the state at every window start;
+//   2. the backward above runs on each window from the last to the first,
+//      starting from that window's state, with the state gradient of the
+//      window after it as its final-state gradient; the initial-state
+//      gradient it returns is the next (earlier) window's.
+// Every token's gradients come from one window, so nothing is accumulated.
+// The workspace then holds one window's backward, the forward's workspace
+// and o for one window, the window-start states and two state gradients.
+constexpr size_t kBwdBudgetDefault = (size_t)2 << 30;
+
+size_t bwd_budget() {
+  const char* e = std::getenv("GDN_BWD_BUDGET_MB");  // tuning and tests: a smaller budget
+  const long long mb = e ? std::atoll(e) : 0;
+  return mb > 0 ? (size_t)mb << 20 : kBwdBudgetDefault;
+}
+
+struct BwdWindows {
+  bool on;
+  int64_t wt;
+  int nwin;
+  size_t o_fwd, o_o, o_ck, o_cy, total;
+};
+
+BwdWindows bwd_windows(int io_dtype, int64_t T, int n_seqs, int h_qk, int h_v, int D, int C) {
+  BwdWindows w{false, T, 1, 0, 0, 0, 0, bwd_sizes(T, n_seqs, h_qk, h_v, D, C).total};
+  const size_t budget = bwd_budget();
+  if (n_seqs != 1 || w.total <= budget || T <= C) return w;
+  const size_t hs = (size_t)h_v * D * D * 4, es = io_dtype == 1 ? 2 : 4;
+  auto layout = [&](int64_t wt) {
+    BwdWindows x{true, wt, (int)((T + wt - 1) / wt), 0, 0, 0, 0, 0};
+    x.o_fwd = bwd_sizes(wt, 1, h_qk, h_v, D, C).total;
+    x.o_o = x.o_fwd + a256(prefill_workspace_bytes(io_dtype, wt, 1, h_v, D, C, 0));
+    x.o_ck = x.o_o + a256((size_t)wt * h_v * D * es);
+    x.o_cy = x.o_ck + a256((size_t)x.nwin * hs);
+    x.total = x.o_cy + 2 * a256(hs);
+    return x;
+  };
+  int64_t wt = (T + C - 1) / C * C;
+  BwdWindows x = layout(wt);
+  while (x.total > budget && wt > C) {
+    wt = ((wt / 2) + C - 1) / C * C;
+    x = layout(wt);
+  }
+  return x;
+}
+
+template <typename T>
+hipError_t prefill_backward_windows(const PrefillBwdParams& p, int D, const BwdWindows& bw, hipStream_t stream) {
+  unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+  const size_t hs = (size_t)p.h_v * D * D;
+  float* ck = reinterpret_cast<float*>(ws + bw.o_ck);  // [nwin][h_v][D][D]: state at each window start
+  float* cy[2] = {reinterpret_cast<float*>(ws + bw.o_cy), reinterpret_cast<float*>(ws + bw.o_cy + a256(hs * 4))};
+  const int64_t ntok = p.total_tokens;
+  auto span = [&](int w, int64_t& t0, int64_t& n) {
+    t0 = (int64_t)w * bw.wt;
+    n = std::min(bw.wt, ntok - t0);
+  };
+  // 1. forward over the windows in order: the state at every window start
+  for (int w = 0; w + 1 < bw.nwin; ++w) {
+    int64_t t0, n;
+    span(w, t0, n);
+    PrefillParams f{static_cast<const T*>(p.q) + t0 * p.q_stride, static_cast<const T*>(p.k) + t0 * p.k_stride,
+                    static_cast<const T*>(p.v) + t0 * p.v_stride, p.q_stride, p.k_stride, p.v_stride,
+                    p.g + t0 * p.h_v, p.beta + t0 * p.h_v,
+                    w == 0 ? static_cast<const void*>(p.initial_state) : static_cast<const void*>(ck + w * hs),
+                    ck + (w + 1) * hs, ws + bw.o_o, nullptr, n, 1, p.h_qk, p.h_v, p.chunk, p.l2norm, p.scale,
+                    ws + bw.o_fwd, bw.o_o - bw.o_fwd, p.erase, 0, nullptr, nullptr, 0};
+    const hipError_t e = launch_prefill(f, std::is_same<T, __bf16>::value ? 1 : 0, D, stream);
+    if (e != hipSuccess) return e;
+  }
+  // 2. the backward of each window, last to first
+  for (int w = bw.nwin - 1; w >= 0; --w) {
+    int64_t t0, n;
+    span(w, t0, n);
+    PrefillBwdParams b = p;
+    b.q = static_cast<const T*>(p.q) + t0 * p.q_stride;
+    b.k = static_cast<const T*>(p.k) + t0 * p.k_stride;
+    b.v = static_cast<const T*>(p.v) + t0 * p.v_stride;
+    b.g = p.g + t0 * p.h_v;
+    b.beta = p.beta + t0 * p.h_v;
+    b.initial_state = w == 0 ? p.initial_state : ck + w * hs;
+    b.d_o = static_cast<const T*>(p.d_o) + t0 * p.h_v * D;
+    b.d_final_state = w == bw.nwin - 1 ? p.d_final_state : cy[(w + 1) & 1];
+    b.dq = static_cast<T*>(p.dq) + t0 * p.dq_stride;
+    b.dk = static_cast<T*>(p.dk) + t0 * p.dk_stride;
+    b.dv = static_cast<T*>(p.dv) + t0 * p.dv_stride;
+    b.dg = p.dg + t0 * p.h_v;
+    b.dbeta = p.dbeta + t0 * p.h_v;
+    b.d_initial_state = w == 0 ? p.d_initial_state : cy[w & 1];
+    b.total_tokens = n;
+    b.workspace = ws;
+    const hipError_t e = prefill_backward_impl<T>(b, D, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
-size_t prefill_backward_workspace_bytes(int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d, int chunk) {
-  return bwd_sizes(total_tokens, n_seqs, h_qk, h_v, d, chunk).total;
+size_t prefill_backward_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d,
+                                        int chunk) {
+  return bwd_windows(io_dtype, total_tokens, n_seqs, h_qk, h_v, d, chunk).total;
 }
 
 hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int d, hipStream_t stream) {
+  const BwdWindows bw = bwd_windows(io_dtype, p.total_tokens, p.n_seqs, p.h_qk, p.h_v, d, p.chunk);
+  if (bw.on)
+    return io_dtype == 1 ? prefill_backward_windows<__bf16>(p, d, bw, stream)
+                         : prefill_backward_windows<float>(p, d, bw, stream);
   return io_dtype == 1 ? prefill_backward_impl<__bf16>(p, d, stream) : prefill_backward_impl<float>(p, d, stream);
 }
 

@@ -178,7 +178,8 @@ gdn_status check_prefill_backward(const gdn_prefill_backward_args* a) {
   for (const R& o : outs)
     for (const R& i : ins)
       if (overlaps(o.p, o.n, i.p, i.n)) return fail(GDN_ERR_INVALID_ARG, "%s: an output overlaps an input", f);
-  const size_t need = gdn::prefill_backward_workspace_bytes(a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->d_k,
+  const size_t need = gdn::prefill_backward_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_qk,
+                                                            a->h_v, a->d_k,
                                                             a->chunk);
   if (!a->workspace || a->workspace_bytes < need)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes required", f, need);
@@ -393,7 +394,8 @@ size_t gdn_prefill_backward_workspace_size(const gdn_prefill_backward_args* a) {
       a->h_qk < 1 || a->h_v < 1 || a->h_v % a->h_qk || a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128) ||
       (a->chunk != 16 && a->chunk != 32 && a->chunk != 64))
     return 0;
-  return gdn::prefill_backward_workspace_bytes(a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->d_k, a->chunk);
+  return gdn::prefill_backward_workspace_bytes(a->io_dtype, a->total_tokens, a->n_seqs, a->h_qk, a->h_v, a->d_k,
+                                               a->chunk);
 }
 
 gdn_status gdn_prefill_backward(const gdn_prefill_backward_args* a, void* stream) {

@@ -118,7 +118,11 @@ struct PrefillBwdParams {
   float scale;
   void* workspace;
 };
-size_t prefill_backward_workspace_bytes(int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d, int chunk);
+// Workspace of gdn_prefill_backward: every chunk's intermediates, or, for one
+// sequence past the budget (2 GiB; GDN_BWD_BUDGET_MB), one window's plus the
+// window-start states
+size_t prefill_backward_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d,
+                                        int chunk);
 hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int d, hipStream_t stream);
 
 struct ConvBwdParams {

@@ -80,6 +80,27 @@ def test_prefill_backward_erase_off(io, h_qk, h_v):
     _run_and_compare([150, 7], h_qk, h_v, 64, io, 64, erase=False, seed=20)
 
 
+@pytest.mark.parametrize("io,d,chunk,T,h_qk,h_v,mb,opt", [
+    ("bf16", 128, 64, 1000, 2, 4, 13, True),   # 4 windows of 256 tokens, the last ragged
+    ("f32", 64, 32, 611, 2, 2, 4, True),       # fp32, chunk 32
+    ("bf16", 64, 64, 777, 1, 3, 8, False),     # grouped heads, no initial state or final-state gradient
+])
+def test_prefill_backward_in_windows(monkeypatch, io, d, chunk, T, h_qk, h_v, mb, opt):
+    """One sequence whose workspace passes the budget runs in windows: a
+    forward pass for the window-start states, then each window's backward from
+    the last to the first with the state gradient carried between them.  A
+    small budget (GDN_BWD_BUDGET_MB) forces several windows here; the results
+    must meet the same bar against the oracle as the whole-call backward."""
+    monkeypatch.setenv("GDN_BWD_BUDGET_MB", str(mb))
+    q = torch.empty((T, h_qk, d), dtype=DT[io])
+    v = torch.empty((T, h_v, d), dtype=DT[io])
+    monkeypatch.delenv("GDN_BWD_BUDGET_MB")
+    full = gdn.prefill_backward_workspace_size(q, v, 1, chunk)
+    monkeypatch.setenv("GDN_BWD_BUDGET_MB", str(mb))
+    assert gdn.prefill_backward_workspace_size(q, v, 1, chunk) < full
+    _run_and_compare([T], h_qk, h_v, d, io, chunk, s0=opt, dsf=opt, seed=90)
+
+
 def test_prefill_backward_without_l2_norm_and_scale():
     """Raw (unnormalised) small keys keep the recurrence bounded without the norm."""
     lens, h, d = [90], 2, 64
@@ -241,7 +262,8 @@ def test_prefill_backward_9b_size_sampled_heads():
 
 def test_prefill_backward_27b_size_sampled_group():
     """The 27B-shaped layer at full length (T = 65,536, 16 QK / 48 V heads,
-    1,024 chunks in one chain, a non-zero initial state) through conv + split,
+    1,024 chunks, a non-zero initial state; the backward runs in windows under
+    the default 2 GiB workspace budget) through conv + split,
     then prefill_backward with a final-state gradient; the oracle checks QK
     head groups 0 and 15 (V heads 0-2 and 45-47: the first and the last group,
     which the workgroup placement puts on different XCDs), whose gradients
