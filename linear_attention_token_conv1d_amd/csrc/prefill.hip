@@ -2096,10 +2096,11 @@ __device__ __forceinline__ void subst16(float (&t)[16], const float (&nn)[16]) {
                : "v"(nn[15]), "v"(t[14]));
 }
 
-template <int D, int C, int NC, int CT>
+template <int D, int C, int NC, int CT, bool W>
 struct FusedLayout {
   static constexpr int NT = C / 16, DT = D / 16;
   static constexpr int cols = 16 * NC * CT;
+  static_assert(!W || (cols == D && CT == 2), "a wide workgroup holds every d_v column, 32 per chain wave");
   static constexpr int RBK = D * 2, RBC = C * 2, RBV = cols * 2, RBS = D * 2, RBU = C * 2;
   using SK = Swz<RBK>;
   using SC = Swz<RBC>;
@@ -2116,8 +2117,10 @@ struct FusedLayout {
   static constexpr int pTb = 0, pP = C * RBC, pVec = 2 * C * RBC;
   static constexpr int prep = pVec + 4 * NVEC * C;
   static constexpr int LDF = C + 4;  // fp32 A / T rows
-  static constexpr int bytes = 2 * raw + 2 * prep + C * LDF * 4 + cols * RBS + cols * RBU;
-  static constexpr int threads = 64 * (2 * NC + 4);
+  // the published state and U: only where separate output waves read them
+  static constexpr int sbytes = W ? 16 : cols * RBS, ubytes = W ? 16 : cols * RBU;
+  static constexpr int bytes = 2 * raw + 2 * prep + C * LDF * 4 + sbytes + ubytes;
+  static constexpr int threads = 64 * (W ? NC + 4 : 2 * NC + 4);
   static_assert(NT == 2 || NT == 4, "chunks of 32 or 64 tokens");
 };
 
@@ -2135,9 +2138,9 @@ constexpr TilePair pair_at(int pw, int i) {
        : pw == 2 ? (i == 0 ? TilePair{3, 0} : TilePair{3, 1})
                  : (i == 0 ? TilePair{2, 1} : TilePair{3, 2});
 }
-template <int D, int C, int NC, int CT>
-__global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams p, const unsigned char* ws) {
-  using L = FusedLayout<D, C, NC, CT>;
+template <int D, int C, int NC, int CT, bool W>
+__global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(PrefillParams p, const unsigned char* ws) {
+  using L = FusedLayout<D, C, NC, CT, W>;
   using T = __bf16;
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -2153,8 +2156,8 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
   __shared__ __align__(16) unsigned char prp0[L::prep];
   __shared__ __align__(16) unsigned char prp1[L::prep];
   __shared__ __align__(16) float sA[C * LDF];
-  __shared__ __align__(16) unsigned char sS[L::cols * L::RBS];
-  __shared__ __align__(16) unsigned char sU[L::cols * L::RBU];
+  __shared__ __align__(16) unsigned char sS[L::sbytes];
+  __shared__ __align__(16) unsigned char sU[L::ubytes];
 
   const PlanView plan = plan_view(p, ws, C);
   const ScanSlot slot = scan_slot(p, plan, NB);
@@ -2179,11 +2182,13 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
   // roles: waves w and w + 4 share a SIMD.  Chain waves come first (one per
   // SIMD), then the output waves, then the four prep waves, numbered so
   // that prep wave 0 (the diagonal solve) sits beside an output wave rather
-  // than a chain wave when the layout allows it.
+  // than a chain wave when the layout allows it.  A wide workgroup has no
+  // output waves: its chain waves form the outputs of their own columns,
+  // and with two chain waves prep waves 0 and 1 have a SIMD each.
   const bool chain = wave < NC;
-  const bool outw = wave >= NC && wave < 2 * NC;
-  const bool prepw = wave >= 2 * NC;
-  const int pi = prepw ? (wave - 2 * NC + (NC == 2 ? 2 : 0)) & 3 : -1;
+  const bool outw = !W && wave >= NC && wave < 2 * NC;
+  const bool prepw = wave >= (W ? NC : 2 * NC);
+  const int pi = !prepw ? -1 : W ? wave - NC : (wave - 2 * NC + (NC == 2 ? 2 : 0)) & 3;
   const int lt = prepw ? pi * 64 + lane : 0;  // loader thread 0..255
 
   // fragment reads of the K, Q tiles (token rows 16 t + l16, d_k 32 s + 8 g
@@ -2213,8 +2218,9 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
   };
   // decay of a lane's four entries (0 where the mask removes them: j > r,
   // or j >= r when strict)
-  auto decay = [&](const float* sc, int mt, int tj, bool strict, float (&w)[4]) __attribute__((always_inline)) {
-    const int r = mt * 16 + l16, j0 = tj * 16 + 4 * g4;
+  // (lx, gx: the lane's l16 and g4, passed where they are formed afresh)
+  auto decay_l = [&](const float* sc, int mt, int tj, bool strict, float (&w)[4], int lx, int gx) __attribute__((always_inline)) {
+    const int r = mt * 16 + lx, j0 = tj * 16 + 4 * gx;
     const float Gr = sc[C + r];
     const float4 Gj = *reinterpret_cast<const float4*>(sc + C + j0);
     const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
@@ -2224,10 +2230,16 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
       w[i] = mt > tj ? x : (strict ? (j0 + i < r ? x : 0.f) : (j0 + i <= r ? x : 0.f));
     }
   };
-  auto put_p = [&](unsigned char* P_s, int mt, int tj, const float (&w)[4], const f32x4& qk) __attribute__((always_inline)) {
-    const int r = mt * 16 + l16, j0 = tj * 16 + 4 * g4;
+  auto decay = [&](const float* sc, int mt, int tj, bool strict, float (&w)[4]) __attribute__((always_inline)) {
+    decay_l(sc, mt, tj, strict, w, l16, g4);
+  };
+  auto put_p_l = [&](unsigned char* P_s, int mt, int tj, const float (&w)[4], const f32x4& qk, int lx, int gx) __attribute__((always_inline)) {
+    const int r = mt * 16 + lx, j0 = tj * 16 + 4 * gx;
     *reinterpret_cast<uint2*>(P_s + SC::off(r, j0 * 2)) =
         make_uint2(pack_bf16x2(w[0] * qk[0], w[1] * qk[1]), pack_bf16x2(w[2] * qk[2], w[3] * qk[3]));
+  };
+  auto put_p = [&](unsigned char* P_s, int mt, int tj, const float (&w)[4], const f32x4& qk) __attribute__((always_inline)) {
+    put_p_l(P_s, mt, tj, w, qk, l16, g4);
   };
 
   // ------------------------------------------------- raw rows (prep waves)
@@ -2298,9 +2310,19 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
       br = p.beta[r * p.h_v + h];
     }
   };
-  // the registers of chunk c into raw buffer b, with beta and G log2(e) (G
-  // the cumulative sum of g; beta = g = 0 past the chunk's end).  Prep wave 1
-  // holds g and beta.
+  // beta and G log2(e) of chunk c into raw buffer b (G the cumulative sum of
+  // g; beta = g = 0 past the chunk's end), from the registers of prep wave 1
+  auto store_sc = [&](int c, unsigned char* b) __attribute__((always_inline)) {
+    const int Lc = chunk_len(c);
+    const float G = wave_prefix_sum(lane < Lc ? gr : 0.f);
+    float* sc = reinterpret_cast<float*>(b + L::rSc);
+    if (lane < C) {
+      sc[lane] = lane < Lc ? br : 0.f;
+      sc[C + lane] = G * kLog2e;
+    }
+  };
+  // the registers of chunk c into raw buffer b, with the scalars.  Prep wave
+  // 1 holds g and beta.
   auto store_raw = [&](int c, unsigned char* b) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NKP; ++i) {
@@ -2312,16 +2334,69 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
 #pragma unroll
     for (int i = 0; i < NVP; ++i)
       if (NLD * (i + 1) <= C * VT || lt + NLD * i < C * VT) *reinterpret_cast<gdn_u4*>(b + L::rV + vso[i]) = vr[i];
-    if (pi == 1) {
-      const int Lc = chunk_len(c);
-      const float G = wave_prefix_sum(lane < Lc ? gr : 0.f);
-      float* sc = reinterpret_cast<float*>(b + L::rSc);
-      if (lane < C) {
-        sc[lane] = lane < Lc ? br : 0.f;
-        sc[C + lane] = G * kLog2e;
-      }
+    if (pi == 1) store_sc(c, b);
+  };
+  // Wide workgroups: the four prep waves copy a chunk's K, Q and V rows
+  // straight into the raw buffer (16 bytes per lane; the lane fetches the
+  // global piece whose swizzled slot is its LDS position), and prep wave 1
+  // loads g and beta into registers.  A full chunk uses per-lane offsets
+  // computed once; a partial one clamps rows past its end to its last row.
+  DmaPlan<SK, C, 4> pk, pq;
+  DmaPlan<SV, C, 4> pv;
+  const int64_t vrow = p.v_stride * 2;
+  const bool dfast = p.q_stride * 2 * C < (1ll << 31) && p.k_stride * 2 * C < (1ll << 31) && vrow * C < (1ll << 31);
+  if (W && prepw && dfast) {
+    pk.init((uint32_t)(p.k_stride * 2), pi, lane);
+    pq.init((uint32_t)(p.q_stride * 2), pi, lane);
+    pv.init((uint32_t)vrow, pi, lane);
+  }
+  auto dma_raw = [&](int c, unsigned char* b) __attribute__((always_inline)) {
+    const int64_t t0 = chunk_t0(c);
+    const int Lc = chunk_len(c);
+    const unsigned char* kc = kg + t0 * p.k_stride * 2;
+    const unsigned char* qc = qg + t0 * p.q_stride * 2;
+    const unsigned char* vc = vg + t0 * vrow;
+    if (dfast && Lc == C) {
+      pk.issue(b + L::rK, kc, pi, lane);
+      pq.issue(b + L::rQ, qc, pi, lane);
+      pv.issue(b + L::rV, vc, pi, lane);
+    } else {
+      dma_tile_s<SK, C, 4>(b + L::rK, kc, p.k_stride * 2, Lc, pi, lane);
+      dma_tile_s<SK, C, 4>(b + L::rQ, qc, p.q_stride * 2, Lc, pi, lane);
+      dma_tile_s<SV, C, 4>(b + L::rV, vc, vrow, Lc, pi, lane);
     }
   };
+  // L2 prefetch for wide workgroups: two 4-byte loads per prep lane touch
+  // every 128-byte line of a chunk's K, Q and V rows and its g and beta
+  // entries, so that the direct-to-LDS copy a step later reads L2 rather
+  // than HBM.  Both loads are issued on every call (a chunk past the end
+  // touches the last chunk again) and stay in flight across B2; the next
+  // call waits for them before reusing their registers.
+  uint32_t tv0 = 0u, tv1 = 0u;
+  auto touch = [&](int c) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(tv0), "v"(tv1));
+    const int cc = min(c, nch - 1);
+    const int64_t t0 = chunk_t0(cc);
+    const int Lc = chunk_len(cc);
+    const int i = lt & 127, half = (i & 1) * 128 < D * 2 ? (i & 1) * 128 : 0;
+    const int64_t r = t0 + min(i >> 1, Lc - 1);
+    const unsigned char* a0 = lt < 128 ? kg + r * p.k_stride * 2 + half : qg + r * p.q_stride * 2 + half;
+    const unsigned char* a1;
+    if (lt < 128) {
+      a1 = vg + r * vrow + half;
+    } else {
+      const int64_t rg = t0 + min(lt & 63, Lc - 1);
+      a1 = reinterpret_cast<const unsigned char*>((lt < 192 ? p.g : p.beta) + rg * p.h_v + h);
+    }
+    tv0 = *reinterpret_cast<const uint32_t*>(a0);
+    tv1 = *reinterpret_cast<const uint32_t*>(a1);
+  };
+  auto load_gb = [&](int c) __attribute__((always_inline)) {  // prep wave 1
+    const int64_t r = chunk_t0(c) + min(lane, chunk_len(c) - 1);
+    gr = p.g[r * p.h_v + h];
+    br = p.beta[r * p.h_v + h];
+  };
+
   // the blocks of Tb and P~ above the diagonal blocks: zero for good
   auto zero_upper = [&](unsigned char* pb) __attribute__((always_inline)) {
     constexpr int NUP = NT * (NT - 1) / 2 * 32;  // 16-byte pieces of one matrix
@@ -2428,18 +2503,38 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
     else if (pi == 2) pairs(b, pb, std::integral_constant<int, 2>{});
     else pairs(b, pb, std::integral_constant<int, 3>{});
   };
-  // output waves: the diagonal tiles of Q K^T (tiles ow, ow + NC, ...)
+  // output waves (chain waves of a wide workgroup): the diagonal tiles of
+  // Q K^T (tiles ow, ow + NC, ...)
   auto prep1_pdiag = [&](const unsigned char* b, unsigned char* pb, int ow) __attribute__((always_inline)) {
     const unsigned char* K_s = b + L::rK;
     const unsigned char* Q_s = b + L::rQ;
     const float* sc = reinterpret_cast<const float*>(b + L::rSc);
+    if constexpr (W) {
+      // chain waves: a loop over the wave's tiles with the tile index known
+      // only at run time, so that their offsets are formed here instead of
+      // being held in registers across the chunk loop
+      int t0 = ow, ln = lane;
+      asm volatile("" : "+s"(t0), "+v"(ln));
+      const int lx = ln & 15, gx = ln >> 4;
+      for (int t = t0; t < NT; t += NC) {
+        f32x4 qk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t % NC != ow) continue;
-      const f32x4 qk = gram(K_s, Q_s, t, t);
-      float w[4];
-      decay(sc, t, t, false, w);
-      put_p(pb + L::pP, t, t, w, qk);
+        for (int s = 0; s < DKS; ++s)
+          M::mma(qk, frag_row_s<T, SK>(K_s, t * 16 + lx, 32 * s + 8 * gx, false),
+                 frag_row_s<T, SK>(Q_s, t * 16 + lx, 32 * s + 8 * gx, false), false);
+        float w[4];
+        decay_l(sc, t, t, false, w, lx, gx);
+        put_p_l(pb + L::pP, t, t, w, qk, lx, gx);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t % NC != ow) continue;
+        const f32x4 qk = gram(K_s, Q_s, t, t);
+        float w[4];
+        decay(sc, t, t, false, w);
+        put_p(pb + L::pP, t, t, w, qk);
+      }
     }
   };
 
@@ -2560,7 +2655,29 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
   };
 
   // ------------------------------------------------------------ prologue
-  if (nch > 0) {
+  if (nch > 0 && W) {
+    if (prepw) {
+      zero_upper(prp0);
+      zero_upper(prp1);
+      dma_raw(0, raw0);
+      if (pi == 1) {
+        load_gb(0);
+        store_sc(0, raw0);
+      }
+    }
+    barrier_vm<0>();  // raw chunk 0 has landed
+    if (prepw) prep_phase1(raw0, prp0);
+    if (chain) prep1_pdiag(raw0, prp0, wave);
+    barrier_vm<63>();  // chunk 0's T_bb, A~ and norms complete
+    if (prepw) {
+      if (nch > 1) {
+        dma_raw(1, raw1);
+        if (pi == 1) load_gb(1);
+      }
+      prep_phase2(raw0, prp0);
+      if (nch > 1 && pi == 1) store_sc(1, raw1);
+    }
+  } else if (nch > 0) {
     if (prepw) {
       zero_upper(prp0);
       zero_upper(prp1);
@@ -2580,6 +2697,255 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
       }
     }
   }
+  if constexpr (W) {
+    if (chain) {
+      // ------------------------------------------------ wide: chain waves
+      // Columns 32 wave .. 32 wave + 31 of the state, S^T in CT x DT
+      // accumulator tiles as in the narrow chain.  Per chunk c, before B1:
+      // X1 = K S^T with Y^T = S Q^T, R, U = Tb R and the state update; after
+      // B1, O^T = scale rq (gamma Y^T + (U diag(rk))^T P~^T), stored, chunk
+      // c+1's diagonal Q K^T tiles and any emitted state.
+      f32x4 st[CT][DT];
+      const int sslot = p.state_idx ? as_const(p.state_idx)[n] : n;
+      // element offset of the lane's tile (ct, dt) inside a head's d x d
+      // state (row = d_v column), from the lane's base offset lb.  The base
+      // passes through an empty asm where it is used, so the compiler forms
+      // the addresses there instead of holding all of them across the loop.
+      const int lb0 = (16 * CT * wave + l16) * D + 8 * g4;
+      auto toff = [&](int lb, int ct, int dt) __attribute__((always_inline)) {
+        return (uint32_t)(lb + 16 * ct * D + pidx<DT>(dt, 0));
+      };
+      auto opaque = [](int x) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(x));
+        return x;
+      };
+      // uniform bases with 32-bit lane offsets (SGPR base + VGPR offset
+      // addressing: no 64-bit address per tile)
+      const size_t sbase = ((size_t)sslot * p.h_v + h) * D * D;
+      auto sptr = [&](void* base, size_t e) __attribute__((always_inline)) {
+        return p.state_bf16 ? (void*)(reinterpret_cast<__bf16*>(base) + e) : (void*)(reinterpret_cast<float*>(base) + e);
+      };
+      const int erow = p.emit_every > 0 ? plan.erow(n) : 0;
+      const int o_stride = p.h_v * D;
+      T* og = reinterpret_cast<T*>(p.o) + (int64_t)h * D;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          st[ct][dt] = p.initial_state ? load_state4(sptr(const_cast<void*>(p.initial_state), sbase), toff(lb0, ct, dt), p.state_bf16)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      barrier_vm<63>();  // chunk 0's preparation and chunk 1's rows are visible
+      // the chunk's LDS buffers pass through an empty asm: every address in
+      // them is then formed in the step rather than held across the loop
+      auto launder = [](const unsigned char* x) __attribute__((always_inline)) {
+        auto q = (__attribute__((address_space(3))) const unsigned char*)x;
+        asm volatile("" : "+v"(q));
+        return (const unsigned char*)q;
+      };
+      auto step = [&](int c, const unsigned char* rb0, const unsigned char* pb0, const unsigned char* rn,
+                      unsigned char* pn) __attribute__((always_inline)) {
+        const unsigned char* rb = launder(rb0);
+        const unsigned char* pb = launder(pb0);
+        const unsigned char* K_t = rb + L::rK;
+        const unsigned char* Q_t = rb + L::rQ;
+        const unsigned char* V_t = rb + L::rV;
+        const unsigned char* Tb_t = pb + L::pTb;
+        const unsigned char* P_t = pb + L::pP;
+        const float* vec = reinterpret_cast<const float*>(pb + L::pVec);
+        // X1 = K S^T and Y^T = S Q^T (raw q): one bf16 fragment of S is the
+        // B operand of the first and the A operand of the second; the lane's
+        // part of |q|^2 comes from the same Q fragments
+        f32x4 x1[CT][NT], o[CT][NT];
+        float qq[NT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          qq[mt] = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) x1[ct][mt] = o[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < DKS; ++s) {
+          frag ak[NT], bq[NT];
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) {
+            ak[mt] = frag_row_s<T, SK>(K_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+            bq[mt] = frag_row_s<T, SK>(Q_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+          }
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const frag bs = M::acc(st[ct][2 * s], st[ct][2 * s + 1]);
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+              M::mma(x1[ct][mt], ak[mt], bs, false);
+              M::mma(o[ct][mt], bs, bq[mt], false);
+            }
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const uint4 w = __builtin_bit_cast(uint4, bq[nt]);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              qq[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ww[j]), __builtin_bit_cast(bf16x2, ww[j]), qq[nt], false);
+          }
+        }
+        // R = V - diag(gamma rk) X1, V[token pidx(mt, 4g) + e][column] by
+        // one transposing read per tile
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          const float4 vq = *reinterpret_cast<const float4*>(vec + pidx<NT>(mt, 4 * g4));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int r0 = pidx<NT>(mt, 4 * g4);
+            const uint2 vw = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(
+                __attribute__((address_space(3))) unsigned char*)(V_t + SV::off(r0 + (l16 >> 2),
+                                                                                (16 * (CT * wave + ct) + 4 * (l16 & 3)) * 2))));
+            x1[ct][mt][0] = bf16_lo(vw.x) - vq.x * x1[ct][mt][0];
+            x1[ct][mt][1] = bf16_hi(vw.x) - vq.y * x1[ct][mt][1];
+            x1[ct][mt][2] = bf16_lo(vw.y) - vq.z * x1[ct][mt][2];
+            x1[ct][mt][3] = bf16_hi(vw.y) - vq.w * x1[ct][mt][3];
+          }
+        }
+        // U = Tb R
+        f32x4 u[CT][NT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) u[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          frag at[NT];
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) at[mt] = frag_row_s<T, SC>(Tb_t, pidx<NT>(mt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const frag bs = M::acc(x1[ct][2 * s], x1[ct][2 * s + 1]);
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) M::mma(u[ct][mt], at[mt], bs, false);
+          }
+        }
+        // (U diag(rk))^T as A fragments of the output product and
+        // U' = diag(e rk) U as B fragments of the state update
+        frag au[KS][CT], bu[KS][CT];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const float4 r0 = *reinterpret_cast<const float4*>(vec + 4 * C + pidx<NT>(2 * s, 4 * g4));
+          const float4 r1 = *reinterpret_cast<const float4*>(vec + 4 * C + pidx<NT>(2 * s + 1, 4 * g4));
+          const float4 e0 = *reinterpret_cast<const float4*>(vec + 2 * C + pidx<NT>(2 * s, 4 * g4));
+          const float4 e1 = *reinterpret_cast<const float4*>(vec + 2 * C + pidx<NT>(2 * s + 1, 4 * g4));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 a = u[ct][2 * s], b = u[ct][2 * s + 1];
+            au[s][ct] = M::acc(f32x4{a[0] * r0.x, a[1] * r0.y, a[2] * r0.z, a[3] * r0.w},
+                               f32x4{b[0] * r1.x, b[1] * r1.y, b[2] * r1.z, b[3] * r1.w});
+            bu[s][ct] = M::acc(f32x4{a[0] * e0.x, a[1] * e0.y, a[2] * e0.z, a[3] * e0.w},
+                               f32x4{b[0] * e1.x, b[1] * e1.y, b[2] * e1.z, b[3] * e1.w});
+          }
+        }
+        // S^T <- gamma_last S^T + K^T U' (the raw buffer is refilled after B1)
+        const float gl = vec[3 * C];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) st[ct][dt] *= gl;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const frag kt = frag_kt<T, L::RBK, DT>(K_t, dt, 32 * s + 8 * g4, l16, false);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], kt, bu[s][ct], false);
+          }
+        barrier_vm<63>();  // B1
+        // O^T = scale rq (gamma Y^T + (U diag(rk))^T P~^T), |q|^2 summed
+        // over the four lane rows
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float gm = vec[C + pidx<NT>(nt, l16)];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= gm;
+          float a = qq[nt], b = qq[nt];
+          swap_hi32(a, b);
+          a += b;
+          b = a;
+          swap_odd16(a, b);
+          qq[nt] = a + b;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          frag bp[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) bp[nt] = frag_row_s<T, SC>(P_t, pidx<NT>(nt, l16), 32 * s + 8 * g4, false);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) M::mma(o[ct][nt], au[s][ct], bp[nt], false);
+        }
+        const int Lc = chunk_len(c);
+        T* oc = og + chunk_t0(c) * (int64_t)o_stride;
+        const int l16s = opaque(l16);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int tok = pidx<NT>(nt, l16s);
+          const float f = p.scale * (p.l2norm ? rsqrtf(qq[nt] + 1e-6f) : 1.0f);
+          if (tok < Lc) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              *reinterpret_cast<uint2*>(oc + (uint32_t)(tok * o_stride + 16 * (CT * wave + ct) + 4 * g4)) =
+                  make_uint2(pack_bf16x2(f * o[ct][nt][0], f * o[ct][nt][1]), pack_bf16x2(f * o[ct][nt][2], f * o[ct][nt][3]));
+          }
+        }
+        // chunk c+1's diagonal Q K^T tiles
+        if (c + 1 < nch) prep1_pdiag(rn, pn, wave);
+        // the state after every emit_every-th whole chunk inside the sequence
+        // (last, when the output tiles are no longer held)
+        if (p.emit_every > 0 && (c + 1) % p.emit_every == 0 && chunk_t0(c) + C < seq_end) {
+          const size_t dst = ((size_t)(erow + (c + 1) / p.emit_every - 1) * p.h_v + h) * D * D;
+          const int lb = opaque(lb0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              store_state4(sptr(p.chunk_states, dst), toff(lb, ct, dt), st[ct][dt], p.state_bf16);
+        }
+        barrier_vm<63>();  // B2
+      };
+      for (int c = 0; c < nch; c += 2) {
+        step(c, raw0, prp0, raw1, prp1);
+        if (c + 1 < nch) step(c + 1, raw1, prp1, raw0, prp0);
+      }
+      if (p.final_state) {
+        const int lb = opaque(lb0);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            store_state4(sptr(p.final_state, sbase), toff(lb, ct, dt), st[ct][dt], p.state_bf16);
+      }
+    } else {
+      // ------------------------------------------------- wide: prep waves
+      // rb: chunk c (free after B1, then filled with chunk c+2 by direct
+      // loads that land before B2); rn, pn: chunk c+1
+      barrier_vm<0>();  // chunk 1's rows have landed
+      auto step = [&](int c, unsigned char* rb, unsigned char* rn, unsigned char* pn) __attribute__((always_inline)) {
+        if (c + 1 < nch) prep_phase1(rn, pn);
+        barrier_vm<63>();  // B1
+        if (c + 2 < nch) {
+          dma_raw(c + 2, rb);
+          if (pi == 1) load_gb(c + 2);
+        }
+        touch(c + 3);
+        if (c + 1 < nch) prep_phase2(rn, pn);
+        if (c + 2 < nch && pi == 1) store_sc(c + 2, rb);
+        barrier_vm<2>();  // B2: chunk c+2 has landed; the two touches stay in flight
+      };
+      for (int c = 0; c < nch; c += 2) {
+        step(c, raw0, raw1, prp1);
+        if (c + 1 < nch) step(c + 1, raw1, raw0, prp0);
+      }
+      asm volatile("" ::"v"(tv0), "v"(tv1));
+    }
+  } else {
   if (chain) {
     // ---------------------------------------------------------- chain waves
     // S^T (d_k x this wave's 16 CT columns) in CT x DT accumulator tiles;
@@ -2850,12 +3216,14 @@ __global__ __launch_bounds__(64 * (2 * NC + 4)) void fused_kernel(PrefillParams 
       if (c + 1 < nch) step(c + 1, raw1, raw0, prp0);
     }
   }
+  }
 }
 
 #define GDN_FUSED(D, C) \
-  template __global__ void fused_kernel<D, C, 1, 1>(PrefillParams, const unsigned char*); \
-  template __global__ void fused_kernel<D, C, 2, 1>(PrefillParams, const unsigned char*); \
-  template __global__ void fused_kernel<D, C, 2, 2>(PrefillParams, const unsigned char*);
+  template __global__ void fused_kernel<D, C, 1, 1, false>(PrefillParams, const unsigned char*); \
+  template __global__ void fused_kernel<D, C, 2, 1, false>(PrefillParams, const unsigned char*); \
+  template __global__ void fused_kernel<D, C, 2, 2, false>(PrefillParams, const unsigned char*); \
+  template __global__ void fused_kernel<D, C, D / 32, 2, true>(PrefillParams, const unsigned char*);
 GDN_FUSED(64, 32) GDN_FUSED(64, 64) GDN_FUSED(128, 32) GDN_FUSED(128, 64)
 #undef GDN_FUSED
 
@@ -2918,25 +3286,24 @@ inline bool use_fused(int io_dtype, int chunk, int n_seqs, int h_v, int d) {
   return (int64_t)n_seqs * h_v * (d / 64) >= kScanCUs;
 }
 
-// Columns per fused workgroup (16, 32 or 64): the narrowest block that
-// still puts every workgroup on the chip at once (the serial chains then run
-// side by side), else the widest (the least preparation repeated per column
-// block).  GDN_FUSED_COLS forces a width (tuning).
-inline int fused_cols(const PrefillParams& p, int d) {
-  const char* e = std::getenv("GDN_FUSED_COLS");
+// Fused workgroup shape: 0 for the wide one (every d_v column of a V head,
+// so each chunk is prepared once per head), else the columns of a narrow
+// block (16, 32 or 64) with separate output waves.  The wide block does the
+// least work per chunk; GDN_FUSED_COLS=16, 32 or 64 forces a narrow width
+// (tuning and comparison).
+inline int fused_cols(const PrefillParams&, int d) {
+  const char* e = std::getenv("GDN_FUSED_COLS");  // read per call: tests switch it in-process
   const int forced = e ? std::atoi(e) : 0;
   if ((forced == 16 || forced == 32 || forced == 64) && forced <= d) return forced;
-  const int64_t units = (int64_t)p.n_seqs * p.h_v;
-  if (units * (d / 16) <= kScanCUs) return 16;
-  if (units * (d / 32) <= kScanCUs) return 32;
-  return 64;
+  return 0;
 }
 
-template <int D, int C, int NC, int CT>
+template <int D, int C, int NC, int CT, bool W>
 hipError_t launch_fused_cfg(const PrefillParams& p, const unsigned char* ws, hipStream_t stream) {
-  using FL = FusedLayout<D, C, NC, CT>;
+  using FL = FusedLayout<D, C, NC, CT, W>;
+  static_assert(FL::bytes <= kLdsMax, "fused workgroup exceeds the LDS");
   const unsigned grid = scan_grid(p.n_seqs, p.h_qk, p.h_v, D / FL::cols);
-  hipLaunchKernelGGL((fused_kernel<D, C, NC, CT>), dim3(grid), dim3(FL::threads), 0, stream, p, ws);
+  hipLaunchKernelGGL((fused_kernel<D, C, NC, CT, W>), dim3(grid), dim3(FL::threads), 0, stream, p, ws);
   return hipGetLastError();
 }
 
@@ -2950,9 +3317,10 @@ hipError_t launch_fused(const PrefillParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   switch (fused_cols(p, D)) {
-    case 16: return launch_fused_cfg<D, C, 1, 1>(p, ws, stream);
-    case 32: return launch_fused_cfg<D, C, 2, 1>(p, ws, stream);
-    default: return launch_fused_cfg<D, C, 2, 2>(p, ws, stream);
+    case 16: return launch_fused_cfg<D, C, 1, 1, false>(p, ws, stream);
+    case 32: return launch_fused_cfg<D, C, 2, 1, false>(p, ws, stream);
+    case 64: return launch_fused_cfg<D, C, 2, 2, false>(p, ws, stream);
+    default: return launch_fused_cfg<D, C, D / 32, 2, true>(p, ws, stream);
   }
 }
 

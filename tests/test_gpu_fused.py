@@ -48,11 +48,11 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("cols", [16, 32, 64])
+@pytest.mark.parametrize("cols", ["16", "32", "64", "wide"])
 @pytest.mark.parametrize("name,fn,kw", CASES, ids=[c[0] for c in CASES])
 def test_fused_kernel_width(monkeypatch, cols, name, fn, kw):
     monkeypatch.setenv("GDN_PREFILL_FUSED", "1")
-    monkeypatch.setenv("GDN_FUSED_COLS", str(cols))
+    monkeypatch.setenv("GDN_FUSED_COLS", cols)
     fn(**kw)
 
 
