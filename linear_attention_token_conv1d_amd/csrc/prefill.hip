@@ -2096,6 +2096,18 @@ __device__ __forceinline__ void subst16(float (&t)[16], const float (&nn)[16]) {
                : "v"(nn[15]), "v"(t[14]));
 }
 
+// r[e] = x of lane 4Q + e of the lane's row of 16 (DPP row_newbcast)
+template <int Q>
+__device__ __forceinline__ void row_bcast4(float (&r)[4], float x) {
+  asm volatile("s_nop 1\n\t"
+               "v_mov_b32_dpp %0, %4 row_newbcast:%c5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_mov_b32_dpp %1, %4 row_newbcast:%c6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_mov_b32_dpp %2, %4 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_mov_b32_dpp %3, %4 row_newbcast:%c8 row_mask:0xf bank_mask:0xf"
+               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+               : "v"(x), "i"(4 * Q), "i"(4 * Q + 1), "i"(4 * Q + 2), "i"(4 * Q + 3));
+}
+
 template <int D, int C, int NC, int CT, bool W>
 struct FusedLayout {
   static constexpr int NT = C / 16, DT = D / 16;
@@ -2125,6 +2137,7 @@ struct FusedLayout {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+
 
 // Off-diagonal tile pairs (row block mt > column block tj) of prep wave pw
 // (1..3), chosen so that a wave's pairs share operand tiles
@@ -2366,30 +2379,36 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
       dma_tile_s<SV, C, 4>(b + L::rV, vc, vrow, Lc, pi, lane);
     }
   };
-  // L2 prefetch for wide workgroups: two 4-byte loads per prep lane touch
-  // every 128-byte line of a chunk's K, Q and V rows and its g and beta
-  // entries, so that the direct-to-LDS copy a step later reads L2 rather
-  // than HBM.  Both loads are issued on every call (a chunk past the end
-  // touches the last chunk again) and stay in flight across B2; the next
-  // call waits for them before reusing their registers.
-  uint32_t tv0 = 0u, tv1 = 0u;
-  auto touch = [&](int c) __attribute__((always_inline)) {
-    asm volatile("" ::"v"(tv0), "v"(tv1));
+  // L2 prefetch for wide workgroups: two 4-byte loads per loader slot lt
+  // (0..255) touch every 128-byte line of a chunk's K, Q and V rows and its
+  // g and beta entries, so that the direct-to-LDS copy a step later reads L2
+  // rather than HBM.  Prep waves 1-3 issue them at the start of phase 1,
+  // while the load path is idle (wave 1 also takes wave 0's slots); both
+  // loads are issued on every call (a chunk past the end touches the last
+  // chunk again), and the next call waits for them before reusing their
+  // registers, a step later.
+  uint32_t tv0 = 0u, tv1 = 0u, tv2 = 0u, tv3 = 0u;
+  auto touch_lt = [&](int c, int lx, uint32_t& va, uint32_t& vb) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(va), "v"(vb));
     const int cc = min(c, nch - 1);
     const int64_t t0 = chunk_t0(cc);
     const int Lc = chunk_len(cc);
-    const int i = lt & 127, half = (i & 1) * 128 < D * 2 ? (i & 1) * 128 : 0;
+    const int i = lx & 127, half = (i & 1) * 128 < D * 2 ? (i & 1) * 128 : 0;
     const int64_t r = t0 + min(i >> 1, Lc - 1);
-    const unsigned char* a0 = lt < 128 ? kg + r * p.k_stride * 2 + half : qg + r * p.q_stride * 2 + half;
+    const unsigned char* a0 = lx < 128 ? kg + r * p.k_stride * 2 + half : qg + r * p.q_stride * 2 + half;
     const unsigned char* a1;
-    if (lt < 128) {
+    if (lx < 128) {
       a1 = vg + r * vrow + half;
     } else {
-      const int64_t rg = t0 + min(lt & 63, Lc - 1);
-      a1 = reinterpret_cast<const unsigned char*>((lt < 192 ? p.g : p.beta) + rg * p.h_v + h);
+      const int64_t rg = t0 + min(lx & 63, Lc - 1);
+      a1 = reinterpret_cast<const unsigned char*>((lx < 192 ? p.g : p.beta) + rg * p.h_v + h);
     }
-    tv0 = *reinterpret_cast<const uint32_t*>(a0);
-    tv1 = *reinterpret_cast<const uint32_t*>(a1);
+    va = *reinterpret_cast<const uint32_t*>(a0);
+    vb = *reinterpret_cast<const uint32_t*>(a1);
+  };
+  auto touch = [&](int c) __attribute__((always_inline)) {  // prep waves 1-3
+    touch_lt(c, lt, tv0, tv1);
+    if (pi == 1) touch_lt(c, lane, tv2, tv3);
   };
   auto load_gb = [&](int c) __attribute__((always_inline)) {  // prep wave 1
     const int64_t r = chunk_t0(c) + min(lane, chunk_len(c) - 1);
@@ -2421,12 +2440,15 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
   auto diag_solve = [&](unsigned char* b, unsigned char* pb) __attribute__((always_inline)) {
     const unsigned char* K_s = b + L::rK;
     float* sc = reinterpret_cast<float*>(b + L::rSc);
+    // after the transpose below, lane (bb, k) holds column k of block cb
+    const int bb = g4, k = l16, cb = bb & (NT - 1);
+    const int j = 16 * cb + k;
     f32x4 col[4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) col[t] = gram(K_s, K_s, t, t);
 #pragma unroll
     for (int t = NT; t < 4; ++t) col[t] = col[t - NT];  // two blocks: lane rows 2, 3 repeat blocks 0, 1
-    {
+    {  // the row norms, for the scalings of the later steps
       const int i = l16 & 3;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -2443,25 +2465,37 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
       swap_odd16(a2, a3);
       col[0][i] = a0; col[1][i] = a1; col[2][i] = a2; col[3][i] = a3;
     }
-    // col[q][e] = k_{16 cb + 4q + e} . k_{16 cb + k}: column k of block cb
-    fence();  // the norms are written
-    const int bb = g4, k = l16, cb = bb & (NT - 1);
-    const int j = 16 * cb + k;
-    const float rkj = sc[2 * C + j], G2j = sc[C + j], bj = sc[j];
-    float nn[16];
+    // col[q][e] = k_{16 cb + 4q + e} . k_{16 cb + k}: column k of block cb.
+    // Its diagonal entry gives rk_j, and the rows' rk_i come from lanes
+    // (bb, i) of the same row of 16 by broadcasts (no LDS round trip for
+    // the norms this wave has just formed).
+    const float G2j = sc[C + j], bj = sc[j];
+    float dj = col[0][0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e == k) dj = col[q][e];
+    const float rkj = p.l2norm ? rsqrtf(dj + 1e-6f) : 1.0f;
+    float nn[16];
+    auto rows = [&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
       const float4 be = *reinterpret_cast<const float4*>(sc + 16 * cb + 4 * q);
       const float4 gg = *reinterpret_cast<const float4*>(sc + C + 16 * cb + 4 * q);
-      const float4 rr = *reinterpret_cast<const float4*>(sc + 2 * C + 16 * cb + 4 * q);
-      const float bq[4] = {be.x, be.y, be.z, be.w}, gq[4] = {gg.x, gg.y, gg.z, gg.w}, rq[4] = {rr.x, rr.y, rr.z, rr.w};
+      float rk[4];
+      row_bcast4<q>(rk, rkj);
+      const float bq[4] = {be.x, be.y, be.z, be.w}, gq[4] = {gg.x, gg.y, gg.z, gg.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * q + e;  // row 16 cb + i; e^{G_i - G_j} <= 1 where kept (i > k)
-        const float a = bq[e] * rq[e] * rkj * __builtin_amdgcn_exp2f(gq[e] - G2j) * col[q][e];
+        const float a = bq[e] * rk[e] * rkj * __builtin_amdgcn_exp2f(gq[e] - G2j) * col[q][e];
         nn[i] = (p.erase && i > k) ? -a : 0.f;
       }
-    }
+    };
+    rows(std::integral_constant<int, 0>{});
+    rows(std::integral_constant<int, 1>{});
+    rows(std::integral_constant<int, 2>{});
+    rows(std::integral_constant<int, 3>{});
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = i == k ? 1.f : 0.f;
@@ -2676,6 +2710,7 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
       }
       prep_phase2(raw0, prp0);
       if (nch > 1 && pi == 1) store_sc(1, raw1);
+      if (nch > 2 && pi == 1) load_gb(2);
     }
   } else if (nch > 0) {
     if (prepw) {
@@ -2925,25 +2960,29 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
     } else {
       // ------------------------------------------------- wide: prep waves
       // rb: chunk c (free after B1, then filled with chunk c+2 by direct
-      // loads that land before B2); rn, pn: chunk c+1
+      // loads that land before B2); rn, pn: chunk c+1.  Prep wave 1 loads g
+      // and beta a step ahead of their use (chunk c+3 in step c), so their
+      // latency is spent across a barrier.
       barrier_vm<0>();  // chunk 1's rows have landed
       auto step = [&](int c, unsigned char* rb, unsigned char* rn, unsigned char* pn) __attribute__((always_inline)) {
+        if (pi != 0) touch(c + 3);
         if (c + 1 < nch) prep_phase1(rn, pn);
         barrier_vm<63>();  // B1
-        if (c + 2 < nch) {
-          dma_raw(c + 2, rb);
-          if (pi == 1) load_gb(c + 2);
-        }
-        touch(c + 3);
+        if (c + 2 < nch) dma_raw(c + 2, rb);
         if (c + 1 < nch) prep_phase2(rn, pn);
-        if (c + 2 < nch && pi == 1) store_sc(c + 2, rb);
-        barrier_vm<2>();  // B2: chunk c+2 has landed; the two touches stay in flight
+        if (pi == 1) {
+          if (c + 2 < nch) store_sc(c + 2, rb);
+          if (c + 3 < nch) load_gb(c + 3);
+          barrier_vm<2>();  // B2: chunk c+2 has landed; g and beta stay in flight
+        } else {
+          barrier_vm<0>();  // B2: chunk c+2 has landed
+        }
       };
       for (int c = 0; c < nch; c += 2) {
         step(c, raw0, raw1, prp1);
         if (c + 1 < nch) step(c + 1, raw1, raw0, prp0);
       }
-      asm volatile("" ::"v"(tv0), "v"(tv1));
+      asm volatile("" ::"v"(tv0), "v"(tv1), "v"(tv2), "v"(tv3));
     }
   } else {
   if (chain) {
