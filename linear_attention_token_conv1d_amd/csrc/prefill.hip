@@ -2186,11 +2186,6 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
   const int nch = plan.off(n + 1) - plan.off(n);
   auto chunk_t0 = [&](int c) __attribute__((always_inline)) { return seq_start + (int64_t)c * C; };
   auto chunk_len = [&](int c) __attribute__((always_inline)) { return (int)min((int64_t)C, seq_end - chunk_t0(c)); };
-  auto fence = [&]() __attribute__((always_inline)) {  // this wave's LDS writes are done
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    wait_vm_lgkm0<63>();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
 
   // roles: waves w and w + 4 share a SIMD.  Chain waves come first (one per
   // SIMD), then the output waves, then the four prep waves, numbered so
@@ -2381,7 +2376,7 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
   };
   // L2 prefetch for wide workgroups: two 4-byte loads per loader slot lt
   // (0..255) touch every 128-byte line of a chunk's K, Q and V rows and its
-  // g and beta entries, so that the direct-to-LDS copy a step later reads L2
+  // g and beta entries, so that the direct-to-LDS copy after B1 reads L2
   // rather than HBM.  Prep waves 1-3 issue them at the start of phase 1,
   // while the load path is idle (wave 1 also takes wave 0's slots); both
   // loads are issued on every call (a chunk past the end touches the last
@@ -2469,7 +2464,7 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
     // Its diagonal entry gives rk_j, and the rows' rk_i come from lanes
     // (bb, i) of the same row of 16 by broadcasts (no LDS round trip for
     // the norms this wave has just formed).
-    const float G2j = sc[C + j], bj = sc[j];
+    const float G2j = sc[C + j];
     float dj = col[0][0];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -2500,14 +2495,10 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = i == k ? 1.f : 0.f;
     subst16(t, nn);
-    if (bb < NT) {
+    if (bb < NT) {  // Tb's diagonal blocks follow in phase 2
       float* out = sA + 16 * bb * LDF + j;
-      unsigned char* tb = pb + L::pTb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        out[i * LDF] = t[i];
-        *reinterpret_cast<__bf16*>(tb + SC::off(16 * bb + i, j * 2)) = (__bf16)(t[i] * bj);
-      }
+      for (int i = 0; i < 16; ++i) out[i * LDF] = t[i];
     }
   };
   // prep waves 1-3: their tiles below the diagonal blocks, K K^T and Q K^T
@@ -2674,6 +2665,25 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
         put_tb(2, 1, t2);
         put_tb(3, 1, t3);
       }
+    }
+    // prep wave 0: Tb's diagonal blocks, T_bb diag(beta) from the fp32
+    // blocks the diagonal solve left in sA (lane 16 bi + r: row r of block
+    // bi, two 16-byte stores)
+    if (pi == 0 && lane < C) {
+      const int bi = lane >> 4, r = lane;
+      const float* a = sA + r * LDF + 16 * bi;
+      const float* bc = sc + 16 * bi;
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t4 = *reinterpret_cast<const float4*>(a + 4 * q);
+        const float4 b4 = *reinterpret_cast<const float4*>(bc + 4 * q);
+        w[2 * q] = pack_bf16x2(t4.x * b4.x, t4.y * b4.y);
+        w[2 * q + 1] = pack_bf16x2(t4.z * b4.z, t4.w * b4.w);
+      }
+      unsigned char* tb = pb + L::pTb;
+      *reinterpret_cast<uint4*>(tb + SC::off(r, 32 * bi)) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(tb + SC::off(r, 32 * bi + 16)) = make_uint4(w[4], w[5], w[6], w[7]);
     }
     // row scalars: gamma rk (0 without the erase: R = V), gamma, e rk,
     // gamma_last (G of padding rows equals the last row's), rk
@@ -2965,7 +2975,7 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
       // latency is spent across a barrier.
       barrier_vm<0>();  // chunk 1's rows have landed
       auto step = [&](int c, unsigned char* rb, unsigned char* rn, unsigned char* pn) __attribute__((always_inline)) {
-        if (pi != 0) touch(c + 3);
+        if (pi != 0) touch(c + 2);
         if (c + 1 < nch) prep_phase1(rn, pn);
         barrier_vm<63>();  // B1
         if (c + 2 < nch) dma_raw(c + 2, rb);
