@@ -2124,8 +2124,9 @@ struct FusedLayout {
   static constexpr int rK = 0, rQ = C * RBK, rV = 2 * C * RBK, rSc = rV + C * RBV;
   static constexpr int raw = rSc + 12 * C;
   // prep buffer: Tb, P~ [C][C] (swizzled), then per-token fp32 rows:
-  // gamma rk (0 without the erase), gamma, e rk, gamma_last, rk
-  static constexpr int NVEC = 5;
+  // gamma rk (0 without the erase), gamma, e rk, gamma_last, rk, and (wide
+  // workgroups) scale rq
+  static constexpr int NVEC = 6;
   static constexpr int pTb = 0, pP = C * RBC, pVec = 2 * C * RBC;
   static constexpr int prep = pVec + 4 * NVEC * C;
   static constexpr int LDF = C + 4;  // fp32 A / T rows
@@ -2523,9 +2524,32 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
     }
   };
   auto prep_phase1 = [&](unsigned char* b, unsigned char* pb) __attribute__((always_inline)) {
-    if (pi == 0) diag_solve(b, pb);
+    if (pi == 0) {
+      __builtin_amdgcn_s_setprio(3);
+      diag_solve(b, pb);
+      __builtin_amdgcn_s_setprio(0);
+    }
     else if (pi == 1) pairs(b, pb, std::integral_constant<int, 1>{});
-    else if (pi == 2) pairs(b, pb, std::integral_constant<int, 2>{});
+    else if (pi == 2) {
+      pairs(b, pb, std::integral_constant<int, 2>{});
+      if constexpr (W) {
+        // scale rq of each row for the outputs (once, rather than in every
+        // chain wave): lane r sums |q_r|^2 over its raw row
+        if (lane < C) {
+          const unsigned char* Q_s = b + L::rQ;
+          float qq = 0.f;
+#pragma unroll
+          for (int j = 0; j < D / 8; ++j) {
+            const uint4 w = *reinterpret_cast<const uint4*>(Q_s + SK::off(lane, j * 16));
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              qq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ww[e]), __builtin_bit_cast(bf16x2, ww[e]), qq, false);
+          }
+          reinterpret_cast<float*>(pb + L::pVec)[5 * C + lane] = p.scale * (p.l2norm ? rsqrtf(qq + 1e-6f) : 1.0f);
+        }
+      }
+    }
     else pairs(b, pb, std::integral_constant<int, 3>{});
   };
   // output waves (chain waves of a wide workgroup): the diagonal tiles of
@@ -2798,16 +2822,12 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
         const unsigned char* P_t = pb + L::pP;
         const float* vec = reinterpret_cast<const float*>(pb + L::pVec);
         // X1 = K S^T and Y^T = S Q^T (raw q): one bf16 fragment of S is the
-        // B operand of the first and the A operand of the second; the lane's
-        // part of |q|^2 comes from the same Q fragments
+        // B operand of the first and the A operand of the second
         f32x4 x1[CT][NT], o[CT][NT];
-        float qq[NT];
 #pragma unroll
-        for (int mt = 0; mt < NT; ++mt) {
-          qq[mt] = 0.f;
+        for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) x1[ct][mt] = o[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
 #pragma unroll
         for (int s = 0; s < DKS; ++s) {
           frag ak[NT], bq[NT];
@@ -2824,14 +2844,6 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
               M::mma(x1[ct][mt], ak[mt], bs, false);
               M::mma(o[ct][mt], bs, bq[mt], false);
             }
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const uint4 w = __builtin_bit_cast(uint4, bq[nt]);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              qq[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ww[j]), __builtin_bit_cast(bf16x2, ww[j]), qq[nt], false);
           }
         }
         // R = V - diag(gamma rk) X1, V[token pidx(mt, 4g) + e][column] by
@@ -2902,19 +2914,12 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
             for (int ct = 0; ct < CT; ++ct) M::mma(st[ct][dt], kt, bu[s][ct], false);
           }
         barrier_vm<63>();  // B1
-        // O^T = scale rq (gamma Y^T + (U diag(rk))^T P~^T), |q|^2 summed
-        // over the four lane rows
+        // O^T = scale rq (gamma Y^T + (U diag(rk))^T P~^T)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const float gm = vec[C + pidx<NT>(nt, l16)];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) o[ct][nt] *= gm;
-          float a = qq[nt], b = qq[nt];
-          swap_hi32(a, b);
-          a += b;
-          b = a;
-          swap_odd16(a, b);
-          qq[nt] = a + b;
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -2932,7 +2937,7 @@ __global__ __launch_bounds__(64 * (W ? NC + 4 : 2 * NC + 4)) void fused_kernel(P
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int tok = pidx<NT>(nt, l16s);
-          const float f = p.scale * (p.l2norm ? rsqrtf(qq[nt] + 1e-6f) : 1.0f);
+          const float f = vec[5 * C + tok];
           if (tok < Lc) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
