@@ -606,8 +606,13 @@ struct PrepLayout {
   static constexpr int oA = 0;
   static constexpr int team_bytes = oA + C * LDF * 4;
   static constexpr int work_bytes = VPW * team_bytes;
+  // with several teams (one K, Q pass), the raw Gram tiles (fp32, 1 KiB
+  // each) formed once for all teams and read by each team's masks
+  static constexpr int NLT = NT * (NT + 1) / 2;
+  static constexpr bool share = VPW > 1 && NH == 1;
+  static constexpr int oStage = kq_bytes > work_bytes ? kq_bytes : work_bytes;
   // row scalars: rk, rq (shared), then g, beta, G per team
-  static constexpr int oVec = kq_bytes > work_bytes ? kq_bytes : work_bytes;
+  static constexpr int oVec = oStage + (share ? 2 * NLT * 1024 : 0);
   static constexpr int bytes = oVec + (2 + 3 * VPW) * C * 4;
   // with split tiles, the waves per SIMD that LDS allows (at most 6) set the
   // register budget; otherwise the compiler's own choice stands
@@ -635,7 +640,10 @@ __attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) voi
   using SK = Swz<L::RBH>;
   constexpr int NT = L::NT;
   constexpr int NLT = NT * (NT + 1) / 2;       // lower-triangular 16x16 tiles
-  constexpr int NJ = (2 * NLT + 3) / 4;        // Gram tiles per wave
+  constexpr int NJ = (2 * NLT + 3) / 4;        // masked tiles per team wave
+  // Gram tiles: shared by all the workgroup's waves when teams share them
+  constexpr int GW = L::share ? 4 * VPW : 4;
+  constexpr int NJG = (2 * NLT + GW - 1) / GW;
   constexpr int RT = D / 8;                    // threads per row in the load layout
   constexpr int NTH = kPrepThreads * VPW;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -763,31 +771,41 @@ __attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) voi
   }
   // transposed Gram tiles below the diagonal: job (mt, tj), tj <= mt, holds
   // rows j = 16 tj + 4g + i, column r = 16 mt + l16 of K K^T (jobs
-  // [0, NLT)) or of K Q^T (jobs [NLT, 2 NLT))
-  f32x4 gram[NJ];
-  int jmt[NJ], jnt[NJ];
+  // [0, NLT)) or of K Q^T (jobs [NLT, 2 NLT)).  jmt/jnt: a team wave's
+  // masked jobs (wave + 4 jj); gmt/gnt: its Gram jobs (gwave + GW jj), the
+  // same ones unless the teams share the tiles.
+  auto job_tile = [](int job, int& mt, int& tj) {
+    tj = job >= NLT ? job - NLT : job;
+    mt = 0;
+    while (tj > mt) { tj -= mt + 1; ++mt; }
+  };
+  const int gwave = L::share ? tid >> 6 : wave;
+  f32x4 gram[NJG];
+  int jmt[NJ], jnt[NJ], gmt[NJG], gnt[NJG];
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) {
     const int job = wave + 4 * jj;
-    gram[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     jmt[jj] = jnt[jj] = 0;
-    if (job < 2 * NLT) {
-      int tj = job >= NLT ? job - NLT : job, mt = 0;
-      while (tj > mt) { tj -= mt + 1; ++mt; }
-      jmt[jj] = mt; jnt[jj] = tj;
-    }
+    if (job < 2 * NLT) job_tile(job, jmt[jj], jnt[jj]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJG; ++jj) {
+    const int job = gwave + GW * jj;
+    gram[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gmt[jj] = gnt[jj] = 0;
+    if (job < 2 * NLT) job_tile(job, gmt[jj], gnt[jj]);
   }
   // the k-steps over the staged part of d_k
   auto gram_pass = [&]() {
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int job = wave + 4 * jj;
+    for (int jj = 0; jj < NJG; ++jj) {
+      const int job = gwave + GW * jj;
       if (job < 2 * NLT) {
         const unsigned char* Bt = job >= NLT ? Q_s : K_s;
 #pragma unroll
         for (int s = 0; s < L::DH / 32; ++s)
-          M::mma(gram[jj], frag_row<T, L::RBH>(K_s, jnt[jj] * 16 + l16, 32 * s + 8 * g4, false),
-                 frag_row<T, L::RBH>(Bt, jmt[jj] * 16 + l16, 32 * s + 8 * g4, false), false);
+          M::mma(gram[jj], frag_row<T, L::RBH>(K_s, gnt[jj] * 16 + l16, 32 * s + 8 * g4, false),
+                 frag_row<T, L::RBH>(Bt, gmt[jj] * 16 + l16, 32 * s + 8 * g4, false), false);
       }
     }
   };
@@ -798,7 +816,14 @@ __attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) voi
     __syncthreads();
     gram_pass();
   }
-  __syncthreads();  // norms and G published; K, Q are dead from here on
+  if constexpr (L::share) {  // the raw tiles, for every team's masks
+#pragma unroll
+    for (int jj = 0; jj < NJG; ++jj) {
+      const int job = gwave + GW * jj;
+      if (job < 2 * NLT) *reinterpret_cast<f32x4*>(smem + L::oStage + job * 1024 + lane * 16) = gram[jj];
+    }
+  }
+  __syncthreads();  // norms, G and the tiles published; K, Q are dead from here on
 
   unsigned char* rec = ws + off_bytes(p.n_seqs) + ((size_t)ci * p.h_v + h) * Rec<T, C>::bytes;
   T* Tb_g = reinterpret_cast<T*>(rec);
@@ -826,12 +851,15 @@ __attribute__((amdgpu_waves_per_eu(PrepLayout<T, D, C, VPW>::waves_per_eu))) voi
       const float4 Gj = *reinterpret_cast<const float4*>(G_s + j0);
       const float4 kj = *reinterpret_cast<const float4*>(rk_s + j0);
       const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w}, rkj[4] = {kj.x, kj.y, kj.z, kj.w};
+      f32x4 gt;
+      if constexpr (L::share) gt = *reinterpret_cast<const f32x4*>(smem + L::oStage + job * 1024 + lane * 16);
+      else gt = gram[jj];
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + i;
         const bool keep = isP ? j <= r : j < r;
-        v[i] = keep ? fr * fexp(Gr - gj[i]) * rkj[i] * gram[jj][i] : 0.f;
+        v[i] = keep ? fr * fexp(Gr - gj[i]) * rkj[i] * gt[i] : 0.f;
       }
       if (isP) {
         if constexpr (sizeof(T) == 2)
