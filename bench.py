@@ -80,7 +80,8 @@ def measured_traffic(summary, source):
     """HBM bytes per launch from a committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy of known
     size reads on the same counter).  None when the summary is missing or was
-    taken on a different version of the kernel source."""
+    taken on a different version of the kernel source (or of any other source
+    whose hash it records)."""
     import hashlib
     path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
@@ -90,9 +91,13 @@ def measured_traffic(summary, source):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip().lstrip("- ")] = v.strip().strip("`")
-    digest = hashlib.sha256(open(os.path.join(CSRC, source), "rb").read()).hexdigest()
-    if fields.get(f"sha256 {source}") != digest or "traffic_bytes_per_launch" not in fields:
+    shas = {k[len("sha256 "):]: v for k, v in fields.items() if k.startswith("sha256 ")}
+    if source not in shas or "traffic_bytes_per_launch" not in fields:
         return None
+    for name, want in shas.items():
+        f = os.path.join(CSRC, name)
+        if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != want:
+            return None
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
