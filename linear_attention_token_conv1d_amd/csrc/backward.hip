@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
+#include <vector>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -1799,14 +1800,71 @@ hipError_t prefill_backward_windows(const PrefillBwdParams& p, int D, const BwdW
   return hipSuccess;
 }
 
+// ------------------------------------------------------- packs, serially
+// A pack whose whole-call workspace would pass the budget runs its sequences
+// one after another, each as one sequence (in windows when it is long), in
+// one workspace sized for the worst case: every token in one sequence, and at
+// least the budget (a shorter sequence may run whole within it).  The
+// sequence offsets are read back first, which synchronises the stream once,
+// so such a call is refused under stream capture.
+bool pack_serial(int64_t T, int n_seqs, int h_qk, int h_v, int D, int C) {
+  return n_seqs > 1 && bwd_sizes(T, n_seqs, h_qk, h_v, D, C).total > bwd_budget();
+}
+size_t pack_serial_bytes(int io_dtype, int64_t T, int h_qk, int h_v, int D, int C) {
+  return a256(std::max(bwd_budget(), bwd_windows(io_dtype, T, 1, h_qk, h_v, D, C).total));
+}
+
 }  // namespace
 
 size_t prefill_backward_workspace_bytes(int io_dtype, int64_t total_tokens, int n_seqs, int h_qk, int h_v, int d,
                                         int chunk) {
+  if (pack_serial(total_tokens, n_seqs, h_qk, h_v, d, chunk))
+    return pack_serial_bytes(io_dtype, total_tokens, h_qk, h_v, d, chunk);
   return bwd_windows(io_dtype, total_tokens, n_seqs, h_qk, h_v, d, chunk).total;
 }
 
+template <typename T>
+hipError_t prefill_backward_pack(const PrefillBwdParams& p, int io_dtype, int D, hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return e;
+  if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  std::vector<int32_t> cu((size_t)p.n_seqs + 1);
+  e = hipMemcpyAsync(cu.data(), p.cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  const size_t hs = (size_t)p.h_v * D * D;
+  for (int n = 0; n < p.n_seqs; ++n) {
+    const int64_t t0 = cu[n], len = (int64_t)cu[n + 1] - cu[n];
+    if (t0 < 0 || len < 0 || t0 + len > p.total_tokens) return hipErrorInvalidValue;
+    PrefillBwdParams b = p;
+    b.q = static_cast<const T*>(p.q) + t0 * p.q_stride;
+    b.k = static_cast<const T*>(p.k) + t0 * p.k_stride;
+    b.v = static_cast<const T*>(p.v) + t0 * p.v_stride;
+    b.g = p.g + t0 * p.h_v;
+    b.beta = p.beta + t0 * p.h_v;
+    b.d_o = static_cast<const T*>(p.d_o) + t0 * p.h_v * D;
+    b.dq = static_cast<T*>(p.dq) + t0 * p.dq_stride;
+    b.dk = static_cast<T*>(p.dk) + t0 * p.dk_stride;
+    b.dv = static_cast<T*>(p.dv) + t0 * p.dv_stride;
+    b.dg = p.dg + t0 * p.h_v;
+    b.dbeta = p.dbeta + t0 * p.h_v;
+    b.initial_state = p.initial_state ? p.initial_state + n * hs : nullptr;
+    b.d_final_state = p.d_final_state ? p.d_final_state + n * hs : nullptr;
+    b.d_initial_state = p.d_initial_state ? p.d_initial_state + n * hs : nullptr;
+    b.cu_seqlens = nullptr;
+    b.n_seqs = 1;
+    b.total_tokens = len;
+    e = launch_prefill_backward(b, io_dtype, D, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_prefill_backward(const PrefillBwdParams& p, int io_dtype, int d, hipStream_t stream) {
+  if (pack_serial(p.total_tokens, p.n_seqs, p.h_qk, p.h_v, d, p.chunk))
+    return io_dtype == 1 ? prefill_backward_pack<__bf16>(p, io_dtype, d, stream)
+                         : prefill_backward_pack<float>(p, io_dtype, d, stream);
   const BwdWindows bw = bwd_windows(io_dtype, p.total_tokens, p.n_seqs, p.h_qk, p.h_v, d, p.chunk);
   if (bw.on)
     return io_dtype == 1 ? prefill_backward_windows<__bf16>(p, d, bw, stream)

@@ -101,6 +101,24 @@ def test_prefill_backward_in_windows(monkeypatch, io, d, chunk, T, h_qk, h_v, mb
     _run_and_compare([T], h_qk, h_v, d, io, chunk, s0=opt, dsf=opt, seed=90)
 
 
+@pytest.mark.parametrize("io,d,chunk,lens,h_qk,h_v,mb,opt", [
+    ("bf16", 128, 64, [520, 0, 333, 127], 2, 4, 13, True),   # the longest sequence also in windows
+    ("f32", 64, 32, [300, 250, 150], 1, 3, 8, False),        # grouped heads, no initial state or final-state gradient
+])
+def test_prefill_backward_pack_one_sequence_at_a_time(monkeypatch, io, d, chunk, lens, h_qk, h_v, mb, opt):
+    """A pack whose whole-call workspace passes the budget runs its sequences
+    one after another (each in windows when long) in a workspace sized for one
+    sequence of every token; the results meet the same bar against the
+    oracle."""
+    T = sum(lens)
+    q = torch.empty((T, h_qk, d), dtype=DT[io])
+    v = torch.empty((T, h_v, d), dtype=DT[io])
+    full = gdn.prefill_backward_workspace_size(q, v, len(lens), chunk)
+    monkeypatch.setenv("GDN_BWD_BUDGET_MB", str(mb))
+    assert gdn.prefill_backward_workspace_size(q, v, len(lens), chunk) < full
+    _run_and_compare(lens, h_qk, h_v, d, io, chunk, s0=opt, dsf=opt, seed=95)
+
+
 def test_prefill_backward_without_l2_norm_and_scale():
     """Raw (unnormalised) small keys keep the recurrence bounded without the norm."""
     lens, h, d = [90], 2, 64
