@@ -345,12 +345,12 @@ gdn_status gdn_decode_step(const gdn_decode_args* args, void* stream);
  *   workspace    at least gdn_prefill_backward_workspace_size() bytes,
  *                256-byte aligned; contents on entry are ignored.  It holds
  *                every chunk's intermediates, except when that would pass
- *                2 GiB.  Then one sequence (n_seqs = 1) runs in windows of
+ *                4 GiB.  Then one sequence (n_seqs = 1) runs in windows of
  *                whole chunks (a forward pass for the window-start states,
  *                then each window's backward, last to first), and the
  *                workspace holds one window plus the window-start states;
  *                a pack (n_seqs > 1) runs its sequences one after another,
- *                each as one sequence, in a workspace of 2 GiB or of one
+ *                each as one sequence, in a workspace of 4 GiB or of one
  *                sequence holding every token, whichever is larger.  Such a
  *                pack call first copies cu_seqlens to the host, which
  *                synchronises the stream once; under stream capture it

@@ -1711,7 +1711,7 @@ hipError_t conv_backward_impl(const ConvBwdParams& p, hipStream_t stream) {
 // Every token's gradients come from one window, so nothing is accumulated.
 // The workspace then holds one window's backward, the forward's workspace
 // and o for one window, the window-start states and two state gradients.
-constexpr size_t kBwdBudgetDefault = (size_t)2 << 30;
+constexpr size_t kBwdBudgetDefault = (size_t)4 << 30;
 
 size_t bwd_budget() {
   const char* e = std::getenv("GDN_BWD_BUDGET_MB");  // tuning and tests: a smaller budget

@@ -281,7 +281,7 @@ def test_prefill_backward_9b_size_sampled_heads():
 def test_prefill_backward_27b_size_sampled_group():
     """The 27B-shaped layer at full length (T = 65,536, 16 QK / 48 V heads,
     1,024 chunks, a non-zero initial state; the backward runs in windows under
-    the default 2 GiB workspace budget) through conv + split,
+    the default 4 GiB workspace budget) through conv + split,
     then prefill_backward with a final-state gradient; the oracle checks QK
     head groups 0 and 15 (V heads 0-2 and 45-47: the first and the last group,
     which the workgroup placement puts on different XCDs), whose gradients
