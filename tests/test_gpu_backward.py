@@ -119,6 +119,35 @@ def test_prefill_backward_pack_one_sequence_at_a_time(monkeypatch, io, d, chunk,
     _run_and_compare(lens, h_qk, h_v, d, io, chunk, s0=opt, dsf=opt, seed=95)
 
 
+def test_prefill_backward_pack_one_at_a_time_refused_under_stream_capture(monkeypatch):
+    """The one-sequence-at-a-time pack reads the sequence offsets back, so
+    under stream capture it returns an error before any launch (nothing is
+    recorded); the same call then runs eagerly and meets the oracle bar."""
+    monkeypatch.setenv("GDN_BWD_BUDGET_MB", "8")
+    lens, h_qk, h_v, d, chunk = [300, 250, 150], 1, 3, 64, 32
+    q, k, v, g, beta, S0, do, dSf, cu = _case(lens, h_qk, h_v, d, "f32", 96)
+    qd, kd, vd, gd, bd, S0d, dod, dSfd, cud = (dev(t) for t in (q, k, v, g, beta, S0, do, dSf, cu))
+    outs = dict(dq=torch.empty_like(qd), dk=torch.empty_like(kd), dv=torch.empty_like(vd), dg=torch.empty_like(gd),
+                dbeta=torch.empty_like(bd), d_initial_state=torch.empty_like(S0d))
+    ws = torch.empty(gdn.prefill_backward_workspace_size(qd, vd, len(lens), chunk), dtype=torch.uint8,
+                     device=qd.device)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    refused = False
+    with torch.cuda.graph(graph):
+        try:
+            gdn.prefill_backward(qd, kd, vd, gd, bd, dod, S0d, dSfd, cud, chunk, workspace=ws, **outs)
+        except gdn.GdnError:
+            refused = True
+    assert refused
+    got = gdn.prefill_backward(qd, kd, vd, gd, bd, dod, S0d, dSfd, cud, chunk, workspace=ws, **outs)
+    torch.cuda.synchronize()
+    ref = orc.gated_delta_rule_backward(np64(q), np64(k), np64(v), np64(g), np64(beta), np64(do), np64(S0),
+                                        np64(dSf), cu.numpy(), 1.0)
+    for n, a, b in zip(NAMES, got, ref):
+        assert rel_err(a, b) < TOL_F32, n
+
+
 def test_prefill_backward_without_l2_norm_and_scale():
     """Raw (unnormalised) small keys keep the recurrence bounded without the norm."""
     lens, h, d = [90], 2, 64
